@@ -1,0 +1,258 @@
+"""fp64 CPU oracle for the fused, chunked KL distillation loss.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or link
+this module: only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` use it.  It shares no code with the HIP library.
+
+It is the plain, slow, obviously correct definition of what the fused kernels
+compute.  Sources, cited by page title and section:
+
+[EKD]    "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and a
+         Fused Chunked KL Loss" (paperlayer.ai summary of arXiv 2608.03796).
+         §1 and §3 "Online distillation": the objective is the forward KL
+         KL(p_teacher || q_student).  §3 "Offline distillation": only the K
+         cached teacher entries are kept; the teacher-entropy, cross and mass
+         terms use support entries only and the student log-normaliser log Z is
+         the one full-vocabulary reduction.  §3 "Offline implementations": the
+         dense reconstruction (scatter the top-K into a dense teacher) is the
+         correctness baseline; the sparse variant writes a scalar log Z per row
+         and scatter-adds over the K retained entries.  §3 "Fused chunked KL":
+         the output projection Z = H.W is part of the loss.
+[KDFlow] KDFlow abstract (thelatestinai.com/papers/2606.20005): full-vocabulary
+         distillation recomputes the teacher logits from the teacher's final
+         hidden states through a frozen copy of the teacher's output head.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of this repository):
+  * Teacher top-K logits are renormalised over the K entries at temperature tau
+    (mass m = 1); the pages' partial-mass form is not this oracle's default.
+  * Both teacher and student logits are divided by tau; there is no tau^2.
+  * The output is per token; the caller reduces.  ``g`` is dLoss/dKL_t.
+  * mask[t] == 1 marks a valid row.  Masked rows give KL = 0, lse = 0,
+    z_topk = 0, dH = 0 and contribute nothing to dW, whatever their contents.
+  * Duplicate indices in a row add (scatter-add).
+  * W is [d, V] row-major; Z = H @ W.
+
+Parity of every function here is pinned by ``tests/test_oracle.py`` against
+closed forms, library routines, finite differences and brute force.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "as_f64", "logsumexp_rows", "teacher_log_probs",
+    "topk_kl_forward", "topk_kl_backward", "topk_kl_rows",
+    "full_kl_forward", "full_kl_backward", "full_kl_rows",
+]
+
+
+def as_f64(x):
+    """Exact float64 copy of a NumPy array or a torch tensor (bf16 included)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: bf16 has no NumPy dtype
+        import torch
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _take_rows(x, rows):
+    """x[rows] for a NumPy array or a torch tensor (no arithmetic)."""
+    if x is None:
+        return None
+    if hasattr(x, "index_select"):
+        import torch
+        return x.index_select(0, torch.as_tensor(rows, dtype=torch.long))
+    return np.asarray(x)[rows]
+
+
+def _valid_rows(mask, T):
+    if mask is None:
+        return np.ones(T, dtype=bool)
+    m = np.asarray(mask.cpu().numpy() if hasattr(mask, "cpu") else mask)
+    return m.astype(np.int64) != 0
+
+
+def logsumexp_rows(x):
+    """log sum_j exp(x[i, j]) per row, max-shifted.  ([EKD] §3: the scalar log Z
+    of each row, computed with a stable vocabulary reduction.)"""
+    x = np.asarray(x, dtype=np.float64)
+    m = x.max(axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    return (m + np.log(np.exp(x - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
+def teacher_log_probs(A, tau):
+    """Teacher log-probabilities over its K cached entries: log softmax(A / tau)
+    per row (top-K renormalised at temperature tau)."""
+    a = np.asarray(A, dtype=np.float64) / tau
+    return a - logsumexp_rows(a)[:, None]
+
+
+def _student_block(Hb, W, tau):
+    """Scaled logits s = (Hb @ W) / tau and their row log-normaliser L."""
+    z = Hb @ W
+    s = z / tau
+    return z, s, logsumexp_rows(s)
+
+
+def topk_kl_forward(H, W, I, A, mask, tau, row_block=64):
+    """Per-token KL(p_t || q_t) against a top-K teacher ([EKD] §3 "Offline
+    distillation").
+
+    For a valid row t with s = (H_t W) / tau, L_t = logsumexp(s) and
+    p = softmax(A_t / tau) over the K entries:
+        KL_t = sum_k p_k (log p_k - s[I_tk] + L_t)
+             = [teacher entropy term] - [cross term] + [mass * log Z], mass = 1.
+    Returns (kl [T], lse [T] = L_t, z_topk [T, K] = z at the cached indices).
+    """
+    H, W, A = as_f64(H), as_f64(W), as_f64(A)
+    I = np.asarray(I.cpu().numpy() if hasattr(I, "cpu") else I, dtype=np.int64)
+    T, K = I.shape
+    valid = _valid_rows(mask, T)
+    kl = np.zeros(T)
+    lse = np.zeros(T)
+    ztk = np.zeros((T, K))
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        z, s, L = _student_block(H[rb], W, tau)
+        logp = teacher_log_probs(A[rb], tau)
+        p = np.exp(logp)
+        s_at = np.take_along_axis(s, I[rb], axis=1)
+        kl[rb] = (p * (logp - s_at + L[:, None])).sum(axis=1)
+        lse[rb] = L
+        ztk[rb] = np.take_along_axis(z, I[rb], axis=1)
+    return kl, lse, ztk
+
+
+def _topk_dz(s, L, I_rows, p, g_rows, tau):
+    """dKL/dz for a block of rows: (g/tau) (softmax(s) - scatter_add(I, p))."""
+    q = np.exp(s - L[:, None])
+    r = np.repeat(np.arange(s.shape[0]), I_rows.shape[1])
+    np.add.at(q, (r, I_rows.reshape(-1)), -p.reshape(-1))  # duplicates add
+    return q * (g_rows / tau)[:, None]
+
+
+def topk_kl_backward(H, W, I, A, mask, tau, g, row_block=64, v_panel=16384):
+    """Gradients of sum_t g_t KL_t w.r.t. H and W ([EKD] §3: the backward pass
+    needs each row's log Z and the scatter over the K retained entries).
+
+    dZ_t = (g_t / tau) (softmax(s_t) - scatter_add(I_t, p_t)); dH = dZ W^T;
+    dW = H^T dZ; masked rows have dZ_t = 0.  Returns (dH [T, d], dW [d, V])."""
+    H, W, A, g = as_f64(H), as_f64(W), as_f64(A), as_f64(g)
+    I = np.asarray(I.cpu().numpy() if hasattr(I, "cpu") else I, dtype=np.int64)
+    T, d = H.shape
+    V = W.shape[1]
+    valid = _valid_rows(mask, T)
+    dH = np.zeros((T, d))
+    dW = np.zeros((d, V))
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        _, s, L = _student_block(H[rb], W, tau)
+        p = np.exp(teacher_log_probs(A[rb], tau))
+        D = _topk_dz(s, L, I[rb], p, g[rb], tau)
+        dH[rb] = D @ W.T
+        for v0 in range(0, V, v_panel):
+            dW[:, v0:v0 + v_panel] += H[rb].T @ D[:, v0:v0 + v_panel]
+    return dH, dW
+
+
+def topk_kl_rows(H, W, I, A, mask, tau, g, rows):
+    """kl, lse, z_topk and dH for selected rows only: each depends on its own
+    row and on W alone, so large workloads are checked on a sample of rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    Hr, Ir, Ar = as_f64(_take_rows(H, rows)), _take_rows(I, rows), _take_rows(A, rows)
+    mr, gr = _take_rows(mask, rows), _take_rows(g, rows)
+    W = as_f64(W)
+    kl, lse, ztk = topk_kl_forward(Hr, W, Ir, Ar, mr, tau)
+    dH, _ = _rows_dh_topk(Hr, W, Ir, Ar, mr, tau, gr)
+    return kl, lse, ztk, dH
+
+
+def _rows_dh_topk(H, W, I, A, mask, tau, g, row_block=64):
+    H, A, g = as_f64(H), as_f64(A), as_f64(g)
+    I = np.asarray(I.cpu().numpy() if hasattr(I, "cpu") else I, dtype=np.int64)
+    T, d = H.shape
+    valid = _valid_rows(mask, T)
+    dH = np.zeros((T, d))
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        _, s, L = _student_block(H[rb], W, tau)
+        p = np.exp(teacher_log_probs(A[rb], tau))
+        dH[rb] = _topk_dz(s, L, I[rb], p, g[rb], tau) @ W.T
+    return dH, None
+
+
+def full_kl_forward(H, Ws, Ht, Wt, mask, tau, row_block=64):
+    """Full-vocabulary KL(p_t || q_t) with teacher logits recomputed through a
+    frozen teacher head ([KDFlow]; objective as [EKD] §1).
+
+    u = (Ht_t Wt) / tau, s = (H_t Ws) / tau, p = softmax(u):
+        KL_t = sum_v p_v (u_v - s_v) - logsumexp(u) + logsumexp(s).
+    Returns (kl [T], lse_s [T], lse_t [T])."""
+    H, Ws, Ht, Wt = as_f64(H), as_f64(Ws), as_f64(Ht), as_f64(Wt)
+    T = H.shape[0]
+    valid = _valid_rows(mask, T)
+    kl, ls, lt = np.zeros(T), np.zeros(T), np.zeros(T)
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        _, s, Ls = _student_block(H[rb], Ws, tau)
+        _, u, Lt = _student_block(Ht[rb], Wt, tau)
+        p = np.exp(u - Lt[:, None])
+        kl[rb] = (p * (u - s)).sum(axis=1) - Lt + Ls
+        ls[rb], lt[rb] = Ls, Lt
+    return kl, ls, lt
+
+
+def full_kl_backward(H, Ws, Ht, Wt, mask, tau, g, row_block=64, v_panel=16384):
+    """Gradients of sum_t g_t KL_t w.r.t. the student's H and Ws only (the
+    teacher head is frozen, [KDFlow]).  dZ_t = (g_t / tau)(softmax(s_t) - p_t);
+    dH = dZ Ws^T; dWs = H^T dZ.  Returns (dH, dWs)."""
+    H, Ws, Ht, Wt, g = as_f64(H), as_f64(Ws), as_f64(Ht), as_f64(Wt), as_f64(g)
+    T, d = H.shape
+    V = Ws.shape[1]
+    valid = _valid_rows(mask, T)
+    dH = np.zeros((T, d))
+    dW = np.zeros((d, V))
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        _, s, Ls = _student_block(H[rb], Ws, tau)
+        _, u, Lt = _student_block(Ht[rb], Wt, tau)
+        D = (np.exp(s - Ls[:, None]) - np.exp(u - Lt[:, None])) * (g[rb] / tau)[:, None]
+        dH[rb] = D @ Ws.T
+        for v0 in range(0, V, v_panel):
+            dW[:, v0:v0 + v_panel] += H[rb].T @ D[:, v0:v0 + v_panel]
+    return dH, dW
+
+
+def full_kl_rows(H, Ws, Ht, Wt, mask, tau, g, rows):
+    """kl, lse_s, lse_t and dH for selected rows (each depends only on its own
+    row and the two heads)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    Hr, Htr = as_f64(_take_rows(H, rows)), as_f64(_take_rows(Ht, rows))
+    mr, gr = _take_rows(mask, rows), _take_rows(g, rows)
+    Ws, Wt = as_f64(Ws), as_f64(Wt)
+    kl, ls, lt = full_kl_forward(Hr, Ws, Htr, Wt, mr, tau)
+    dH, _ = _rows_dh_full(Hr, Ws, Htr, Wt, mr, tau, gr)
+    return kl, ls, lt, dH
+
+
+def _rows_dh_full(H, Ws, Ht, Wt, mask, tau, g, row_block=64):
+    H, Ws, Ht, Wt, g = as_f64(H), as_f64(Ws), as_f64(Ht), as_f64(Wt), as_f64(g)
+    T, d = H.shape
+    valid = _valid_rows(mask, T)
+    dH = np.zeros((T, d))
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        _, s, Ls = _student_block(H[rb], Ws, tau)
+        _, u, Lt = _student_block(Ht[rb], Wt, tau)
+        D = (np.exp(s - Ls[:, None]) - np.exp(u - Lt[:, None])) * (g[rb] / tau)[:, None]
+        dH[rb] = D @ Ws.T
+    return dH, None
