@@ -1,0 +1,126 @@
+"""Fused, chunked KL distillation loss over the LM output head, for MI355X.
+
+The loss of "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and
+a Fused Chunked KL Loss" (§3 "Offline distillation", "Fused chunked KL") and its
+full-vocabulary variant through a frozen teacher head (KDFlow abstract).  All
+arithmetic runs in the HIP kernels of libkdloss.so; this package only allocates
+outputs and workspace with torch and passes pointers.
+
+    kl = topk_kl(H, W, topk_idx, topk_logits, mask, tau)        # autograd
+    kl = full_kl(H, Ws, Ht, Wt, mask, tau)                      # autograd
+    kl, lse, z = topk_kl_forward(...); dH, dW = topk_kl_backward(...)
+
+The C-ABI mirrors (kd_topk_kl_fwd, ...) are re-exported with the header's names.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._binding import (  # noqa: F401
+    EXPORTS, KD_BF16, KD_DEFAULT_CHUNK_ROWS, KD_F32, KD_MAX_K, LIB_PATH, KDError, kd_full_kl_bwd, kd_full_kl_fwd,
+    kd_full_kl_workspace_size, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_workspace_size, kd_version, lib,
+    profile_enable, profile_read, profile_reset,
+)
+
+__all__ = [
+    "topk_kl", "full_kl", "topk_kl_forward", "topk_kl_backward", "full_kl_forward", "full_kl_backward",
+    "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_full_kl_fwd", "kd_full_kl_bwd",
+    "kd_topk_kl_workspace_size", "kd_full_kl_workspace_size", "KDError",
+]
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def topk_kl_forward(H, W, topk_idx, topk_logits, mask=None, tau=1.0, want_z_topk=False, workspace=None):
+    """Per-token KL, log-normaliser and (optionally) the gathered raw logits."""
+    T, d = H.shape
+    V, K = W.shape[1], topk_idx.shape[1]
+    kl = torch.empty(T, dtype=torch.float32, device=H.device)
+    lse = torch.empty(T, dtype=torch.float32, device=H.device)
+    z = torch.empty(T, K, dtype=torch.float32, device=H.device) if want_z_topk else None
+    if workspace is None:
+        workspace = _workspace(kd_topk_kl_workspace_size(T, d, V, K, H.dtype), H.device)
+    kd_topk_kl_fwd(H, W, topk_idx, topk_logits, mask, tau, kl, lse, z, workspace)
+    return kl, lse, z
+
+
+def topk_kl_backward(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl, chunk_rows=0, workspace=None):
+    """dH (dtype of H) and dW (float32) for the per-token upstream gradient."""
+    T, d = H.shape
+    V, K = W.shape[1], topk_idx.shape[1]
+    dH = torch.empty_like(H)
+    dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
+    if workspace is None:
+        workspace = _workspace(kd_topk_kl_workspace_size(T, d, V, K, H.dtype, chunk_rows), H.device)
+    kd_topk_kl_bwd(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl.float().contiguous(), dH, dW, chunk_rows,
+                   workspace)
+    return dH, dW
+
+
+def full_kl_forward(H, Ws, Ht, Wt, mask=None, tau=1.0, workspace=None):
+    T, d = H.shape
+    dt, V = Ht.shape[1], Ws.shape[1]
+    kl = torch.empty(T, dtype=torch.float32, device=H.device)
+    ls = torch.empty(T, dtype=torch.float32, device=H.device)
+    lt = torch.empty(T, dtype=torch.float32, device=H.device)
+    if workspace is None:
+        workspace = _workspace(kd_full_kl_workspace_size(T, d, dt, V, H.dtype), H.device)
+    kd_full_kl_fwd(H, Ws, Ht, Wt, mask, tau, kl, ls, lt, workspace)
+    return kl, ls, lt
+
+
+def full_kl_backward(H, Ws, Ht, Wt, mask, tau, lse_s, lse_t, grad_kl, chunk_rows=0, workspace=None):
+    T, d = H.shape
+    dt, V = Ht.shape[1], Ws.shape[1]
+    dH = torch.empty_like(H)
+    dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
+    if workspace is None:
+        workspace = _workspace(kd_full_kl_workspace_size(T, d, dt, V, H.dtype, chunk_rows), H.device)
+    kd_full_kl_bwd(H, Ws, Ht, Wt, mask, tau, lse_s, lse_t, grad_kl.float().contiguous(), dH, dW, chunk_rows,
+                   workspace)
+    return dH, dW
+
+
+class _TopkKL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, H, W, topk_idx, topk_logits, mask, tau, chunk_rows):
+        kl, lse, _ = topk_kl_forward(H, W, topk_idx, topk_logits, mask, tau)
+        ctx.save_for_backward(H, W, topk_idx, topk_logits, lse)
+        ctx.mask, ctx.tau, ctx.chunk_rows = mask, tau, chunk_rows
+        return kl
+
+    @staticmethod
+    def backward(ctx, g):
+        H, W, idx, logits, lse = ctx.saved_tensors
+        dH, dW = topk_kl_backward(H, W, idx, logits, ctx.mask, ctx.tau, lse, g, ctx.chunk_rows)
+        return dH, dW.to(W.dtype), None, None, None, None, None
+
+
+class _FullKL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, H, Ws, Ht, Wt, mask, tau, chunk_rows):
+        kl, ls, lt = full_kl_forward(H, Ws, Ht, Wt, mask, tau)
+        ctx.save_for_backward(H, Ws, Ht, Wt, ls, lt)
+        ctx.mask, ctx.tau, ctx.chunk_rows = mask, tau, chunk_rows
+        return kl
+
+    @staticmethod
+    def backward(ctx, g):
+        H, Ws, Ht, Wt, ls, lt = ctx.saved_tensors
+        dH, dW = full_kl_backward(H, Ws, Ht, Wt, ctx.mask, ctx.tau, ls, lt, g, ctx.chunk_rows)
+        return dH, dW.to(Ws.dtype), None, None, None, None, None
+
+
+def topk_kl(H, W, topk_idx, topk_logits, mask=None, tau=1.0, chunk_rows=0):
+    """Per-token KL(p_teacher || q_student) with a top-K teacher; differentiable
+    in H and W (W's gradient is cast to W's dtype; the float32 one is available
+    from topk_kl_backward)."""
+    return _TopkKL.apply(H, W, topk_idx, topk_logits, mask, float(tau), int(chunk_rows))
+
+
+def full_kl(H, Ws, Ht, Wt, mask=None, tau=1.0, chunk_rows=0):
+    """Per-token full-vocabulary KL through a frozen teacher head; differentiable
+    in H and Ws only."""
+    return _FullKL.apply(H, Ws, Ht, Wt, mask, float(tau), int(chunk_rows))

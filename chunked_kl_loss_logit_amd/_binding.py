@@ -1,0 +1,190 @@
+"""ctypes binding of libkdloss (include/kdloss.h).
+
+Argument marshalling only: every step of the loss runs in the library's HIP
+kernels.  torch provides device memory and the current stream.  There is no
+fallback: if libkdloss.so is missing, or a tensor is not on the GPU, the call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkdloss.so")
+
+KD_F32, KD_BF16 = 0, 1
+KD_MAX_K = 8192
+KD_DEFAULT_CHUNK_ROWS = 4096
+STATUS = {
+    0: "KD_OK", 1: "KD_ERR_INVALID_ARG", 2: "KD_ERR_UNSUPPORTED", 3: "KD_ERR_ALIGNMENT",
+    4: "KD_ERR_WORKSPACE_TOO_SMALL", 5: "KD_ERR_INDEX_OUT_OF_RANGE", 6: "KD_ERR_HIP",
+}
+
+EXPORTS = (
+    "kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd",
+    "kd_full_kl_workspace_size", "kd_full_kl_fwd", "kd_full_kl_bwd",
+    "kd_status_string", "kd_last_error", "kd_version",
+    "kd_profile_enable", "kd_profile_count", "kd_profile_get", "kd_profile_reset",
+)
+
+
+class KDError(RuntimeError):
+    """A libkdloss call returned a status other than KD_OK."""
+
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{where}: {self.name}: {detail}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m chunked_kl_loss_logit_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, f32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    st = ctypes.c_int
+    L.kd_topk_kl_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
+    L.kd_topk_kl_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, sz, vp]
+    L.kd_topk_kl_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, i64, vp, sz, vp]
+    L.kd_full_kl_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
+    L.kd_full_kl_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, sz, vp]
+    L.kd_full_kl_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, i64, vp, sz,
+                                 vp]
+    for f in ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_full_kl_workspace_size",
+              "kd_full_kl_fwd", "kd_full_kl_bwd", "kd_profile_enable", "kd_profile_get", "kd_profile_reset"):
+        getattr(L, f).restype = st
+    L.kd_status_string.argtypes = [st]
+    L.kd_status_string.restype = ctypes.c_char_p
+    L.kd_last_error.argtypes = []
+    L.kd_last_error.restype = ctypes.c_char_p
+    L.kd_version.restype = ctypes.c_int
+    L.kd_profile_enable.argtypes = [ctypes.c_int]
+    L.kd_profile_count.restype = ctypes.c_int
+    L.kd_profile_get.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(i64),
+                                 ctypes.POINTER(ctypes.c_double)]
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise KDError(status, where, lib().kd_last_error().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return KD_BF16
+    if t == torch.float32:
+        return KD_F32
+    raise TypeError(f"unsupported dtype {t}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libkdloss tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("libkdloss tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------- C-ABI mirrors
+def kd_topk_kl_workspace_size(T, d, V, K, dtype, chunk_rows=0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().kd_topk_kl_workspace_size(T, d, V, K, _dtype_code(dtype), chunk_rows, ctypes.byref(out)),
+           "kd_topk_kl_workspace_size")
+    return out.value
+
+
+def kd_full_kl_workspace_size(T, d, dt_hidden, V, dtype, chunk_rows=0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().kd_full_kl_workspace_size(T, d, dt_hidden, V, _dtype_code(dtype), chunk_rows, ctypes.byref(out)),
+           "kd_full_kl_workspace_size")
+    return out.value
+
+
+def kd_topk_kl_fwd(H, W, topk_idx, topk_logits, mask, tau, kl, lse, z_topk, workspace, stream=None):
+    """Enqueue the top-K forward; outputs kl, lse (and z_topk if given) in place."""
+    T, d = H.shape
+    V = W.shape[1]
+    K = topk_idx.shape[1]
+    _check(lib().kd_topk_kl_fwd(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask), float(tau),
+                                T, d, V, K, _dtype_code(H.dtype), _ptr(kl), _ptr(lse), _ptr(z_topk),
+                                _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                _stream(stream)), "kd_topk_kl_fwd")
+
+
+def kd_topk_kl_bwd(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl, dH, dW, chunk_rows, workspace,
+                   stream=None):
+    """Enqueue the top-K backward; outputs dH and dW in place."""
+    T, d = H.shape
+    V = W.shape[1]
+    K = topk_idx.shape[1]
+    _check(lib().kd_topk_kl_bwd(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask), float(tau),
+                                T, d, V, K, _dtype_code(H.dtype), _ptr(lse), _ptr(grad_kl), _ptr(dH), _ptr(dW),
+                                int(chunk_rows), _ptr(workspace),
+                                workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "kd_topk_kl_bwd")
+
+
+def kd_full_kl_fwd(H, Ws, Ht, Wt, mask, tau, kl, lse_s, lse_t, workspace, stream=None):
+    T, d = H.shape
+    dt = Ht.shape[1]
+    V = Ws.shape[1]
+    _check(lib().kd_full_kl_fwd(_ptr(H), _ptr(Ws), _ptr(Ht), _ptr(Wt), _ptr(mask), float(tau), T, d, dt, V,
+                                _dtype_code(H.dtype), _ptr(kl), _ptr(lse_s), _ptr(lse_t), _ptr(workspace),
+                                workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "kd_full_kl_fwd")
+
+
+def kd_full_kl_bwd(H, Ws, Ht, Wt, mask, tau, lse_s, lse_t, grad_kl, dH, dWs, chunk_rows, workspace, stream=None):
+    T, d = H.shape
+    dt = Ht.shape[1]
+    V = Ws.shape[1]
+    _check(lib().kd_full_kl_bwd(_ptr(H), _ptr(Ws), _ptr(Ht), _ptr(Wt), _ptr(mask), float(tau), T, d, dt, V,
+                                _dtype_code(H.dtype), _ptr(lse_s), _ptr(lse_t), _ptr(grad_kl), _ptr(dH),
+                                _ptr(dWs), int(chunk_rows), _ptr(workspace),
+                                workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "kd_full_kl_bwd")
+
+
+def kd_version() -> int:
+    return lib().kd_version()
+
+
+# ---------------------------------------------------------------- profiling
+def profile_enable(on: bool = True) -> None:
+    _check(lib().kd_profile_enable(1 if on else 0), "kd_profile_enable")
+
+
+def profile_reset() -> None:
+    _check(lib().kd_profile_reset(), "kd_profile_reset")
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total ms)} of the events recorded so far."""
+    L = lib()
+    n = L.kd_profile_count()
+    out = {}
+    for i in range(n):
+        name, launches, ms = ctypes.c_char_p(), ctypes.c_int64(), ctypes.c_double()
+        _check(L.kd_profile_get(i, ctypes.byref(name), ctypes.byref(launches), ctypes.byref(ms)), "kd_profile_get")
+        out[name.value.decode()] = (launches.value, ms.value)
+    return out

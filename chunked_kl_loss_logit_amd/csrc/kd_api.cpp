@@ -1,0 +1,611 @@
+// C-ABI entry points of libkdloss: argument checks, workspace planning and the
+// launch sequence of each call.  Every argument check runs on the host before
+// any HIP call, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kd_launch.h"
+#include "kdloss.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+kd_status fail(kd_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+// ------------------------------------------------------------------ profiling
+struct ProfEvent {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfEvent> g_prof_pending;
+std::vector<std::string> g_prof_names;
+std::map<std::string, std::pair<int64_t, double>> g_prof_tot;
+
+// Runs one launcher; while profiling, brackets it with events on `st`.
+template <class F>
+hipError_t run(const char* name, hipStream_t st, F&& launch) {
+  if (!g_prof_on) return launch();
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return launch();
+  (void)hipEventRecord(a, st);
+  const hipError_t e = launch();
+  (void)hipEventRecord(b, st);
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_pending.push_back({name, a, b});
+  return e;
+}
+
+void prof_fold() {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (auto& p : g_prof_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+      auto it = g_prof_tot.find(p.name);
+      if (it == g_prof_tot.end()) {
+        g_prof_names.push_back(p.name);
+        it = g_prof_tot.emplace(p.name, std::make_pair(int64_t(0), 0.0)).first;
+      }
+      it->second.first += 1;
+      it->second.second += ms;
+    }
+    (void)hipEventDestroy(p.a);
+    (void)hipEventDestroy(p.b);
+  }
+  g_prof_pending.clear();
+}
+
+// ------------------------------------------------------------------ shapes and checks
+constexpr size_t kAlign = 256;
+inline size_t up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int elem_of(kd_dtype dt) { return dt == KD_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+kd_status check_common(int64_t T, int64_t d, int64_t V, kd_dtype dt, float tau) {
+  if (dt != KD_F32 && dt != KD_BF16) return fail(KD_ERR_INVALID_ARG, "dtype must be KD_F32 or KD_BF16");
+  if (T < 0) return fail(KD_ERR_INVALID_ARG, "T must be >= 0");
+  if (d < 1) return fail(KD_ERR_INVALID_ARG, "d must be >= 1");
+  if (V < 1) return fail(KD_ERR_INVALID_ARG, "V must be >= 1");
+  if (!(tau > 0.f) || !std::isfinite(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be finite and > 0");
+  const int64_t epc = dt == KD_BF16 ? 8 : 4;
+  if (d % epc) return fail(KD_ERR_UNSUPPORTED, "d must be a multiple of 8 (bf16) or 4 (fp32)");
+  if (V % epc) return fail(KD_ERR_UNSUPPORTED, "V must be a multiple of 8 (bf16) or 4 (fp32)");
+  if (T > INT32_MAX / 2 || V > INT32_MAX / 2 || d > INT32_MAX / 2)
+    return fail(KD_ERR_UNSUPPORTED, "T, d and V must be below 2^30");
+  return KD_OK;
+}
+
+kd_status check_k(int64_t K, int64_t V) {
+  if (K < 1) return fail(KD_ERR_INVALID_ARG, "K must be >= 1");
+  if (K > V) return fail(KD_ERR_INVALID_ARG, "K must be <= V");
+  if (K > KD_MAX_K) return fail(KD_ERR_UNSUPPORTED, "K above KD_MAX_K");
+  return KD_OK;
+}
+
+kd_status need(const void* p, const char* name) {
+  if (p == nullptr) return fail(KD_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  return KD_OK;
+}
+
+kd_status need_align(const void* p, size_t a, const char* name) {
+  if (p != nullptr && !aligned(p, a))
+    return fail(KD_ERR_ALIGNMENT, std::string(name) + " must be " + std::to_string(a) + "-byte aligned");
+  return KD_OK;
+}
+
+#define KD_TRY(x)                   \
+  do {                              \
+    const kd_status _s = (x);       \
+    if (_s != KD_OK) return _s;     \
+  } while (0)
+
+#define KD_LAUNCH(name, st, call)                                                              \
+  do {                                                                                         \
+    const hipError_t _e = run(name, st, [&]() { return (call); });                             \
+    if (_e != hipSuccess) return fail(KD_ERR_HIP, std::string(name) + ": " + hipGetErrorString(_e)); \
+  } while (0)
+
+// Vocabulary splits: enough workgroups to cover the 256 compute units once.
+int splits_for(int64_t nrb, int64_t ntiles) {
+  int64_t s = cdiv(256, std::max<int64_t>(1, nrb));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, ntiles));
+}
+
+int64_t chunk_of(int64_t T, int64_t chunk_rows) {
+  int64_t C = chunk_rows <= 0 ? KD_DEFAULT_CHUNK_ROWS : chunk_rows;
+  C = (int64_t)up((size_t)C, 256);
+  return std::min<int64_t>(C, (int64_t)up((size_t)std::max<int64_t>(T, 1), 256));
+}
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = up(off + bytes, kAlign);
+    return o;
+  }
+};
+
+// Backward chunk buffers shared by both variants.
+struct ChunkPlan {
+  int64_t C, ldz;
+  int nrb_c, nrb_dh, ncb_dh, S_dh, nrb_dw, ncb_dw;
+  size_t o_dz, o_hT, o_dhp;
+};
+
+ChunkPlan plan_chunk(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows, Carver& cv) {
+  ChunkPlan p{};
+  p.C = chunk_of(T, chunk_rows);
+  p.ldz = cdiv(V, kd::kTileN) * kd::kTileN;
+  p.nrb_c = (int)(p.C / kd::kTileM);
+  p.nrb_dh = p.nrb_c;
+  p.ncb_dh = (int)cdiv(d, 256);
+  const int64_t nstv = cdiv(V * elem, 128);
+  p.S_dh = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(768, (int64_t)p.nrb_dh * p.ncb_dh), nstv));
+  p.nrb_dw = (int)cdiv(d, 256);
+  p.ncb_dw = (int)cdiv(V, 256);
+  p.o_dz = cv.take((size_t)p.C * p.ldz * elem);
+  p.o_hT = cv.take((size_t)d * p.C * elem);
+  p.o_dhp = cv.take((size_t)p.S_dh * p.C * d * 4);
+  return p;
+}
+
+struct TopkPlan {
+  int ntiles, nrb, S;
+  size_t o_idx, o_perm, o_p, o_ent, o_rows, o_count, o_part;
+  ChunkPlan ch;
+  size_t fwd_total, total;  // bytes the forward call needs; bytes both calls need
+};
+
+TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t chunk_rows) {
+  TopkPlan p{};
+  p.ntiles = (int)cdiv(V, kd::kTileN);
+  p.nrb = (int)cdiv(T, kd::kTileM);
+  p.S = splits_for(p.nrb, p.ntiles);
+  Carver cv;
+  p.o_idx = cv.take((size_t)T * K * 4);
+  p.o_perm = cv.take((size_t)T * K * 2);
+  p.o_p = cv.take((size_t)T * K * 4);
+  p.o_ent = cv.take((size_t)T * 4);
+  p.o_rows = cv.take((size_t)T * 4);
+  p.o_count = cv.take(16);
+  Carver fw = cv, bw = cv;  // forward partials and backward chunk buffers overlap
+  p.o_part = fw.take((size_t)p.S * T * 16);
+  p.ch = plan_chunk(T, d, V, elem, chunk_rows, bw);
+  p.fwd_total = fw.off;
+  p.total = std::max(fw.off, bw.off);
+  return p;
+}
+
+struct FullPlan {
+  int ntiles, nrb, S;
+  size_t o_rows, o_count, o_part;
+  ChunkPlan ch;
+  size_t fwd_total, total;
+};
+
+FullPlan plan_full(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows) {
+  FullPlan p{};
+  p.ntiles = (int)cdiv(V, kd::kTileNFull);
+  p.nrb = (int)cdiv(T, kd::kTileM);
+  p.S = splits_for(p.nrb, p.ntiles);
+  Carver cv;
+  p.o_rows = cv.take((size_t)T * 4);
+  p.o_count = cv.take(16);
+  Carver fw = cv, bw = cv;
+  p.o_part = fw.take((size_t)p.S * T * 32);
+  p.ch = plan_chunk(T, d, V, elem, chunk_rows, bw);
+  p.fwd_total = fw.off;
+  p.total = std::max(fw.off, bw.off);
+  return p;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+kd_status check_workspace(const void* ws, size_t have, size_t want) {
+  if (want > 0) KD_TRY(need(ws, "workspace"));
+  KD_TRY(need_align(ws, kAlign, "workspace"));
+  if (have < want)
+    return fail(KD_ERR_WORKSPACE_TOO_SMALL,
+                "workspace has " + std::to_string(have) + " bytes, needs " + std::to_string(want));
+  return KD_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+const char* kd_status_string(kd_status s) {
+  switch (s) {
+    case KD_OK: return "KD_OK";
+    case KD_ERR_INVALID_ARG: return "KD_ERR_INVALID_ARG";
+    case KD_ERR_UNSUPPORTED: return "KD_ERR_UNSUPPORTED";
+    case KD_ERR_ALIGNMENT: return "KD_ERR_ALIGNMENT";
+    case KD_ERR_WORKSPACE_TOO_SMALL: return "KD_ERR_WORKSPACE_TOO_SMALL";
+    case KD_ERR_INDEX_OUT_OF_RANGE: return "KD_ERR_INDEX_OUT_OF_RANGE";
+    case KD_ERR_HIP: return "KD_ERR_HIP";
+  }
+  return "KD_ERR_UNKNOWN";
+}
+
+const char* kd_last_error(void) { return g_err.c_str(); }
+
+int kd_version(void) { return 10000; }
+
+kd_status kd_profile_enable(int on) {
+  g_prof_on = on != 0;
+  return KD_OK;
+}
+
+int kd_profile_count(void) {
+  prof_fold();
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  return (int)g_prof_names.size();
+}
+
+kd_status kd_profile_get(int i, const char** name, int64_t* launches, double* total_ms) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  if (i < 0 || i >= (int)g_prof_names.size()) return fail(KD_ERR_INVALID_ARG, "profile index out of range");
+  const auto& e = g_prof_tot[g_prof_names[i]];
+  if (name) *name = g_prof_names[i].c_str();
+  if (launches) *launches = e.first;
+  if (total_ms) *total_ms = e.second;
+  return KD_OK;
+}
+
+kd_status kd_profile_reset(void) {
+  prof_fold();
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_names.clear();
+  g_prof_tot.clear();
+  return KD_OK;
+}
+
+// ---------------------------------------------------------------- top-K
+kd_status kd_topk_kl_workspace_size(int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt, int64_t chunk_rows,
+                                    size_t* bytes) {
+  g_err.clear();
+  KD_TRY(need(bytes, "bytes"));
+  KD_TRY(check_common(T, d, V, dt, 1.0f));
+  KD_TRY(check_k(K, V));
+  *bytes = T == 0 ? 0 : plan_topk(T, d, V, K, elem_of(dt), chunk_rows).total;
+  return KD_OK;
+}
+
+kd_status kd_topk_kl_fwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                         const uint8_t* mask, float tau, int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                         float* kl, float* lse, float* z_topk, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_err.clear();
+  KD_TRY(check_common(T, d, V, dt, tau));
+  KD_TRY(check_k(K, V));
+  if (T == 0) return KD_OK;
+  KD_TRY(need(H, "H"));
+  KD_TRY(need(W, "W"));
+  KD_TRY(need(topk_idx, "topk_idx"));
+  KD_TRY(need(topk_logits, "topk_logits"));
+  KD_TRY(need(kl, "kl"));
+  KD_TRY(need(lse, "lse"));
+  KD_TRY(need_align(H, 16, "H"));
+  KD_TRY(need_align(W, 16, "W"));
+  KD_TRY(need_align(topk_idx, 4, "topk_idx"));
+  KD_TRY(need_align(topk_logits, 4, "topk_logits"));
+  KD_TRY(need_align(kl, 4, "kl"));
+  KD_TRY(need_align(lse, 4, "lse"));
+  KD_TRY(need_align(z_topk, 4, "z_topk"));
+  const int elem = elem_of(dt);
+  const TopkPlan p = plan_topk(T, d, V, K, elem, 0);
+  KD_TRY(check_workspace(workspace, workspace_bytes, p.fwd_total));
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
+  kd::TopkRowData rd{at<int32_t>(workspace, p.o_idx), at<uint16_t>(workspace, p.o_perm), at<float>(workspace, p.o_p),
+                     at<float>(workspace, p.o_ent)};
+  float* part = at<float>(workspace, p.o_part);
+
+  KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
+  KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, tau, rd, z_topk, st));
+  kd::TopkFwdArgs a{};
+  a.H = static_cast<const char*>(H);
+  a.W = static_cast<const char*>(W);
+  a.c = c;
+  a.rd = rd;
+  a.z_topk = z_topk;
+  a.part = part;
+  a.part_stride = T;
+  a.d = d;
+  a.V = V;
+  a.K = K;
+  a.nrb = p.nrb;
+  a.S = p.S;
+  a.ntiles = p.ntiles;
+  a.c2 = (float)(1.4426950408889634 / (double)tau);
+  KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
+  KD_LAUNCH("topk_combine", st, kd::launch_topk_combine(part, p.S, T, c, mask, rd.ent, T, tau, kl, lse, st));
+  return KD_OK;
+}
+
+kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                         const uint8_t* mask, float tau, int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                         const float* lse, const float* grad_kl, void* dH, float* dW, int64_t chunk_rows,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  KD_TRY(check_common(T, d, V, dt, tau));
+  KD_TRY(check_k(K, V));
+  KD_TRY(need(dW, "dW"));
+  KD_TRY(need_align(dW, 16, "dW"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    KD_LAUNCH("fill_zero", st, kd::launch_fill_zero(dW, d * V * 4, st));
+    return KD_OK;
+  }
+  KD_TRY(need(H, "H"));
+  KD_TRY(need(W, "W"));
+  KD_TRY(need(topk_idx, "topk_idx"));
+  KD_TRY(need(topk_logits, "topk_logits"));
+  KD_TRY(need(lse, "lse"));
+  KD_TRY(need(grad_kl, "grad_kl"));
+  KD_TRY(need(dH, "dH"));
+  KD_TRY(need_align(H, 16, "H"));
+  KD_TRY(need_align(W, 16, "W"));
+  KD_TRY(need_align(dH, 16, "dH"));
+  KD_TRY(need_align(topk_idx, 4, "topk_idx"));
+  KD_TRY(need_align(topk_logits, 4, "topk_logits"));
+  KD_TRY(need_align(lse, 4, "lse"));
+  KD_TRY(need_align(grad_kl, 4, "grad_kl"));
+  if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
+  const int elem = elem_of(dt);
+  const TopkPlan p = plan_topk(T, d, V, K, elem, chunk_rows);
+  KD_TRY(check_workspace(workspace, workspace_bytes, p.total));
+
+  kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
+  kd::TopkRowData rd{at<int32_t>(workspace, p.o_idx), at<uint16_t>(workspace, p.o_perm), at<float>(workspace, p.o_p),
+                     at<float>(workspace, p.o_ent)};
+  KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
+  KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, tau, rd, nullptr, st));
+  KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * elem, dH, st));
+
+  const ChunkPlan& ch = p.ch;
+  char* dz = at<char>(workspace, ch.o_dz);
+  char* hT = at<char>(workspace, ch.o_hT);
+  float* dhp = at<float>(workspace, ch.o_dhp);
+  const int64_t nchunks = cdiv(T, ch.C);
+  for (int64_t k = 0; k < nchunks; ++k) {
+    const int64_t c0 = k * ch.C;
+    kd::TopkDzArgs za{};
+    za.H = static_cast<const char*>(H);
+    za.W = static_cast<const char*>(W);
+    za.c = c;
+    za.rd = rd;
+    za.lse = lse;
+    za.g = grad_kl;
+    za.dz = dz;
+    za.ldz = ch.ldz;
+    za.c0 = c0;
+    za.C = ch.C;
+    za.d = d;
+    za.V = V;
+    za.K = K;
+    za.nrb = ch.nrb_c;
+    za.ntiles = p.ntiles;
+    za.S = splits_for(ch.nrb_c, p.ntiles);
+    za.c2 = (float)(1.4426950408889634 / (double)tau);
+    za.inv_tau = 1.0f / tau;
+    KD_LAUNCH("topk_dz_tile", st, kd::launch_topk_dz(elem, za, st));
+    KD_LAUNCH("gather_transpose", st, kd::launch_gather_transpose(H, elem, d, c, c0, ch.C, hT, st));
+    kd::DhArgs ha{};
+    ha.dz = dz;
+    ha.W = static_cast<const char*>(W);
+    ha.part = dhp;
+    ha.count = c.count;
+    ha.c0 = c0;
+    ha.C = ch.C;
+    ha.ldz = ch.ldz;
+    ha.d = d;
+    ha.V = V;
+    ha.nrb = ch.nrb_dh;
+    ha.ncb = ch.ncb_dh;
+    ha.S = ch.S_dh;
+    KD_LAUNCH("dh_tile", st, kd::launch_dh(elem, ha, st));
+    KD_LAUNCH("reduce_dh", st, kd::launch_reduce_dh(dhp, ch.S_dh, ch.C, d, c, c0, dH, elem, st));
+    kd::DwArgs wa{};
+    wa.hT = hT;
+    wa.dz = dz;
+    wa.dW = dW;
+    wa.count = c.count;
+    wa.c0 = c0;
+    wa.C = ch.C;
+    wa.ldz = ch.ldz;
+    wa.d = d;
+    wa.V = V;
+    wa.nrb = ch.nrb_dw;
+    wa.ncb = ch.ncb_dw;
+    wa.accumulate = k > 0;
+    KD_LAUNCH("dw_tile", st, kd::launch_dw(elem, wa, st));
+  }
+  return KD_OK;
+}
+
+// ---------------------------------------------------------------- full vocabulary
+kd_status kd_full_kl_workspace_size(int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                                    int64_t chunk_rows, size_t* bytes) {
+  g_err.clear();
+  KD_TRY(need(bytes, "bytes"));
+  KD_TRY(check_common(T, d, V, dt, 1.0f));
+  KD_TRY(check_common(T, dt_hidden, V, dt, 1.0f));
+  *bytes = T == 0 ? 0 : plan_full(T, d, V, elem_of(dt), chunk_rows).total;
+  return KD_OK;
+}
+
+kd_status kd_full_kl_fwd(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask, float tau,
+                         int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt, float* kl, float* lse_s,
+                         float* lse_t, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  KD_TRY(check_common(T, d, V, dt, tau));
+  KD_TRY(check_common(T, dt_hidden, V, dt, tau));
+  if (T == 0) return KD_OK;
+  KD_TRY(need(H, "H"));
+  KD_TRY(need(Ws, "Ws"));
+  KD_TRY(need(Ht, "Ht"));
+  KD_TRY(need(Wt, "Wt"));
+  KD_TRY(need(kl, "kl"));
+  KD_TRY(need(lse_s, "lse_s"));
+  KD_TRY(need(lse_t, "lse_t"));
+  KD_TRY(need_align(H, 16, "H"));
+  KD_TRY(need_align(Ws, 16, "Ws"));
+  KD_TRY(need_align(Ht, 16, "Ht"));
+  KD_TRY(need_align(Wt, 16, "Wt"));
+  KD_TRY(need_align(kl, 4, "kl"));
+  KD_TRY(need_align(lse_s, 4, "lse_s"));
+  KD_TRY(need_align(lse_t, 4, "lse_t"));
+  const int elem = elem_of(dt);
+  const FullPlan p = plan_full(T, d, V, elem, 0);
+  KD_TRY(check_workspace(workspace, workspace_bytes, p.fwd_total));
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
+  float* part = at<float>(workspace, p.o_part);
+  KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
+  kd::FullFwdArgs a{};
+  a.H = static_cast<const char*>(H);
+  a.Ws = static_cast<const char*>(Ws);
+  a.Ht = static_cast<const char*>(Ht);
+  a.Wt = static_cast<const char*>(Wt);
+  a.c = c;
+  a.part = part;
+  a.part_stride = T;
+  a.d = d;
+  a.dt = dt_hidden;
+  a.V = V;
+  a.nrb = p.nrb;
+  a.S = p.S;
+  a.ntiles = p.ntiles;
+  a.c2 = (float)(1.4426950408889634 / (double)tau);
+  KD_LAUNCH("full_fwd_tile", st, kd::launch_full_fwd(elem, a, st));
+  KD_LAUNCH("full_combine", st, kd::launch_full_combine(part, p.S, T, c, mask, T, kl, lse_s, lse_t, st));
+  return KD_OK;
+}
+
+kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask, float tau,
+                         int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt, const float* lse_s,
+                         const float* lse_t, const float* grad_kl, void* dH, float* dWs, int64_t chunk_rows,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  KD_TRY(check_common(T, d, V, dt, tau));
+  KD_TRY(check_common(T, dt_hidden, V, dt, tau));
+  KD_TRY(need(dWs, "dWs"));
+  KD_TRY(need_align(dWs, 16, "dWs"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    KD_LAUNCH("fill_zero", st, kd::launch_fill_zero(dWs, d * V * 4, st));
+    return KD_OK;
+  }
+  KD_TRY(need(H, "H"));
+  KD_TRY(need(Ws, "Ws"));
+  KD_TRY(need(Ht, "Ht"));
+  KD_TRY(need(Wt, "Wt"));
+  KD_TRY(need(lse_s, "lse_s"));
+  KD_TRY(need(lse_t, "lse_t"));
+  KD_TRY(need(grad_kl, "grad_kl"));
+  KD_TRY(need(dH, "dH"));
+  KD_TRY(need_align(H, 16, "H"));
+  KD_TRY(need_align(Ws, 16, "Ws"));
+  KD_TRY(need_align(Ht, 16, "Ht"));
+  KD_TRY(need_align(Wt, 16, "Wt"));
+  KD_TRY(need_align(dH, 16, "dH"));
+  KD_TRY(need_align(lse_s, 4, "lse_s"));
+  KD_TRY(need_align(lse_t, 4, "lse_t"));
+  KD_TRY(need_align(grad_kl, 4, "grad_kl"));
+  if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
+  const int elem = elem_of(dt);
+  const FullPlan p = plan_full(T, d, V, elem, chunk_rows);
+  KD_TRY(check_workspace(workspace, workspace_bytes, p.total));
+
+  kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
+  KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
+  KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * elem, dH, st));
+
+  const ChunkPlan& ch = p.ch;
+  char* dz = at<char>(workspace, ch.o_dz);
+  char* hT = at<char>(workspace, ch.o_hT);
+  float* dhp = at<float>(workspace, ch.o_dhp);
+  const int64_t nchunks = cdiv(T, ch.C);
+  for (int64_t k = 0; k < nchunks; ++k) {
+    const int64_t c0 = k * ch.C;
+    kd::FullDzArgs za{};
+    za.H = static_cast<const char*>(H);
+    za.Ws = static_cast<const char*>(Ws);
+    za.Ht = static_cast<const char*>(Ht);
+    za.Wt = static_cast<const char*>(Wt);
+    za.c = c;
+    za.lse_s = lse_s;
+    za.lse_t = lse_t;
+    za.g = grad_kl;
+    za.dz = dz;
+    za.ldz = ch.ldz;
+    za.c0 = c0;
+    za.C = ch.C;
+    za.d = d;
+    za.dt = dt_hidden;
+    za.V = V;
+    za.nrb = ch.nrb_c;
+    za.ntiles = p.ntiles;
+    za.S = splits_for(ch.nrb_c, p.ntiles);
+    za.c2 = (float)(1.4426950408889634 / (double)tau);
+    za.inv_tau = 1.0f / tau;
+    KD_LAUNCH("full_dz_tile", st, kd::launch_full_dz(elem, za, st));
+    KD_LAUNCH("gather_transpose", st, kd::launch_gather_transpose(H, elem, d, c, c0, ch.C, hT, st));
+    kd::DhArgs ha{};
+    ha.dz = dz;
+    ha.W = static_cast<const char*>(Ws);
+    ha.part = dhp;
+    ha.count = c.count;
+    ha.c0 = c0;
+    ha.C = ch.C;
+    ha.ldz = ch.ldz;
+    ha.d = d;
+    ha.V = V;
+    ha.nrb = ch.nrb_dh;
+    ha.ncb = ch.ncb_dh;
+    ha.S = ch.S_dh;
+    KD_LAUNCH("dh_tile", st, kd::launch_dh(elem, ha, st));
+    KD_LAUNCH("reduce_dh", st, kd::launch_reduce_dh(dhp, ch.S_dh, ch.C, d, c, c0, dH, elem, st));
+    kd::DwArgs wa{};
+    wa.hT = hT;
+    wa.dz = dz;
+    wa.dW = dWs;
+    wa.count = c.count;
+    wa.c0 = c0;
+    wa.C = ch.C;
+    wa.ldz = ch.ldz;
+    wa.d = d;
+    wa.V = V;
+    wa.nrb = ch.nrb_dw;
+    wa.ncb = ch.ncb_dw;
+    wa.accumulate = k > 0;
+    KD_LAUNCH("dw_tile", st, kd::launch_dw(elem, wa, st));
+  }
+  return KD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// Internal interface between the C-ABI layer (kd_api.cpp) and the kernels.
+// Every launcher enqueues on the given stream and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kd {
+
+constexpr int kTileN = 256;      // vocabulary columns per tile (top-K kernels, dW)
+constexpr int kTileNFull = 128;  // vocabulary columns per tile (dual-accumulator kernels)
+constexpr int kTileM = 256;      // token rows per tile
+
+// Per-row teacher data of the top-K loss, written by the prep kernel for
+// every valid row t (row-major [T][K], sorted by vocabulary index).
+struct TopkRowData {
+  int32_t* idx;     // cached indices, ascending
+  uint16_t* perm;   // original position k of each sorted entry
+  float* p;         // teacher probability of each sorted entry
+  float* ent;       // [T] sum_k p_k log p_k
+};
+
+struct Compact {
+  int32_t* rows;   // [T] original row of each valid row, in order
+  int32_t* count;  // [1] number of valid rows
+};
+
+// ---------------------------------------------------------------- small kernels
+hipError_t launch_compact(const uint8_t* mask, int64_t T, Compact c, hipStream_t st);
+hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8_t* mask, int64_t T, int64_t K,
+                            float tau, TopkRowData rd, float* z_topk, hipStream_t st);
+hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
+                               const float* ent, int64_t T, float tau, float* kl, float* lse, hipStream_t st);
+hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
+                               int64_t T, float* kl, float* lse_s, float* lse_t, hipStream_t st);
+// H^T of one chunk of compacted rows: out[j][i] = H[rows[c0 + i]][j] for
+// i < valid rows of the chunk, 0 up to C.
+hipError_t launch_gather_transpose(const void* H, int elem, int64_t d, Compact c, int64_t c0, int64_t C, void* out,
+                                   hipStream_t st);
+// dH[rows[c0 + i]] = sum_s part[s][i] (converted to the element type)
+hipError_t launch_reduce_dh(const float* part, int S, int64_t C, int64_t d, Compact c, int64_t c0, void* dH,
+                            int elem, hipStream_t st);
+hipError_t launch_zero_masked_rows(const uint8_t* mask, int64_t T, int64_t row_bytes, void* out, hipStream_t st);
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);
+
+// ---------------------------------------------------------------- top-K tiles
+struct TopkFwdArgs {
+  const char* H;  // [T][d]
+  const char* W;  // [d][V]
+  Compact c;
+  TopkRowData rd;
+  float* z_topk;  // nullable
+  float* part;    // [S][part_stride][4]
+  int64_t part_stride;
+  int64_t d, V, K;
+  int nrb, S, ntiles;
+  float c2;  // log2(e) / tau
+};
+hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st);
+
+struct TopkDzArgs {
+  const char* H;
+  const char* W;
+  Compact c;
+  TopkRowData rd;
+  const float* lse;
+  const float* g;
+  char* dz;        // [C][ldz] chunk of dZ
+  int64_t ldz;     // padded vocabulary (multiple of the tile width)
+  int64_t c0, C;   // first compacted row of the chunk, chunk capacity
+  int64_t d, V, K;
+  int nrb, S, ntiles;
+  float c2, inv_tau;
+};
+hipError_t launch_topk_dz(int elem, const TopkDzArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- full-vocabulary tiles
+struct FullFwdArgs {
+  const char* H;   // [T][d]
+  const char* Ws;  // [d][V]
+  const char* Ht;  // [T][dt]
+  const char* Wt;  // [dt][V]
+  Compact c;
+  float* part;     // [S][part_stride][8]
+  int64_t part_stride;
+  int64_t d, dt, V;
+  int nrb, S, ntiles;
+  float c2;
+};
+hipError_t launch_full_fwd(int elem, const FullFwdArgs& a, hipStream_t st);
+
+struct FullDzArgs {
+  const char* H;
+  const char* Ws;
+  const char* Ht;
+  const char* Wt;
+  Compact c;
+  const float* lse_s;
+  const float* lse_t;
+  const float* g;
+  char* dz;
+  int64_t ldz, c0, C;
+  int64_t d, dt, V;
+  int nrb, S, ntiles;
+  float c2, inv_tau;
+};
+hipError_t launch_full_dz(int elem, const FullDzArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- gradient contractions
+// part[s][i][j] = sum over the s-th vocabulary range of dz[i][v] * W[j][v]
+struct DhArgs {
+  const char* dz;  // [C][ldz]
+  const char* W;   // [d][V]
+  float* part;     // [S][C][d]
+  const int32_t* count;
+  int64_t c0, C, ldz, d, V;
+  int nrb, ncb, S;
+};
+hipError_t launch_dh(int elem, const DhArgs& a, hipStream_t st);
+
+// dW[j][v] (+)= sum_i hT[j][i] * dz[i][v]
+struct DwArgs {
+  const char* hT;  // [d][C]
+  const char* dz;  // [C][ldz]
+  float* dW;       // [d][V]
+  const int32_t* count;
+  int64_t c0, C, ldz, d, V;
+  int nrb, ncb;
+  int accumulate;
+};
+hipError_t launch_dw(int elem, const DwArgs& a, hipStream_t st);
+
+}  // namespace kd

@@ -1,0 +1,359 @@
+// Per-row and elementwise kernels around the tile contractions.
+//
+//   compact        valid-row list from the mask, in row order (masked rows
+//                  skip all contraction work and are never read)
+//   topk_prep      teacher side of each valid row, from "Efficient Knowledge
+//                  Distillation for LLMs: Offline Top-K Logits and a Fused
+//                  Chunked KL Loss", §3 "Offline distillation": the teacher
+//                  terms need the K cached entries only.  p = softmax(A / tau),
+//                  sum p log p, and the (index, p, position) triples sorted by
+//                  index so the tile epilogue can gather with one cursor.
+//   *_combine      merge the per-split running max / sum partials into the
+//                  row's log Z and KL (§3: each row keeps a scalar log Z)
+//   gather_transpose, reduce_dh, zero_masked_rows, fill_zero: chunk plumbing
+//                  of the backward pass
+#include <stdint.h>
+
+#include "kd_gemm.h"
+#include "kd_launch.h"
+
+namespace kd {
+
+namespace {
+
+constexpr int kCompactThreads = 1024;
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <int NT>
+__device__ inline float block_max(float v, float* red) {
+  v = wave_max(v);
+  if constexpr (NT > 64) {
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) v = fmaxf(v, red[i]);
+  }
+  return v;
+}
+template <int NT>
+__device__ inline float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if constexpr (NT > 64) {
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) v += red[i];
+  }
+  return v;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ compaction
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(const uint8_t* mask, long T, int32_t* rows,
+                                                                  int32_t* count) {
+  __shared__ int sums[kCompactThreads];
+  const long per = (T + kCompactThreads - 1) / kCompactThreads;
+  const long b = (long)threadIdx.x * per, e = min(T, b + per);
+  int n = 0;
+  for (long t = b; t < e; ++t) n += (mask == nullptr || mask[t] != 0);
+  sums[threadIdx.x] = n;
+  __syncthreads();
+  for (int off = 1; off < kCompactThreads; off <<= 1) {
+    const int v = threadIdx.x >= off ? sums[threadIdx.x - off] : 0;
+    __syncthreads();
+    sums[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int pos = sums[threadIdx.x] - n;
+  for (long t = b; t < e; ++t)
+    if (mask == nullptr || mask[t] != 0) rows[pos++] = (int32_t)t;
+  if (threadIdx.x == kCompactThreads - 1) *count = sums[kCompactThreads - 1];
+}
+
+hipError_t launch_compact(const uint8_t* mask, int64_t T, Compact c, hipStream_t st) {
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(kCompactThreads), 0, st, mask, (long)T, c.rows, c.count);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ teacher prep
+// One workgroup per row.  Dynamic LDS: KP sort keys (64-bit: biased index in
+// the high word, position k in the low word) and K probabilities.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_prep_kernel(const float* logits, const int32_t* idx, const uint8_t* mask,
+                                                       int K, int KP, float inv_tau, TopkRowData rd, float* z_topk) {
+  extern __shared__ __attribute__((aligned(16))) char sm[];
+  __shared__ float red[NT / 64 > 0 ? NT / 64 : 1];
+  uint64_t* key = reinterpret_cast<uint64_t*>(sm);
+  float* p = reinterpret_cast<float*>(key + KP);
+  const long t = blockIdx.x;
+  const long base = t * K;
+  if (z_topk)
+    for (int k = threadIdx.x; k < K; k += NT) z_topk[base + k] = 0.f;
+  if (mask != nullptr && mask[t] == 0) return;
+
+  // p = softmax(A_t / tau) over the K cached entries, and sum p log p
+  float mx = -INFINITY;
+  for (int k = threadIdx.x; k < K; k += NT) {
+    const float a = logits[base + k] * inv_tau;
+    p[k] = a;
+    mx = fmaxf(mx, a);
+  }
+  mx = block_max<NT>(mx, red);
+  float s = 0.f;
+  for (int k = threadIdx.x; k < K; k += NT) s += expf(p[k] - mx);
+  s = block_sum<NT>(s, red);
+  const float lz = mx + logf(s);
+  float ent = 0.f;
+  for (int k = threadIdx.x; k < K; k += NT) {
+    const float lp = p[k] - lz;
+    const float pk = expf(lp);
+    p[k] = pk;
+    ent = fmaf(pk, lp, ent);
+  }
+  ent = block_sum<NT>(ent, red);
+
+  // sort (index, position) pairs by index; ties keep position order
+  for (int j = threadIdx.x; j < KP; j += NT)
+    key[j] = j < K ? ((uint64_t)((uint32_t)idx[base + j] ^ 0x80000000u) << 32) | (uint32_t)j : ~0ull;
+  for (int size = 2; size <= KP; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < (KP >> 1); i += NT) {
+        const int lo = 2 * stride * (i / stride) + (i % stride);
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t x = key[lo], y = key[hi];
+        if ((x > y) == up) {
+          key[lo] = y;
+          key[hi] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < K; j += NT) {
+    const uint64_t kv = key[j];
+    const uint32_t k = (uint32_t)(kv & 0xffffffffu);
+    rd.idx[base + j] = (int32_t)((uint32_t)(kv >> 32) ^ 0x80000000u);
+    rd.perm[base + j] = (uint16_t)k;
+    rd.p[base + j] = p[k];
+  }
+  if (threadIdx.x == 0) rd.ent[t] = ent;
+}
+
+hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8_t* mask, int64_t T, int64_t K,
+                            float tau, TopkRowData rd, float* z_topk, hipStream_t st) {
+  int KP = 1;
+  while (KP < K) KP <<= 1;
+  const size_t shm = (size_t)KP * 8 + (size_t)K * 4;
+  const float inv_tau = 1.0f / tau;
+  const dim3 grid((unsigned)T);
+  if (shm > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_prep_kernel<256>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+  }
+  if (K <= 64)
+    hipLaunchKernelGGL(topk_prep_kernel<64>, grid, dim3(64), shm, st, logits, idx, mask, (int)K, KP, inv_tau, rd,
+                       z_topk);
+  else
+    hipLaunchKernelGGL(topk_prep_kernel<256>, grid, dim3(256), shm, st, logits, idx, mask, (int)K, KP, inv_tau, rd,
+                       z_topk);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ combines
+// Thread j: (a) zero kl/lse of row j if it is masked, (b) if j is a valid
+// compacted row, merge its S partials (m2, l, x) in split order.
+__global__ void topk_combine_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask,
+                                    const float* ent, long T, float inv_tau, float* kl, float* lse) {
+  const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= T) return;
+  if (mask != nullptr && mask[j] == 0) {
+    kl[j] = 0.f;
+    lse[j] = 0.f;
+  }
+  if (j >= *c.count) return;
+  const float4* pp = reinterpret_cast<const float4*>(part);
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pp[(long)s * stride + j].x);
+  float l = 0.f, x = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float4 q = pp[(long)s * stride + j];
+    l += q.y * exp2f(q.x - M);
+    x += q.z;
+  }
+  const long t = c.rows[j];
+  const float L = (M + log2f(l)) * kLn2;
+  lse[t] = L;
+  kl[t] = ent[t] - x * inv_tau + L;
+}
+
+hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
+                               const float* ent, int64_t T, float tau, float* kl, float* lse, hipStream_t st) {
+  const dim3 grid((unsigned)((T + 255) / 256));
+  hipLaunchKernelGGL(topk_combine_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, ent, (long)T,
+                     1.0f / tau, kl, lse);
+  return hipGetLastError();
+}
+
+// Partials per (split, row): (ms, ls, mt, lt), (R, -, -, -) in base 2.
+__global__ void full_combine_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask, long T,
+                                    float* kl, float* lse_s, float* lse_t) {
+  const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= T) return;
+  if (mask != nullptr && mask[j] == 0) {
+    kl[j] = 0.f;
+    lse_s[j] = 0.f;
+    lse_t[j] = 0.f;
+  }
+  if (j >= *c.count) return;
+  const float4* pp = reinterpret_cast<const float4*>(part);
+  float Ms = -INFINITY, Mt = -INFINITY;
+  for (int s = 0; s < S; ++s) {
+    const float4 q = pp[2 * ((long)s * stride + j)];
+    Ms = fmaxf(Ms, q.x);
+    Mt = fmaxf(Mt, q.z);
+  }
+  float ls = 0.f, lt = 0.f, R = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float4 q = pp[2 * ((long)s * stride + j)];
+    const float r = pp[2 * ((long)s * stride + j) + 1].x;
+    ls += q.y * exp2f(q.x - Ms);
+    const float f = exp2f(q.z - Mt);
+    lt += q.w * f;
+    R += r * f;
+  }
+  const long t = c.rows[j];
+  const float Ls2 = Ms + log2f(ls), Lt2 = Mt + log2f(lt);
+  lse_s[t] = Ls2 * kLn2;
+  lse_t[t] = Lt2 * kLn2;
+  kl[t] = (R / lt - Lt2 + Ls2) * kLn2;
+}
+
+hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
+                               int64_t T, float* kl, float* lse_s, float* lse_t, hipStream_t st) {
+  const dim3 grid((unsigned)((T + 255) / 256));
+  hipLaunchKernelGGL(full_combine_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, (long)T, kl,
+                     lse_s, lse_t);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ chunk plumbing
+// out[j][i] = H[rows[c0 + i]][j] for i < M (valid rows of the chunk), 0 for
+// M <= i < C.  64 x 64 tiles through LDS.
+template <typename U>
+__global__ __launch_bounds__(256) void gather_transpose_kernel(const U* H, long d, Compact c, long c0, long C,
+                                                               U* out) {
+  __shared__ U tile[64][65];
+  const long M = min(C, (long)*c.count - c0);
+  const long i0 = (long)blockIdx.x * 64, j0 = (long)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int ii = ty; ii < 64; ii += 4) {
+    const long i = i0 + ii, j = j0 + tx;
+    U v = 0;
+    if (i < M && j < d) v = H[(long)c.rows[c0 + i] * d + j];
+    tile[ii][tx] = v;
+  }
+  __syncthreads();
+  for (int jj = ty; jj < 64; jj += 4) {
+    const long j = j0 + jj, i = i0 + tx;
+    if (j < d && i < C) out[j * C + i] = tile[tx][jj];
+  }
+}
+
+hipError_t launch_gather_transpose(const void* H, int elem, int64_t d, Compact c, int64_t c0, int64_t C, void* out,
+                                   hipStream_t st) {
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((d + 63) / 64));
+  if (elem == 2)
+    hipLaunchKernelGGL(gather_transpose_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)H, (long)d, c,
+                       (long)c0, (long)C, (uint16_t*)out);
+  else
+    hipLaunchKernelGGL(gather_transpose_kernel<uint32_t>, grid, dim3(256), 0, st, (const uint32_t*)H, (long)d, c,
+                       (long)c0, (long)C, (uint32_t*)out);
+  return hipGetLastError();
+}
+
+// dH[rows[c0 + i]][j..j+3] = sum over s of part[s][i][j..j+3], in split order.
+template <int ELEM>
+__global__ void reduce_dh_kernel(const float* part, int S, long C, long d, Compact c, long c0, void* dH) {
+  const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index within [C][d]
+  const long d4 = d / 4;
+  const long i = q / d4, j = (q % d4) * 4;
+  const long M = min(C, (long)*c.count - c0);
+  if (i >= M) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < S; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(part + ((long)s * C + i) * d + j);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  const long t = c.rows[c0 + i];
+  if constexpr (ELEM == 2) {
+    uint2 o;
+    o.x = Bf16::pack2(acc.x, acc.y);
+    o.y = Bf16::pack2(acc.z, acc.w);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dH) + t * d + j) = o;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(dH) + t * d + j) = acc;
+  }
+}
+
+hipError_t launch_reduce_dh(const float* part, int S, int64_t C, int64_t d, Compact c, int64_t c0, void* dH,
+                            int elem, hipStream_t st) {
+  const long n = C * (d / 4);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (elem == 2)
+    hipLaunchKernelGGL(reduce_dh_kernel<2>, grid, dim3(256), 0, st, part, S, (long)C, (long)d, c, (long)c0, dH);
+  else
+    hipLaunchKernelGGL(reduce_dh_kernel<4>, grid, dim3(256), 0, st, part, S, (long)C, (long)d, c, (long)c0, dH);
+  return hipGetLastError();
+}
+
+__global__ void zero_masked_rows_kernel(const uint8_t* mask, long T, long row16, u32x4_t* out) {
+  const long q = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long t = q / row16;
+  if (t >= T || mask[t] != 0) return;
+  out[q] = zero4();
+}
+
+hipError_t launch_zero_masked_rows(const uint8_t* mask, int64_t T, int64_t row_bytes, void* out, hipStream_t st) {
+  if (mask == nullptr || T == 0) return hipSuccess;
+  const long row16 = row_bytes / 16;
+  const long n = T * row16;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  hipLaunchKernelGGL(zero_masked_rows_kernel, grid, dim3(256), 0, st, mask, (long)T, row16, (u32x4_t*)out);
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(u32x4_t* p, long n16) {
+  for (long q = (long)blockIdx.x * blockDim.x + threadIdx.x; q < n16; q += (long)gridDim.x * blockDim.x)
+    p[q] = zero4();
+}
+
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st) {
+  const long n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const long blocks = min(4096L, (n16 + 255) / 256);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (u32x4_t*)p, n16);
+  return hipGetLastError();
+}
+
+}  // namespace kd

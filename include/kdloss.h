@@ -1,0 +1,185 @@
+/*
+ * libkdloss: fused, chunked KL distillation loss over a language model's
+ * output head, for AMD Instinct MI355X (gfx950).
+ *
+ * The loss is the forward KL divergence KL(p_teacher || q_student) of
+ * "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and a Fused
+ * Chunked KL Loss" (§1; §3 "Online distillation").  Two variants:
+ *
+ *  - top-K (§3 "Offline distillation"): the teacher is a cached top-K per
+ *    token.  Its K logits are renormalised at temperature tau; the student's
+ *    log-probabilities are gathered at the K cached indices, and log Z over the
+ *    whole vocabulary is the only full-vocabulary reduction.
+ *  - full vocabulary (KDFlow abstract, thelatestinai.com/papers/2606.20005):
+ *    teacher logits are recomputed from the teacher's final hidden states
+ *    through a frozen copy of the teacher's output head.
+ *
+ * Both are fused with the output projection Z = H.W (§3 "Fused chunked KL"):
+ * logit tiles live on chip only, the full [T, V] logit tensor is never
+ * written, and the backward pass recomputes the projection chunk by chunk of
+ * token rows (one extra projection per chunk, as in output-head gradient
+ * checkpointing).
+ *
+ * Definitions, per valid row t (s = z / tau with z = H_t . W, L_t = logsumexp(s)):
+ *   top-K:  p = softmax(A_t / tau) over the K entries;
+ *           KL_t = sum_k p_k (log p_k - s[I_tk] + L_t)
+ *           dZ_t = (g_t / tau) (softmax(s) - scatter_add(I_t, p))
+ *   full:   u = (Ht_t . Wt) / tau, p = softmax(u), Lt = logsumexp(u);
+ *           KL_t = sum_v p_v (u_v - s_v) - Lt + L_t
+ *           dZ_t = (g_t / tau) (softmax(s) - p)
+ *   dH = dZ . W^T, dW = H^T . dZ.  There is no tau^2 factor; the caller may
+ *   scale g.  Duplicate top-K indices add (scatter-add).
+ *
+ * Conventions shared by every call:
+ *  - All tensors are dense and row-major.  H [T,d], W [d,V], Ht [T,dt],
+ *    Wt [dt,V], topk_idx [T,K] int32, topk_logits [T,K] float32, mask [T]
+ *    uint8 (1 = valid row, 0 = masked; NULL = all rows valid), grad_kl [T]
+ *    float32, kl/lse [T] float32, z_topk [T,K] float32, dH [T,d] in the input
+ *    dtype, dW [d,V] float32.  A weight stored as nn.Linear's [V,d] must be
+ *    transposed by the caller.
+ *  - dtype KD_BF16: H, W, Ht, Wt and dH are bfloat16; products accumulate in
+ *    float32.  KD_F32: they are float32 and the contraction runs on fp32
+ *    matrix cores.  kl, lse, grad_kl, dW are float32 in both cases.
+ *  - d, dt and V must be multiples of 8 (bf16) or 4 (fp32); 1 <= K <= V and
+ *    K <= KD_MAX_K.  Otherwise the call returns KD_ERR_UNSUPPORTED.
+ *  - Pointers to H, W, Ht, Wt, dH, dW must be 16-byte aligned, all other
+ *    arrays 4-byte aligned, the workspace 256-byte aligned
+ *    (KD_ERR_ALIGNMENT).
+ *  - Masked rows get kl = 0, lse = 0, z_topk = 0 and dH = 0, add nothing to
+ *    dW and are never read beyond mask[t] (NaN or out-of-range indices there
+ *    do not leak).  Their flops are skipped: valid rows are compacted on the
+ *    device.
+ *  - Ownership: the caller allocates every buffer, including the workspace.
+ *    The library never allocates device memory, so the extra device memory of
+ *    a call is exactly its workspace.  The library keeps no state between
+ *    calls except the optional profiling record (kd_profile_*), is safe to
+ *    call from several host threads, and is asynchronous: each call enqueues
+ *    its kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *    returns without synchronising.
+ *  - Errors: arguments are checked on the host before any kernel is
+ *    enqueued; a failed check returns its status and enqueues nothing.  A
+ *    failed launch returns KD_ERR_HIP.  kd_last_error() gives a message for
+ *    the last failure on the calling thread.  Index range is not checked on
+ *    the device: an index outside [0, V) in a valid row is ignored by the
+ *    gather (its teacher probability still counts in the teacher terms).
+ *  - T = 0: the forward calls enqueue nothing; the backward calls set dW to
+ *    zero (the gradient of an empty sum) and touch nothing else.
+ *  - Deterministic: split reductions run in a fixed order, so the same call
+ *    on the same inputs gives the same bits.
+ */
+#ifndef KDLOSS_H
+#define KDLOSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KD_MAX_K 8192
+#define KD_DEFAULT_CHUNK_ROWS 4096
+
+typedef enum kd_status {
+  KD_OK = 0,
+  KD_ERR_INVALID_ARG = 1,          /* null pointer, negative size, bad tau, K < 1 ... */
+  KD_ERR_UNSUPPORTED = 2,          /* valid but not handled: K > KD_MAX_K, d or V not a multiple of 8/4 */
+  KD_ERR_ALIGNMENT = 3,            /* a pointer is not aligned as required */
+  KD_ERR_WORKSPACE_TOO_SMALL = 4,  /* workspace_bytes below the size query's answer */
+  KD_ERR_INDEX_OUT_OF_RANGE = 5,   /* reserved for an index check; not returned by the calls below */
+  KD_ERR_HIP = 6                   /* a HIP launch or runtime call failed */
+} kd_status;
+
+typedef enum kd_dtype { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
+
+/* ---------------------------------------------------------------- top-K */
+
+/* Workspace bytes that both kd_topk_kl_fwd and kd_topk_kl_bwd need for this
+ * shape (one size serves both calls).  chunk_rows: token rows per backward
+ * chunk (0 = KD_DEFAULT_CHUNK_ROWS; rounded up to a multiple of 256; clamped
+ * to the rows present).  The size is affine in T for a fixed chunk size: the
+ * per-row part is about 10*K + 32 bytes, the rest does not depend on T.
+ * Returns KD_OK and writes *bytes, or an argument error. */
+kd_status kd_topk_kl_workspace_size(int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                                    int64_t chunk_rows, size_t* bytes);
+
+/* Forward: per-token KL and the saved log-normaliser.
+ *   H [T,d], W [d,V] (dtype dt); topk_idx [T,K]; topk_logits [T,K];
+ *   mask [T] or NULL; tau > 0 and finite.
+ *   kl [T] (out), lse [T] (out: L_t = logsumexp_v(z_tv / tau), kept for the
+ *   backward call), z_topk [T,K] (out, optional: the raw logits z at the
+ *   cached indices, NULL to skip).
+ * Logits are produced tile by tile on chip; a running max and sum give
+ * lse and the index-match epilogue gathers the K cached entries
+ * (§3 "Offline distillation" and "Fused chunked KL"). */
+kd_status kd_topk_kl_fwd(const void* H, const void* W, const int32_t* topk_idx,
+                         const float* topk_logits, const uint8_t* mask, float tau,
+                         int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                         float* kl, float* lse, float* z_topk,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward: dH [T,d] (dtype dt, overwritten) and dW [d,V] (float32,
+ * overwritten) for the upstream per-token gradient grad_kl [T] (the caller
+ * owns the reduction: a mean over N valid tokens passes 1/N).  lse must be
+ * the forward call's output for the same inputs.  Rows are processed in
+ * chunks of chunk_rows valid rows: each chunk recomputes its logit tiles,
+ * writes dZ for that chunk only, then runs dH = dZ.W^T and dW += H^T.dZ
+ * (§3 "Fused chunked KL": one extra output projection per chunk). */
+kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx,
+                         const float* topk_logits, const uint8_t* mask, float tau,
+                         int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                         const float* lse, const float* grad_kl,
+                         void* dH, float* dW, int64_t chunk_rows,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- full vocabulary */
+
+/* Workspace bytes for kd_full_kl_fwd and kd_full_kl_bwd (one size serves
+ * both).  dt_hidden is the teacher's hidden width. */
+kd_status kd_full_kl_workspace_size(int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                                    int64_t chunk_rows, size_t* bytes);
+
+/* Forward: kl [T], lse_s [T] (student), lse_t [T] (teacher), all float32 out.
+ * Student logits H.Ws and teacher logits Ht.Wt are produced tile by tile
+ * side by side; a dual running max/sum and the running sum of
+ * p_v (u_v - s_v) give the KL without either [T,V] tensor. */
+kd_status kd_full_kl_fwd(const void* H, const void* Ws, const void* Ht, const void* Wt,
+                         const uint8_t* mask, float tau,
+                         int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                         float* kl, float* lse_s, float* lse_t,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward to the student only: dH [T,d] (dtype dt) and dWs [d,V] float32,
+ * both overwritten.  No gradient flows to Ht or the frozen Wt. */
+kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const void* Wt,
+                         const uint8_t* mask, float tau,
+                         int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                         const float* lse_s, const float* lse_t, const float* grad_kl,
+                         void* dH, float* dWs, int64_t chunk_rows,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- errors, version */
+
+const char* kd_status_string(kd_status s);
+/* Message for the last failed call on the calling thread ("" if none). */
+const char* kd_last_error(void);
+/* Library version as major*10000 + minor*100 + patch. */
+int kd_version(void);
+
+/* ---------------------------------------------------------------- profiling
+ * While enabled, every kernel the library enqueues is bracketed by a pair of
+ * HIP events on the same stream.  kd_profile_count() waits for the recorded
+ * events and folds them into per-kernel totals; kd_profile_get() reads entry
+ * i: the kernel's name, its launch count and its summed duration in ms.
+ * kd_profile_reset() drops the record.  Not thread-safe against concurrent
+ * calls that profile. */
+kd_status kd_profile_enable(int on);
+int kd_profile_count(void);
+kd_status kd_profile_get(int i, const char** name, int64_t* launches, double* total_ms);
+kd_status kd_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDLOSS_H */

@@ -1,0 +1,178 @@
+"""The C-ABI boundary on the CPU: the library loads, exports what the header
+declares, sizes its workspace affinely in T, and rejects bad arguments on the
+host before any HIP call (so none of these tests touches a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdloss.h")
+
+kdl = pytest.importorskip("chunked_kl_loss_logit_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kdl.LIB_PATH):
+        pytest.fail("libkdloss.so is not built (run __graft_entry__.build())")
+    return kdl.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in kdloss.h but not exported"
+    assert sorted(kdl.EXPORTS) == names
+
+
+def test_status_strings_and_version(L):
+    for code, name in kdl._binding.STATUS.items():
+        assert L.kd_status_string(code).decode() == name
+    assert L.kd_version() == 10000
+
+
+# ---------------------------------------------------------------- workspace sizing
+def ws_topk(T, d=3072, V=128256, K=64, dt=kdl.KD_BF16, chunk=0):
+    out = ctypes.c_size_t()
+    st = kdl.lib().kd_topk_kl_workspace_size(T, d, V, K, dt, chunk, ctypes.byref(out))
+    return st, out.value
+
+
+def ws_full(T, d=3072, dtt=4096, V=128256, dt=kdl.KD_BF16, chunk=0):
+    out = ctypes.c_size_t()
+    st = kdl.lib().kd_full_kl_workspace_size(T, d, dtt, V, dt, chunk, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_zero_rows(L):
+    assert ws_topk(0) == (0, 0)
+    assert ws_full(0) == (0, 0)
+
+
+def test_workspace_is_affine_in_T_with_small_slope(L):
+    # extra device memory = the workspace: a constant (the chunk buffers) plus a
+    # per-token part (teacher data and split partials), never a [T, V] buffer
+    Ts = [16384, 65536, 262144]
+    sizes = [ws_topk(T)[1] for T in Ts]
+    slope = (sizes[2] - sizes[1]) / (Ts[2] - Ts[1])
+    assert slope <= 1024, slope  # bytes per token
+    assert slope >= 10 * 64      # at least the sorted teacher data
+    pred = sizes[1] + slope * (Ts[0] - Ts[1])
+    assert abs(pred - sizes[0]) / sizes[0] < 0.01
+    # a bf16 [T, V] buffer alone would be 250 KiB per token
+    assert sizes[2] < 262144 * 128256 * 2 / 40
+    fs = [ws_full(T)[1] for T in Ts]
+    assert (fs[2] - fs[1]) / (Ts[2] - Ts[1]) <= 1024
+
+
+def test_workspace_chunk_rows(L):
+    s_small = ws_topk(32768, chunk=1024)[1]
+    s_big = ws_topk(32768, chunk=8192)[1]
+    assert s_small < s_big
+    # chunk rows round up to 256 and clamp to the rows present
+    assert ws_topk(1000, chunk=100000)[1] == ws_topk(1000, chunk=1024)[1]
+    assert ws_topk(4096, chunk=300)[1] == ws_topk(4096, chunk=512)[1]
+
+
+# ---------------------------------------------------------------- argument errors
+FAKE = 0x10000  # 64 KiB: aligned to 256, never dereferenced (calls fail before any HIP call)
+
+
+def fwd(T=8, d=64, V=256, K=4, dt=kdl.KD_BF16, tau=1.0, H=FAKE, W=FAKE, idx=FAKE, lg=FAKE, kl=FAKE, lse=FAKE,
+        z=None, ws=FAKE, wsb=0):
+    L = kdl.lib()
+    vp = ctypes.c_void_p
+    return L.kd_topk_kl_fwd(vp(H), vp(W), vp(idx), vp(lg), None, ctypes.c_float(tau), T, d, V, K, dt, vp(kl),
+                            vp(lse), vp(z) if z else None, vp(ws) if ws else None, wsb, None)
+
+
+def bwd(T=8, d=64, V=256, K=4, dt=kdl.KD_BF16, tau=1.0, dH=FAKE, dW=FAKE, chunk=0, ws=FAKE, wsb=0, lse=FAKE):
+    L = kdl.lib()
+    vp = ctypes.c_void_p
+    return L.kd_topk_kl_bwd(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(tau), T, d, V, K, dt,
+                            vp(lse) if lse else None, vp(FAKE), vp(dH) if dH else None, vp(dW) if dW else None,
+                            chunk, vp(ws) if ws else None, wsb, None)
+
+
+def full_fwd(T=8, d=64, dtt=64, V=256, dt=kdl.KD_BF16, tau=1.0, Ht=FAKE, wsb=0):
+    L = kdl.lib()
+    vp = ctypes.c_void_p
+    return L.kd_full_kl_fwd(vp(FAKE), vp(FAKE), vp(Ht) if Ht else None, vp(FAKE), None, ctypes.c_float(tau), T, d,
+                            dtt, V, dt, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), wsb, None)
+
+
+def last_error():
+    return kdl.lib().kd_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), 1), (dict(K=300), 1), (dict(T=-1), 1), (dict(d=0), 1), (dict(V=0), 1),
+    (dict(tau=0.0), 1), (dict(tau=-1.0), 1), (dict(tau=math.nan), 1), (dict(tau=math.inf), 1),
+    (dict(dt=7), 1), (dict(H=0), 1), (dict(W=0), 1), (dict(idx=0), 1), (dict(lg=0), 1), (dict(kl=0), 1),
+    (dict(lse=0), 1),
+    (dict(d=60), 2), (dict(V=260), 2), (dict(V=20000, K=9000), 2), (dict(d=6, dt=kdl.KD_F32), 2),
+    (dict(H=FAKE + 8), 3), (dict(W=FAKE + 4), 3), (dict(kl=FAKE + 2), 3), (dict(z=FAKE + 1), 3),
+    (dict(ws=FAKE + 128, wsb=1 << 40), 3),
+    (dict(wsb=16), 4),
+])
+def test_topk_fwd_rejects(L, kw, code):
+    assert fwd(**kw) == code
+    assert last_error() != ""
+
+
+def test_fp32_allows_multiples_of_four(L):
+    # d = 12, V = 260 are fine for fp32 (4 per 16 bytes) but not bf16
+    assert fwd(d=12, V=260, dt=kdl.KD_F32, wsb=16) == 4  # reaches the workspace check
+    assert fwd(d=12, V=260, dt=kdl.KD_BF16, wsb=16) == 2
+
+
+def test_zero_rows_forward_is_a_noop(L):
+    assert fwd(T=0, H=0, W=0, idx=0, lg=0, kl=0, lse=0, ws=0) == 0
+    assert last_error() == ""
+    assert full_fwd(T=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dW=0), 1), (dict(dH=0), 1), (dict(lse=0), 1), (dict(chunk=-1), 1), (dict(dW=FAKE + 4), 3),
+    (dict(dH=FAKE + 8), 3), (dict(wsb=16), 4), (dict(tau=0.0), 1), (dict(K=0), 1),
+])
+def test_topk_bwd_rejects(L, kw, code):
+    assert bwd(**kw) == code
+
+
+def test_full_fwd_rejects(L):
+    assert full_fwd(Ht=0) == 1
+    assert full_fwd(dtt=60) == 2
+    assert full_fwd(tau=0.0) == 1
+    assert full_fwd(Ht=FAKE + 8) == 3
+    assert full_fwd(wsb=16) == 4
+
+
+def test_workspace_query_rejects(L):
+    assert ws_topk(8, K=0)[0] == 1
+    assert ws_topk(8, d=12)[0] == 2
+    assert L.kd_topk_kl_workspace_size(8, 64, 256, 4, 1, 0, None) == 1
+
+
+def test_profile_api_without_gpu(L):
+    assert L.kd_profile_enable(0) == 0
+    assert L.kd_profile_reset() == 0
+    assert L.kd_profile_count() == 0
+    assert L.kd_profile_get(0, None, None, None) == 1
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    H = torch.zeros(8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kdl._binding._ptr(H)

@@ -1,0 +1,72 @@
+"""GPU parity of the full-vocabulary loss (teacher logits recomputed through a
+frozen teacher head) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import kdinputs as G
+from oracle import kd_oracle as O
+from tests.gpu_util import assert_grad, assert_kl, assert_lse, run_full, say
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_all(inp):
+    kl, ls, lt = O.full_kl_forward(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], inp["mask"], inp["tau"])
+    dH, dW = O.full_kl_backward(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], inp["mask"], inp["tau"], inp["g"])
+    return dict(kl=kl, lse_s=ls, lse_t=lt, dH=dH, dW=dW)
+
+
+def check_all(got, want, inp, dtype):
+    T = inp["H"].shape[0]
+    v = np.ones(T, bool) if inp["mask"] is None else inp["mask"].numpy() != 0
+    assert_kl(got["kl"], want["kl"], dtype, v)
+    assert_lse(got["lse_s"], want["lse_s"], dtype, v)
+    assert_lse(got["lse_t"], want["lse_t"], dtype, v)
+    assert np.all(got["kl"][~v] == 0) and np.all(got["dH"][~v] == 0)
+    assert_grad(got["dH"], want["dH"], dtype, "dH")
+    assert_grad(got["dW"], want["dW"], dtype, "dWs")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("T,d,dt,V,tau,mask", [
+    (300, 136, 72, 1032, 1.0, "none"),
+    (513, 64, 128, 520, 0.8, "random10"),
+    (1, 40, 24, 264, 2.0, "none"),
+])
+def test_ragged_shapes(dtype, T, d, dt, V, tau, mask):
+    inp = G.make_full(T, d, dt, V, dtype, tau=tau, mask=mask, number=21, g="normal")
+    say(f"full ragged T={T} d={d} dt={dt} V={V} {dtype}")
+    check_all(run_full(inp), oracle_all(inp), inp, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_equal_heads_give_exact_zero(dtype):
+    # teacher and student run the same instructions on the same data
+    inp = G.make_full(300, 64, 64, 520, dtype, number=22, g="normal")
+    inp["Ht"], inp["Wt"] = inp["H"].clone(), inp["Ws"].clone()
+    say(f"full equal heads {dtype}")
+    got = run_full(inp)
+    assert np.all(got["kl"] == 0)
+    assert np.all(got["dH"] == 0) and np.all(got["dW"] == 0)
+
+
+def test_full_slice_at_head_width():
+    inp = G.make_full(256, 3072, 4096, 128256, torch.bfloat16, number=5, g="normal")
+    say("full slice T=256 d=3072 dt=4096 V=128256")
+    check_all(run_full(inp), oracle_all(inp), inp, torch.bfloat16)
+
+
+def test_full_t16384_sampled_rows():
+    p = G.PRESETS["full_vocab_t16384"]
+    inp = G.make_preset(p, g="normal")
+    say("full T=16384 sampled rows")
+    got = run_full(inp)
+    rng = np.random.default_rng(1)
+    rows = np.array(sorted(set(rng.choice(16384, 48, replace=False).tolist()) | {0, 255, 256, 16383}))
+    kl, ls, lt, dH = O.full_kl_rows(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], None, p.tau, inp["g"], rows)
+    assert_kl(got["kl"][rows], kl, torch.bfloat16)
+    assert_lse(got["lse_s"][rows], ls, torch.bfloat16)
+    assert_lse(got["lse_t"][rows], lt, torch.bfloat16)
+    assert_grad(got["dH"][rows], dH, torch.bfloat16, "dH rows")
+    assert np.all(np.isfinite(got["dW"]))
