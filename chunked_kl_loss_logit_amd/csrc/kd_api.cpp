@@ -403,6 +403,7 @@ kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx, 
     za.ldz = ch.ldz;
     za.c0 = c0;
     za.C = ch.C;
+    za.T = T;
     za.d = d;
     za.V = V;
     za.K = K;
@@ -565,6 +566,7 @@ kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const vo
     za.ldz = ch.ldz;
     za.c0 = c0;
     za.C = ch.C;
+    za.T = T;
     za.d = d;
     za.dt = dt_hidden;
     za.V = V;

@@ -7,24 +7,45 @@
 //                         the reduce kernel, so results are deterministic).
 //   dW      += H^T . dZ   [d, C] x [C, V]: H^T of the chunk is a gathered,
 //                         transposed copy (contiguous along the chunk's rows);
-//                         dZ is [rows][V] and goes through the transposing
-//                         column loader.  The first chunk stores, later chunks
-//                         add in place, so chunks act as a fixed-order split
-//                         over tokens.
+//                         dZ is [rows][V], n-contiguous.  The first chunk
+//                         stores, later chunks add in place, so chunks act as
+//                         a fixed-order split over tokens.
 // "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and a Fused
 // Chunked KL Loss", §3 "Fused chunked KL": per chunk, the backward pass costs
 // the recomputed projection plus these two products.
 #include "kd_gemm.h"
 #include "kd_launch.h"
+#include "kd_main.h"
 
 namespace kd {
 
-template <class E>
+namespace {
+
+template <int NBI>
+__device__ inline void f32_round(const Slots& sl, const f32x16_t (&acc)[4][4], float* dst, long ld, long row0,
+                                 long n0, long nrows, long ncols, bool accumulate) {
+  const StPair s0 = st_pair<0>(sl), s1 = st_pair<1>(sl);
+  stage_block<NBI, 4>(s0, s1, acc);
+  __syncthreads();
+  rmw_block_f32(s0, dst, ld, row0, n0 + NBI * 32, nrows, ncols, accumulate);
+  rmw_block_f32(s1, dst, ld, row0, n0 + 128 + NBI * 32, nrows, ncols, accumulate);
+  __syncthreads();
+}
+
+__device__ inline void store_tile_f32(const Slots& sl, const f32x16_t (&acc)[4][4], float* dst, long ld, long row0,
+                                      long n0, long nrows, long ncols, bool accumulate) {
+  f32_round<0>(sl, acc, dst, ld, row0, n0, nrows, ncols, accumulate);
+  f32_round<1>(sl, acc, dst, ld, row0, n0, nrows, ncols, accumulate);
+  f32_round<2>(sl, acc, dst, ld, row0, n0, nrows, ncols, accumulate);
+  f32_round<3>(sl, acc, dst, ld, row0, n0, nrows, ncols, accumulate);
+}
+
+}  // namespace
+
+template <class Main, class E>
 __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   constexpr int BN = 256;
-  using S = TileShape<BN>;
-  static_assert(Stage<BN>::kBytes <= S::kLds, "epilogue slice must fit the operand buffers");
-  __shared__ __attribute__((aligned(16))) char lds[S::kLds];
+  KD_DECLARE_SLOTS(sl);
 
   const long count = *a.count;
   const long M = min(a.C, count - a.c0);
@@ -37,118 +58,60 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   const long row0 = (long)rb * kBM, n0 = (long)cb * BN;
   if (row0 >= M) return;
 
-  // contraction over the vocabulary, split in S contiguous ranges; columns
-  // past V are never read from either operand (V is a whole number of chunks)
-  const long kza = a.V * E::kElem;
-  const long kwb = a.V * E::kElem;
-  const long nst = (kza + kStageBytes - 1) / kStageBytes;
+  // contraction over the first V columns of both operands, split in S ranges
+  Main mainloop;
+  mainloop.init(a.dz, [&](int r) -> const char* { return row0 + r < M ? a.dz + (row0 + r) * a.ldz * E::kElem : nullptr; },
+                a.W, [&](int r) -> const char* { return n0 + r < a.d ? a.W + (n0 + r) * a.V * E::kElem : nullptr; },
+                a.V);
+  const long nst = mainloop.nst;
   const long s0 = nst * sp / a.S, s1 = nst * (sp + 1) / a.S;
-
-  KRowLoader<kBM> al, bl;
-  al.init_q();
-  bl.init_q();
-#pragma unroll
-  for (int j = 0; j < KRowLoader<kBM>::kPer; ++j) {
-    const long i = row0 + al.row_of(j);
-    al.rp[j] = (i < M) ? a.dz + i * a.ldz * E::kElem : nullptr;
-    const long n = n0 + bl.row_of(j);
-    bl.rp[j] = (n < a.d) ? a.W + n * a.V * E::kElem : nullptr;
-  }
-
   f32x16_t acc[4][BN / 64];
-  zero_acc<BN>(acc);
-  contract<E, BN>(
-      lds, s0, s1, acc,
-      [&](long s) {
-        al.load(s * kStageBytes, kza);
-        bl.load(s * kStageBytes, kwb);
-      },
-      [&](char* buf) {
-        al.store(buf);
-        bl.store(buf + S::kABytes);
-      });
-
-  float* out = a.part + (long)sp * a.C * a.d;
-  float* st = reinterpret_cast<float*>(lds);
-#pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
-    stage_acc<BN>(st, acc, half);
-    __syncthreads();
-    rmw_slice_f32<BN / 2>(st, out, a.d, row0, n0 + half * (BN / 2), M, a.d, false);
-    __syncthreads();
-  }
+  mainloop.tile(sl, s0, s1, acc);
+  store_tile_f32(sl, acc, a.part + (long)sp * a.C * a.d, a.d, row0, n0, M, a.d, false);
 }
 
-template <class E>
+template <class Main, class E>
 __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   constexpr int BN = 256;
-  using S = TileShape<BN>;
-  static_assert(Stage<BN>::kBytes <= S::kLds, "epilogue slice must fit the operand buffers");
-  __shared__ __attribute__((aligned(16))) char lds[S::kLds];
+  KD_DECLARE_SLOTS(sl);
 
   const long count = *a.count;
-  const long M = max(0L, min(a.C, count - a.c0));  // contraction length: valid rows of the chunk
+  const long M = max(0L, min(a.C, count - a.c0));  // valid rows of the chunk
   if (M == 0 && a.accumulate) return;              // nothing to add
   int rb, cb;
   grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.ncb, 4, rb, cb);
   const long row0 = (long)rb * kBM, n0 = (long)cb * BN;
 
-  const long kb = M * E::kElem;
-  const long nst = (kb + kStageBytes - 1) / kStageBytes;
-
-  KRowLoader<kBM> al;
-  al.init_q();
-#pragma unroll
-  for (int j = 0; j < KRowLoader<kBM>::kPer; ++j) {
-    const long r = row0 + al.row_of(j);
-    al.rp[j] = (r < a.d) ? a.hT + r * a.C * E::kElem : nullptr;
-  }
-  NColLoader<E, BN> bl;
-  bl.base = a.dz + n0 * E::kElem;
-  bl.ld = a.ldz * E::kElem;
-  bl.N = a.V;
-  bl.n0 = n0;
-  bl.K = M;
-  constexpr int KS = kStageBytes / E::kElem;
-
+  // contraction over the chunk's rows, rounded up to 32: both buffers hold
+  // zeros between M and the end of their last 256-row tile
+  const long K = (M + 31) / 32 * 32;
+  Main mainloop;
+  mainloop.init(a.hT, [&](int r) -> const char* { return row0 + r < a.d ? a.hT + (row0 + r) * a.C * E::kElem : nullptr; },
+                a.dz, a.ldz * E::kElem, a.V, K);
   f32x16_t acc[4][BN / 64];
-  zero_acc<BN>(acc);
-  contract<E, BN>(
-      lds, 0, nst, acc,
-      [&](long s) {
-        al.load(s * kStageBytes, kb);
-        bl.load(s * KS);
-      },
-      [&](char* buf) {
-        al.store(buf);
-        bl.store(buf + S::kABytes);
-      });
-
-  float* st = reinterpret_cast<float*>(lds);
-#pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
-    stage_acc<BN>(st, acc, half);
-    __syncthreads();
-    rmw_slice_f32<BN / 2>(st, a.dW, a.V, row0, n0 + half * (BN / 2), a.d, a.V, a.accumulate != 0);
-    __syncthreads();
-  }
+  mainloop.tile(sl, n0, acc);
+  store_tile_f32(sl, acc, a.dW, a.V, row0, n0, a.d, a.V, a.accumulate != 0);
 }
 
 hipError_t launch_dh(int elem, const DhArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.ncb * a.S), block(kThreads);
-  if (elem == 2)
-    hipLaunchKernelGGL(dh_kernel<Bf16>, grid, block, 0, st, a);
+  if (elem == 2 && a.V % kDmaKs == 0 && fits32(a.C * a.ldz * 2) && fits32(a.d * a.V * 2))
+    hipLaunchKernelGGL((dh_kernel<DmaNT<256>, Bf16>), grid, block, 0, st, a);
+  else if (elem == 2)
+    hipLaunchKernelGGL((dh_kernel<GenNT<Bf16, 256>, Bf16>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(dh_kernel<F32>, grid, block, 0, st, a);
+    hipLaunchKernelGGL((dh_kernel<GenNT<F32, 256>, F32>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dw(int elem, const DwArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.ncb), block(kThreads);
-  if (elem == 2)
-    hipLaunchKernelGGL(dw_kernel<Bf16>, grid, block, 0, st, a);
+  if (elem == 2 && fits32(a.C * a.ldz * 2) && fits32(a.d * a.C * 2))
+    hipLaunchKernelGGL((dw_kernel<DmaNN<256>, Bf16>), grid, block, 0, st, a);
+  else if (elem == 2)
+    hipLaunchKernelGGL((dw_kernel<GenNN<Bf16, 256>, Bf16>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(dw_kernel<F32>, grid, block, 0, st, a);
+    hipLaunchKernelGGL((dw_kernel<GenNN<F32, 256>, F32>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -11,6 +11,9 @@ constexpr int kTileN = 256;      // vocabulary columns per tile (top-K kernels, 
 constexpr int kTileNFull = 128;  // vocabulary columns per tile (dual-accumulator kernels)
 constexpr int kTileM = 256;      // token rows per tile
 
+// The direct-load path addresses each operand with 32-bit offsets.
+inline bool fits32(int64_t bytes) { return bytes < (int64_t(1) << 32) - 65536; }
+
 // Per-row teacher data of the top-K loss, written by the prep kernel for
 // every valid row t (row-major [T][K], sorted by vocabulary index).
 struct TopkRowData {
@@ -51,7 +54,7 @@ struct TopkFwdArgs {
   TopkRowData rd;
   float* z_topk;  // nullable
   float* part;    // [S][part_stride][4]
-  int64_t part_stride;
+  int64_t part_stride;  // rows of H (T)
   int64_t d, V, K;
   int nrb, S, ntiles;
   float c2;  // log2(e) / tau
@@ -68,7 +71,7 @@ struct TopkDzArgs {
   char* dz;        // [C][ldz] chunk of dZ
   int64_t ldz;     // padded vocabulary (multiple of the tile width)
   int64_t c0, C;   // first compacted row of the chunk, chunk capacity
-  int64_t d, V, K;
+  int64_t T, d, V, K;
   int nrb, S, ntiles;
   float c2, inv_tau;
 };
@@ -100,7 +103,7 @@ struct FullDzArgs {
   const float* g;
   char* dz;
   int64_t ldz, c0, C;
-  int64_t d, dt, V;
+  int64_t T, d, dt, V;
   int nrb, S, ntiles;
   float c2, inv_tau;
 };
