@@ -39,7 +39,24 @@ def parse():
     ap.add_argument("--chunk-rows", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 4 times (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe(nbytes: int):
+    """A plain copy kernel of known size: reads and writes nbytes per launch.
+
+    Its FETCH_SIZE / WRITE_SIZE counter readings give the factor that turns
+    those counters into bytes for the loss kernels."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 4}))
 
 
 def traffic_from_profiles(kernel: str):
@@ -79,6 +96,10 @@ def main():
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if a.copy_probe:
+        copy_probe(a.copy_probe)
+        return
 
     import torch
     import chunked_kl_loss_logit_amd as kd
