@@ -59,17 +59,33 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 4}))
 
 
-def traffic_from_profiles(kernel: str):
-    """HBM bytes per launch of `kernel` from committed counter summaries, or None."""
+def source_digest() -> str:
+    """SHA-256 over the library's device and interface sources (names + bytes)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_kl_loss_logit_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)) + [os.path.join(ROOT, "include", "kdloss.h")]
+    for p in files:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter table, or
+    None when there is none for this workload or the sources changed since."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             data = json.load(f)
-        return data.get(kernel, {}).get("bytes_per_launch")
     except (OSError, ValueError):
         return None
+    if data.get("workload") != workload or data.get("source_digest") != source_digest():
+        return None
+    return data.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
 
 def cpu_baseline(inp, rows: int):
@@ -164,7 +180,8 @@ def main():
     # each tile kernel contracts one chunk: 2 * rows * d * V flops per launch
     rows_per_launch = n_valid if dom == "topk_fwd_tile" else n_valid / (n_l / a.steps)
     achieved = 2.0 * rows_per_launch * d * V / (avg_ms * 1e-3) / 1e12
-    traffic = traffic_from_profiles(dom)
+    workload = p.name if not a.T else f"head_topk_t{T}"
+    traffic = traffic_from_profiles(dom, workload)
 
     out = {
         "metric": METRIC,
@@ -179,7 +196,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{p.name}" if not a.T else f"head_topk_t{T}", "T": T, "d": d, "V": V, "K": K,
+        "config": {"workload": workload, "T": T, "d": d, "V": V, "K": K,
                    "tau": tau, "valid_rows": n_valid, "chunk_rows": a.chunk_rows or 4096},
         "valid_tokens_per_s": n_valid / (ms * 1e-3),
         "credited_tflops": tflops,

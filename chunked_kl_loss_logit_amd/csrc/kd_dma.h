@@ -23,8 +23,8 @@
 // waits on its own loads with explicit vmcnt counts.
 //
 // Requirements (the launchers fall back to the general path otherwise): bf16
-// and a contraction length that is a multiple of 32 whose data is readable
-// (real data or zero padding).  Rows or columns outside the operand are
+// and a contraction length that is a multiple of 128 (whole ring turns)
+// whose data is readable (real data or zero padding).  Rows or columns outside the operand are
 // loaded from a clamped valid address; they only feed accumulator rows or
 // columns that the epilogues discard.
 #pragma once
@@ -37,8 +37,9 @@ namespace kd {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRing = 4;    // slots
-constexpr int kDmaKs = 32;  // k per stage
+constexpr int kRing = 4;                   // slots
+constexpr int kDmaKs = 32;                 // k per stage
+constexpr int kDmaKMult = kRing * kDmaKs;  // the contraction length must be a multiple of this
 
 // Direct loads are buffer loads: a resource descriptor (scalar registers) for
 // the operand, a per-lane 32-bit offset that stays in the same register for
@@ -53,6 +54,12 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const char* base) {
 
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, char* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (KD_LDS void*)(lds_wave_base), 16, (int)voff, (int)soff, 0, 0);
+}
+
+// 16 bytes of LDS at a byte offset from a slot array (one offset, so the
+// compiler keeps the array's alias information)
+__device__ inline u32x4_t ld_lds16(const char* slot, int off) {
+  return *reinterpret_cast<const u32x4_t*>(slot + off);
 }
 
 // k-contiguous operand with NR rows: NR / 16 direct loads per stage, NR / 64
@@ -117,94 +124,251 @@ struct DmaCols {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) dma16(rs, off[i], (uint32_t)(s * kDmaKs * ld), dst + (w * kPer + i) * 1024);
   }
-  // B fragment of a 32x32x16 MFMA out of the slot starting at `slot` (B half
-  // at boff): columns col0 .. col0 + 31 (col0 % 32 == 0), k = 16 kg +
-  // 8 (lane / 32) + 0..7 of the stage.  Each address is one integer offset
-  // from the slot array: a deeper chain of pointer arithmetic loses the
-  // alias information that keeps the compiler from waiting on in-flight
-  // direct loads.
-  __device__ inline static u32x4_t frag(const char* slot, int boff, int col0, int kg) {
-    const int l = threadIdx.x & 63;
-    const int j = l & 15;
-    const int col = col0 + 16 * ((l >> 4) & 1) + 4 * (j & 3);
-    const int c = col >> 3;
-    const int hb = (col & 7) * 2;
-    u32x4_t out;
+  // stage s of the panel that starts col0 columns after the one init() saw
+  __device__ inline void issue(long s, long col0, char* dst) const {
+    const int w = wave_id();
+    const uint32_t soff = (uint32_t)(s * kDmaKs * ld + col0 * 2);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int k = 16 * kg + 8 * (l >> 5) + 4 * q + (j >> 2);
-      const int off = boff + k * kRowBytes + 16 * (c ^ (4 * (k & 3))) + hb;
-      const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((KD_LDS s16x4_t*)(const_cast<char*>(slot) + off));
-      const uint2 u = __builtin_bit_cast(uint2, v);
-      out[2 * q] = u.x;
-      out[2 * q + 1] = u.y;
-    }
-    return out;
+    for (int i = 0; i < kPer; ++i) dma16(rs, off[i], soff, dst + (w * kPer + i) * 1024);
   }
 };
 
-// One step of the ring: stage i sits in slot J.  The step always issues a
-// stage into slot (J + 3) % 4 (which every wave finished reading before this
-// step's barrier): stage i + 3, or past the end a repeat of the last stage,
-// which lands in a slot nobody reads.  Steps past the last stage still wait,
-// meet at the barrier and issue; they only skip the multiply.  Keeping every
-// direct load unconditional keeps the compiler's bookkeeping of in-flight
-// loads identical on all paths; with a conditional one it makes every LDS
-// read wait for all outstanding loads.
-template <int J, int LPW, class Issue, class Mma>
-__device__ inline void ring_step(const Slots& sl, int i, int nst, Issue& issue, Mma& mma) {
-  constexpr int JN = (J + kRing - 1) % kRing;
-  wait_vm<(kRing - 2) * LPW>();  // this wave's loads of stage i have landed
-  ring_barrier();                // ... and every other wave's; slot JN is free
-  issue((long)min(i + kRing - 1, nst - 1), sl.template A<JN>(), sl.template B<JN>());
-  if (i < nst) mma(static_cast<const char*>(sl.template A<J>()), static_cast<const char*>(sl.template B<J>()));
+// ------------------------------------------------------------------ register fragments
+// One stage's operand fragments for one wave: for each of the two k-groups,
+// 4 A fragments (rows wm*128 + 32 mb + lane % 32) and NB B fragments.
+template <int NB, int NDS>
+struct Frags {
+  static constexpr int kMma = 2 * 4 * NB;  // matrix instructions per stage
+  static constexpr int kDs = NDS;          // LDS read instructions per stage
+  u32x4_t a[2][4];
+  u32x4_t b[2][NB];
+};
+
+template <int NB, int NDS>
+__device__ inline void mma_frags(const Frags<NB, NDS>& f, f32x16_t (&acc)[4][NB]) {
+#pragma unroll
+  for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) Bf16::mma(acc[mb][nb], f.a[kg][mb], f.b[kg][nb]);
 }
 
-// One tile's contraction over stages [0, nst): kRing - 1 stages are issued
-// ahead.  `issue(s, A, B)` enqueues stage s into a slot's halves, `mma(A, B)`
-// multiplies one stage out of LDS.  Each wave issues LPW direct loads per
-// stage.  Drains vector memory on entry (so the counts it waits on are its
-// own) and on exit, then ends with a barrier, after which the caller may use
-// the slots.
-template <int LPW, class Issue, class Mma>
-__device__ inline void ring_contract(const Slots& sl, int nst, Issue&& issue, Mma&& mma) {
-  static_assert(LPW * (kRing - 2) < 64, "vmcnt range");
+template <int BN>
+using FragsNN = Frags<BN / 64, 2 * (4 + 2 * (BN / 64))>;  // b128 A reads, two transposing reads per B
+
+template <int BN>
+using FragsRows = Frags<BN / 64, 2 * (4 + BN / 64)>;
+
+// Per-lane byte offsets of this wave's fragments inside a stage slot,
+// computed once.  Every fragment read is then one of these registers plus an
+// immediate, and the compiler keeps a handful of address registers instead of
+// re-deriving the swizzled address of each read.
+//   k-contiguous rows (A, and B of NT): row m = base + 32 mb + lane % 32 with
+//     base a multiple of 128; chunk 2 kg + lane / 32 sits at position
+//     c ^ ((m >> 2) & 3) = c ^ ((lane >> 2) & 3): offset a_off[kg] + 2048 mb.
+//   n-contiguous B (NN): lane j of a 16-lane group reads k-row kl + 16 kg + 4 q
+//     (kl = 8 (lane / 32) + j / 4) at column col0 + 16 ((lane >> 4) & 1) +
+//     4 (j % 4); the swizzle key 4 (k & 3) only depends on kl, so the read is
+//     b_off[nb] + (16 kg + 4 q) * row bytes.
+template <int BN>
+struct FragReader {
+  static constexpr int NB = BN / 64;
+  static constexpr int kRowBytes = BN * 2;  // one k-row of an n-contiguous B stage
+  int a_off[2];
+  int b_off[NB];  // NN: per column block; NT: entries 0 and 1 per k-group
+
+  __device__ inline void init_nn() {
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int h = l >> 5, x = (l >> 2) & 3;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) a_off[kg] = (wm * 128 + (l & 31)) * kRowB + 16 * ((2 * kg + h) ^ x);
+    const int j = l & 15;
+    const int kl = 8 * h + (j >> 2);
+    const int cl = 2 * ((l >> 4) & 1) + ((j & 3) >> 1);
+    const int hb = ((4 * (j & 3)) & 7) * 2;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int c = (wn * (BN / 2) + nb * 32) / 8 + cl;
+      b_off[nb] = kHalfBytes + kl * kRowBytes + 16 * (c ^ (4 * (kl & 3))) + hb;
+    }
+  }
+
+  __device__ inline void init_rows() {
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int h = l >> 5, x = (l >> 2) & 3;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+      a_off[kg] = (wm * 128 + (l & 31)) * kRowB + 16 * ((2 * kg + h) ^ x);
+      b_off[kg] = kHalfBytes + (wn * (BN / 2) + (l & 31)) * kRowB + 16 * ((2 * kg + h) ^ x);
+    }
+  }
+
+  // A (256 rows, k-contiguous) and B (BN columns, n-contiguous) of the stage
+  // in `slot` into this wave's fragments.
+  __device__ inline void read_nn(const char* slot, FragsNN<BN>& f) const {
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) f.a[kg][mb] = ld_lds16(slot, a_off[kg] + mb * 32 * kRowB);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        u32x4_t o;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int off = b_off[nb] + (16 * kg + 4 * q) * kRowBytes;
+          const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((KD_LDS s16x4_t*)(const_cast<char*>(slot) + off));
+          const uint2 u = __builtin_bit_cast(uint2, v);
+          o[2 * q] = u.x;
+          o[2 * q + 1] = u.y;
+        }
+        f.b[kg][nb] = o;
+      }
+    }
+  }
+
+  // A (256 rows) and B (BN rows), both k-contiguous.
+  __device__ inline void read_rows(const char* slot, FragsRows<BN>& f) const {
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) f.a[kg][mb] = ld_lds16(slot, a_off[kg] + mb * 32 * kRowB);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) f.b[kg][nb] = ld_lds16(slot, b_off[kg] + nb * 32 * kRowB);
+    }
+  }
+};
+
+// Instruction interleave of one ring step: each matrix instruction is
+// followed by one LDS read (the next stage's fragments) while reads remain,
+// then by one direct load.  Without it the scheduler issues each fragment
+// read just before its first use, and the matrix pipe waits on LDS latency.
+template <int NMMA, int NDS, int NVM>
+__device__ inline void ring_sched() {
+#pragma unroll
+  for (int m = 0; m < NMMA; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if (m < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    else if (m - NDS < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+  }
+}
+
+// ------------------------------------------------------------------ the ring
+// Stages move HBM -> LDS slot (direct loads, issued kRing stages ahead of the
+// matrix cores) -> registers (read one stage ahead) -> matrix cores.  Step i
+// (stage i sits in slot J = i % 4 and already in registers `cur`):
+//   wait until stage i + 1 has landed and every wave passed the barrier (so
+//   every wave has also finished reading slot J into registers);
+//   issue stage i + 4 into slot J (past the end: the last stage again, which
+//   nobody reads, so every step issues the same number of loads and the
+//   compiler's bookkeeping of in-flight loads stays exact);
+//   read stage i + 1 from slot J + 1 into `nxt` while multiplying `cur`.
+template <int J, int LPW, class Frag, class Issue, class Read, class Mma>
+__device__ inline void ring_step(const Slots& sl, int i, int nst, Frag& cur, Frag& nxt, Issue& issue, Read& read,
+                                 Mma& mma) {
+  constexpr int JN = (J + 1) % kRing;
+  wait_vm<(kRing - 2) * LPW>();
+  ring_barrier();
+  issue((long)min(i + kRing, nst - 1), sl.template A<J>(), sl.template B<J>());
+  read(static_cast<const char*>(sl.template A<JN>()), nxt);
+  mma(cur);
+  ring_sched<Frag::kMma, Frag::kDs, LPW>();
+}
+
+// One tile's contraction over stages [0, nst), nst a multiple of 4 (the
+// launchers choose this path only then).  `issue(s, A, B)` enqueues
+// stage s into a slot's halves (LPW direct loads per wave), `read(slot, f)`
+// loads one stage's fragments, `mma(f)` multiplies them.  Drains vector
+// memory on entry (so the counts it waits on are its own) and on exit, then
+// ends with a barrier, after which the caller may use the slots.
+template <int LPW, class Frag, class Issue, class Read, class Mma>
+__device__ inline void ring_contract(const Slots& sl, int nst, Issue&& issue, Read&& read, Mma&& mma) {
+  static_assert(LPW * kRing < 64, "vmcnt range");
   wait_vm<0>();
   __syncthreads();
   if (nst > 0) {
+    Frag f0, f1;
     issue(0L, sl.A<0>(), sl.B<0>());
     issue((long)min(1, nst - 1), sl.A<1>(), sl.B<1>());
     issue((long)min(2, nst - 1), sl.A<2>(), sl.B<2>());
+    issue((long)min(3, nst - 1), sl.A<3>(), sl.B<3>());
+    wait_vm<(kRing - 1) * LPW>();
+    ring_barrier();
+    read(static_cast<const char*>(sl.A<0>()), f0);
     for (int i = 0; i < nst; i += kRing) {
-      ring_step<0, LPW>(sl, i, nst, issue, mma);
-      ring_step<1, LPW>(sl, i + 1, nst, issue, mma);
-      ring_step<2, LPW>(sl, i + 2, nst, issue, mma);
-      ring_step<3, LPW>(sl, i + 3, nst, issue, mma);
+      ring_step<0, LPW>(sl, i, nst, f0, f1, issue, read, mma);
+      ring_step<1, LPW>(sl, i + 1, nst, f1, f0, issue, read, mma);
+      ring_step<2, LPW>(sl, i + 2, nst, f0, f1, issue, read, mma);
+      ring_step<3, LPW>(sl, i + 3, nst, f1, f0, issue, read, mma);
     }
     wait_vm<0>();
   }
   __syncthreads();
 }
 
-// A (256 rows, k-contiguous) x B (n-contiguous) stage product into a
-// 128 x (BN/2) wave tile.
-template <int BN>
-__device__ inline void mma_stage_nn(const char* As, const char* /*Bs = As + kHalfBytes*/, f32x16_t (&acc)[4][BN / 64]) {
-  constexpr int NB = BN / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
-#pragma unroll
-  for (int kg = 0; kg < 2; ++kg) {
-    u32x4_t a[4], b[NB];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) a[mb] = row_frag(As, wm * 128 + mb * 32 + (lane & 31), 2 * kg + (lane >> 5));
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) b[nb] = DmaCols<BN>::frag(As, kHalfBytes, wn * (BN / 2) + nb * 32, kg);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) Bf16::mma(acc[mb][nb], a[mb], b[nb]);
+// ------------------------------------------------------------------ the ring across tiles
+// One step of ring_run: like ring_step, but the stage to issue is given as
+// (tile, stage), and the read of the next stage can be left out (kRead).
+template <int J, int LPW, bool kRead, class Frag, class Issue, class Read, class Mma>
+__device__ inline void run_step(const Slots& sl, long it, int is, Frag& cur, Frag& nxt, Issue& issue, Read& read,
+                                Mma& mma) {
+  constexpr int JN = (J + 1) % kRing;
+  wait_vm<(kRing - 2) * LPW>();
+  ring_barrier();
+  issue(it, is, sl.template A<J>(), sl.template B<J>());
+  if constexpr (kRead) read(static_cast<const char*>(sl.template A<JN>()), nxt);
+  mma(cur);
+  ring_sched<Frag::kMma, kRead ? Frag::kDs : 0, LPW>();
+}
+
+// ntiles contractions of nst stages each (nst a multiple of 4, at least 4)
+// through one ring that never drains between tiles: the last four steps of
+// tile t issue the first four stages of tile t + 1, and while `done(t)`
+// consumes the accumulators the loads keep landing.  `issue(t, s, A, B)`,
+// `read` and `mma` are as in ring_contract.  done(t) runs after the last
+// multiply of tile t, on every wave; it may use the epilogue array and
+// ring_barrier(), but not the slots, and must not wait for vector memory
+// (__syncthreads would).  Loads and stores it issues only make the next
+// step's wait longer.
+template <int LPW, class Frag, class Issue, class Read, class Mma, class Done>
+__device__ inline void ring_run(const Slots& sl, int ntiles, int nst, Issue&& issue, Read&& read, Mma&& mma,
+                                Done&& done) {
+  static_assert(LPW * kRing < 64, "vmcnt range");
+  wait_vm<0>();
+  __syncthreads();
+  if (ntiles > 0) {
+    Frag f0, f1;
+    issue(0L, 0, sl.A<0>(), sl.B<0>());
+    issue(0L, 1, sl.A<1>(), sl.B<1>());
+    issue(0L, 2, sl.A<2>(), sl.B<2>());
+    issue(0L, 3, sl.A<3>(), sl.B<3>());
+    wait_vm<(kRing - 1) * LPW>();
+    ring_barrier();
+    read(static_cast<const char*>(sl.A<0>()), f0);
+    for (int t = 0; t < ntiles; ++t) {
+      for (int s = 0; s + kRing < nst; s += kRing) {
+        run_step<0, LPW, true>(sl, t, s + 4, f0, f1, issue, read, mma);
+        run_step<1, LPW, true>(sl, t, s + 5, f1, f0, issue, read, mma);
+        run_step<2, LPW, true>(sl, t, s + 6, f0, f1, issue, read, mma);
+        run_step<3, LPW, true>(sl, t, s + 7, f1, f0, issue, read, mma);
+      }
+      // last four stages: issue the next tile's first four (after the last
+      // tile, this tile's last stage again, into slots nobody reads)
+      const bool more = t + 1 < ntiles;
+      const long tn = more ? t + 1 : t;
+      run_step<0, LPW, true>(sl, tn, more ? 0 : nst - 1, f0, f1, issue, read, mma);
+      run_step<1, LPW, true>(sl, tn, more ? 1 : nst - 1, f1, f0, issue, read, mma);
+      run_step<2, LPW, true>(sl, tn, more ? 2 : nst - 1, f0, f1, issue, read, mma);
+      run_step<3, LPW, false>(sl, tn, more ? 3 : nst - 1, f1, f0, issue, read, mma);
+      done(t);
+      // stage 0 of the next tile landed before the last step's barrier
+      read(static_cast<const char*>(sl.A<0>()), f0);
+    }
+    wait_vm<0>();
   }
+  __syncthreads();
 }
 
 }  // namespace kd

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads, 1) void full_fwd_kernel(FullFwdArgs a) {
 
   const int count = *a.c.count;
   int rb, sp;
-  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, 4, rb, sp);
+  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, a.group, rb, sp);
   const int row0 = rb * kBM;
   if (row0 >= count) return;
   const int tb = (int)((long)a.ntiles * sp / a.S);
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 1) void full_dz_kernel(FullDzArgs a) {
   const long M = min(a.C, count - a.c0);
   if (M <= 0) return;
   int rb, sp;
-  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, 4, rb, sp);
+  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, a.group, rb, sp);
   const int row0 = rb * kBM;
   if (row0 >= M) return;
   const int tb = (int)((long)a.ntiles * sp / a.S);
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void full_dz_kernel(FullDzArgs a) {
 
 // The direct-load ring needs bf16 and both hidden widths multiples of 32.
 static bool full_dma_ok(int64_t T, int64_t d, int64_t dt, int64_t V) {
-  return d % kDmaKs == 0 && dt % kDmaKs == 0 && fits32(T * d * 2) && fits32(T * dt * 2) && fits32(d * V * 2) &&
+  return d % kDmaKMult == 0 && dt % kDmaKMult == 0 && fits32(T * d * 2) && fits32(T * dt * 2) && fits32(d * V * 2) &&
          fits32(dt * V * 2);
 }
 

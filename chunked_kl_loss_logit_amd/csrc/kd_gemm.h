@@ -69,6 +69,14 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // wave index within the workgroup, known to the compiler to be wave-uniform
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// A copy of x the compiler cannot see through: values derived from it are
+// recomputed after each call instead of being hoisted out of enclosing loops
+// (where they would hold registers across the matrix-core loop).
+__device__ inline int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // ------------------------------------------------------------------ synchronisation
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)
 template <int N>
@@ -85,14 +93,18 @@ __device__ inline void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_
 // Four stage slots of 32 KB, separate __shared__ arrays: the A half of a
 // stage at offset 0, the B half at offset 16 KB.  Addressing every slot by a
 // compile-time slot number lets the compiler tell the slots apart (kd_dma.h).
+// A fifth 32 KB array stages epilogue blocks while the slots keep receiving
+// the next tile's operands: 160 KB, the whole LDS of a CU.
 constexpr int kHalfBytes = 16384;
 constexpr int kSlotBytes = 2 * kHalfBytes;
+constexpr int kEpBytes = 32768;
 
 struct Slots {
   char* s0;
   char* s1;
   char* s2;
   char* s3;
+  float* ep;  // epilogue staging, [256][32] floats
   template <int J>
   __device__ inline char* at() const {
     static_assert(J >= 0 && J < 4, "slot");
@@ -112,7 +124,8 @@ struct Slots {
   __shared__ __attribute__((aligned(16))) char name##_1[kSlotBytes]; \
   __shared__ __attribute__((aligned(16))) char name##_2[kSlotBytes]; \
   __shared__ __attribute__((aligned(16))) char name##_3[kSlotBytes]; \
-  const Slots name{name##_0, name##_1, name##_2, name##_3}
+  __shared__ __attribute__((aligned(16))) float name##_e[kEpBytes / 4]; \
+  const Slots name{name##_0, name##_1, name##_2, name##_3, name##_e}
 
 // 16-byte fragment of a k-contiguous stage: row m, logical chunk c (0..3)
 __device__ inline u32x4_t row_frag(const char* st, int m, int c) {
@@ -122,11 +135,11 @@ __device__ inline int row_pos(int m, int c) { return m * kRowB + 16 * (c ^ ((m >
 
 // ------------------------------------------------------------------ workgroup placement
 // Workgroups are handed to the 8 XCDs round-robin by id.  Renumber them so that
-// consecutive logical ids share an XCD (and its L2): XCD x runs logical ids
-// [x*n/8, (x+1)*n/8).  Only done when n divides evenly.
+// consecutive logical ids share an XCD (and its L2): XCD x runs one contiguous
+// range of logical ids, of n/8 (rounded up for the first n%8 XCDs) ids.
 __device__ inline int xcd_remap(int id, int n) {
-  if (n % 8) return id;
-  return (id % 8) * (n / 8) + id / 8;
+  const int q = n >> 3, r = n & 7, x = id & 7, j = id >> 3;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
 }
 
 // Grouped raster over an nrb x ncb grid: G row-blocks form a group; inside a
@@ -193,18 +206,37 @@ __device__ inline void stage_block(StPair st0, StPair st1, const f32x16_t (&acc)
     }
 }
 
+// Block NBI of the waves of column half h (wave index & 1 == h) into st; the
+// other two waves write nothing.
+template <int NBI, int NB>
+__device__ inline void stage_half(StPair st, int h, const f32x16_t (&acc)[4][NB]) {
+  const int w = wave_id();
+  const int wm = w >> 1, wn = w & 1;
+  if (wn != h) return;
+  const int lane = opaque((int)threadIdx.x) & 63;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = wm * 128 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      st[row * 32 + st_pos(row, lane & 31)] = acc[mb][NBI][i];
+    }
+}
+
 // Store a staged [256][32] float block as the element type into a row-major
 // destination (`ld` elements per row): rows [row0, row0 + 256) clipped to
-// nrows, columns [col0, col0 + 32) clipped to ncols (a multiple of 4/8).
+// nrows, columns [col0, col0 + 32) clipped to [clo, ncols) (both multiples
+// of 4/8).
 template <class E>
 __device__ inline void store_block(StPair st, char* dst, long ld, long row0, long col0, long nrows,
-                                   long ncols) {
+                                   long ncols, long clo = 0) {
   constexpr int CPR = 32 * E::kElem / 16;  // 16-byte chunks per row
   constexpr int RPP = kThreads / CPR;
-  const int q = threadIdx.x % CPR;
+  const int tid = opaque((int)threadIdx.x);
+  const int q = tid % CPR;
   const long col = col0 + (long)q * E::kEpc;
-  if (col >= ncols) return;
-  for (int r = threadIdx.x / CPR; r < kBM; r += RPP) {
+  if (col >= ncols || col < clo) return;
+  for (int r = tid / CPR; r < kBM; r += RPP) {
     if (row0 + r >= nrows) break;
     u32x4_t o;
     if constexpr (E::kEpc == 8) {

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   const int per_split = a.nrb * a.ncb;
   const int sp = logical / per_split;
   int rb, cb;
-  grouped_coords(logical - sp * per_split, a.nrb, a.ncb, 4, rb, cb);
+  grouped_coords(logical - sp * per_split, a.nrb, a.ncb, a.group, rb, cb);
   const long row0 = (long)rb * kBM, n0 = (long)cb * BN;
   if (row0 >= M) return;
 
@@ -63,8 +63,9 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   mainloop.init(a.dz, [&](int r) -> const char* { return row0 + r < M ? a.dz + (row0 + r) * a.ldz * E::kElem : nullptr; },
                 a.W, [&](int r) -> const char* { return n0 + r < a.d ? a.W + (n0 + r) * a.V * E::kElem : nullptr; },
                 a.V);
-  const long nst = mainloop.nst;
-  const long s0 = nst * sp / a.S, s1 = nst * (sp + 1) / a.S;
+  // split boundaries on whole groups of Main::kStageGroup stages
+  const long ng = mainloop.nst / Main::kStageGroup;
+  const long s0 = ng * sp / a.S * Main::kStageGroup, s1 = ng * (sp + 1) / a.S * Main::kStageGroup;
   f32x16_t acc[4][BN / 64];
   mainloop.tile(sl, s0, s1, acc);
   store_tile_f32(sl, acc, a.part + (long)sp * a.C * a.d, a.d, row0, n0, M, a.d, false);
@@ -79,12 +80,13 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   const long M = max(0L, min(a.C, count - a.c0));  // valid rows of the chunk
   if (M == 0 && a.accumulate) return;              // nothing to add
   int rb, cb;
-  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.ncb, 4, rb, cb);
+  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.ncb, a.group, rb, cb);
   const long row0 = (long)rb * kBM, n0 = (long)cb * BN;
 
-  // contraction over the chunk's rows, rounded up to 32: both buffers hold
-  // zeros between M and the end of their last 256-row tile
-  const long K = (M + 31) / 32 * 32;
+  // contraction over the chunk's rows, rounded up to Main::kKMult (at most
+  // 256): both buffers hold zeros between M and the end of their last
+  // 256-row tile
+  const long K = (M + Main::kKMult - 1) / Main::kKMult * Main::kKMult;
   Main mainloop;
   mainloop.init(a.hT, [&](int r) -> const char* { return row0 + r < a.d ? a.hT + (row0 + r) * a.C * E::kElem : nullptr; },
                 a.dz, a.ldz * E::kElem, a.V, K);
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
 
 hipError_t launch_dh(int elem, const DhArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.ncb * a.S), block(kThreads);
-  if (elem == 2 && a.V % kDmaKs == 0 && fits32(a.C * a.ldz * 2) && fits32(a.d * a.V * 2))
+  if (elem == 2 && a.V % kDmaKMult == 0 && fits32(a.C * a.ldz * 2) && fits32(a.d * a.V * 2))
     hipLaunchKernelGGL((dh_kernel<DmaNT<256>, Bf16>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((dh_kernel<GenNT<Bf16, 256>, Bf16>), grid, block, 0, st, a);

@@ -17,9 +17,8 @@ inline bool fits32(int64_t bytes) { return bytes < (int64_t(1) << 32) - 65536; }
 // Per-row teacher data of the top-K loss, written by the prep kernel for
 // every valid row t (row-major [T][K], sorted by vocabulary index).
 struct TopkRowData {
-  int32_t* idx;     // cached indices, ascending
+  int2* pair;       // (cached index, teacher probability bits), ascending index
   uint16_t* perm;   // original position k of each sorted entry
-  float* p;         // teacher probability of each sorted entry
   float* ent;       // [T] sum_k p_k log p_k
 };
 
@@ -57,6 +56,7 @@ struct TopkFwdArgs {
   int64_t part_stride;  // rows of H (T)
   int64_t d, V, K;
   int nrb, S, ntiles;
+  int group;  // row blocks per raster group (grouped_coords)
   float c2;  // log2(e) / tau
 };
 hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st);
@@ -73,6 +73,7 @@ struct TopkDzArgs {
   int64_t c0, C;   // first compacted row of the chunk, chunk capacity
   int64_t T, d, V, K;
   int nrb, S, ntiles;
+  int group;  // row blocks per raster group (grouped_coords)
   float c2, inv_tau;
 };
 hipError_t launch_topk_dz(int elem, const TopkDzArgs& a, hipStream_t st);
@@ -88,6 +89,7 @@ struct FullFwdArgs {
   int64_t part_stride;
   int64_t d, dt, V;
   int nrb, S, ntiles;
+  int group;  // row blocks per raster group (grouped_coords)
   float c2;
 };
 hipError_t launch_full_fwd(int elem, const FullFwdArgs& a, hipStream_t st);
@@ -105,6 +107,7 @@ struct FullDzArgs {
   int64_t ldz, c0, C;
   int64_t T, d, dt, V;
   int nrb, S, ntiles;
+  int group;  // row blocks per raster group (grouped_coords)
   float c2, inv_tau;
 };
 hipError_t launch_full_dz(int elem, const FullDzArgs& a, hipStream_t st);
@@ -118,6 +121,7 @@ struct DhArgs {
   const int32_t* count;
   int64_t c0, C, ldz, d, V;
   int nrb, ncb, S;
+  int group;
 };
 hipError_t launch_dh(int elem, const DhArgs& a, hipStream_t st);
 
@@ -129,6 +133,7 @@ struct DwArgs {
   const int32_t* count;
   int64_t c0, C, ldz, d, V;
   int nrb, ncb;
+  int group;
   int accumulate;
 };
 hipError_t launch_dw(int elem, const DwArgs& a, hipStream_t st);

@@ -14,6 +14,8 @@
 // nullptr outside the operand; NT policies take a second one for B rows.
 #pragma once
 
+#include <climits>
+
 #include "kd_dma.h"
 #include "kd_gemm.h"
 
@@ -139,6 +141,7 @@ __device__ inline void gen_contract(const Slots& sl, long nst, Load&& load, Stor
 // ------------------------------------------------------------------ NN policies
 template <class E, int BN>
 struct GenNN {
+  static constexpr int kKMult = 1;
   GRows<kBM> al;
   GCols<E, BN> bl;
   const char* B;
@@ -154,6 +157,16 @@ struct GenNN {
     bl.K = K;
     kbytes = K * E::kElem;
     nst = (kbytes + kRowB - 1) / kRowB;
+  }
+
+  // tiles t = 0 .. ntiles-1 at columns n0_of(t); done(t, acc) after each
+  template <class N0, class Done>
+  __device__ inline void run(const Slots& sl, int ntiles, N0&& n0_of, Done&& done) {
+    f32x16_t acc[4][BN / 64];
+    for (int t = 0; t < ntiles; ++t) {
+      tile(sl, n0_of(t), acc);
+      done(t, acc);
+    }
   }
 
   __device__ inline void tile(const Slots& sl, long n0, f32x16_t (&acc)[4][BN / 64]) {
@@ -179,10 +192,12 @@ struct GenNN {
 // must lie within 4 GiB of it; so must the B panel's rows.
 template <int BN>
 struct DmaNN {
+  static constexpr int kKMult = kDmaKMult;
   static constexpr int kLpw = DmaRows<kBM>::kPer + DmaCols<BN>::kPer;
   static_assert(DmaRows<kBM>::kBytes <= kHalfBytes && DmaCols<BN>::kBytes <= kHalfBytes, "stage must fit a slot");
   DmaRows<kBM> a;
   DmaCols<BN> b;
+  FragReader<BN> rd;
   const char* B;
   long N;
   int nst;
@@ -198,24 +213,49 @@ struct DmaNN {
     b.ld = ldb;
     N = Nn;
     nst = (int)(K / kDmaKs);
+    rd.init_nn();
+  }
+
+  // Tiles t = 0 .. ntiles-1 at columns n0_of(t) through one ring; done(t, acc)
+  // after each (see ring_run for what it may do).  Every tile must lie inside
+  // the operand: no column is clamped.
+  template <class N0, class Done>
+  __device__ inline void run(const Slots& sl, int ntiles, N0&& n0_of, Done&& done) {
+    b.init(B, LONG_MAX);
+    f32x16_t acc[4][BN / 64];
+    zero_acc<BN / 64>(acc);
+    ring_run<kLpw, FragsNN<BN>>(
+        sl, ntiles, nst,
+        [&](long t, int s, char* da, char* db) {
+          a.issue(s, da);
+          b.issue(s, n0_of(t), db);
+        },
+        [&](const char* slot, FragsNN<BN>& f) { rd.read_nn(slot, f); },
+        [&](const FragsNN<BN>& f) { mma_frags(f, acc); },
+        [&](int t) {
+          done(t, acc);
+          zero_acc<BN / 64>(acc);
+        });
   }
 
   __device__ inline void tile(const Slots& sl, long n0, f32x16_t (&acc)[4][BN / 64]) {
     b.init(B + n0 * 2, N - n0);
     zero_acc<BN / 64>(acc);
-    ring_contract<kLpw>(
+    ring_contract<kLpw, FragsNN<BN>>(
         sl, nst,
         [&](long s, char* da, char* db) {
           a.issue(s, da);
           b.issue(s, db);
         },
-        [&](const char* as, const char* bs) { mma_stage_nn<BN>(as, bs, acc); });
+        [&](const char* slot, FragsNN<BN>& f) { rd.read_nn(slot, f); },
+        [&](const FragsNN<BN>& f) { mma_frags(f, acc); });
   }
 };
 
 // ------------------------------------------------------------------ NT policies
 template <class E, int BN>
 struct GenNT {
+  static constexpr int kStageGroup = 1;
   GRows<kBM> al;
   GRows<BN> bl;
   long kbytes, nst;
@@ -249,10 +289,12 @@ struct GenNT {
 
 template <int BN>
 struct DmaNT {
+  static constexpr int kStageGroup = kRing;
   static constexpr int kLpw = DmaRows<kBM>::kPer + DmaRows<BN>::kPer;
   static_assert(DmaRows<kBM>::kBytes <= kHalfBytes && DmaRows<BN>::kBytes <= kHalfBytes, "stage must fit a slot");
   DmaRows<kBM> a;
   DmaRows<BN> b;
+  FragReader<BN> rd;
   long nst;
 
   template <class RowPtrA, class RowPtrB>
@@ -268,17 +310,19 @@ struct DmaNT {
       return p ? p : sb;
     });
     nst = K / kDmaKs;
+    rd.init_rows();
   }
 
   __device__ inline void tile(const Slots& sl, long s0, long s1, f32x16_t (&acc)[4][BN / 64]) {
     zero_acc<BN / 64>(acc);
-    ring_contract<kLpw>(
+    ring_contract<kLpw, FragsRows<BN>>(
         sl, (int)(s1 - s0),
         [&](long s, char* da, char* db) {
           a.issue(s0 + s, da);
           b.issue(s0 + s, db);
         },
-        [&](const char* as, const char* bs) { mma_stage_rows<Bf16, BN>(as, bs, acc); });
+        [&](const char* slot, FragsRows<BN>& f) { rd.read_rows(slot, f); },
+        [&](const FragsRows<BN>& f) { mma_frags(f, acc); });
   }
 };
 

@@ -149,9 +149,8 @@ __global__ __launch_bounds__(NT) void topk_prep_kernel(const float* logits, cons
   for (int j = threadIdx.x; j < K; j += NT) {
     const uint64_t kv = key[j];
     const uint32_t k = (uint32_t)(kv & 0xffffffffu);
-    rd.idx[base + j] = (int32_t)((uint32_t)(kv >> 32) ^ 0x80000000u);
+    rd.pair[base + j] = make_int2((int32_t)((uint32_t)(kv >> 32) ^ 0x80000000u), __float_as_int(p[k]));
     rd.perm[base + j] = (uint16_t)k;
-    rd.p[base + j] = p[k];
   }
   if (threadIdx.x == 0) rd.ent[t] = ent;
 }

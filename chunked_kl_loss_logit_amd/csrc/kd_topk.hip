@@ -9,13 +9,13 @@
 //
 // Grid: (valid-row block of 256) x (vocabulary split).  A workgroup walks the
 // 256-wide vocabulary tiles of its split in ascending order; each tile is
-// Z = H_rows . W[:, tile] on matrix cores.  The tile is then staged through LDS
-// in four rounds of 2 x 32 columns (one 32-column block from each wave column
-// half) and read back one row per thread:
+// Z = H_rows . W[:, tile] on matrix cores, and the operand loads of the next
+// tile run while the epilogue of this one works.  The epilogue stages the
+// tile through LDS one 256 x 32 block at a time and reads it back one row per
+// thread:
 //   forward  : running base-2 max / sum per row, plus the index-match gather.
-//              The row's cached indices are sorted, so two cursors (one per
-//              128-column half of the tile) walk them in step with the rounds
-//              and pick the hits out of LDS.
+//              The row's cached indices are sorted, so one cursor walks them
+//              in step with the column blocks and picks the hits out of LDS.
 //   backward : dZ = (g/tau) (2^(y - L2) - sum of p over hits), written in the
 //              input dtype to the chunk's dZ buffer.
 #include <climits>
@@ -30,134 +30,172 @@ namespace {
 
 constexpr int kBN = kTileN;
 
-// First sorted position at or after `from` whose index is >= v.
-__device__ inline int seek(const int32_t* idx, int K, int from, long v) {
-  int lo = from, hi = K;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if ((long)idx[mid] < v) lo = mid + 1; else hi = mid;
+// First sorted position of row entries [b, e) whose index is >= v.
+__device__ inline int lower_bound(const int2* pair, int b, int e, long v) {
+  while (b < e) {
+    const int mid = (b + e) >> 1;
+    if ((long)pair[mid].x < v) b = mid + 1; else e = mid;
   }
-  return lo;
+  return b;
 }
 
-// Per-thread row state shared by the forward and backward epilogues.
-struct RowCursor {
-  const int32_t* idx;
-  const float* p;
-  int K;
-  int cur[2];   // sorted positions for the lower / upper 128 columns of a tile
-  long nxt[2];  // index at cur (LONG_MAX past the end)
+// A row's cached entries, sorted by vocabulary index, walked in step with the
+// epilogue's column blocks (ascending across the tiles of a split).
+//
+// No epilogue may wait on a load it issues itself: vector-memory counters
+// complete in order, so that wait would also wait for the operand loads of
+// the next tile that the ring issued just before the epilogue.  The cursor
+// therefore keeps a window of the two entries at its position, loaded at the
+// end of the previous tile's epilogue (refill) and complete long before they
+// are used.  A third hit inside one tile (rare) loads synchronously and waits
+// on the spot, so no load is ever pending where code paths merge.
+// Positions are offsets into the [T][K] pair array (32-bit, which the
+// argument checks guarantee).
+struct Cursor {
+  const int2* pair;  // uniform base
+  int c, end;        // next position, end of the row (= its start for a row that is not valid)
+  int cw;            // position of e0
+  int2 e0, e1;       // entries cw and cw + 1 (meaningful below end)
 
-  __device__ inline long at(int c) const { return c < K ? (long)idx[c] : LONG_MAX; }
-  // entering tile [n0, n0 + 256): cur[0] already points at the first index >= n0
-  __device__ inline void enter_tile(long n0) {
-    cur[1] = seek(idx, K, cur[0], n0 + 128);
-    nxt[0] = at(cur[0]);
-    nxt[1] = at(cur[1]);
+  // load the window at c; every lane loads, from a valid address
+  __device__ inline void refill() {
+    cw = c;
+    e0 = pair[c < end ? c : 0];
+    e1 = pair[c + 1 < end ? c + 1 : 0];
   }
-  __device__ inline void leave_tile() { cur[0] = cur[1]; }
+  // entry at c (c < end)
+  __device__ inline int2 entry() const {
+    if (c == cw) return e0;
+    if (c == cw + 1) return e1;
+    const int2 x = pair[c];
+    wait_vm<0>();
+    return x;
+  }
+  // calls f(index, p, position) for every entry below `lim`, moving past them
+  template <class F>
+  __device__ inline void take_below(int lim, F&& f) {
+    while (c < end) {
+      const int2 x = entry();
+      if (x.x >= lim) break;
+      f(x.x, __int_as_float(x.y), c);
+      ++c;
+    }
+  }
 };
 
+// valid columns of the 32-column block at cb: [lo, hi) relative to cb, both
+// multiples of 4.  Column arithmetic is 32-bit (V < 2^30): 64-bit compares
+// would need vector registers.
+__device__ inline void block_range(int cb, int clo, int chi, int& lo, int& hi) {
+  lo = min(32, max(0, clo - cb));
+  hi = max(0, min(32, chi - cb));
+}
+
 struct FwdRow {
-  RowCursor rc;
-  const uint16_t* perm;
-  float* ztk;  // z_topk row (nullable)
+  Cursor cur;
+  const uint16_t* perm;  // uniform bases, indexed by pair position
+  float* ztk;            // z_topk (nullable), indexed by row_k + original position
+  long row_k;            // t * K
   float m2, l, x;
   bool rv;
 
-  // 32 columns [cb, cb + 32) of this row, staged in st; V bounds the valid ones
-  __device__ inline void consume(StPair st, long cb, long V, int half, float c2) {
-    if (!rv) return;
-    const int nv = (int)max(0L, min(32L, V - cb));
-    if (nv == 0) return;
-    const int r = threadIdx.x;
-    // two passes over the staged row: block maximum, then the scaled sum
+  // 32 columns [cb, cb + 32) of this row, staged in st; [clo, chi) are the
+  // columns this tile accounts for.  Blocks arrive in ascending column order.
+  __device__ inline void consume(StPair st, int cb, int clo, int chi, float c2) {
+    int lo, hi;
+    block_range(cb, clo, chi, lo, hi);
+    if (lo >= hi || !rv) return;
+    const int r = opaque((int)threadIdx.x);
+    float4 f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = st_read4(st, r, j);
+    // block maximum over the valid chunks, then the scaled sum
     float cm = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (4 * j < nv) {
-        const float4 f = st_read4(st, r, j);
-        cm = fmaxf(cm, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
-      }
+      const float b = fmaxf(fmaxf(f[j].x, f[j].y), fmaxf(f[j].z, f[j].w));
+      cm = (4 * j >= lo && 4 * j < hi) ? fmaxf(cm, b) : cm;
     }
     const float cmy = cm * c2;
-    if (cmy > m2) {
-      l *= fast_exp2(m2 - cmy);
-      m2 = cmy;
-    }
+    l = cmy > m2 ? l * fast_exp2(m2 - cmy) : l;  // 2^(-inf) = 0 while l is still 0
+    m2 = fmaxf(m2, cmy);
     float sum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (4 * j < nv) {
-        const float4 f = st_read4(st, r, j);
-        sum += fast_exp2(fmaf(f.x, c2, -m2)) + fast_exp2(fmaf(f.y, c2, -m2)) + fast_exp2(fmaf(f.z, c2, -m2)) +
-               fast_exp2(fmaf(f.w, c2, -m2));
-      }
+      const float e = fast_exp2(fmaf(f[j].x, c2, -m2)) + fast_exp2(fmaf(f[j].y, c2, -m2)) +
+                      fast_exp2(fmaf(f[j].z, c2, -m2)) + fast_exp2(fmaf(f[j].w, c2, -m2));
+      sum += (4 * j >= lo && 4 * j < hi) ? e : 0.f;
     }
     l += sum;
     // index-match gather: cached indices that fall in this block
-    while (rc.nxt[half] < cb + nv) {
-      const int c = rc.cur[half];
-      const float z = st_row(st, r)[st_pos(r, (int)(rc.nxt[half] - cb))];
-      x = fmaf(rc.p[c], z, x);
-      if (ztk) ztk[perm[c]] = z;
-      rc.cur[half] = c + 1;
-      rc.nxt[half] = rc.at(c + 1);
-    }
+    cur.take_below(cb + hi, [&](int v, float pv, int c) {
+      const float z = st_row(st, r)[st_pos(r, v - cb)];
+      x = fmaf(pv, z, x);
+      if (ztk) ztk[row_k + perm[c]] = z;
+    });
   }
 };
 
 struct DzRow {
-  RowCursor rc;
+  Cursor cur;
   float L2, gs;
   bool rv;
 
   // replace the staged logits of this row by dZ (zero outside the valid rows
-  // and columns)
-  __device__ inline void consume(StPair st, long cb, long V, int half, float c2) {
-    const int r = threadIdx.x;
-    const int nv = rv ? (int)max(0L, min(32L, V - cb)) : 0;
+  // and the columns [clo, chi))
+  __device__ inline void consume(StPair st, int cb, int clo, int chi, float c2) {
+    const int r = opaque((int)threadIdx.x);
+    int lo, hi;
+    block_range(cb, clo, chi, lo, hi);
+    if (!rv) hi = 0;
+    float4 f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = st_read4(st, r, j);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float4 f = st_read4(st, r, j);
-      f.x = 4 * j + 0 < nv ? gs * fast_exp2(fmaf(f.x, c2, -L2)) : 0.f;
-      f.y = 4 * j + 1 < nv ? gs * fast_exp2(fmaf(f.y, c2, -L2)) : 0.f;
-      f.z = 4 * j + 2 < nv ? gs * fast_exp2(fmaf(f.z, c2, -L2)) : 0.f;
-      f.w = 4 * j + 3 < nv ? gs * fast_exp2(fmaf(f.w, c2, -L2)) : 0.f;
-      st_write4(st, r, j, f);
+      const bool v = 4 * j >= lo && 4 * j < hi;
+      float4 o;
+      o.x = v ? gs * fast_exp2(fmaf(f[j].x, c2, -L2)) : 0.f;
+      o.y = v ? gs * fast_exp2(fmaf(f[j].y, c2, -L2)) : 0.f;
+      o.z = v ? gs * fast_exp2(fmaf(f[j].z, c2, -L2)) : 0.f;
+      o.w = v ? gs * fast_exp2(fmaf(f[j].w, c2, -L2)) : 0.f;
+      st_write4(st, r, j, o);
     }
-    while (rc.nxt[half] < cb + nv) {  // scatter-add of the teacher mass
-      const int c = rc.cur[half];
-      st_row(st, r)[st_pos(r, (int)(rc.nxt[half] - cb))] -= gs * rc.p[c];
-      rc.cur[half] = c + 1;
-      rc.nxt[half] = rc.at(c + 1);
-    }
+    cur.take_below(cb + hi, [&](int v, float pv, int) {  // scatter-add of the teacher mass
+      st_row(st, r)[st_pos(r, v - cb)] -= gs * pv;
+    });
   }
 };
 
-template <int NBI>
-__device__ inline void fwd_round(const Slots& sl, const f32x16_t (&acc)[4][4], long n0, FwdRow& R,
-                                 const TopkFwdArgs& a) {
-  const StPair s0 = st_pair<0>(sl), s1 = st_pair<1>(sl);
-  stage_block<NBI, 4>(s0, s1, acc);
-  __syncthreads();
-  R.consume(s0, n0 + NBI * 32, a.V, 0, a.c2);
-  R.consume(s1, n0 + 128 + NBI * 32, a.V, 1, a.c2);
-  __syncthreads();
+// Vocabulary tile vt of a split is staged from column n0 = min(256 vt, V - 256)
+// and accounts for columns [256 vt, min(256 vt + 256, V)): a last partial
+// tile is shifted left so that every operand load stays inside W (its first
+// columns were the previous tile's).  Vocabularies under 256 columns take one
+// tile at 0 whose loads are bounded by the general mainloop.
+__device__ inline int tile_n0(int vt, int V) { return V >= kBN ? min(vt * kBN, V - kBN) : 0; }
+
+// The epilogue walks the 256 x 256 tile in eight rounds of one 32-column
+// block (wave column half h, block NBI) staged in the epilogue array, in
+// ascending column order: half 0 blocks 0..3, then half 1.
+template <int H, int NBI>
+__device__ inline void fwd_round(const Slots& sl, const f32x16_t (&acc)[4][4], int n0, int lo, int hi, FwdRow& R,
+                                 float c2) {
+  stage_half<NBI, 4>(sl.ep, H, acc);
+  ring_barrier();
+  R.consume(sl.ep, n0 + H * 128 + NBI * 32, lo, hi, c2);
+  ring_barrier();
 }
 
-template <class E, int NBI>
-__device__ inline void dz_round(const Slots& sl, const f32x16_t (&acc)[4][4], long n0, long row0, DzRow& R,
-                                const TopkDzArgs& a) {
-  const StPair s0 = st_pair<0>(sl), s1 = st_pair<1>(sl);
-  stage_block<NBI, 4>(s0, s1, acc);
-  __syncthreads();
-  R.consume(s0, n0 + NBI * 32, a.V, 0, a.c2);
-  R.consume(s1, n0 + 128 + NBI * 32, a.V, 1, a.c2);
-  __syncthreads();
-  store_block<E>(s0, a.dz, a.ldz, row0, n0 + NBI * 32, LONG_MAX, a.ldz);
-  store_block<E>(s1, a.dz, a.ldz, row0, n0 + 128 + NBI * 32, LONG_MAX, a.ldz);
-  __syncthreads();
+template <class E, int H, int NBI>
+__device__ inline void dz_round(const Slots& sl, const f32x16_t (&acc)[4][4], int n0, int lo, int hi, long row0,
+                                DzRow& R, const TopkDzArgs& a) {
+  const int cb = n0 + H * 128 + NBI * 32;
+  stage_half<NBI, 4>(sl.ep, H, acc);
+  ring_barrier();
+  R.consume(sl.ep, cb, lo, hi, a.c2);
+  ring_barrier();
+  store_block<E>(sl.ep, a.dz, a.ldz, row0, cb, LONG_MAX, a.ldz, lo);
+  ring_barrier();
 }
 
 }  // namespace
@@ -168,11 +206,12 @@ __global__ __launch_bounds__(kThreads, 1) void topk_fwd_kernel(TopkFwdArgs a) {
 
   const int count = *a.c.count;
   int rb, sp;
-  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, 4, rb, sp);
+  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, a.group, rb, sp);
   const int row0 = rb * kBM;
   if (row0 >= count) return;
   const int tb = (int)((long)a.ntiles * sp / a.S);
   const int te = (int)((long)a.ntiles * (sp + 1) / a.S);
+  const int V = (int)a.V;
 
   Main mainloop;
   mainloop.init(
@@ -187,27 +226,31 @@ __global__ __launch_bounds__(kThreads, 1) void topk_fwd_kernel(TopkFwdArgs a) {
   FwdRow R;
   R.rv = ti < count;
   const long t = R.rv ? a.c.rows[ti] : 0;
-  R.rc.idx = a.rd.idx + t * a.K;
-  R.rc.p = a.rd.p + t * a.K;
-  R.rc.K = R.rv ? (int)a.K : 0;
-  R.rc.cur[0] = seek(R.rc.idx, R.rc.K, 0, (long)tb * kBN);
-  R.perm = a.rd.perm + t * a.K;
-  R.ztk = a.z_topk ? a.z_topk + t * a.K : nullptr;
+  R.cur.pair = a.rd.pair;
+  R.cur.end = (int)(t * a.K + (R.rv ? a.K : 0));
+  R.cur.c = lower_bound(a.rd.pair, (int)(t * a.K), R.cur.end, (long)tb * kBN);
+  R.cur.refill();
+  R.perm = a.rd.perm;
+  R.ztk = a.z_topk;
+  R.row_k = t * a.K;
   R.m2 = -INFINITY;
   R.l = 0.f;
   R.x = 0.f;
 
-  f32x16_t acc[4][kBN / 64];
-  for (int vt = tb; vt < te; ++vt) {
-    const long n0 = (long)vt * kBN;
-    mainloop.tile(sl, n0, acc);
-    R.rc.enter_tile(n0);
-    fwd_round<0>(sl, acc, n0, R, a);
-    fwd_round<1>(sl, acc, n0, R, a);
-    fwd_round<2>(sl, acc, n0, R, a);
-    fwd_round<3>(sl, acc, n0, R, a);
-    R.rc.leave_tile();
-  }
+  mainloop.run(
+      sl, te - tb, [&](int i) -> long { return tile_n0(tb + i, V); },
+      [&](int i, const f32x16_t (&acc)[4][4]) {
+        const int vt = tb + i, n0 = tile_n0(vt, V), lo = vt * kBN, hi = min(lo + kBN, V);
+        fwd_round<0, 0>(sl, acc, n0, lo, hi, R, a.c2);
+        fwd_round<0, 1>(sl, acc, n0, lo, hi, R, a.c2);
+        fwd_round<0, 2>(sl, acc, n0, lo, hi, R, a.c2);
+        fwd_round<0, 3>(sl, acc, n0, lo, hi, R, a.c2);
+        fwd_round<1, 0>(sl, acc, n0, lo, hi, R, a.c2);
+        fwd_round<1, 1>(sl, acc, n0, lo, hi, R, a.c2);
+        fwd_round<1, 2>(sl, acc, n0, lo, hi, R, a.c2);
+        fwd_round<1, 3>(sl, acc, n0, lo, hi, R, a.c2);
+        R.cur.refill();
+      });
   if (R.rv) {
     float4* o = reinterpret_cast<float4*>(a.part) + (long)sp * a.part_stride + ti;
     *o = make_float4(R.m2, R.l, R.x, 0.f);
@@ -222,11 +265,12 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_kernel(TopkDzArgs a) {
   const long M = min(a.C, count - a.c0);  // valid rows in this chunk
   if (M <= 0) return;
   int rb, sp;
-  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, 4, rb, sp);
+  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, a.group, rb, sp);
   const int row0 = rb * kBM;
   if (row0 >= M) return;
   const int tb = (int)((long)a.ntiles * sp / a.S);
   const int te = (int)((long)a.ntiles * (sp + 1) / a.S);
+  const int V = (int)a.V;
   const int32_t* rows = a.c.rows + a.c0;
 
   Main mainloop;
@@ -242,30 +286,34 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_kernel(TopkDzArgs a) {
   DzRow R;
   R.rv = ti < M;
   const long t = R.rv ? rows[ti] : 0;
-  R.rc.idx = a.rd.idx + t * a.K;
-  R.rc.p = a.rd.p + t * a.K;
-  R.rc.K = R.rv ? (int)a.K : 0;
-  R.rc.cur[0] = seek(R.rc.idx, R.rc.K, 0, (long)tb * kBN);
+  R.cur.pair = a.rd.pair;
+  R.cur.end = (int)(t * a.K + (R.rv ? a.K : 0));
+  R.cur.c = lower_bound(a.rd.pair, (int)(t * a.K), R.cur.end, (long)tb * kBN);
+  R.cur.refill();
   R.L2 = R.rv ? a.lse[t] * kLog2e : 0.f;
   R.gs = R.rv ? a.g[t] * a.inv_tau : 0.f;
 
-  f32x16_t acc[4][kBN / 64];
-  for (int vt = tb; vt < te; ++vt) {
-    const long n0 = (long)vt * kBN;
-    mainloop.tile(sl, n0, acc);
-    R.rc.enter_tile(n0);
-    dz_round<E, 0>(sl, acc, n0, row0, R, a);
-    dz_round<E, 1>(sl, acc, n0, row0, R, a);
-    dz_round<E, 2>(sl, acc, n0, row0, R, a);
-    dz_round<E, 3>(sl, acc, n0, row0, R, a);
-    R.rc.leave_tile();
-  }
+  mainloop.run(
+      sl, te - tb, [&](int i) -> long { return tile_n0(tb + i, V); },
+      [&](int i, const f32x16_t (&acc)[4][4]) {
+        const int vt = tb + i, n0 = tile_n0(vt, V), lo = vt * kBN, hi = min(lo + kBN, V);
+        dz_round<E, 0, 0>(sl, acc, n0, lo, hi, row0, R, a);
+        dz_round<E, 0, 1>(sl, acc, n0, lo, hi, row0, R, a);
+        dz_round<E, 0, 2>(sl, acc, n0, lo, hi, row0, R, a);
+        dz_round<E, 0, 3>(sl, acc, n0, lo, hi, row0, R, a);
+        dz_round<E, 1, 0>(sl, acc, n0, lo, hi, row0, R, a);
+        dz_round<E, 1, 1>(sl, acc, n0, lo, hi, row0, R, a);
+        dz_round<E, 1, 2>(sl, acc, n0, lo, hi, row0, R, a);
+        dz_round<E, 1, 3>(sl, acc, n0, lo, hi, row0, R, a);
+        R.cur.refill();
+      });
 }
 
-// The direct-load ring needs bf16 and a hidden width that is a multiple of 32.
+// The direct-load ring needs bf16, a hidden width that is a multiple of 128
+// and at least one whole 256-column tile of vocabulary.
 hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
-  if (elem == 2 && a.d % kDmaKs == 0 && fits32(a.part_stride * a.d * 2) && fits32(a.d * a.V * 2))
+  if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.part_stride * a.d * 2) && fits32(a.d * a.V * 2))
     hipLaunchKernelGGL((topk_fwd_kernel<DmaNN<kBN>, Bf16>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((topk_fwd_kernel<GenNN<Bf16, kBN>, Bf16>), grid, block, 0, st, a);
@@ -276,7 +324,7 @@ hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st) {
 
 hipError_t launch_topk_dz(int elem, const TopkDzArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
-  if (elem == 2 && a.d % kDmaKs == 0 && fits32(a.T * a.d * 2) && fits32(a.d * a.V * 2))
+  if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.T * a.d * 2) && fits32(a.d * a.V * 2))
     hipLaunchKernelGGL((topk_dz_kernel<DmaNN<kBN>, Bf16>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((topk_dz_kernel<GenNN<Bf16, kBN>, Bf16>), grid, block, 0, st, a);

@@ -40,8 +40,9 @@
  *  - dtype KD_BF16: H, W, Ht, Wt and dH are bfloat16; products accumulate in
  *    float32.  KD_F32: they are float32 and the contraction runs on fp32
  *    matrix cores.  kl, lse, grad_kl, dW are float32 in both cases.
- *  - d, dt and V must be multiples of 8 (bf16) or 4 (fp32); 1 <= K <= V and
- *    K <= KD_MAX_K.  Otherwise the call returns KD_ERR_UNSUPPORTED.
+ *  - d, dt and V must be multiples of 8 (bf16) or 4 (fp32); 1 <= K <= V,
+ *    K <= KD_MAX_K and T * K < 2^31.  Otherwise the call returns
+ *    KD_ERR_UNSUPPORTED.
  *  - Pointers to H, W, Ht, Wt, dH, dW must be 16-byte aligned, all other
  *    arrays 4-byte aligned, the workspace 256-byte aligned
  *    (KD_ERR_ALIGNMENT).
