@@ -1,11 +1,16 @@
-"""Throughput of the fused top-K KL loss, forward + backward, on one MI355X.
+"""Throughput of the fused chunked KL loss, forward + backward, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py --sweep          # loss-only scaling sweep, one line per T
+    python bench.py --copy-probe N   # plain copy of N bytes (counter calibration)
 
-A step is one kd_topk_kl_fwd plus one kd_topk_kl_bwd over one batch of
-synthetic rows (inputs already in HBM): the output projection, online log Z,
-top-K gather, per-token KL, and the chunked backward (recomputed projection,
-dZ, dH, dW).  Prints one JSON line.
+A step of the top-K workloads is one kd_topk_kl_fwd plus one kd_topk_kl_bwd
+over one batch of synthetic rows (inputs already in HBM): the output
+projection, online log Z, top-K gather, per-token KL, and the chunked backward
+(recomputed projection, dZ, dH, dW).  A step of the full-vocabulary workload
+is kd_full_kl_fwd plus kd_full_kl_bwd.  The default run prints ONE JSON line
+for the output-head workload (T=4096, d=3072, V=128256, K=64); the packed
+long-context and full-vocabulary workloads ride along in its "extra" object.
 
 The loss-only benchmark of "Efficient Knowledge Distillation for LLMs: Offline
 Top-K Logits and a Fused Chunked KL Loss" (App. B) times the same path: output
@@ -25,8 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "fused KL fwd+bwd tokens/s (d=3072,V=128256) + % bf16 MFMA peak; peak extra HBM"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
-PEAK_HBM_GBS = 8000.0
-TILE_KERNELS = ("topk_fwd_tile", "topk_dz_tile", "dh_tile", "dw_tile")
+TILE_KERNELS = ("topk_fwd_tile", "topk_dz_tile", "full_fwd_tile", "full_dz_tile", "dh_tile", "dw_tile")
 
 
 def parse():
@@ -35,10 +39,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="head_topk_t4096")
-    ap.add_argument("--T", type=int, default=0, help="override the row count (sweep)")
+    ap.add_argument("--T", type=int, default=0, help="override the row count")
     ap.add_argument("--chunk-rows", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-extra", action="store_true", help="skip the packed and full-vocabulary workloads")
     ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--sweep", action="store_true", help="T in 4096, 16384, 65536, 262144: one line each")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 4 times (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -90,7 +96,6 @@ def traffic_from_profiles(kernel: str, workload: str):
 
 def cpu_baseline(inp, rows: int):
     """The oracle, as it stands, on the first `rows` rows of the same workload."""
-    import numpy as np
     from oracle import kd_oracle as O
     sl = {k: (v[:rows] if hasattr(v, "shape") and v.shape[0] == inp["H"].shape[0] else v) for k, v in inp.items()}
     W = O.as_f64(inp["W"])
@@ -107,25 +112,44 @@ def cpu_baseline(inp, rows: int):
                       f"(BLAS threads = cores), {dt:.1f} s"}
 
 
-def main():
-    a = parse()
-    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+def timed(step, steps: int, warmup: int):
+    """Run warmup + timed steps; returns (ms per step, {kernel: (launches, total ms)})."""
+    import torch
+    import chunked_kl_loss_logit_amd as kd
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    kd.profile_reset()
+    kd.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kd.profile_enable(False)
+    return elapsed / steps * 1e3, kd.profile_read()
 
-    if a.copy_probe:
-        copy_probe(a.copy_probe)
-        return
 
+def kernel_table(prof, ms: float, steps: int):
+    return {k: {"launches": n, "avg_ms": tot / n, "share": tot / (ms * steps)} for k, (n, tot) in prof.items()}
+
+
+def dominant(prof, flops_per_step: dict, steps: int):
+    """The tile kernel with the most GPU time, and its achieved rate:
+    algorithmic flops of one launch / its average launch duration."""
+    dom = max((k for k in prof if k in TILE_KERNELS), key=lambda k: prof[k][1])
+    n_l, tot_ms = prof[dom]
+    per_launch = flops_per_step[dom] / (n_l / steps)
+    return dom, per_launch / (tot_ms / n_l * 1e-3) / 1e12
+
+
+def run_topk(p, T: int, steps: int, warmup: int, chunk_rows: int):
+    """Time the top-K loss on preset p at T rows."""
     import torch
     import chunked_kl_loss_logit_amd as kd
     import kdinputs as G
 
-    p = G.PRESETS[a.workload] if a.workload in G.PRESETS else None
-    if p is None or p.full_vocab:
-        print(f"unknown top-K workload {a.workload}", file=sys.stderr)
-        sys.exit(2)
-    T = a.T or p.T
     inp = G.make_topk(T, p.d, p.V, p.K, p.dtype, tau=p.tau, teacher_var=p.teacher_var, mask=p.mask,
                       number=p.number, seq_len=p.seq_len, n_pad=p.n_pad, g="mean")
     dev = torch.device("cuda:0")
@@ -133,7 +157,6 @@ def main():
     M = None if inp["mask"] is None else inp["mask"].to(dev)
     n_valid = T if inp["mask"] is None else int(inp["mask"].sum())
     d, V, K, tau = p.d, p.V, p.K, p.tau
-
     kl = torch.empty(T, device=dev)
     lse = torch.empty(T, device=dev)
     dH = torch.empty_like(H)
@@ -144,71 +167,153 @@ def main():
     # allocation the calls need (the library allocates nothing itself)
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
-    ws = torch.empty(kd.kd_topk_kl_workspace_size(T, d, V, K, p.dtype, a.chunk_rows), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kd.kd_topk_kl_workspace_size(T, d, V, K, p.dtype, chunk_rows), dtype=torch.uint8, device=dev)
     kd.kd_topk_kl_fwd(H, W, I, A, M, tau, kl, lse, None, ws)
-    kd.kd_topk_kl_bwd(H, W, I, A, M, tau, lse, g, dH, dW, a.chunk_rows, ws)
+    kd.kd_topk_kl_bwd(H, W, I, A, M, tau, lse, g, dH, dW, chunk_rows, ws)
     torch.cuda.synchronize()
     peak_extra = torch.cuda.max_memory_allocated() - base + lse.numel() * 4  # + saved lse
 
     def step():
         kd.kd_topk_kl_fwd(H, W, I, A, M, tau, kl, lse, None, ws)
-        kd.kd_topk_kl_bwd(H, W, I, A, M, tau, lse, g, dH, dW, a.chunk_rows, ws)
+        kd.kd_topk_kl_bwd(H, W, I, A, M, tau, lse, g, dH, dW, chunk_rows, ws)
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    kd.profile_reset()
-    kd.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kd.profile_enable(False)
-    prof = kd.profile_read()
-    print(f"[bench] {a.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+    ms, prof = timed(step, steps, warmup)
+    # algorithmic flops per step of each tile kernel (valid rows only)
+    fl = {k: 2.0 * n_valid * d * V for k in ("topk_fwd_tile", "topk_dz_tile", "dh_tile", "dw_tile")}
+    dom, achieved = dominant(prof, fl, steps)
+    out = {"workload": p.name, "T": T, "valid_rows": n_valid, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+           "valid_tokens_per_s": n_valid / (ms * 1e-3),
+           "credited_tflops": 6.0 * n_valid * d * V / (ms * 1e-3) / 1e12,
+           "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
+           "kernels": kernel_table(prof, ms, steps)}
+    out["mfma_frac_credited"] = out["credited_tflops"] / PEAK_BF16_TFLOPS
+    out["mfma_frac_executed"] = out["mfma_frac_credited"] * 8.0 / 6.0  # the backward recomputes the projection
+    del H, W, I, A, g, M, kl, lse, dH, dW, ws
+    torch.cuda.empty_cache()
+    return out, inp
 
-    ms = elapsed / a.steps * 1e3
-    credited = 6.0 * n_valid * d * V          # 2dV forward + 4dV backward per token
-    executed = 8.0 * n_valid * d * V          # the backward recomputes the projection
-    tflops = credited / (ms * 1e-3) / 1e12
-    per_kernel = {k: {"launches": n, "avg_ms": tot / n, "share": tot / (ms * a.steps)} for k, (n, tot) in prof.items()}
-    dom = max((k for k in prof if k in TILE_KERNELS), key=lambda k: prof[k][1])
-    n_l, tot_ms = prof[dom]
-    avg_ms = tot_ms / n_l
-    # each tile kernel contracts one chunk: 2 * rows * d * V flops per launch
-    rows_per_launch = n_valid if dom == "topk_fwd_tile" else n_valid / (n_l / a.steps)
-    achieved = 2.0 * rows_per_launch * d * V / (avg_ms * 1e-3) / 1e12
-    workload = p.name if not a.T else f"head_topk_t{T}"
-    traffic = traffic_from_profiles(dom, workload)
 
+def run_full(p, steps: int, warmup: int, chunk_rows: int):
+    """Time the full-vocabulary loss on preset p."""
+    import torch
+    import chunked_kl_loss_logit_amd as kd
+    import kdinputs as G
+
+    T, d, dt, V, tau = p.T, p.d, p.dt_hidden, p.V, p.tau
+    inp = G.make_full(T, d, dt, V, p.dtype, tau=tau, number=p.number, g="mean")
+    dev = torch.device("cuda:0")
+    H, Ws, Ht, Wt, g = (inp[k].to(dev) for k in ("H", "Ws", "Ht", "Wt", "g"))
+    del inp
+    kl = torch.empty(T, device=dev)
+    ls = torch.empty(T, device=dev)
+    lt = torch.empty(T, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty(d, V, device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    ws = torch.empty(kd.kd_full_kl_workspace_size(T, d, dt, V, p.dtype, chunk_rows), dtype=torch.uint8, device=dev)
+    kd.kd_full_kl_fwd(H, Ws, Ht, Wt, None, tau, kl, ls, lt, ws)
+    kd.kd_full_kl_bwd(H, Ws, Ht, Wt, None, tau, ls, lt, g, dH, dW, chunk_rows, ws)
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated() - base + 2 * T * 4  # + saved lse_s, lse_t
+
+    def step():
+        kd.kd_full_kl_fwd(H, Ws, Ht, Wt, None, tau, kl, ls, lt, ws)
+        kd.kd_full_kl_bwd(H, Ws, Ht, Wt, None, tau, ls, lt, g, dH, dW, chunk_rows, ws)
+
+    ms, prof = timed(step, steps, warmup)
+    fl = {"full_fwd_tile": 2.0 * T * (d + dt) * V, "full_dz_tile": 2.0 * T * (d + dt) * V,
+          "dh_tile": 2.0 * T * d * V, "dw_tile": 2.0 * T * d * V}
+    dom, achieved = dominant(prof, fl, steps)
+    credited = (2.0 * (d + dt) + 4.0 * d) * V * T
+    executed = (4.0 * (d + dt) + 4.0 * d) * V * T
+    out = {"workload": p.name, "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+           "credited_tflops": credited / (ms * 1e-3) / 1e12,
+           "mfma_frac_credited": credited / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "mfma_frac_executed": executed / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
+           "kernels": kernel_table(prof, ms, steps)}
+    del H, Ws, Ht, Wt, g, kl, ls, lt, dH, dW, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def brief(r):
+    keep = ("workload", "T", "valid_rows", "ms_per_step", "tokens_per_s", "valid_tokens_per_s", "credited_tflops",
+            "mfma_frac_credited", "mfma_frac_executed", "peak_extra_hbm_bytes", "dominant", "dominant_tflops")
+    return {k: r[k] for k in keep if k in r}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if a.copy_probe:
+        copy_probe(a.copy_probe)
+        return
+
+    import kdinputs as G
+
+    if a.sweep:
+        for T in G.SWEEP_T:
+            p = G.sweep_preset(T)
+            steps = max(2, min(a.steps, (4 * 4096 * 10) // T))
+            r, _ = run_topk(p, T, steps, 1, a.chunk_rows)
+            print(json.dumps({"sweep": p.name, "steps": steps, **brief(r)}), flush=True)
+        return
+
+    p = G.PRESETS.get(a.workload)
+    if p is None:
+        print(f"unknown workload {a.workload}", file=sys.stderr)
+        sys.exit(2)
+    if p.full_vocab:
+        r = run_full(p, a.steps, a.warmup, a.chunk_rows)
+        print(json.dumps({"metric": "full-vocab KL fwd+bwd tokens/s", "value": r["tokens_per_s"],
+                          "unit": "tokens/s", **brief(r)}))
+        return
+
+    T = a.T or p.T
+    r, inp = run_topk(p, T, a.steps, a.warmup, a.chunk_rows)
+    workload = p.name if not a.T else f"{p.name}_T{T}"
+    dom = r["dominant"]
+    n_l = r["kernels"][dom]["launches"]
+    rows_per_launch = r["valid_rows"] if dom == "topk_fwd_tile" else r["valid_rows"] / (n_l / a.steps)
     out = {
         "metric": METRIC,
-        "value": T / (ms * 1e-3),
+        "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workload, "T": T, "d": d, "V": V, "K": K,
-                   "tau": tau, "valid_rows": n_valid, "chunk_rows": a.chunk_rows or 4096},
-        "valid_tokens_per_s": n_valid / (ms * 1e-3),
-        "credited_tflops": tflops,
-        "mfma_frac_credited": tflops / PEAK_BF16_TFLOPS,
-        "mfma_frac_executed": executed / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "peak_extra_hbm_bytes": int(peak_extra),
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
-        "kernels": per_kernel,
+        "config": {"workload": workload, "T": T, "d": p.d, "V": p.V, "K": p.K, "tau": p.tau,
+                   "valid_rows": r["valid_rows"], "chunk_rows": a.chunk_rows or 4096},
+        "valid_tokens_per_s": r["valid_tokens_per_s"],
+        "credited_tflops": r["credited_tflops"],
+        "mfma_frac_credited": r["mfma_frac_credited"],
+        "mfma_frac_executed": r["mfma_frac_executed"],
+        "peak_extra_hbm_bytes": r["peak_extra_hbm_bytes"],
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": r["dominant_tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": r["dominant_tflops"] / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_from_profiles(dom, workload),
+                     "flops_per_launch": 2.0 * rows_per_launch * p.d * p.V},
+        "kernels": r["kernels"],
     }
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, min(a.cpu_rows, T))
+    del inp
+    if not a.no_extra and not a.T and a.workload == "head_topk_t4096":
+        pk = G.PRESETS["head_topk_t32768_packed"]
+        fv = G.PRESETS["full_vocab_t16384"]
+        out["extra"] = {pk.name: brief(run_topk(pk, pk.T, 3, 1, a.chunk_rows)[0]),
+                        fv.name: brief(run_full(fv, 3, 1, a.chunk_rows))}
     print(json.dumps(out))
 
 
