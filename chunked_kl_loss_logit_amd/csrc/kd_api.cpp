@@ -128,8 +128,11 @@ kd_status need_align(const void* p, size_t a, const char* name) {
 // Sweeping 1..16 at the 4096 x 3072 x 128256 head moved each kernel by under 4%.
 constexpr int kRasterGroup = 4;
 
+// Vocabulary splits of the tile kernels: enough workgroups to fill the CUs,
+// and at least 8 so that at large T the workgroups running together read
+// several W panels instead of all hammering one.
 int splits_for(int64_t nrb, int64_t ntiles) {
-  int64_t s = cdiv(256, std::max<int64_t>(1, nrb));
+  int64_t s = std::max<int64_t>(cdiv(256, std::max<int64_t>(1, nrb)), 8);
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, ntiles));
 }
 

@@ -85,11 +85,15 @@ struct DmaRows {
       off[i] = (uint32_t)(row_ptr(i) - b) + 16u * ((threadIdx.x & 3) ^ ((m >> 2) & 3));
     }
   }
-  __device__ inline void issue(long s, char* dst) const {
+  // stage s of the rows `extra` bytes further on (a uniform offset, such as
+  // another row block of the same operand)
+  __device__ inline void issue(long s, long extra, char* dst) const {
     const int w = wave_id();
+    const uint32_t soff = (uint32_t)(s * kRowB + extra);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) dma16(rs, off[i], (uint32_t)(s * kRowB), dst + (w * kPer + i) * 1024);
+    for (int i = 0; i < kPer; ++i) dma16(rs, off[i], soff, dst + (w * kPer + i) * 1024);
   }
+  __device__ inline void issue(long s, char* dst) const { issue(s, 0L, dst); }
 };
 
 // n-contiguous operand ([K][N] row-major), BN columns per tile.

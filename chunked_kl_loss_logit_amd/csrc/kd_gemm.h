@@ -253,14 +253,17 @@ __device__ inline void store_block(StPair st, char* dst, long ld, long row0, lon
   }
 }
 
-// Float32 destination: store (or add to) a staged [256][32] block.
+// Float32 destination: store (or add to) a staged [256][32] block, rows
+// [max(row0, rlo), min(row0 + 256, nrows)).
 __device__ inline void rmw_block_f32(StPair st, float* dst, long ld, long row0, long col0, long nrows,
-                                     long ncols, bool accumulate) {
-  const int q = threadIdx.x & 7;  // float4 chunk of the row
+                                     long ncols, bool accumulate, long rlo = 0) {
+  const int tid = opaque((int)threadIdx.x);
+  const int q = tid & 7;  // float4 chunk of the row
   const long col = col0 + 4 * q;
   if (col >= ncols) return;
-  for (int r = threadIdx.x >> 3; r < kBM; r += kThreads / 8) {
+  for (int r = tid >> 3; r < kBM; r += kThreads / 8) {
     if (row0 + r >= nrows) break;
+    if (row0 + r < rlo) continue;
     float4 v = st_read4(st, r, q);
     float4* p = reinterpret_cast<float4*>(dst + (row0 + r) * ld + col);
     if (accumulate) {

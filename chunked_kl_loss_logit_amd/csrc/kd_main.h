@@ -21,6 +21,13 @@
 
 namespace kd {
 
+// One output tile of a persistent run: A is the operand's rows `a_off` bytes
+// after the rows init() saw, B is the panel at column n0.
+struct TileAt {
+  long a_off;
+  long n0;
+};
+
 // ------------------------------------------------------------------ shared stage product
 // Both operands k-contiguous rows.
 template <class E, int BN>
@@ -52,11 +59,11 @@ struct GRows {
   const char* rp[kPer];
   u32x4_t r[kPer];
   __device__ inline static int row_of(int j) { return (threadIdx.x >> 2) + 64 * j; }
-  __device__ inline void load(long kbyte0, long kbytes) {
+  __device__ inline void load(long kbyte0, long kbytes, long extra = 0) {
     const long off = kbyte0 + 16 * (threadIdx.x & 3);
     const bool kv = off < kbytes;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) r[j] = (kv && rp[j]) ? ld16(rp[j] + off) : zero4();
+    for (int j = 0; j < kPer; ++j) r[j] = (kv && rp[j]) ? ld16(rp[j] + extra + off) : zero4();
   }
   __device__ inline void store(char* dst) const {
 #pragma unroll
@@ -159,17 +166,18 @@ struct GenNN {
     nst = (kbytes + kRowB - 1) / kRowB;
   }
 
-  // tiles t = 0 .. ntiles-1 at columns n0_of(t); done(t, acc) after each
-  template <class N0, class Done>
-  __device__ inline void run(const Slots& sl, int ntiles, N0&& n0_of, Done&& done) {
+  // tiles t = 0 .. ntiles-1 described by at(t); done(t, acc) after each
+  template <class At, class Done>
+  __device__ inline void run(const Slots& sl, int ntiles, At&& at, Done&& done) {
     f32x16_t acc[4][BN / 64];
     for (int t = 0; t < ntiles; ++t) {
-      tile(sl, n0_of(t), acc);
+      const TileAt ta = at(t);
+      tile(sl, ta.n0, acc, ta.a_off);
       done(t, acc);
     }
   }
 
-  __device__ inline void tile(const Slots& sl, long n0, f32x16_t (&acc)[4][BN / 64]) {
+  __device__ inline void tile(const Slots& sl, long n0, f32x16_t (&acc)[4][BN / 64], long a_off = 0) {
     constexpr int KS = kRowB / E::kElem;
     bl.base = B + n0 * E::kElem;
     bl.n0 = n0;
@@ -177,7 +185,7 @@ struct GenNN {
     gen_contract(
         sl, nst,
         [&](long s) {
-          al.load(s * kRowB, kbytes);
+          al.load(s * kRowB, kbytes, a_off);
           bl.load(s * KS);
         },
         [&](char* da, char* db) {
@@ -216,19 +224,20 @@ struct DmaNN {
     rd.init_nn();
   }
 
-  // Tiles t = 0 .. ntiles-1 at columns n0_of(t) through one ring; done(t, acc)
-  // after each (see ring_run for what it may do).  Every tile must lie inside
-  // the operand: no column is clamped.
-  template <class N0, class Done>
-  __device__ inline void run(const Slots& sl, int ntiles, N0&& n0_of, Done&& done) {
+  // Tiles t = 0 .. ntiles-1 described by at(t), through one ring; done(t,
+  // acc) after each (see ring_run for what it may do).  Every tile must lie
+  // inside both operands: no row or column is clamped.
+  template <class At, class Done>
+  __device__ inline void run(const Slots& sl, int ntiles, At&& at, Done&& done) {
     b.init(B, LONG_MAX);
     f32x16_t acc[4][BN / 64];
     zero_acc<BN / 64>(acc);
     ring_run<kLpw, FragsNN<BN>>(
         sl, ntiles, nst,
         [&](long t, int s, char* da, char* db) {
-          a.issue(s, da);
-          b.issue(s, n0_of(t), db);
+          const TileAt ta = at((int)t);
+          a.issue(s, ta.a_off, da);
+          b.issue(s, ta.n0, db);
         },
         [&](const char* slot, FragsNN<BN>& f) { rd.read_nn(slot, f); },
         [&](const FragsNN<BN>& f) { mma_frags(f, acc); },

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_fwd_kernel(TopkFwdArgs a) {
   R.x = 0.f;
 
   mainloop.run(
-      sl, te - tb, [&](int i) -> long { return tile_n0(tb + i, V); },
+      sl, te - tb, [&](int i) { return TileAt{0, tile_n0(tb + i, V)}; },
       [&](int i, const f32x16_t (&acc)[4][4]) {
         const int vt = tb + i, n0 = tile_n0(vt, V), lo = vt * kBN, hi = min(lo + kBN, V);
         fwd_round<0, 0>(sl, acc, n0, lo, hi, R, a.c2);
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_kernel(TopkDzArgs a) {
   R.gs = R.rv ? a.g[t] * a.inv_tau : 0.f;
 
   mainloop.run(
-      sl, te - tb, [&](int i) -> long { return tile_n0(tb + i, V); },
+      sl, te - tb, [&](int i) { return TileAt{0, tile_n0(tb + i, V)}; },
       [&](int i, const f32x16_t (&acc)[4][4]) {
         const int vt = tb + i, n0 = tile_n0(vt, V), lo = vt * kBN, hi = min(lo + kBN, V);
         dz_round<E, 0, 0>(sl, acc, n0, lo, hi, row0, R, a);

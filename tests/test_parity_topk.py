@@ -50,6 +50,45 @@ def test_tiny_fp32_workload(g):
     check_all(got, oracle_all(inp), inp, torch.float32)
 
 
+# ---------------------------------------------------------------- direct-load path, several backward chunks
+# bf16 with d a multiple of 128 and V >= 256 takes the direct-load tile kernels:
+# d % 256 = 128 gives a dW row block that is shifted up (its first rows are
+# the previous block's and must not be added twice), V % 256 != 0 a last
+# vocabulary tile shifted left, V % 128 != 0 the general dH mainloop, and a
+# chunk smaller than T makes later chunks add to dW in place.
+@pytest.mark.parametrize("T,d,V,K,tau,mask,chunk", [
+    (700, 384, 1280, 16, 1.0, "none", 256),        # 3 chunks (256, 256, 188), dH on the direct-load path
+    (900, 640, 2568, 24, 1.7, "random10", 512),    # partial last vocab tile, V % 128 = 8, masked rows
+    (520, 256, 1024, 1, 1.0, "none", 256),         # K = 1, one row block, whole tiles only
+])
+def test_direct_load_path_chunks(T, d, V, K, tau, mask, chunk):
+    inp = G.make_topk(T, d, V, K, torch.bfloat16, tau=tau, mask=mask, number=12, g="normal")
+    say(f"direct-load T={T} d={d} V={V} K={K} chunk={chunk}")
+    got = run_topk(inp, chunk_rows=chunk)
+    check_all(got, oracle_all(inp), inp, torch.bfloat16, z_rtol=1e-4)
+
+
+def test_chunk_size_does_not_change_the_result():
+    # the chunked backward is a fixed-order split over tokens: any chunk size
+    # gives the oracle's gradients (to rounding), and the forward is untouched
+    inp = G.make_topk(1100, 384, 1536, 12, torch.bfloat16, tau=1.0, number=13, g="normal")
+    say("chunk sizes 256 / 512 / 4096 on T=1100 d=384 V=1536")
+    want = oracle_all(inp)
+    runs = [run_topk(inp, want_z=False, chunk_rows=c) for c in (256, 512, 4096)]
+    for r in runs:
+        assert_grad(r["dH"], want["dH"], torch.bfloat16, "dH")
+        assert_grad(r["dW"], want["dW"], torch.bfloat16, "dW")
+        np.testing.assert_array_equal(r["kl"], runs[0]["kl"])
+
+
+def test_runs_are_bitwise_deterministic():
+    inp = G.make_topk(800, 384, 2568, 16, torch.bfloat16, tau=1.3, mask="random10", number=14, g="normal")
+    say("determinism T=800 d=384 V=2568, two runs")
+    a, b = run_topk(inp, chunk_rows=256), run_topk(inp, chunk_rows=256)
+    for k in ("kl", "lse", "z", "dH", "dW"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
 # ---------------------------------------------------------------- ragged shapes, both dtypes
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("T,d,V,K,tau,mask", [
