@@ -9,8 +9,10 @@ over one batch of synthetic rows (inputs already in HBM): the output
 projection, online log Z, top-K gather, per-token KL, and the chunked backward
 (recomputed projection, dZ, dH, dW).  A step of the full-vocabulary workload
 is kd_full_kl_fwd plus kd_full_kl_bwd.  The default run prints ONE JSON line
-for the output-head workload (T=4096, d=3072, V=128256, K=64); the packed
-long-context and full-vocabulary workloads ride along in its "extra" object.
+for the output-head workload (T=4096, d=3072, V=128256, K=64); the same
+workload through the single-call kd_topk_kl_fwd_bwd (no recompute), the packed
+long-context and the full-vocabulary workloads ride along in its "extra"
+object.
 
 The loss-only benchmark of "Efficient Knowledge Distillation for LLMs: Offline
 Top-K Logits and a Fused Chunked KL Loss" (App. B) times the same path: output
@@ -185,12 +187,56 @@ def run_topk(p, T: int, steps: int, warmup: int, chunk_rows: int):
            "valid_tokens_per_s": n_valid / (ms * 1e-3),
            "credited_tflops": 6.0 * n_valid * d * V / (ms * 1e-3) / 1e12,
            "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
-           "kernels": kernel_table(prof, ms, steps)}
+           "kernels": kernel_table(prof, ms, steps), "steps_timed": steps}
     out["mfma_frac_credited"] = out["credited_tflops"] / PEAK_BF16_TFLOPS
     out["mfma_frac_executed"] = out["mfma_frac_credited"] * 8.0 / 6.0  # the backward recomputes the projection
     del H, W, I, A, g, M, kl, lse, dH, dW, ws
     torch.cuda.empty_cache()
     return out, inp
+
+
+def run_topk_fused(p, T: int, steps: int, warmup: int, chunk_rows: int):
+    """Time the single-call forward + backward (kd_topk_kl_fwd_bwd, no recompute) on preset p."""
+    import torch
+    import chunked_kl_loss_logit_amd as kd
+    import kdinputs as G
+
+    inp = G.make_topk(T, p.d, p.V, p.K, p.dtype, tau=p.tau, teacher_var=p.teacher_var, mask=p.mask,
+                      number=p.number, seq_len=p.seq_len, n_pad=p.n_pad, g="mean")
+    dev = torch.device("cuda:0")
+    H, W, I, A, g = (inp[k].to(dev) for k in ("H", "W", "I", "A", "g"))
+    M = None if inp["mask"] is None else inp["mask"].to(dev)
+    n_valid = T if inp["mask"] is None else int(inp["mask"].sum())
+    del inp
+    d, V, K, tau = p.d, p.V, p.K, p.tau
+    kl = torch.empty(T, device=dev)
+    lse = torch.empty(T, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty(d, V, device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    ws = torch.empty(kd.kd_topk_kl_fwd_bwd_workspace_size(T, d, V, K, p.dtype, chunk_rows), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        kd.kd_topk_kl_fwd_bwd(H, W, I, A, M, tau, g, kl, lse, None, dH, dW, chunk_rows, ws)
+
+    step()
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated() - base
+    ms, prof = timed(step, steps, warmup)
+    fl = {k: 2.0 * n_valid * d * V for k in ("topk_fwd_tile", "dh_tile", "dw_tile")}
+    dom, achieved = dominant(prof, fl, steps)
+    cred = 6.0 * n_valid * d * V / (ms * 1e-3) / 1e12
+    out = {"workload": p.name + "_one_call", "T": T, "valid_rows": n_valid, "ms_per_step": ms,
+           "tokens_per_s": T / (ms * 1e-3), "valid_tokens_per_s": n_valid / (ms * 1e-3), "credited_tflops": cred,
+           "mfma_frac_credited": cred / PEAK_BF16_TFLOPS, "mfma_frac_executed": cred / PEAK_BF16_TFLOPS,
+           "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
+           "kernels": kernel_table(prof, ms, steps), "steps_timed": steps}
+    del H, W, I, A, g, M, kl, lse, dH, dW, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_full(p, steps: int, warmup: int, chunk_rows: int):
@@ -233,7 +279,7 @@ def run_full(p, steps: int, warmup: int, chunk_rows: int):
            "mfma_frac_credited": credited / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
            "mfma_frac_executed": executed / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
            "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
-           "kernels": kernel_table(prof, ms, steps)}
+           "kernels": kernel_table(prof, ms, steps), "steps_timed": steps}
     del H, Ws, Ht, Wt, g, kl, ls, lt, dH, dW, ws
     torch.cuda.empty_cache()
     return out
@@ -242,7 +288,10 @@ def run_full(p, steps: int, warmup: int, chunk_rows: int):
 def brief(r):
     keep = ("workload", "T", "valid_rows", "ms_per_step", "tokens_per_s", "valid_tokens_per_s", "credited_tflops",
             "mfma_frac_credited", "mfma_frac_executed", "peak_extra_hbm_bytes", "dominant", "dominant_tflops")
-    return {k: r[k] for k in keep if k in r}
+    out = {k: r[k] for k in keep if k in r}
+    out["kernel_ms"] = {k: round(v["avg_ms"] * v["launches"] / r["steps_timed"], 4) for k, v in r["kernels"].items()} \
+        if "steps_timed" in r else None
+    return out
 
 
 def main():
@@ -312,7 +361,9 @@ def main():
     if not a.no_extra and not a.T and a.workload == "head_topk_t4096":
         pk = G.PRESETS["head_topk_t32768_packed"]
         fv = G.PRESETS["full_vocab_t16384"]
-        out["extra"] = {pk.name: brief(run_topk(pk, pk.T, 3, 1, a.chunk_rows)[0]),
+        one = run_topk_fused(p, T, a.steps, a.warmup, a.chunk_rows)
+        out["extra"] = {one["workload"]: brief(one),
+                        pk.name: brief(run_topk(pk, pk.T, 3, 1, a.chunk_rows)[0]),
                         fv.name: brief(run_full(fv, 3, 1, a.chunk_rows))}
     print(json.dumps(out))
 

@@ -18,14 +18,15 @@ import torch
 
 from ._binding import (  # noqa: F401
     EXPORTS, KD_BF16, KD_DEFAULT_CHUNK_ROWS, KD_F32, KD_MAX_K, LIB_PATH, KDError, kd_full_kl_bwd, kd_full_kl_fwd,
-    kd_full_kl_workspace_size, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_workspace_size, kd_version, lib,
+    kd_full_kl_workspace_size, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd, kd_topk_kl_fwd_bwd_workspace_size,
+    kd_topk_kl_workspace_size, kd_version, lib,
     profile_enable, profile_read, profile_reset,
 )
 
 __all__ = [
-    "topk_kl", "full_kl", "topk_kl_forward", "topk_kl_backward", "full_kl_forward", "full_kl_backward",
-    "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_full_kl_fwd", "kd_full_kl_bwd",
-    "kd_topk_kl_workspace_size", "kd_full_kl_workspace_size", "KDError",
+    "topk_kl", "full_kl", "topk_kl_forward", "topk_kl_backward", "topk_kl_forward_backward", "full_kl_forward",
+    "full_kl_backward", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_topk_kl_fwd_bwd", "kd_full_kl_fwd", "kd_full_kl_bwd",
+    "kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd_workspace_size", "kd_full_kl_workspace_size", "KDError",
 ]
 
 
@@ -57,6 +58,23 @@ def topk_kl_backward(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl, chunk
     kd_topk_kl_bwd(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl.float().contiguous(), dH, dW, chunk_rows,
                    workspace)
     return dH, dW
+
+
+def topk_kl_forward_backward(H, W, topk_idx, topk_logits, mask, tau, grad_kl, chunk_rows=0, want_z_topk=False,
+                             workspace=None):
+    """kl, lse, z_topk (or None), dH and dW in one call, for a known grad_kl."""
+    T, d = H.shape
+    V, K = W.shape[1], topk_idx.shape[1]
+    kl = torch.empty(T, dtype=torch.float32, device=H.device)
+    lse = torch.empty(T, dtype=torch.float32, device=H.device)
+    z = torch.empty(T, K, dtype=torch.float32, device=H.device) if want_z_topk else None
+    dH = torch.empty_like(H)
+    dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
+    if workspace is None:
+        workspace = _workspace(kd_topk_kl_fwd_bwd_workspace_size(T, d, V, K, H.dtype, chunk_rows), H.device)
+    kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logits, mask, tau, grad_kl.float().contiguous(), kl, lse, z, dH, dW,
+                       chunk_rows, workspace)
+    return kl, lse, z, dH, dW
 
 
 def full_kl_forward(H, Ws, Ht, Wt, mask=None, tau=1.0, workspace=None):

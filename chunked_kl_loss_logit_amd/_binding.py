@@ -25,6 +25,7 @@ STATUS = {
 
 EXPORTS = (
     "kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd",
+    "kd_topk_kl_fwd_bwd_workspace_size", "kd_topk_kl_fwd_bwd",
     "kd_full_kl_workspace_size", "kd_full_kl_fwd", "kd_full_kl_bwd",
     "kd_status_string", "kd_last_error", "kd_version",
     "kd_profile_enable", "kd_profile_count", "kd_profile_get", "kd_profile_reset",
@@ -56,11 +57,15 @@ def lib() -> ctypes.CDLL:
     L.kd_topk_kl_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
     L.kd_topk_kl_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, sz, vp]
     L.kd_topk_kl_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, i64, vp, sz, vp]
+    L.kd_topk_kl_fwd_bwd_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
+    L.kd_topk_kl_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp, i64,
+                                     vp, sz, vp]
     L.kd_full_kl_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
     L.kd_full_kl_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, sz, vp]
     L.kd_full_kl_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, i64, vp, sz,
                                  vp]
-    for f in ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_full_kl_workspace_size",
+    for f in ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_topk_kl_fwd_bwd_workspace_size",
+              "kd_topk_kl_fwd_bwd", "kd_full_kl_workspace_size",
               "kd_full_kl_fwd", "kd_full_kl_bwd", "kd_profile_enable", "kd_profile_get", "kd_profile_reset"):
         getattr(L, f).restype = st
     L.kd_status_string.argtypes = [st]
@@ -113,6 +118,13 @@ def kd_topk_kl_workspace_size(T, d, V, K, dtype, chunk_rows=0) -> int:
     return out.value
 
 
+def kd_topk_kl_fwd_bwd_workspace_size(T, d, V, K, dtype, chunk_rows=0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().kd_topk_kl_fwd_bwd_workspace_size(T, d, V, K, _dtype_code(dtype), chunk_rows, ctypes.byref(out)),
+           "kd_topk_kl_fwd_bwd_workspace_size")
+    return out.value
+
+
 def kd_full_kl_workspace_size(T, d, dt_hidden, V, dtype, chunk_rows=0) -> int:
     out = ctypes.c_size_t(0)
     _check(lib().kd_full_kl_workspace_size(T, d, dt_hidden, V, _dtype_code(dtype), chunk_rows, ctypes.byref(out)),
@@ -142,6 +154,19 @@ def kd_topk_kl_bwd(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl, dH, dW,
                                 int(chunk_rows), _ptr(workspace),
                                 workspace.numel() if workspace is not None else 0, _stream(stream)),
            "kd_topk_kl_bwd")
+
+
+def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logits, mask, tau, grad_kl, kl, lse, z_topk, dH, dW, chunk_rows,
+                       workspace, stream=None):
+    """Enqueue the top-K forward and backward in one call (no recompute)."""
+    T, d = H.shape
+    V = W.shape[1]
+    K = topk_idx.shape[1]
+    _check(lib().kd_topk_kl_fwd_bwd(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask), float(tau),
+                                    T, d, V, K, _dtype_code(H.dtype), _ptr(grad_kl), _ptr(kl), _ptr(lse),
+                                    _ptr(z_topk), _ptr(dH), _ptr(dW), int(chunk_rows), _ptr(workspace),
+                                    workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "kd_topk_kl_fwd_bwd")
 
 
 def kd_full_kl_fwd(H, Ws, Ht, Wt, mask, tau, kl, lse_s, lse_t, workspace, stream=None):

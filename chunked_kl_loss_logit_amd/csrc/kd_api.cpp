@@ -122,7 +122,6 @@ kd_status need_align(const void* p, size_t a, const char* name) {
     if (_e != hipSuccess) return fail(KD_ERR_HIP, std::string(name) + ": " + hipGetErrorString(_e)); \
   } while (0)
 
-// Vocabulary splits: enough workgroups to cover the 256 compute units once.
 // Row blocks per raster group of the tile kernels: consecutive workgroups of
 // one XCD share a row block's operand across this many row blocks (grouped_coords).
 // Sweeping 1..16 at the 4096 x 3072 x 128256 head moved each kernel by under 4%.
@@ -180,6 +179,11 @@ struct TopkPlan {
   size_t o_pair, o_perm, o_ent, o_rows, o_count, o_part;
   ChunkPlan ch;
   size_t fwd_total, total;  // bytes the forward call needs; bytes both calls need
+  // single-call forward + backward: per-chunk partials, the chunk's fp32
+  // logits and the backward chunk buffers all live at once
+  int S_c;
+  ChunkPlan ch_f;
+  size_t o_part_c, o_z, fused_total;
 };
 
 TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t chunk_rows) {
@@ -198,6 +202,12 @@ TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t
   p.ch = plan_chunk(T, d, V, elem, chunk_rows, bw);
   p.fwd_total = fw.off;
   p.total = std::max(fw.off, bw.off);
+  Carver fu = cv;
+  p.S_c = splits_for(cdiv(chunk_of(T, chunk_rows), kd::kTileM), p.ntiles);
+  p.o_part_c = fu.take((size_t)p.S_c * chunk_of(T, chunk_rows) * 16);
+  p.ch_f = plan_chunk(T, d, V, elem, chunk_rows, fu);
+  p.o_z = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
+  p.fused_total = fu.off;
   return p;
 }
 
@@ -238,6 +248,47 @@ kd_status check_workspace(const void* ws, size_t have, size_t want) {
   return KD_OK;
 }
 
+// dH and dW of one backward chunk whose dZ sits in the chunk buffer:
+// H^T of the chunk's rows, dH split over the vocabulary and reduced in a
+// fixed order, dW stored (first chunk) or added in place.
+kd_status grad_chunk(const void* H, const void* W, void* dH, float* dW, int elem, int64_t d, int64_t V,
+                     const kd::Compact& c, const ChunkPlan& ch, char* dz, char* hT, float* dhp, int64_t c0,
+                     bool accumulate, hipStream_t st) {
+  KD_LAUNCH("gather_transpose", st, kd::launch_gather_transpose(H, elem, d, c, c0, ch.C, hT, st));
+  kd::DhArgs ha{};
+  ha.dz = dz;
+  ha.W = static_cast<const char*>(W);
+  ha.part = dhp;
+  ha.count = c.count;
+  ha.c0 = c0;
+  ha.C = ch.C;
+  ha.ldz = ch.ldz;
+  ha.d = d;
+  ha.V = V;
+  ha.nrb = ch.nrb_dh;
+  ha.ncb = ch.ncb_dh;
+  ha.group = kRasterGroup;
+  ha.S = ch.S_dh;
+  KD_LAUNCH("dh_tile", st, kd::launch_dh(elem, ha, st));
+  KD_LAUNCH("reduce_dh", st, kd::launch_reduce_dh(dhp, ch.S_dh, ch.C, d, c, c0, dH, elem, st));
+  kd::DwArgs wa{};
+  wa.hT = hT;
+  wa.dz = dz;
+  wa.dW = dW;
+  wa.count = c.count;
+  wa.c0 = c0;
+  wa.C = ch.C;
+  wa.ldz = ch.ldz;
+  wa.d = d;
+  wa.V = V;
+  wa.nrb = ch.nrb_dw;
+  wa.ncb = ch.ncb_dw;
+  wa.group = kRasterGroup;
+  wa.accumulate = accumulate;
+  KD_LAUNCH("dw_tile", st, kd::launch_dw(elem, wa, st));
+  return KD_OK;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -258,7 +309,7 @@ const char* kd_status_string(kd_status s) {
 
 const char* kd_last_error(void) { return g_err.c_str(); }
 
-int kd_version(void) { return 10000; }
+int kd_version(void) { return 10100; }
 
 kd_status kd_profile_enable(int on) {
   g_prof_on = on != 0;
@@ -340,6 +391,10 @@ kd_status kd_topk_kl_fwd(const void* H, const void* W, const int32_t* topk_idx, 
   a.z_topk = z_topk;
   a.part = part;
   a.part_stride = T;
+  a.part_row0 = 0;
+  a.c0 = 0;
+  a.C = T;
+  a.T = T;
   a.d = d;
   a.V = V;
   a.K = K;
@@ -349,7 +404,7 @@ kd_status kd_topk_kl_fwd(const void* H, const void* W, const int32_t* topk_idx, 
   a.group = kRasterGroup;
   a.c2 = (float)(1.4426950408889634 / (double)tau);
   KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
-  KD_LAUNCH("topk_combine", st, kd::launch_topk_combine(part, p.S, T, c, mask, rd.ent, T, tau, kl, lse, st));
+  KD_LAUNCH("topk_combine", st, kd::launch_topk_combine(part, p.S, T, c, mask, rd.ent, T, tau, kl, lse, 0, T, true, st));
   return KD_OK;
 }
 
@@ -421,38 +476,7 @@ kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx, 
     za.c2 = (float)(1.4426950408889634 / (double)tau);
     za.inv_tau = 1.0f / tau;
     KD_LAUNCH("topk_dz_tile", st, kd::launch_topk_dz(elem, za, st));
-    KD_LAUNCH("gather_transpose", st, kd::launch_gather_transpose(H, elem, d, c, c0, ch.C, hT, st));
-    kd::DhArgs ha{};
-    ha.dz = dz;
-    ha.W = static_cast<const char*>(W);
-    ha.part = dhp;
-    ha.count = c.count;
-    ha.c0 = c0;
-    ha.C = ch.C;
-    ha.ldz = ch.ldz;
-    ha.d = d;
-    ha.V = V;
-    ha.nrb = ch.nrb_dh;
-    ha.ncb = ch.ncb_dh;
-    ha.group = kRasterGroup;
-    ha.S = ch.S_dh;
-    KD_LAUNCH("dh_tile", st, kd::launch_dh(elem, ha, st));
-    KD_LAUNCH("reduce_dh", st, kd::launch_reduce_dh(dhp, ch.S_dh, ch.C, d, c, c0, dH, elem, st));
-    kd::DwArgs wa{};
-    wa.hT = hT;
-    wa.dz = dz;
-    wa.dW = dW;
-    wa.count = c.count;
-    wa.c0 = c0;
-    wa.C = ch.C;
-    wa.ldz = ch.ldz;
-    wa.d = d;
-    wa.V = V;
-    wa.nrb = ch.nrb_dw;
-    wa.ncb = ch.ncb_dw;
-    wa.group = kRasterGroup;
-    wa.accumulate = k > 0;
-    KD_LAUNCH("dw_tile", st, kd::launch_dw(elem, wa, st));
+    KD_TRY(grad_chunk(H, W, dH, dW, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
   }
   return KD_OK;
 }
@@ -588,38 +612,118 @@ kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const vo
     za.c2 = (float)(1.4426950408889634 / (double)tau);
     za.inv_tau = 1.0f / tau;
     KD_LAUNCH("full_dz_tile", st, kd::launch_full_dz(elem, za, st));
-    KD_LAUNCH("gather_transpose", st, kd::launch_gather_transpose(H, elem, d, c, c0, ch.C, hT, st));
-    kd::DhArgs ha{};
-    ha.dz = dz;
-    ha.W = static_cast<const char*>(Ws);
-    ha.part = dhp;
-    ha.count = c.count;
-    ha.c0 = c0;
-    ha.C = ch.C;
-    ha.ldz = ch.ldz;
-    ha.d = d;
-    ha.V = V;
-    ha.nrb = ch.nrb_dh;
-    ha.ncb = ch.ncb_dh;
-    ha.group = kRasterGroup;
-    ha.S = ch.S_dh;
-    KD_LAUNCH("dh_tile", st, kd::launch_dh(elem, ha, st));
-    KD_LAUNCH("reduce_dh", st, kd::launch_reduce_dh(dhp, ch.S_dh, ch.C, d, c, c0, dH, elem, st));
-    kd::DwArgs wa{};
-    wa.hT = hT;
-    wa.dz = dz;
-    wa.dW = dWs;
-    wa.count = c.count;
-    wa.c0 = c0;
-    wa.C = ch.C;
-    wa.ldz = ch.ldz;
-    wa.d = d;
-    wa.V = V;
-    wa.nrb = ch.nrb_dw;
-    wa.ncb = ch.ncb_dw;
-    wa.group = kRasterGroup;
-    wa.accumulate = k > 0;
-    KD_LAUNCH("dw_tile", st, kd::launch_dw(elem, wa, st));
+    KD_TRY(grad_chunk(H, Ws, dH, dWs, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
+  }
+  return KD_OK;
+}
+
+// ---------------------------------------------------------------- top-K, forward and backward in one call
+kd_status kd_topk_kl_fwd_bwd_workspace_size(int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                                            int64_t chunk_rows, size_t* bytes) {
+  g_err.clear();
+  KD_TRY(need(bytes, "bytes"));
+  KD_TRY(check_common(T, d, V, dt, 1.0f));
+  KD_TRY(check_k(T, K, V));
+  if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
+  *bytes = T == 0 ? 0 : plan_topk(T, d, V, K, elem_of(dt), chunk_rows).fused_total;
+  return KD_OK;
+}
+
+kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                             const uint8_t* mask, float tau, int64_t T, int64_t d, int64_t V, int64_t K,
+                             kd_dtype dt, const float* grad_kl, float* kl, float* lse, float* z_topk, void* dH,
+                             float* dW, int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  KD_TRY(check_common(T, d, V, dt, tau));
+  KD_TRY(check_k(T, K, V));
+  KD_TRY(need(dW, "dW"));
+  KD_TRY(need_align(dW, 16, "dW"));
+  if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    KD_LAUNCH("fill_zero", st, kd::launch_fill_zero(dW, d * V * 4, st));
+    return KD_OK;
+  }
+  KD_TRY(need(H, "H"));
+  KD_TRY(need(W, "W"));
+  KD_TRY(need(topk_idx, "topk_idx"));
+  KD_TRY(need(topk_logits, "topk_logits"));
+  KD_TRY(need(grad_kl, "grad_kl"));
+  KD_TRY(need(kl, "kl"));
+  KD_TRY(need(lse, "lse"));
+  KD_TRY(need(dH, "dH"));
+  KD_TRY(need_align(H, 16, "H"));
+  KD_TRY(need_align(W, 16, "W"));
+  KD_TRY(need_align(dH, 16, "dH"));
+  KD_TRY(need_align(topk_idx, 4, "topk_idx"));
+  KD_TRY(need_align(topk_logits, 4, "topk_logits"));
+  KD_TRY(need_align(grad_kl, 4, "grad_kl"));
+  KD_TRY(need_align(kl, 4, "kl"));
+  KD_TRY(need_align(lse, 4, "lse"));
+  KD_TRY(need_align(z_topk, 4, "z_topk"));
+  const int elem = elem_of(dt);
+  const TopkPlan p = plan_topk(T, d, V, K, elem, chunk_rows);
+  KD_TRY(check_workspace(workspace, workspace_bytes, p.fused_total));
+
+  kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
+  kd::TopkRowData rd{at<int2>(workspace, p.o_pair), at<uint16_t>(workspace, p.o_perm), at<float>(workspace, p.o_ent)};
+  float* part = at<float>(workspace, p.o_part_c);
+  float* z = at<float>(workspace, p.o_z);
+  const ChunkPlan& ch = p.ch_f;
+  char* dz = at<char>(workspace, ch.o_dz);
+  char* hT = at<char>(workspace, ch.o_hT);
+  float* dhp = at<float>(workspace, ch.o_dhp);
+  const float c2 = (float)(1.4426950408889634 / (double)tau);
+
+  KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
+  KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, tau, rd, z_topk, st));
+  KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * elem, dH, st));
+  const int64_t nchunks = cdiv(T, ch.C);
+  for (int64_t k = 0; k < nchunks; ++k) {
+    const int64_t c0 = k * ch.C;
+    // the chunk's logits: log Z partials, the top-K gather, and z kept in fp32
+    kd::TopkFwdArgs a{};
+    a.H = static_cast<const char*>(H);
+    a.W = static_cast<const char*>(W);
+    a.c = c;
+    a.rd = rd;
+    a.z_topk = z_topk;
+    a.part = part;
+    a.part_stride = ch.C;
+    a.part_row0 = c0;
+    a.c0 = c0;
+    a.C = ch.C;
+    a.zout = z;
+    a.ldz = ch.ldz;
+    a.T = T;
+    a.d = d;
+    a.V = V;
+    a.K = K;
+    a.nrb = ch.nrb_c;
+    a.S = p.S_c;
+    a.ntiles = p.ntiles;
+    a.group = kRasterGroup;
+    a.c2 = c2;
+    KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
+    KD_LAUNCH("topk_combine", st,
+              kd::launch_topk_combine(part, p.S_c, ch.C, c, mask, rd.ent, T, tau, kl, lse, c0, c0 + ch.C, k == 0, st));
+    // dZ from the kept logits: no second projection
+    kd::TopkDzFromZArgs za{};
+    za.z = z;
+    za.dz = dz;
+    za.ldz = ch.ldz;
+    za.c = c;
+    za.c0 = c0;
+    za.C = ch.C;
+    za.V = V;
+    za.K = K;
+    za.rd = rd;
+    za.lse = lse;
+    za.g = grad_kl;
+    za.c2 = c2;
+    za.inv_tau = 1.0f / tau;
+    KD_LAUNCH("topk_dz_from_z", st, kd::launch_topk_dz_from_z(elem, za, st));
+    KD_TRY(grad_chunk(H, W, dH, dW, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
   }
   return KD_OK;
 }

@@ -31,8 +31,12 @@ struct Compact {
 hipError_t launch_compact(const uint8_t* mask, int64_t T, Compact c, hipStream_t st);
 hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8_t* mask, int64_t T, int64_t K,
                             float tau, TopkRowData rd, float* z_topk, hipStream_t st);
+// Merges the split partials of compacted rows [jb, je) (partial row p holds
+// compacted row jb + p) into kl and lse; with zero_masked, also zeroes kl and
+// lse of every masked row.
 hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
-                               const float* ent, int64_t T, float tau, float* kl, float* lse, hipStream_t st);
+                               const float* ent, int64_t T, float tau, float* kl, float* lse, int64_t jb, int64_t je,
+                               bool zero_masked, hipStream_t st);
 hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
                                int64_t T, float* kl, float* lse_s, float* lse_t, hipStream_t st);
 // H^T of one chunk of compacted rows: out[j][i] = H[rows[c0 + i]][j] for
@@ -52,9 +56,12 @@ struct TopkFwdArgs {
   Compact c;
   TopkRowData rd;
   float* z_topk;  // nullable
-  float* part;    // [S][part_stride][4]
-  int64_t part_stride;  // rows of H (T)
-  int64_t d, V, K;
+  float* part;    // [S][part_stride][4], row p of a split is compacted row part_row0 + p
+  int64_t part_stride, part_row0;
+  int64_t c0, C;  // compacted rows [c0, c0 + C) (all rows: 0, T)
+  float* zout;    // nullable: the logits of those rows, fp32 [C][ldz]
+  int64_t ldz;
+  int64_t T, d, V, K;
   int nrb, S, ntiles;
   int group;  // row blocks per raster group (grouped_coords)
   float c2;  // log2(e) / tau
@@ -77,6 +84,22 @@ struct TopkDzArgs {
   float c2, inv_tau;
 };
 hipError_t launch_topk_dz(int elem, const TopkDzArgs& a, hipStream_t st);
+
+// dZ of a chunk from its stored fp32 logits (no recompute):
+// dz[i][v] = (g/tau) (2^(z c2 - L2) - sum of p over hits) for the chunk's
+// valid rows i and v < V; zero for the chunk's other rows.
+struct TopkDzFromZArgs {
+  const float* z;    // [C][ldz]
+  char* dz;          // [C][ldz], element type
+  int64_t ldz;
+  Compact c;
+  int64_t c0, C, V, K;
+  TopkRowData rd;
+  const float* lse;
+  const float* g;
+  float c2, inv_tau;
+};
+hipError_t launch_topk_dz_from_z(int elem, const TopkDzFromZArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- full-vocabulary tiles
 struct FullFwdArgs {

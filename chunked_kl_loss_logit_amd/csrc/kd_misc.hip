@@ -180,20 +180,21 @@ hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8
 // Thread j: (a) zero kl/lse of row j if it is masked, (b) if j is a valid
 // compacted row, merge its S partials (m2, l, x) in split order.
 __global__ void topk_combine_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask,
-                                    const float* ent, long T, float inv_tau, float* kl, float* lse) {
+                                    const float* ent, long T, float inv_tau, float* kl, float* lse, long jb, long je,
+                                    int zero_masked) {
   const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= T) return;
-  if (mask != nullptr && mask[j] == 0) {
+  if (zero_masked && mask != nullptr && mask[j] == 0) {
     kl[j] = 0.f;
     lse[j] = 0.f;
   }
-  if (j >= *c.count) return;
-  const float4* pp = reinterpret_cast<const float4*>(part);
+  if (j < jb || j >= je || j >= *c.count) return;
+  const float4* pp = reinterpret_cast<const float4*>(part) + (j - jb);
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, pp[(long)s * stride + j].x);
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pp[(long)s * stride].x);
   float l = 0.f, x = 0.f;
   for (int s = 0; s < S; ++s) {
-    const float4 q = pp[(long)s * stride + j];
+    const float4 q = pp[(long)s * stride];
     l += q.y * exp2f(q.x - M);
     x += q.z;
   }
@@ -204,10 +205,11 @@ __global__ void topk_combine_kernel(const float* part, int S, long stride, Compa
 }
 
 hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
-                               const float* ent, int64_t T, float tau, float* kl, float* lse, hipStream_t st) {
+                               const float* ent, int64_t T, float tau, float* kl, float* lse, int64_t jb, int64_t je,
+                               bool zero_masked, hipStream_t st) {
   const dim3 grid((unsigned)((T + 255) / 256));
   hipLaunchKernelGGL(topk_combine_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, ent, (long)T,
-                     1.0f / tau, kl, lse);
+                     1.0f / tau, kl, lse, (long)jb, (long)je, zero_masked ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -179,10 +179,13 @@ __device__ inline int tile_n0(int vt, int V) { return V >= kBN ? min(vt * kBN, V
 // ascending column order: half 0 blocks 0..3, then half 1.
 template <int H, int NBI>
 __device__ inline void fwd_round(const Slots& sl, const f32x16_t (&acc)[4][4], int n0, int lo, int hi, FwdRow& R,
-                                 float c2) {
+                                 const TopkFwdArgs& a, long row0, long M) {
+  const int cb = n0 + H * 128 + NBI * 32;
   stage_half<NBI, 4>(sl.ep, H, acc);
   ring_barrier();
-  R.consume(sl.ep, n0 + H * 128 + NBI * 32, lo, hi, c2);
+  R.consume(sl.ep, cb, lo, hi, a.c2);
+  // both only read the staged block: the logits go out as they are
+  if (a.zout) store_block<F32>(sl.ep, reinterpret_cast<char*>(a.zout), a.ldz, row0, cb, M, a.ldz, lo);
   ring_barrier();
 }
 
@@ -200,32 +203,38 @@ __device__ inline void dz_round(const Slots& sl, const f32x16_t (&acc)[4][4], in
 
 }  // namespace
 
+// Rows: the compacted valid rows [c0, c0 + C) (the plain forward takes them
+// all); partials are indexed by compacted position, and with zout set the
+// tile's logits are also written out, fp32, one row per compacted row.
 template <class Main, class E>
 __global__ __launch_bounds__(kThreads, 1) void topk_fwd_kernel(TopkFwdArgs a) {
   KD_DECLARE_SLOTS(sl);
 
-  const int count = *a.c.count;
+  const long count = *a.c.count;
+  const long M = min(a.C, count - a.c0);  // rows of this launch
+  if (M <= 0) return;
   int rb, sp;
   grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, a.group, rb, sp);
   const int row0 = rb * kBM;
-  if (row0 >= count) return;
+  if (row0 >= M) return;
   const int tb = (int)((long)a.ntiles * sp / a.S);
   const int te = (int)((long)a.ntiles * (sp + 1) / a.S);
   const int V = (int)a.V;
+  const int32_t* rows = a.c.rows + a.c0;
 
   Main mainloop;
   mainloop.init(
       a.H,
       [&](int r) -> const char* {
-        const int i = row0 + r;
-        return i < count ? a.H + (long)a.c.rows[i] * a.d * E::kElem : nullptr;
+        const long i = row0 + r;
+        return i < M ? a.H + (long)rows[i] * a.d * E::kElem : nullptr;
       },
       a.W, a.V * E::kElem, a.V, a.d);
 
   const int ti = row0 + (int)threadIdx.x;
   FwdRow R;
-  R.rv = ti < count;
-  const long t = R.rv ? a.c.rows[ti] : 0;
+  R.rv = ti < M;
+  const long t = R.rv ? rows[ti] : 0;
   R.cur.pair = a.rd.pair;
   R.cur.end = (int)(t * a.K + (R.rv ? a.K : 0));
   R.cur.c = lower_bound(a.rd.pair, (int)(t * a.K), R.cur.end, (long)tb * kBN);
@@ -241,18 +250,18 @@ __global__ __launch_bounds__(kThreads, 1) void topk_fwd_kernel(TopkFwdArgs a) {
       sl, te - tb, [&](int i) { return TileAt{0, tile_n0(tb + i, V)}; },
       [&](int i, const f32x16_t (&acc)[4][4]) {
         const int vt = tb + i, n0 = tile_n0(vt, V), lo = vt * kBN, hi = min(lo + kBN, V);
-        fwd_round<0, 0>(sl, acc, n0, lo, hi, R, a.c2);
-        fwd_round<0, 1>(sl, acc, n0, lo, hi, R, a.c2);
-        fwd_round<0, 2>(sl, acc, n0, lo, hi, R, a.c2);
-        fwd_round<0, 3>(sl, acc, n0, lo, hi, R, a.c2);
-        fwd_round<1, 0>(sl, acc, n0, lo, hi, R, a.c2);
-        fwd_round<1, 1>(sl, acc, n0, lo, hi, R, a.c2);
-        fwd_round<1, 2>(sl, acc, n0, lo, hi, R, a.c2);
-        fwd_round<1, 3>(sl, acc, n0, lo, hi, R, a.c2);
+        fwd_round<0, 0>(sl, acc, n0, lo, hi, R, a, row0, M);
+        fwd_round<0, 1>(sl, acc, n0, lo, hi, R, a, row0, M);
+        fwd_round<0, 2>(sl, acc, n0, lo, hi, R, a, row0, M);
+        fwd_round<0, 3>(sl, acc, n0, lo, hi, R, a, row0, M);
+        fwd_round<1, 0>(sl, acc, n0, lo, hi, R, a, row0, M);
+        fwd_round<1, 1>(sl, acc, n0, lo, hi, R, a, row0, M);
+        fwd_round<1, 2>(sl, acc, n0, lo, hi, R, a, row0, M);
+        fwd_round<1, 3>(sl, acc, n0, lo, hi, R, a, row0, M);
         R.cur.refill();
       });
   if (R.rv) {
-    float4* o = reinterpret_cast<float4*>(a.part) + (long)sp * a.part_stride + ti;
+    float4* o = reinterpret_cast<float4*>(a.part) + (long)sp * a.part_stride + (a.c0 - a.part_row0) + ti;
     *o = make_float4(R.m2, R.l, R.x, 0.f);
   }
 }
@@ -309,11 +318,67 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_kernel(TopkDzArgs a) {
       });
 }
 
+// ---------------------------------------------------------------- dZ from stored logits
+// One thread: EPT consecutive columns (16 bytes of dZ) of one row.  The row's
+// cached entries are sorted, so the hits of [v0, v0 + EPT) are found with a
+// binary search over the K entries (shared by the block, so L1-resident) and
+// subtracted before the one rounding to the element type.
+template <class E>
+__global__ __launch_bounds__(256) void topk_dz_from_z_kernel(TopkDzFromZArgs a) {
+  constexpr int EPT = E::kEpc;
+  const long i = blockIdx.y;  // row of the chunk
+  const long v0 = ((long)blockIdx.x * 256 + threadIdx.x) * EPT;
+  if (v0 >= a.V) return;
+  const long M = min(a.C, (long)*a.c.count - a.c0);
+  float o[EPT];
+  if (i < M) {
+    const long t = a.c.rows[a.c0 + i];
+    const float L2 = a.lse[t] * kLog2e, gs = a.g[t] * a.inv_tau;
+    const float* zr = a.z + i * a.ldz + v0;
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) {
+      const float4 z4 = *reinterpret_cast<const float4*>(zr + e);
+      o[e + 0] = gs * fast_exp2(fmaf(z4.x, a.c2, -L2));
+      o[e + 1] = gs * fast_exp2(fmaf(z4.y, a.c2, -L2));
+      o[e + 2] = gs * fast_exp2(fmaf(z4.z, a.c2, -L2));
+      o[e + 3] = gs * fast_exp2(fmaf(z4.w, a.c2, -L2));
+    }
+    const int b = (int)(t * a.K), e = (int)(t * a.K + a.K);
+    for (int c = lower_bound(a.rd.pair, b, e, v0); c < e; ++c) {
+      const int2 pr = a.rd.pair[c];
+      if ((long)pr.x >= v0 + EPT) break;
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) o[q] = (long)pr.x == v0 + q ? o[q] - gs * __int_as_float(pr.y) : o[q];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) o[q] = 0.f;
+  }
+  char* dst = a.dz + (i * a.ldz + v0) * E::kElem;
+  if constexpr (EPT == 8) {
+    const u32x4_t w{Bf16::pack2(o[0], o[1]), Bf16::pack2(o[2], o[3]), Bf16::pack2(o[4], o[5]),
+                    Bf16::pack2(o[6], o[7])};
+    *reinterpret_cast<u32x4_t*>(dst) = w;
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_topk_dz_from_z(int elem, const TopkDzFromZArgs& a, hipStream_t st) {
+  const int ept = elem == 2 ? Bf16::kEpc : F32::kEpc;
+  const dim3 grid((unsigned)((a.V + 256L * ept - 1) / (256L * ept)), (unsigned)a.C), block(256);
+  if (elem == 2)
+    hipLaunchKernelGGL(topk_dz_from_z_kernel<Bf16>, grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL(topk_dz_from_z_kernel<F32>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
 // The direct-load ring needs bf16, a hidden width that is a multiple of 128
 // and at least one whole 256-column tile of vocabulary.
 hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
-  if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.part_stride * a.d * 2) && fits32(a.d * a.V * 2))
+  if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.T * a.d * 2) && fits32(a.d * a.V * 2))
     hipLaunchKernelGGL((topk_fwd_kernel<DmaNN<kBN>, Bf16>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((topk_fwd_kernel<GenNN<Bf16, kBN>, Bf16>), grid, block, 0, st, a);

@@ -133,6 +133,25 @@ kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx,
                          void* dH, float* dW, int64_t chunk_rows,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward and backward in one call, for callers that know grad_kl before
+ * the loss is evaluated (a mean over a known token count, the loss-only
+ * benchmark).  Same arguments and outputs as kd_topk_kl_fwd followed by
+ * kd_topk_kl_bwd with the same chunk_rows, and the same bits: each chunk's
+ * forward keeps its logits (fp32, in the workspace), so dZ is computed from
+ * them instead of from a second projection.  That trades the pages'
+ * recompute (§3 "Fused chunked KL": one extra output projection per chunk,
+ * like output-head gradient checkpointing) for C * roundup(V, 256) * 4 more
+ * workspace bytes, where C is the chunk size.  kd_topk_kl_fwd_bwd_workspace_size
+ * gives the size; T = 0 sets dW to zero and touches nothing else. */
+kd_status kd_topk_kl_fwd_bwd_workspace_size(int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                                            int64_t chunk_rows, size_t* bytes);
+kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_idx,
+                             const float* topk_logits, const uint8_t* mask, float tau,
+                             int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                             const float* grad_kl, float* kl, float* lse, float* z_topk,
+                             void* dH, float* dW, int64_t chunk_rows,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- full vocabulary */
 
 /* Workspace bytes for kd_full_kl_fwd and kd_full_kl_bwd (one size serves

@@ -29,7 +29,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), f"{n} declared in kdloss.h but not exported"
     assert sorted(kdl.EXPORTS) == names
@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
 def test_status_strings_and_version(L):
     for code, name in kdl._binding.STATUS.items():
         assert L.kd_status_string(code).decode() == name
-    assert L.kd_version() == 10000
+    assert L.kd_version() == 10100
 
 
 # ---------------------------------------------------------------- workspace sizing
@@ -148,6 +148,38 @@ def test_zero_rows_forward_is_a_noop(L):
 ])
 def test_topk_bwd_rejects(L, kw, code):
     assert bwd(**kw) == code
+
+
+def fwd_bwd(T=8, d=64, V=256, K=4, dt=kdl.KD_BF16, tau=1.0, g=FAKE, kl=FAKE, lse=FAKE, dH=FAKE, dW=FAKE, chunk=0,
+            wsb=0):
+    vp = ctypes.c_void_p
+    L = kdl.lib()
+    return L.kd_topk_kl_fwd_bwd(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(tau), T, d, V, K, dt,
+                                vp(g) if g else None, vp(kl) if kl else None, vp(lse) if lse else None, None,
+                                vp(dH) if dH else None, vp(dW) if dW else None, chunk, vp(FAKE), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(g=0), 1), (dict(kl=0), 1), (dict(lse=0), 1), (dict(dH=0), 1), (dict(dW=0), 1), (dict(chunk=-1), 1),
+    (dict(dW=FAKE + 4), 3), (dict(dH=FAKE + 8), 3), (dict(wsb=16), 4), (dict(tau=0.0), 1), (dict(K=0), 1),
+    (dict(d=12), 2),
+])
+def test_topk_fwd_bwd_rejects(L, kw, code):
+    assert fwd_bwd(**kw) == code
+
+
+def test_fwd_bwd_workspace_adds_one_fp32_logit_chunk(L):
+    # same per-row buffers and backward chunk buffers as the two-call path, plus
+    # per-chunk forward partials and the chunk's fp32 logits [C, roundup(V, 256)]
+    for T, chunk in ((4096, 0), (10000, 1024), (300, 0)):
+        out = ctypes.c_size_t(0)
+        assert L.kd_topk_kl_fwd_bwd_workspace_size(T, 3072, 128256, 64, kdl.KD_BF16, chunk, ctypes.byref(out)) == 0
+        C = min(4096 if chunk == 0 else chunk, (T + 255) // 256 * 256)
+        two_call = ws_topk(T, chunk=chunk)[1]
+        assert two_call + C * 128256 * 4 <= out.value <= two_call + C * 128256 * 4 + 256 * C * 16 + (1 << 20)
+    out = ctypes.c_size_t(0)
+    assert L.kd_topk_kl_fwd_bwd_workspace_size(0, 3072, 128256, 64, kdl.KD_BF16, 0, ctypes.byref(out)) == 0
+    assert out.value == 0
 
 
 def test_full_fwd_rejects(L):

@@ -1,0 +1,82 @@
+"""GPU parity of the single-call top-K forward + backward (kd_topk_kl_fwd_bwd).
+
+It computes what kd_topk_kl_fwd followed by kd_topk_kl_bwd computes, from the
+chunk's kept fp32 logits instead of a second projection.  When one chunk
+holds every row, the vocabulary splits and every formula are the same as in
+the two-call path, so the outputs must be bit-identical to it; with several
+chunks the split count per chunk differs and the outputs are checked against
+the fp64 oracle instead.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunked_kl_loss_logit_amd as kd
+import kdinputs as G
+from oracle import kd_oracle as O
+from tests.gpu_util import assert_grad, assert_kl, assert_lse, dev, run_topk, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fused(inp, chunk_rows=0, want_z=True):
+    H, W, I, A, M, g = (dev(inp[k]) for k in ("H", "W", "I", "A", "mask", "g"))
+    kl, lse, z, dH, dW = kd.topk_kl_forward_backward(H, W, I, A, M, inp["tau"], g, chunk_rows, want_z_topk=want_z)
+    torch.cuda.synchronize()
+    return dict(kl=kl.cpu().double().numpy(), lse=lse.cpu().double().numpy(),
+                z=None if z is None else z.cpu().double().numpy(),
+                dH=dH.cpu().double().numpy(), dW=dW.cpu().double().numpy())
+
+
+@pytest.mark.parametrize("dtype,T,d,V,K,tau,mask", [
+    (torch.bfloat16, 512, 3072, 128256, 64, 1.0, "none"),     # the output head, direct-load kernels
+    (torch.bfloat16, 700, 384, 2568, 16, 1.3, "random10"),    # direct-load, last vocab tile shifted, masked
+    (torch.bfloat16, 300, 136, 1032, 7, 1.0, "none"),         # general mainloop, ragged everything
+    (torch.float32, 513, 64, 520, 33, 0.7, "random10"),       # fp32 matrix cores
+])
+def test_single_chunk_matches_two_calls_bitwise(dtype, T, d, V, K, tau, mask):
+    inp = G.make_topk(T, d, V, K, dtype, tau=tau, mask=mask, number=21, g="normal")
+    say(f"fused vs two calls T={T} d={d} V={V} K={K} {dtype}")
+    two = run_topk(inp)
+    one = run_fused(inp)
+    for k in ("kl", "lse", "z", "dH", "dW"):
+        np.testing.assert_array_equal(one[k], two[k], err_msg=k)
+
+
+@pytest.mark.parametrize("dtype,T,d,V,K,chunk,mask", [
+    (torch.bfloat16, 900, 384, 1280, 24, 256, "random10"),    # 4 chunks (last ragged), direct-load
+    (torch.bfloat16, 600, 200, 2056, 5, 256, "none"),         # general mainloop, 3 chunks
+    (torch.float32, 520, 64, 1032, 9, 256, "random10"),       # fp32, 3 chunks
+])
+def test_several_chunks_match_the_oracle(dtype, T, d, V, K, chunk, mask):
+    inp = G.make_topk(T, d, V, K, dtype, tau=1.2, mask=mask, number=22, g="normal")
+    say(f"fused chunks={chunk} T={T} d={d} V={V} K={K} {dtype}")
+    got = run_fused(inp, chunk_rows=chunk)
+    kl, lse, z = O.topk_kl_forward(inp["H"], inp["W"], inp["I"], inp["A"], inp["mask"], inp["tau"])
+    dH, dW = O.topk_kl_backward(inp["H"], inp["W"], inp["I"], inp["A"], inp["mask"], inp["tau"], inp["g"])
+    v = np.ones(T, bool) if inp["mask"] is None else inp["mask"].numpy() != 0
+    assert_kl(got["kl"], kl, dtype, v)
+    assert_lse(got["lse"], lse, dtype, v)
+    assert np.all(got["kl"][~v] == 0) and np.all(got["lse"][~v] == 0) and np.all(got["dH"][~v] == 0)
+    np.testing.assert_allclose(got["z"][v], z[v], rtol=1e-4, atol=1e-5)
+    assert np.all(got["z"][~v] == 0)
+    assert_grad(got["dH"], dH, dtype, "dH")
+    assert_grad(got["dW"], dW, dtype, "dW")
+
+
+def test_all_rows_masked_and_empty_batch():
+    inp = G.make_topk(300, 64, 520, 4, torch.bfloat16, number=23, g="normal")
+    inp["mask"] = torch.zeros(300, dtype=torch.uint8)
+    say("fused, every row masked")
+    got = run_fused(inp, chunk_rows=256)
+    for k in ("kl", "lse", "z", "dH", "dW"):
+        assert np.all(got[k] == 0), k
+    say("fused, T = 0")
+    H = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    W = torch.randn(64, 520, device="cuda").to(torch.bfloat16)
+    I = torch.empty(0, 4, dtype=torch.int32, device="cuda")
+    A = torch.empty(0, 4, device="cuda")
+    g = torch.empty(0, device="cuda")
+    kl, lse, z, dH, dW = kd.topk_kl_forward_backward(H, W, I, A, None, 1.0, g)
+    torch.cuda.synchronize()
+    assert kl.numel() == 0 and dH.numel() == 0 and torch.all(dW == 0)
