@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--chunk-rows", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extra", action="store_true", help="skip the packed and full-vocabulary workloads")
+    ap.add_argument("--one-call", action="store_true",
+                    help="full-vocabulary workload: time the single forward + backward call")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--sweep", action="store_true", help="T in 4096, 16384, 65536, 262144: one line each")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -239,8 +241,10 @@ def run_topk_fused(p, T: int, steps: int, warmup: int, chunk_rows: int):
     return out
 
 
-def run_full(p, steps: int, warmup: int, chunk_rows: int):
-    """Time the full-vocabulary loss on preset p."""
+def run_full(p, steps: int, warmup: int, chunk_rows: int, one_call: bool = False):
+    """Time the full-vocabulary loss on preset p: the forward and backward
+    calls, or with one_call the single call that keeps both heads' logits of
+    a chunk instead of recomputing them (kd_full_kl_fwd_bwd)."""
     import torch
     import chunked_kl_loss_logit_amd as kd
     import kdinputs as G
@@ -258,23 +262,31 @@ def run_full(p, steps: int, warmup: int, chunk_rows: int):
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
-    ws = torch.empty(kd.kd_full_kl_workspace_size(T, d, dt, V, p.dtype, chunk_rows), dtype=torch.uint8, device=dev)
-    kd.kd_full_kl_fwd(H, Ws, Ht, Wt, None, tau, kl, ls, lt, ws)
-    kd.kd_full_kl_bwd(H, Ws, Ht, Wt, None, tau, ls, lt, g, dH, dW, chunk_rows, ws)
+    if one_call:
+        ws = torch.empty(kd.kd_full_kl_fwd_bwd_workspace_size(T, d, dt, V, p.dtype, chunk_rows), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            kd.kd_full_kl_fwd_bwd(H, Ws, Ht, Wt, None, tau, g, kl, ls, lt, dH, dW, chunk_rows, ws)
+    else:
+        ws = torch.empty(kd.kd_full_kl_workspace_size(T, d, dt, V, p.dtype, chunk_rows), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            kd.kd_full_kl_fwd(H, Ws, Ht, Wt, None, tau, kl, ls, lt, ws)
+            kd.kd_full_kl_bwd(H, Ws, Ht, Wt, None, tau, ls, lt, g, dH, dW, chunk_rows, ws)
+
+    step()
     torch.cuda.synchronize()
-    peak_extra = torch.cuda.max_memory_allocated() - base + 2 * T * 4  # + saved lse_s, lse_t
-
-    def step():
-        kd.kd_full_kl_fwd(H, Ws, Ht, Wt, None, tau, kl, ls, lt, ws)
-        kd.kd_full_kl_bwd(H, Ws, Ht, Wt, None, tau, ls, lt, g, dH, dW, chunk_rows, ws)
-
+    peak_extra = torch.cuda.max_memory_allocated() - base + (0 if one_call else 2 * T * 4)  # + saved lse_s, lse_t
     ms, prof = timed(step, steps, warmup)
     fl = {"full_fwd_tile": 2.0 * T * (d + dt) * V, "full_dz_tile": 2.0 * T * (d + dt) * V,
           "dh_tile": 2.0 * T * d * V, "dw_tile": 2.0 * T * d * V}
     dom, achieved = dominant(prof, fl, steps)
     credited = (2.0 * (d + dt) + 4.0 * d) * V * T
-    executed = (4.0 * (d + dt) + 4.0 * d) * V * T
-    out = {"workload": p.name, "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+    executed = ((2.0 if one_call else 4.0) * (d + dt) + 4.0 * d) * V * T
+    out = {"workload": p.name + ("_one_call" if one_call else ""), "T": T, "ms_per_step": ms,
+           "tokens_per_s": T / (ms * 1e-3),
            "credited_tflops": credited / (ms * 1e-3) / 1e12,
            "mfma_frac_credited": credited / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
            "mfma_frac_executed": executed / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -318,7 +330,7 @@ def main():
         print(f"unknown workload {a.workload}", file=sys.stderr)
         sys.exit(2)
     if p.full_vocab:
-        r = run_full(p, a.steps, a.warmup, a.chunk_rows)
+        r = run_full(p, a.steps, a.warmup, a.chunk_rows, a.one_call)
         print(json.dumps({"metric": "full-vocab KL fwd+bwd tokens/s", "value": r["tokens_per_s"],
                           "unit": "tokens/s", **brief(r)}))
         return
@@ -364,7 +376,8 @@ def main():
         one = run_topk_fused(p, T, a.steps, a.warmup, a.chunk_rows)
         out["extra"] = {one["workload"]: brief(one),
                         pk.name: brief(run_topk(pk, pk.T, 3, 1, a.chunk_rows)[0]),
-                        fv.name: brief(run_full(fv, 3, 1, a.chunk_rows))}
+                        fv.name: brief(run_full(fv, 3, 1, a.chunk_rows)),
+                        fv.name + "_one_call": brief(run_full(fv, 3, 1, a.chunk_rows, one_call=True))}
     print(json.dumps(out))
 
 

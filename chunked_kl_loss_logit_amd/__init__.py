@@ -18,15 +18,16 @@ import torch
 
 from ._binding import (  # noqa: F401
     EXPORTS, KD_BF16, KD_DEFAULT_CHUNK_ROWS, KD_F32, KD_MAX_K, LIB_PATH, KDError, kd_full_kl_bwd, kd_full_kl_fwd,
-    kd_full_kl_workspace_size, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd, kd_topk_kl_fwd_bwd_workspace_size,
+    kd_full_kl_fwd_bwd, kd_full_kl_fwd_bwd_workspace_size, kd_full_kl_workspace_size, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd, kd_topk_kl_fwd_bwd_workspace_size,
     kd_topk_kl_workspace_size, kd_version, lib,
     profile_enable, profile_read, profile_reset,
 )
 
 __all__ = [
     "topk_kl", "full_kl", "topk_kl_forward", "topk_kl_backward", "topk_kl_forward_backward", "full_kl_forward",
-    "full_kl_backward", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_topk_kl_fwd_bwd", "kd_full_kl_fwd", "kd_full_kl_bwd",
-    "kd_topk_kl_workspace_size", "kd_topk_kl_fwd_bwd_workspace_size", "kd_full_kl_workspace_size", "KDError",
+    "full_kl_backward", "full_kl_forward_backward", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_topk_kl_fwd_bwd",
+    "kd_full_kl_fwd", "kd_full_kl_bwd", "kd_full_kl_fwd_bwd", "kd_topk_kl_workspace_size",
+    "kd_topk_kl_fwd_bwd_workspace_size", "kd_full_kl_workspace_size", "kd_full_kl_fwd_bwd_workspace_size", "KDError",
 ]
 
 
@@ -99,6 +100,22 @@ def full_kl_backward(H, Ws, Ht, Wt, mask, tau, lse_s, lse_t, grad_kl, chunk_rows
     kd_full_kl_bwd(H, Ws, Ht, Wt, mask, tau, lse_s, lse_t, grad_kl.float().contiguous(), dH, dW, chunk_rows,
                    workspace)
     return dH, dW
+
+
+def full_kl_forward_backward(H, Ws, Ht, Wt, mask, tau, grad_kl, chunk_rows=0, workspace=None):
+    """kl, lse_s, lse_t, dH and dWs in one call, for a known grad_kl."""
+    T, d = H.shape
+    dt, V = Ht.shape[1], Ws.shape[1]
+    kl = torch.empty(T, dtype=torch.float32, device=H.device)
+    ls = torch.empty(T, dtype=torch.float32, device=H.device)
+    lt = torch.empty(T, dtype=torch.float32, device=H.device)
+    dH = torch.empty_like(H)
+    dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
+    if workspace is None:
+        workspace = _workspace(kd_full_kl_fwd_bwd_workspace_size(T, d, dt, V, H.dtype, chunk_rows), H.device)
+    kd_full_kl_fwd_bwd(H, Ws, Ht, Wt, mask, tau, grad_kl.float().contiguous(), kl, ls, lt, dH, dW, chunk_rows,
+                       workspace)
+    return kl, ls, lt, dH, dW
 
 
 class _TopkKL(torch.autograd.Function):

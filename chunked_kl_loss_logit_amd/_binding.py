@@ -27,6 +27,7 @@ EXPORTS = (
     "kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd",
     "kd_topk_kl_fwd_bwd_workspace_size", "kd_topk_kl_fwd_bwd",
     "kd_full_kl_workspace_size", "kd_full_kl_fwd", "kd_full_kl_bwd",
+    "kd_full_kl_fwd_bwd_workspace_size", "kd_full_kl_fwd_bwd",
     "kd_status_string", "kd_last_error", "kd_version",
     "kd_profile_enable", "kd_profile_count", "kd_profile_get", "kd_profile_reset",
 )
@@ -64,9 +65,13 @@ def lib() -> ctypes.CDLL:
     L.kd_full_kl_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, sz, vp]
     L.kd_full_kl_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, i64, vp, sz,
                                  vp]
+    L.kd_full_kl_fwd_bwd_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
+    L.kd_full_kl_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp, i64,
+                                     vp, sz, vp]
     for f in ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_topk_kl_fwd_bwd_workspace_size",
               "kd_topk_kl_fwd_bwd", "kd_full_kl_workspace_size",
-              "kd_full_kl_fwd", "kd_full_kl_bwd", "kd_profile_enable", "kd_profile_get", "kd_profile_reset"):
+              "kd_full_kl_fwd", "kd_full_kl_bwd", "kd_full_kl_fwd_bwd_workspace_size", "kd_full_kl_fwd_bwd",
+              "kd_profile_enable", "kd_profile_get", "kd_profile_reset"):
         getattr(L, f).restype = st
     L.kd_status_string.argtypes = [st]
     L.kd_status_string.restype = ctypes.c_char_p
@@ -188,6 +193,27 @@ def kd_full_kl_bwd(H, Ws, Ht, Wt, mask, tau, lse_s, lse_t, grad_kl, dH, dWs, chu
                                 _ptr(dWs), int(chunk_rows), _ptr(workspace),
                                 workspace.numel() if workspace is not None else 0, _stream(stream)),
            "kd_full_kl_bwd")
+
+
+def kd_full_kl_fwd_bwd_workspace_size(T, d, dt_hidden, V, dtype, chunk_rows=0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().kd_full_kl_fwd_bwd_workspace_size(T, d, dt_hidden, V, _dtype_code(dtype), chunk_rows,
+                                                   ctypes.byref(out)),
+           "kd_full_kl_fwd_bwd_workspace_size")
+    return out.value
+
+
+def kd_full_kl_fwd_bwd(H, Ws, Ht, Wt, mask, tau, grad_kl, kl, lse_s, lse_t, dH, dWs, chunk_rows, workspace,
+                       stream=None):
+    """Enqueue the full-vocabulary forward and backward in one call (no recompute)."""
+    T, d = H.shape
+    dt = Ht.shape[1]
+    V = Ws.shape[1]
+    _check(lib().kd_full_kl_fwd_bwd(_ptr(H), _ptr(Ws), _ptr(Ht), _ptr(Wt), _ptr(mask), float(tau), T, d, dt, V,
+                                    _dtype_code(H.dtype), _ptr(grad_kl), _ptr(kl), _ptr(lse_s), _ptr(lse_t),
+                                    _ptr(dH), _ptr(dWs), int(chunk_rows), _ptr(workspace),
+                                    workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "kd_full_kl_fwd_bwd")
 
 
 def kd_version() -> int:

@@ -216,6 +216,11 @@ struct FullPlan {
   size_t o_rows, o_count, o_part;
   ChunkPlan ch;
   size_t fwd_total, total;
+  // single-call forward + backward: per-chunk partials, the chunk's fp32
+  // student and teacher logits and the backward chunk buffers
+  int S_c;
+  ChunkPlan ch_f;
+  size_t o_part_c, o_zs, o_zt, fused_total;
 };
 
 FullPlan plan_full(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows) {
@@ -231,6 +236,13 @@ FullPlan plan_full(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows
   p.ch = plan_chunk(T, d, V, elem, chunk_rows, bw);
   p.fwd_total = fw.off;
   p.total = std::max(fw.off, bw.off);
+  Carver fu = cv;
+  p.S_c = splits_for(cdiv(chunk_of(T, chunk_rows), kd::kTileM), p.ntiles);
+  p.o_part_c = fu.take((size_t)p.S_c * chunk_of(T, chunk_rows) * 32);
+  p.ch_f = plan_chunk(T, d, V, elem, chunk_rows, fu);
+  p.o_zs = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
+  p.o_zt = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
+  p.fused_total = fu.off;
   return p;
 }
 
@@ -309,7 +321,7 @@ const char* kd_status_string(kd_status s) {
 
 const char* kd_last_error(void) { return g_err.c_str(); }
 
-int kd_version(void) { return 10100; }
+int kd_version(void) { return 10200; }
 
 kd_status kd_profile_enable(int on) {
   g_prof_on = on != 0;
@@ -529,6 +541,10 @@ kd_status kd_full_kl_fwd(const void* H, const void* Ws, const void* Ht, const vo
   a.c = c;
   a.part = part;
   a.part_stride = T;
+  a.part_row0 = 0;
+  a.c0 = 0;
+  a.C = T;
+  a.T = T;
   a.d = d;
   a.dt = dt_hidden;
   a.V = V;
@@ -538,7 +554,7 @@ kd_status kd_full_kl_fwd(const void* H, const void* Ws, const void* Ht, const vo
   a.group = kRasterGroup;
   a.c2 = (float)(1.4426950408889634 / (double)tau);
   KD_LAUNCH("full_fwd_tile", st, kd::launch_full_fwd(elem, a, st));
-  KD_LAUNCH("full_combine", st, kd::launch_full_combine(part, p.S, T, c, mask, T, kl, lse_s, lse_t, st));
+  KD_LAUNCH("full_combine", st, kd::launch_full_combine(part, p.S, T, c, mask, T, kl, lse_s, lse_t, 0, T, true, st));
   return KD_OK;
 }
 
@@ -612,6 +628,118 @@ kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const vo
     za.c2 = (float)(1.4426950408889634 / (double)tau);
     za.inv_tau = 1.0f / tau;
     KD_LAUNCH("full_dz_tile", st, kd::launch_full_dz(elem, za, st));
+    KD_TRY(grad_chunk(H, Ws, dH, dWs, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
+  }
+  return KD_OK;
+}
+
+// ---------------------------------------------------------------- full vocabulary, forward and backward in one call
+kd_status kd_full_kl_fwd_bwd_workspace_size(int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                                            int64_t chunk_rows, size_t* bytes) {
+  g_err.clear();
+  KD_TRY(need(bytes, "bytes"));
+  KD_TRY(check_common(T, d, V, dt, 1.0f));
+  KD_TRY(check_common(T, dt_hidden, V, dt, 1.0f));
+  if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
+  *bytes = T == 0 ? 0 : plan_full(T, d, V, elem_of(dt), chunk_rows).fused_total;
+  return KD_OK;
+}
+
+kd_status kd_full_kl_fwd_bwd(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask,
+                             float tau, int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                             const float* grad_kl, float* kl, float* lse_s, float* lse_t, void* dH, float* dWs,
+                             int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  KD_TRY(check_common(T, d, V, dt, tau));
+  KD_TRY(check_common(T, dt_hidden, V, dt, tau));
+  KD_TRY(need(dWs, "dWs"));
+  KD_TRY(need_align(dWs, 16, "dWs"));
+  if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    KD_LAUNCH("fill_zero", st, kd::launch_fill_zero(dWs, d * V * 4, st));
+    return KD_OK;
+  }
+  KD_TRY(need(H, "H"));
+  KD_TRY(need(Ws, "Ws"));
+  KD_TRY(need(Ht, "Ht"));
+  KD_TRY(need(Wt, "Wt"));
+  KD_TRY(need(grad_kl, "grad_kl"));
+  KD_TRY(need(kl, "kl"));
+  KD_TRY(need(lse_s, "lse_s"));
+  KD_TRY(need(lse_t, "lse_t"));
+  KD_TRY(need(dH, "dH"));
+  KD_TRY(need_align(H, 16, "H"));
+  KD_TRY(need_align(Ws, 16, "Ws"));
+  KD_TRY(need_align(Ht, 16, "Ht"));
+  KD_TRY(need_align(Wt, 16, "Wt"));
+  KD_TRY(need_align(dH, 16, "dH"));
+  KD_TRY(need_align(grad_kl, 4, "grad_kl"));
+  KD_TRY(need_align(kl, 4, "kl"));
+  KD_TRY(need_align(lse_s, 4, "lse_s"));
+  KD_TRY(need_align(lse_t, 4, "lse_t"));
+  const int elem = elem_of(dt);
+  const FullPlan p = plan_full(T, d, V, elem, chunk_rows);
+  KD_TRY(check_workspace(workspace, workspace_bytes, p.fused_total));
+
+  kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
+  float* part = at<float>(workspace, p.o_part_c);
+  float* zs = at<float>(workspace, p.o_zs);
+  float* zt = at<float>(workspace, p.o_zt);
+  const ChunkPlan& ch = p.ch_f;
+  char* dz = at<char>(workspace, ch.o_dz);
+  char* hT = at<char>(workspace, ch.o_hT);
+  float* dhp = at<float>(workspace, ch.o_dhp);
+  const float c2 = (float)(1.4426950408889634 / (double)tau);
+
+  KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
+  KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * elem, dH, st));
+  const int64_t nchunks = cdiv(T, ch.C);
+  for (int64_t k = 0; k < nchunks; ++k) {
+    const int64_t c0 = k * ch.C;
+    // both heads' logits of the chunk: the coupled partials, kept in fp32
+    kd::FullFwdArgs a{};
+    a.H = static_cast<const char*>(H);
+    a.Ws = static_cast<const char*>(Ws);
+    a.Ht = static_cast<const char*>(Ht);
+    a.Wt = static_cast<const char*>(Wt);
+    a.c = c;
+    a.part = part;
+    a.part_stride = ch.C;
+    a.part_row0 = c0;
+    a.c0 = c0;
+    a.C = ch.C;
+    a.zs = zs;
+    a.zt = zt;
+    a.ldz = ch.ldz;
+    a.T = T;
+    a.d = d;
+    a.dt = dt_hidden;
+    a.V = V;
+    a.nrb = ch.nrb_c;
+    a.S = p.S_c;
+    a.ntiles = p.ntiles;
+    a.group = kRasterGroup;
+    a.c2 = c2;
+    KD_LAUNCH("full_fwd_tile", st, kd::launch_full_fwd(elem, a, st));
+    KD_LAUNCH("full_combine", st,
+              kd::launch_full_combine(part, p.S_c, ch.C, c, mask, T, kl, lse_s, lse_t, c0, c0 + ch.C, k == 0, st));
+    // dZ from the kept logits: no second pair of projections
+    kd::FullDzFromZArgs za{};
+    za.zs = zs;
+    za.zt = zt;
+    za.dz = dz;
+    za.ldz = ch.ldz;
+    za.c = c;
+    za.c0 = c0;
+    za.C = ch.C;
+    za.V = V;
+    za.lse_s = lse_s;
+    za.lse_t = lse_t;
+    za.g = grad_kl;
+    za.c2 = c2;
+    za.inv_tau = 1.0f / tau;
+    KD_LAUNCH("full_dz_from_z", st, kd::launch_full_dz_from_z(elem, za, st));
     KD_TRY(grad_chunk(H, Ws, dH, dWs, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
   }
   return KD_OK;

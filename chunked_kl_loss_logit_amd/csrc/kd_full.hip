@@ -109,11 +109,20 @@ __device__ inline void stage_pair(const Slots& sl, const f32x16_t (&acc_s)[4][2]
 
 template <int NBI>
 __device__ inline void full_fwd_round(const Slots& sl, const f32x16_t (&acc_s)[4][2],
-                                      const f32x16_t (&acc_t)[4][2], long n0, FullFwdRow& R, const FullFwdArgs& a) {
+                                      const f32x16_t (&acc_t)[4][2], long n0, FullFwdRow& R, const FullFwdArgs& a,
+                                      long row0, long M) {
   stage_pair<NBI>(sl, acc_s, acc_t);
   __syncthreads();
   R.consume(st_pair<0>(sl), st_pair<2>(sl), n0 + NBI * 32, a.V, a.c2);
   R.consume(st_pair<1>(sl), st_pair<3>(sl), n0 + 64 + NBI * 32, a.V, a.c2);
+  if (a.zs) {  // the consume only read the staged blocks: the logits go out as they are
+    char* zs = reinterpret_cast<char*>(a.zs);
+    char* zt = reinterpret_cast<char*>(a.zt);
+    store_block<F32>(st_pair<0>(sl), zs, a.ldz, row0, n0 + NBI * 32, M, a.ldz);
+    store_block<F32>(st_pair<1>(sl), zs, a.ldz, row0, n0 + 64 + NBI * 32, M, a.ldz);
+    store_block<F32>(st_pair<2>(sl), zt, a.ldz, row0, n0 + NBI * 32, M, a.ldz);
+    store_block<F32>(st_pair<3>(sl), zt, a.ldz, row0, n0 + 64 + NBI * 32, M, a.ldz);
+  }
   __syncthreads();
 }
 
@@ -132,47 +141,45 @@ __device__ inline void full_dz_round(const Slots& sl, const f32x16_t (&acc_s)[4]
 
 }  // namespace
 
+// Rows: the compacted valid rows [c0, c0 + C) (the plain forward takes them
+// all); partials are indexed by compacted position, and with zs set both
+// tiles' logits are also written out, fp32, one row per compacted row.
 template <class Main, class E>
 __global__ __launch_bounds__(kThreads, 1) void full_fwd_kernel(FullFwdArgs a) {
   KD_DECLARE_SLOTS(sl);
 
-  const int count = *a.c.count;
+  const long count = *a.c.count;
+  const long M = min(a.C, count - a.c0);  // rows of this launch
+  if (M <= 0) return;
   int rb, sp;
   grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, a.group, rb, sp);
   const int row0 = rb * kBM;
-  if (row0 >= count) return;
+  if (row0 >= M) return;
   const int tb = (int)((long)a.ntiles * sp / a.S);
   const int te = (int)((long)a.ntiles * (sp + 1) / a.S);
+  const int32_t* rows = a.c.rows + a.c0;
 
   Main ms, mt;
-  ms.init(
-      a.H,
-      [&](int r) -> const char* {
-        const int i = row0 + r;
-        return i < count ? a.H + (long)a.c.rows[i] * a.d * E::kElem : nullptr;
-      },
-      a.Ws, a.V * E::kElem, a.V, a.d);
-  mt.init(
-      a.Ht,
-      [&](int r) -> const char* {
-        const int i = row0 + r;
-        return i < count ? a.Ht + (long)a.c.rows[i] * a.dt * E::kElem : nullptr;
-      },
-      a.Wt, a.V * E::kElem, a.V, a.dt);
+  ms.init(a.H,
+          [&](int r) -> const char* { return row0 + r < M ? a.H + (long)rows[row0 + r] * a.d * E::kElem : nullptr; },
+          a.Ws, a.V * E::kElem, a.V, a.d);
+  mt.init(a.Ht,
+          [&](int r) -> const char* { return row0 + r < M ? a.Ht + (long)rows[row0 + r] * a.dt * E::kElem : nullptr; },
+          a.Wt, a.V * E::kElem, a.V, a.dt);
 
   const int ti = row0 + (int)threadIdx.x;
-  FullFwdRow R{-INFINITY, 0.f, -INFINITY, 0.f, 0.f, ti < count};
+  FullFwdRow R{-INFINITY, 0.f, -INFINITY, 0.f, 0.f, ti < M};
 
   f32x16_t acc_s[4][2], acc_t[4][2];
   for (int vt = tb; vt < te; ++vt) {
     const long n0 = (long)vt * kBN;
     mt.tile(sl, n0, acc_t);
     ms.tile(sl, n0, acc_s);
-    full_fwd_round<0>(sl, acc_s, acc_t, n0, R, a);
-    full_fwd_round<1>(sl, acc_s, acc_t, n0, R, a);
+    full_fwd_round<0>(sl, acc_s, acc_t, n0, R, a, row0, M);
+    full_fwd_round<1>(sl, acc_s, acc_t, n0, R, a, row0, M);
   }
   if (R.rv) {
-    float4* o = reinterpret_cast<float4*>(a.part) + 2 * ((long)sp * a.part_stride + ti);
+    float4* o = reinterpret_cast<float4*>(a.part) + 2 * ((long)sp * a.part_stride + (a.c0 - a.part_row0) + ti);
     o[0] = make_float4(R.ms, R.ls, R.mt, R.lt);
     o[1] = make_float4(R.R, 0.f, 0.f, 0.f);
   }
@@ -219,7 +226,55 @@ __global__ __launch_bounds__(kThreads, 1) void full_dz_kernel(FullDzArgs a) {
   }
 }
 
-// The direct-load ring needs bf16 and both hidden widths multiples of 32.
+// One thread: EPT consecutive columns (16 bytes of dZ) of one row, the same
+// formula as the recomputing tile's epilogue.
+template <class E>
+__global__ __launch_bounds__(256) void full_dz_from_z_kernel(FullDzFromZArgs a) {
+  constexpr int EPT = E::kEpc;
+  const long i = blockIdx.y;  // row of the chunk
+  const long v0 = ((long)blockIdx.x * 256 + threadIdx.x) * EPT;
+  if (v0 >= a.V) return;
+  const long M = min(a.C, (long)*a.c.count - a.c0);
+  float o[EPT];
+  if (i < M) {
+    const long t = a.c.rows[a.c0 + i];
+    const float Ls2 = a.lse_s[t] * kLog2e, Lt2 = a.lse_t[t] * kLog2e, gs = a.g[t] * a.inv_tau;
+    const float* sr = a.zs + i * a.ldz + v0;
+    const float* ur = a.zt + i * a.ldz + v0;
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) {
+      const float4 fs = *reinterpret_cast<const float4*>(sr + e);
+      const float4 fu = *reinterpret_cast<const float4*>(ur + e);
+      o[e + 0] = gs * (fast_exp2(fmaf(fs.x, a.c2, -Ls2)) - fast_exp2(fmaf(fu.x, a.c2, -Lt2)));
+      o[e + 1] = gs * (fast_exp2(fmaf(fs.y, a.c2, -Ls2)) - fast_exp2(fmaf(fu.y, a.c2, -Lt2)));
+      o[e + 2] = gs * (fast_exp2(fmaf(fs.z, a.c2, -Ls2)) - fast_exp2(fmaf(fu.z, a.c2, -Lt2)));
+      o[e + 3] = gs * (fast_exp2(fmaf(fs.w, a.c2, -Ls2)) - fast_exp2(fmaf(fu.w, a.c2, -Lt2)));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) o[q] = 0.f;
+  }
+  char* dst = a.dz + (i * a.ldz + v0) * E::kElem;
+  if constexpr (EPT == 8) {
+    const u32x4_t w{Bf16::pack2(o[0], o[1]), Bf16::pack2(o[2], o[3]), Bf16::pack2(o[4], o[5]),
+                    Bf16::pack2(o[6], o[7])};
+    *reinterpret_cast<u32x4_t*>(dst) = w;
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_full_dz_from_z(int elem, const FullDzFromZArgs& a, hipStream_t st) {
+  const int ept = elem == 2 ? Bf16::kEpc : F32::kEpc;
+  const dim3 grid((unsigned)((a.V + 256L * ept - 1) / (256L * ept)), (unsigned)a.C), block(256);
+  if (elem == 2)
+    hipLaunchKernelGGL(full_dz_from_z_kernel<Bf16>, grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL(full_dz_from_z_kernel<F32>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// The direct-load ring needs bf16 and both hidden widths multiples of 128.
 static bool full_dma_ok(int64_t T, int64_t d, int64_t dt, int64_t V) {
   return d % kDmaKMult == 0 && dt % kDmaKMult == 0 && fits32(T * d * 2) && fits32(T * dt * 2) && fits32(d * V * 2) &&
          fits32(dt * V * 2);
@@ -227,7 +282,7 @@ static bool full_dma_ok(int64_t T, int64_t d, int64_t dt, int64_t V) {
 
 hipError_t launch_full_fwd(int elem, const FullFwdArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
-  if (elem == 2 && full_dma_ok(a.part_stride, a.d, a.dt, a.V))
+  if (elem == 2 && full_dma_ok(a.T, a.d, a.dt, a.V))
     hipLaunchKernelGGL((full_fwd_kernel<DmaNN<kBN>, Bf16>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((full_fwd_kernel<GenNN<Bf16, kBN>, Bf16>), grid, block, 0, st, a);

@@ -38,7 +38,8 @@ hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Co
                                const float* ent, int64_t T, float tau, float* kl, float* lse, int64_t jb, int64_t je,
                                bool zero_masked, hipStream_t st);
 hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
-                               int64_t T, float* kl, float* lse_s, float* lse_t, hipStream_t st);
+                               int64_t T, float* kl, float* lse_s, float* lse_t, int64_t jb, int64_t je,
+                               bool zero_masked, hipStream_t st);
 // H^T of one chunk of compacted rows: out[j][i] = H[rows[c0 + i]][j] for
 // i < valid rows of the chunk, 0 up to C.
 hipError_t launch_gather_transpose(const void* H, int elem, int64_t d, Compact c, int64_t c0, int64_t C, void* out,
@@ -108,9 +109,13 @@ struct FullFwdArgs {
   const char* Ht;  // [T][dt]
   const char* Wt;  // [dt][V]
   Compact c;
-  float* part;     // [S][part_stride][8]
-  int64_t part_stride;
-  int64_t d, dt, V;
+  float* part;     // [S][part_stride][8], row p of a split is compacted row part_row0 + p
+  int64_t part_stride, part_row0;
+  int64_t c0, C;   // compacted rows [c0, c0 + C) (all rows: 0, T)
+  float* zs;       // nullable: student logits of those rows, fp32 [C][ldz]
+  float* zt;       // teacher logits, same layout (set together with zs)
+  int64_t ldz;
+  int64_t T, d, dt, V;
   int nrb, S, ntiles;
   int group;  // row blocks per raster group (grouped_coords)
   float c2;
@@ -134,6 +139,23 @@ struct FullDzArgs {
   float c2, inv_tau;
 };
 hipError_t launch_full_dz(int elem, const FullDzArgs& a, hipStream_t st);
+
+// dZ of a chunk from its stored fp32 student and teacher logits:
+// dz[i][v] = (g/tau) (2^(zs c2 - Ls2) - 2^(zt c2 - Lt2)) for the chunk's
+// valid rows i and v < V; zero for the chunk's other rows.
+struct FullDzFromZArgs {
+  const float* zs;   // [C][ldz]
+  const float* zt;   // [C][ldz]
+  char* dz;          // [C][ldz], element type
+  int64_t ldz;
+  Compact c;
+  int64_t c0, C, V;
+  const float* lse_s;
+  const float* lse_t;
+  const float* g;
+  float c2, inv_tau;
+};
+hipError_t launch_full_dz_from_z(int elem, const FullDzFromZArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- gradient contractions
 // part[s][i][j] = sum over the s-th vocabulary range of dz[i][v] * W[j][v]

@@ -213,28 +213,30 @@ hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Co
   return hipGetLastError();
 }
 
-// Partials per (split, row): (ms, ls, mt, lt), (R, -, -, -) in base 2.
+// Partials per (split, row): (ms, ls, mt, lt), (R, -, -, -) in base 2; the
+// partial row p holds compacted row jb + p.
 __global__ void full_combine_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask, long T,
-                                    float* kl, float* lse_s, float* lse_t) {
+                                    float* kl, float* lse_s, float* lse_t, long jb, long je, int zero_masked) {
   const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= T) return;
-  if (mask != nullptr && mask[j] == 0) {
+  if (zero_masked && mask != nullptr && mask[j] == 0) {
     kl[j] = 0.f;
     lse_s[j] = 0.f;
     lse_t[j] = 0.f;
   }
-  if (j >= *c.count) return;
+  if (j < jb || j >= je || j >= *c.count) return;
   const float4* pp = reinterpret_cast<const float4*>(part);
+  const long p = j - jb;  // partial row
   float Ms = -INFINITY, Mt = -INFINITY;
   for (int s = 0; s < S; ++s) {
-    const float4 q = pp[2 * ((long)s * stride + j)];
+    const float4 q = pp[2 * ((long)s * stride + p)];
     Ms = fmaxf(Ms, q.x);
     Mt = fmaxf(Mt, q.z);
   }
   float ls = 0.f, lt = 0.f, R = 0.f;
   for (int s = 0; s < S; ++s) {
-    const float4 q = pp[2 * ((long)s * stride + j)];
-    const float r = pp[2 * ((long)s * stride + j) + 1].x;
+    const float4 q = pp[2 * ((long)s * stride + p)];
+    const float r = pp[2 * ((long)s * stride + p) + 1].x;
     ls += q.y * exp2f(q.x - Ms);
     const float f = exp2f(q.z - Mt);
     lt += q.w * f;
@@ -248,10 +250,11 @@ __global__ void full_combine_kernel(const float* part, int S, long stride, Compa
 }
 
 hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
-                               int64_t T, float* kl, float* lse_s, float* lse_t, hipStream_t st) {
+                               int64_t T, float* kl, float* lse_s, float* lse_t, int64_t jb, int64_t je,
+                               bool zero_masked, hipStream_t st) {
   const dim3 grid((unsigned)((T + 255) / 256));
   hipLaunchKernelGGL(full_combine_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, (long)T, kl,
-                     lse_s, lse_t);
+                     lse_s, lse_t, (long)jb, (long)je, zero_masked ? 1 : 0);
   return hipGetLastError();
 }
 

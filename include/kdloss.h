@@ -160,9 +160,11 @@ kd_status kd_full_kl_workspace_size(int64_t T, int64_t d, int64_t dt_hidden, int
                                     int64_t chunk_rows, size_t* bytes);
 
 /* Forward: kl [T], lse_s [T] (student), lse_t [T] (teacher), all float32 out.
- * Student logits H.Ws and teacher logits Ht.Wt are produced tile by tile
- * side by side; a dual running max/sum and the running sum of
- * p_v (u_v - s_v) give the KL without either [T,V] tensor. */
+ * Student logits H.Ws and teacher logits Ht.Wt (the teacher's final hidden
+ * states through its frozen output head: KDFlow abstract) are produced tile
+ * by tile side by side; a dual running max/sum and the running sum of
+ * p_v (u_v - s_v) give the KL without either [T,V] tensor (the online
+ * coupled two-distribution form of the StreamKL abstract). */
 kd_status kd_full_kl_fwd(const void* H, const void* Ws, const void* Ht, const void* Wt,
                          const uint8_t* mask, float tau,
                          int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
@@ -177,6 +179,23 @@ kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const vo
                          const float* lse_s, const float* lse_t, const float* grad_kl,
                          void* dH, float* dWs, int64_t chunk_rows,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward and backward in one call, when grad_kl is known up front.  Same
+ * arguments and outputs as kd_full_kl_fwd followed by kd_full_kl_bwd with
+ * the same chunk_rows, and the same bits: each chunk's forward keeps both
+ * heads' logits (fp32, in the workspace), so dZ comes from them instead of
+ * from recomputing both projections (the trade of §3 "Fused chunked KL",
+ * made the other way).  That costs 2 * C * roundup(V, 256) * 4 more
+ * workspace bytes for a chunk of C rows; kd_full_kl_fwd_bwd_workspace_size
+ * gives the size.  T = 0 sets dWs to zero and touches nothing else. */
+kd_status kd_full_kl_fwd_bwd_workspace_size(int64_t T, int64_t d, int64_t dt_hidden, int64_t V,
+                                            kd_dtype dt, int64_t chunk_rows, size_t* bytes);
+kd_status kd_full_kl_fwd_bwd(const void* H, const void* Ws, const void* Ht, const void* Wt,
+                             const uint8_t* mask, float tau,
+                             int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                             const float* grad_kl, float* kl, float* lse_s, float* lse_t,
+                             void* dH, float* dWs, int64_t chunk_rows,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- errors, version */
 

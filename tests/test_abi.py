@@ -29,7 +29,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), f"{n} declared in kdloss.h but not exported"
     assert sorted(kdl.EXPORTS) == names
@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
 def test_status_strings_and_version(L):
     for code, name in kdl._binding.STATUS.items():
         assert L.kd_status_string(code).decode() == name
-    assert L.kd_version() == 10100
+    assert L.kd_version() == 10200
 
 
 # ---------------------------------------------------------------- workspace sizing
@@ -208,3 +208,42 @@ def test_binding_refuses_cpu_tensors(L):
     H = torch.zeros(8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         kdl._binding._ptr(H)
+
+
+def full_fwd_bwd(T=8, d=64, dtt=64, V=256, dt=kdl.KD_BF16, tau=1.0, Ht=FAKE, g=FAKE, kl=FAKE, dH=FAKE, dW=FAKE,
+                 chunk=0, wsb=0):
+    vp = ctypes.c_void_p
+    L = kdl.lib()
+    return L.kd_full_kl_fwd_bwd(vp(FAKE), vp(FAKE), vp(Ht) if Ht else None, vp(FAKE), None, ctypes.c_float(tau), T,
+                                d, dtt, V, dt, vp(g) if g else None, vp(kl) if kl else None, vp(FAKE), vp(FAKE),
+                                vp(dH) if dH else None, vp(dW) if dW else None, chunk, vp(FAKE), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Ht=0), 1), (dict(g=0), 1), (dict(kl=0), 1), (dict(dH=0), 1), (dict(dW=0), 1), (dict(chunk=-1), 1),
+    (dict(tau=0.0), 1), (dict(dtt=60), 2), (dict(V=260), 2), (dict(dW=FAKE + 4), 3), (dict(dH=FAKE + 8), 3),
+    (dict(Ht=FAKE + 8), 3), (dict(wsb=16), 4),
+])
+def test_full_fwd_bwd_rejects(L, kw, code):
+    assert full_fwd_bwd(**kw) == code
+    assert last_error() != ""
+
+
+def test_full_fwd_bwd_zero_rows_needs_only_dw(L):
+    assert full_fwd_bwd(T=0, Ht=0, g=0, kl=0, dH=0, dW=0) == 1  # dW is still written
+    out = ctypes.c_size_t(7)
+    assert L.kd_full_kl_fwd_bwd_workspace_size(0, 3072, 4096, 128256, kdl.KD_BF16, 0, ctypes.byref(out)) == 0
+    assert out.value == 0
+
+
+def test_full_fwd_bwd_workspace_adds_two_fp32_logit_chunks(L):
+    # the two-call path's buffers, per-chunk partials, and the chunk's student
+    # and teacher logits, fp32 [C, roundup(V, 256)] each
+    for T, chunk in ((16384, 0), (10000, 2048), (300, 0)):
+        out = ctypes.c_size_t(0)
+        assert L.kd_full_kl_fwd_bwd_workspace_size(T, 3072, 4096, 128256, kdl.KD_BF16, chunk,
+                                                   ctypes.byref(out)) == 0
+        C = min(4096 if chunk == 0 else chunk, (T + 255) // 256 * 256)
+        two_call = ws_full(T, chunk=chunk)[1]
+        extra = 2 * C * 128256 * 4
+        assert two_call + extra <= out.value <= two_call + extra + 256 * C * 32 + (1 << 20)

@@ -70,3 +70,24 @@ def test_full_t16384_sampled_rows():
     assert_lse(got["lse_t"][rows], lt, torch.bfloat16)
     assert_grad(got["dH"][rows], dH, torch.bfloat16, "dH rows")
     assert np.all(np.isfinite(got["dW"]))
+
+
+@pytest.mark.parametrize("T,d,dt,V,tau,mask,chunk", [
+    (700, 384, 256, 1288, 1.0, "none", 256),       # last vocabulary tile shifted back, ragged row tile
+    (900, 256, 640, 2568, 1.6, "random10", 512),   # teacher wider than student, masked rows
+    (520, 128, 128, 128, 0.9, "none", 256),        # one vocabulary tile
+])
+def test_direct_load_path_chunks(T, d, dt, V, tau, mask, chunk):
+    # d and dt multiples of 128: the direct-to-LDS mainloop with one ring over
+    # both heads; several backward chunks accumulate into dW
+    inp = G.make_full(T, d, dt, V, torch.bfloat16, tau=tau, mask=mask, number=24, g="normal")
+    say(f"full direct-load T={T} d={d} dt={dt} V={V} chunk={chunk}")
+    check_all(run_full(inp, chunk_rows=chunk), oracle_all(inp), inp, torch.bfloat16)
+
+
+def test_full_runs_are_bitwise_deterministic():
+    inp = G.make_full(600, 256, 384, 2056, torch.bfloat16, mask="random10", number=25, g="normal")
+    say("full determinism")
+    a, b = run_full(inp, chunk_rows=256), run_full(inp, chunk_rows=256)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
