@@ -22,10 +22,22 @@ compute.  Sources, cited by page title and section:
          distillation recomputes the teacher logits from the teacher's final
          hidden states through a frozen copy of the teacher's output head.
 
+[AKD]    Adaptive-distillation abstract (on the WASD page,
+         thelatestinai.com/papers/2610.07706): the distillation temperature is
+         adjusted per token.
+[TS]     Teacher-strength abstract (thelatestinai.com/papers/2605.11513): the
+         language-modelling and distillation losses are mixed.
+
 Readings where the pages are silent (each is listed with its reason in the
 design notes of this repository):
   * Teacher top-K logits are renormalised over the K entries at temperature tau
-    (mass m = 1); the pages' partial-mass form is not this oracle's default.
+    (mass m = 1) by default.  ``topk_loss_*`` also take the pages' partial-mass
+    form: a per-row teacher log-normaliser gives the cached probabilities
+    p_k = exp(A_k / tau - teacher_lse), whose mass m = sum_k p_k may be < 1.
+  * Per-token temperature: tau_t replaces tau for row t, on both sides.
+  * The LM cross-entropy term is the K = 1 case of the same loss (one cached
+    entry, the label, with p = 1) at the same temperature; the mixed loss is
+    (1 - beta) KD + beta CE.
   * Both teacher and student logits are divided by tau; there is no tau^2.
   * The output is per token; the caller reduces.  ``g`` is dLoss/dKL_t.
   * mask[t] == 1 marks a valid row.  Masked rows give KL = 0, lse = 0,
@@ -43,6 +55,7 @@ import numpy as np
 __all__ = [
     "as_f64", "logsumexp_rows", "teacher_log_probs",
     "topk_kl_forward", "topk_kl_backward", "topk_kl_rows",
+    "topk_loss_forward", "topk_loss_backward", "topk_loss_rows",
     "full_kl_forward", "full_kl_backward", "full_kl_rows",
 ]
 
@@ -185,6 +198,124 @@ def _rows_dh_topk(H, W, I, A, mask, tau, g, row_block=64):
         p = np.exp(teacher_log_probs(A[rb], tau))
         dH[rb] = _topk_dz(s, L, I[rb], p, g[rb], tau) @ W.T
     return dH, None
+
+
+def _row_values(x, T, default):
+    """Per-row array of length T from an optional NumPy array / tensor."""
+    if x is None:
+        return np.full(T, default, dtype=np.float64)
+    return as_f64(x).reshape(T)
+
+
+def _loss_block(H, W, A, rb, taus, tlse):
+    """What the general top-K loss needs for a block of valid rows rb: raw
+    logits z, scaled logits s, their log-normaliser L, the teacher's
+    probabilities p and log-probabilities, and the mass m = sum_k p_k."""
+    tau = taus[rb][:, None]
+    z = H[rb] @ W
+    s = z / tau
+    L = logsumexp_rows(s)
+    a = A[rb] / tau
+    if tlse is None:   # renormalised over the K entries
+        logp = a - logsumexp_rows(a)[:, None]
+    else:              # the cached probabilities of the full teacher softmax
+        logp = a - tlse[rb][:, None]
+    p = np.exp(logp)
+    m = p.sum(axis=1)
+    return z, s, L, p, logp, m
+
+
+def topk_loss_forward(H, W, I, A, mask, tau, tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0,
+                      row_block=64):
+    """Per-token top-K distillation loss with the optional parts of the method.
+
+    For a valid row t, with tau_t the row's temperature ([AKD]; tau when
+    tau_rows is None), s = (H_t W) / tau_t, L_t = logsumexp(s) and the cached
+    teacher probabilities p (renormalised, or with mass m_t = sum_k p_k when
+    teacher_lse is given: [EKD] §3 "Offline distillation", partial mass):
+        KD_t = sum_k p_k log p_k - sum_k p_k s[I_tk] + m_t L_t
+    (teacher-entropy, cross and mass terms; only L_t needs the vocabulary).
+    With labels y ([TS]):  CE_t = L_t - s[y_t],  loss_t = (1 - beta) KD_t + beta CE_t.
+    Returns (loss [T], lse [T] = L_t, z_topk [T, K])."""
+    H, W, A = as_f64(H), as_f64(W), as_f64(A)
+    I = np.asarray(I.cpu().numpy() if hasattr(I, "cpu") else I, dtype=np.int64)
+    T, K = I.shape
+    taus = _row_values(tau_rows, T, tau)
+    tlse = None if teacher_lse is None else _row_values(teacher_lse, T, 0.0)
+    y = None if labels is None else np.asarray(labels.cpu().numpy() if hasattr(labels, "cpu") else labels,
+                                               dtype=np.int64)
+    beta = float(ce_weight)
+    valid = _valid_rows(mask, T)
+    loss, lse, ztk = np.zeros(T), np.zeros(T), np.zeros((T, K))
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        z, s, L, p, logp, m = _loss_block(H, W, A, rb, taus, tlse)
+        s_at = np.take_along_axis(s, I[rb], axis=1)
+        kd = (p * logp).sum(axis=1) - (p * s_at).sum(axis=1) + m * L
+        if y is not None and beta != 0.0:
+            ce = L - s[np.arange(rb.size), y[rb]]
+            loss[rb] = (1.0 - beta) * kd + beta * ce
+        else:
+            loss[rb] = kd
+        lse[rb] = L
+        ztk[rb] = np.take_along_axis(z, I[rb], axis=1)
+    return loss, lse, ztk
+
+
+def _loss_dz(s, L, I_rows, p, m, y_rows, beta, g_rows, tau_rows):
+    """dLoss/dz for a block of rows:
+    (g/tau) [(1 - beta)(m q - scatter_add(I, p)) + beta (q - onehot(y))]."""
+    q = np.exp(s - L[:, None])
+    D = q * m[:, None]
+    r = np.repeat(np.arange(s.shape[0]), I_rows.shape[1])
+    np.add.at(D, (r, I_rows.reshape(-1)), -p.reshape(-1))  # duplicates add
+    if y_rows is not None and beta != 0.0:
+        E = q.copy()
+        E[np.arange(s.shape[0]), y_rows] -= 1.0
+        D = (1.0 - beta) * D + beta * E
+    return D * (g_rows / tau_rows)[:, None]
+
+
+def topk_loss_backward(H, W, I, A, mask, tau, g, tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0,
+                       row_block=64, v_panel=16384, want_dw=True):
+    """Gradients of sum_t g_t loss_t (topk_loss_forward) w.r.t. H and W:
+    dZ_t as in _loss_dz, dH = dZ W^T, dW = H^T dZ, masked rows contribute
+    nothing.  Returns (dH [T, d], dW [d, V] or None without want_dw)."""
+    H, W, A, g = as_f64(H), as_f64(W), as_f64(A), as_f64(g)
+    I = np.asarray(I.cpu().numpy() if hasattr(I, "cpu") else I, dtype=np.int64)
+    T, d = H.shape
+    V = W.shape[1]
+    taus = _row_values(tau_rows, T, tau)
+    tlse = None if teacher_lse is None else _row_values(teacher_lse, T, 0.0)
+    y = None if labels is None else np.asarray(labels.cpu().numpy() if hasattr(labels, "cpu") else labels,
+                                               dtype=np.int64)
+    beta = float(ce_weight)
+    valid = _valid_rows(mask, T)
+    dH, dW = np.zeros((T, d)), (np.zeros((d, V)) if want_dw else None)
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        _, s, L, p, _, m = _loss_block(H, W, A, rb, taus, tlse)
+        D = _loss_dz(s, L, I[rb], p, m, None if y is None else y[rb], beta, g[rb], taus[rb])
+        dH[rb] = D @ W.T
+        if want_dw:
+            for v0 in range(0, V, v_panel):
+                dW[:, v0:v0 + v_panel] += H[rb].T @ D[:, v0:v0 + v_panel]
+    return dH, dW
+
+
+def topk_loss_rows(H, W, I, A, mask, tau, g, rows, tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0):
+    """loss, lse, z_topk and dH of topk_loss_* for selected rows only."""
+    rows = np.asarray(rows, dtype=np.int64)
+    Hr, Ir, Ar = as_f64(_take_rows(H, rows)), _take_rows(I, rows), _take_rows(A, rows)
+    mr, gr = _take_rows(mask, rows), _take_rows(g, rows)
+    kw = dict(tau_rows=_take_rows(tau_rows, rows), teacher_lse=_take_rows(teacher_lse, rows),
+              labels=_take_rows(labels, rows), ce_weight=ce_weight)
+    W = as_f64(W)
+    loss, lse, ztk = topk_loss_forward(Hr, W, Ir, Ar, mr, tau, **kw)
+    dH, _ = topk_loss_backward(Hr, W, Ir, Ar, mr, tau, gr, want_dw=False, **kw)
+    return loss, lse, ztk, dH
 
 
 def full_kl_forward(H, Ws, Ht, Wt, mask, tau, row_block=64):

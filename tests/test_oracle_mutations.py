@@ -10,6 +10,7 @@ import pytest
 
 from oracle import kd_oracle as O
 from tests import test_oracle as P
+from tests import test_oracle_options as Q
 
 PINS = [
     P.test_lse_constant_rows_closed_form, P.test_lse_matches_scipy, P.test_teacher_equal_logits,
@@ -21,6 +22,11 @@ PINS = [
     P.test_full_vocab_grad_autograd, P.test_full_vocab_zero_when_heads_equal,
     P.test_masked_rows_are_exact_zero_and_nan_does_not_leak, P.test_all_rows_masked,
     P.test_index_gather_exact_on_integer_inputs, P.test_row_block_independence_and_slice_additivity,
+    Q.test_partial_mass_with_every_entry_is_torch_kl_div, Q.test_partial_mass_scaling_identity,
+    Q.test_partial_mass_matches_autograd_of_dense_reconstruction, Q.test_partial_mass_gradient_rows_sum_to_zero,
+    Q.test_per_token_tau_is_row_scaling, Q.test_per_token_tau_gradient_is_row_scaled_plain_gradient,
+    Q.test_ce_weight_one_is_torch_cross_entropy, Q.test_ce_mix_is_the_convex_combination,
+    Q.test_ce_gradient_matches_torch_autograd, Q.test_all_options_finite_differences,
 ]
 
 
@@ -122,7 +128,62 @@ def _full_fwd_swapped(H, Ws, Ht, Wt, mask, tau, row_block=64):
 
 _ORIG_FULL = O.full_kl_forward
 
+_ORIG_LOSS_BLOCK = O._loss_block
+_ORIG_LOSS_DZ = O._loss_dz
+_ORIG_LOSS_FWD = O.topk_loss_forward
+
+
+def _loss_block_unit_mass(H, W, A, rb, taus, tlse):
+    z, s, L, p, logp, m = _ORIG_LOSS_BLOCK(H, W, A, rb, taus, tlse)
+    return z, s, L, p, logp, np.ones_like(m)  # the mass term drops to 1 * log Z
+
+
+def _loss_block_renormalised(H, W, A, rb, taus, tlse):
+    return _ORIG_LOSS_BLOCK(H, W, A, rb, taus, None)  # teacher_lse ignored
+
+
+def _row_values_ignored(x, T, default):
+    return np.full(T, default, dtype=np.float64)  # tau_rows (and teacher_lse) ignored
+
+
+def _loss_dz_no_onehot(s, L, I_rows, p, m, y_rows, beta, g_rows, tau_rows):
+    D = _ORIG_LOSS_DZ(s, L, I_rows, p, m, y_rows, beta, g_rows, tau_rows)
+    if y_rows is not None and beta != 0.0:
+        D[np.arange(s.shape[0]), y_rows] += beta * g_rows / tau_rows  # the label's -1 dropped
+    return D
+
+
+def _loss_dz_no_mass(s, L, I_rows, p, m, y_rows, beta, g_rows, tau_rows):
+    return _ORIG_LOSS_DZ(s, L, I_rows, p, np.ones_like(m), y_rows, beta, g_rows, tau_rows)
+
+
+def _loss_dz_scalar_tau(s, L, I_rows, p, m, y_rows, beta, g_rows, tau_rows):
+    return _ORIG_LOSS_DZ(s, L, I_rows, p, m, y_rows, beta, g_rows, np.full_like(tau_rows, tau_rows.mean()))
+
+
+def _loss_fwd_weights_swapped(*args, labels=None, ce_weight=0.0, **kw):
+    b = 1.0 - ce_weight if labels is not None else ce_weight
+    return _ORIG_LOSS_FWD(*args, labels=labels, ce_weight=b, **kw)
+
+
+def _loss_fwd_ce_sign(*args, labels=None, ce_weight=0.0, **kw):
+    mix = _ORIG_LOSS_FWD(*args, labels=labels, ce_weight=ce_weight, **kw)
+    if labels is None or ce_weight == 0.0:
+        return mix
+    kd = _ORIG_LOSS_FWD(*args, **kw)[0]
+    ce = (mix[0] - (1.0 - ce_weight) * kd) / ce_weight
+    return ((1.0 - ce_weight) * kd - ce_weight * ce,) + tuple(mix[1:])
+
+
 MUTATIONS = {
+    "loss_mass_term_unit": ("_loss_block", _loss_block_unit_mass),
+    "loss_partial_mass_renormalised": ("_loss_block", _loss_block_renormalised),
+    "loss_tau_rows_ignored": ("_row_values", _row_values_ignored),
+    "loss_dz_label_onehot_dropped": ("_loss_dz", _loss_dz_no_onehot),
+    "loss_dz_mass_dropped": ("_loss_dz", _loss_dz_no_mass),
+    "loss_dz_scalar_tau": ("_loss_dz", _loss_dz_scalar_tau),
+    "loss_ce_weights_swapped": ("topk_loss_forward", _loss_fwd_weights_swapped),
+    "loss_ce_sign_flipped": ("topk_loss_forward", _loss_fwd_ce_sign),
     "lse_without_max_shift": ("logsumexp_rows", _lse_no_shift),
     "teacher_without_tau": ("teacher_log_probs", _teacher_no_tau),
     "student_without_tau": ("_student_block", _student_no_tau),

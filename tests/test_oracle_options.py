@@ -1,0 +1,232 @@
+"""Pins of the oracle's general top-K loss (``topk_loss_*``): the partial-mass
+teacher, per-token temperature and the LM cross-entropy mix.  CPU only.
+
+Sources: "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and a
+Fused Chunked KL Loss", §3 "Offline distillation" (cached probabilities keep
+their unnormalised partial mass; teacher-entropy, cross and mass terms over
+the support, plus the one full-vocabulary log Z) and "Offline
+implementations" (the dense reconstruction is the correctness baseline); the
+adaptive-distillation abstract on the WASD page (per-token temperature); the
+teacher-strength abstract (mixing the LM and KD losses).  Every pin checks the
+oracle against something other than its own formula: a library routine, an
+identity that relates it to the already pinned renormalised oracle, autograd
+of the dense reconstruction, or finite differences.
+"""
+import numpy as np
+import pytest
+import scipy.special as sps
+import torch
+
+from oracle import kd_oracle as O
+
+
+def case(T=6, d=8, V=32, K=5, seed=0, dup=False):
+    rng = np.random.default_rng(seed)
+    H = rng.standard_normal((T, d))
+    W = rng.standard_normal((d, V)) / np.sqrt(d)
+    A = -np.sort(-rng.standard_normal((T, K)) * 1.7, axis=1)
+    I = np.stack([rng.choice(V, K, replace=False) for _ in range(T)]).astype(np.int64)
+    if dup:
+        I[:, 1] = I[:, 0]
+    g = rng.standard_normal(T)
+    taus = rng.uniform(0.6, 2.5, T)
+    y = rng.integers(0, V, T)
+    return H, W, I, A, g, taus, y
+
+
+def teacher_lse_for_mass(A, taus, rng):
+    """A per-row log-normaliser that leaves mass m_t in (0.15, 0.95) on the K entries."""
+    a = A / taus[:, None]
+    m = rng.uniform(0.15, 0.95, A.shape[0])
+    return sps.logsumexp(a, axis=1) - np.log(m), m
+
+
+# ---------------------------------------------------------------- partial mass
+def test_partial_mass_with_every_entry_is_torch_kl_div():
+    # K = V, the full teacher softmax cached (teacher_lse its true log Z):
+    # the support identity must equal the full-vocabulary KL of torch
+    rng = np.random.default_rng(1)
+    T, d, V = 5, 8, 24
+    H = rng.standard_normal((T, d))
+    W = rng.standard_normal((d, V)) / np.sqrt(d)
+    U = rng.standard_normal((T, V)) * 2.0
+    I = np.stack([rng.permutation(V) for _ in range(T)])
+    A = np.take_along_axis(U, I, axis=1)
+    for tau in (1.0, 1.7):
+        tl = sps.logsumexp(U / tau, axis=1)
+        got, _, _ = O.topk_loss_forward(H, W, I, A, None, tau, teacher_lse=tl)
+        logq = torch.log_softmax(torch.tensor(H @ W) / tau, dim=1)
+        logp = torch.log_softmax(torch.tensor(U) / tau, dim=1)
+        want = torch.nn.functional.kl_div(logq, logp, log_target=True, reduction="none").sum(1).numpy()
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_partial_mass_scaling_identity():
+    # p = m p~ with p~ the renormalised teacher: KD = m (KL_renormalised + log m)
+    H, W, I, A, g, _, _ = case(T=8, seed=2)
+    rng = np.random.default_rng(3)
+    for tau in (1.0, 0.7, 2.2):
+        tl, m = teacher_lse_for_mass(A, np.full(8, tau), rng)
+        got, lse, _ = O.topk_loss_forward(H, W, I, A, None, tau, teacher_lse=tl)
+        ren, lse2, _ = O.topk_kl_forward(H, W, I, A, None, tau)
+        np.testing.assert_allclose(got, m * (ren + np.log(m)), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse, lse2, rtol=1e-14)
+
+
+def _dense_partial_mass(Ht, Wt, I, A, tl, taus, g):
+    """Dense reconstruction ([EKD] §3 "Offline implementations") with the
+    cached probabilities scattered unnormalised into a [T, V] tensor."""
+    T, V = Ht.shape[0], Wt.shape[1]
+    tau = torch.tensor(taus)[:, None]
+    logq = torch.log_softmax((Ht @ Wt) / tau, dim=1)
+    p = torch.exp(torch.tensor(A) / tau - torch.tensor(tl)[:, None])
+    P = torch.zeros(T, V, dtype=torch.float64).scatter_add_(1, torch.tensor(I), p)
+    plogp = torch.where(P > 0, P * torch.log(torch.where(P > 0, P, torch.ones_like(P))), torch.zeros_like(P))
+    kd = (plogp - P * logq).sum(1)
+    return (kd * torch.tensor(g)).sum(), kd
+
+
+def test_partial_mass_matches_autograd_of_dense_reconstruction():
+    H, W, I, A, g, taus, _ = case(T=7, d=6, V=25, seed=4)
+    rng = np.random.default_rng(5)
+    tl, _ = teacher_lse_for_mass(A, taus, rng)
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    loss, kd = _dense_partial_mass(Ht, Wt, I, A, tl, taus, g)
+    loss.backward()
+    got, _, _ = O.topk_loss_forward(H, W, I, A, None, 1.0, tau_rows=taus, teacher_lse=tl)
+    np.testing.assert_allclose(got, kd.detach().numpy(), rtol=1e-12)
+    dH, dW = O.topk_loss_backward(H, W, I, A, None, 1.0, g, tau_rows=taus, teacher_lse=tl)
+    np.testing.assert_allclose(dH, Ht.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+def test_partial_mass_gradient_rows_sum_to_zero():
+    # sum_v dZ_tv = (g_t / tau_t) (m_t - m_t) = 0 for KD alone: the mass term
+    # of the gradient (m q) balances the scattered p exactly, so dW . 1 = 0
+    H, W, I, A, g, taus, _ = case(T=6, seed=6)
+    tl, _ = teacher_lse_for_mass(A, taus, np.random.default_rng(7))
+    _, dW = O.topk_loss_backward(H, W, I, A, None, 1.0, g, tau_rows=taus, teacher_lse=tl)
+    np.testing.assert_allclose(dW.sum(1), 0.0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- per-token temperature
+def test_per_token_tau_is_row_scaling():
+    # row t at tau_t equals the tau = 1 loss of (H_t / tau_t, A_t / tau_t)
+    H, W, I, A, g, taus, _ = case(T=7, seed=8)
+    got, _, _ = O.topk_loss_forward(H, W, I, A, None, 1.0, tau_rows=taus)
+    want, _, _ = O.topk_kl_forward(H / taus[:, None], W, I, A / taus[:, None], None, 1.0)
+    np.testing.assert_allclose(got, want, rtol=1e-12)
+    # one row at a time through the scalar-tau oracle
+    for t in range(7):
+        one, _, _ = O.topk_kl_forward(H[t:t + 1], W, I[t:t + 1], A[t:t + 1], None, taus[t])
+        assert got[t] == pytest.approx(one[0], rel=1e-12)
+
+
+def test_per_token_tau_gradient_is_row_scaled_plain_gradient():
+    # dH_t at tau_t equals the plain oracle's dH of (H_t / tau_t, A_t / tau_t) at
+    # tau = 1, divided by tau_t (chain rule through H / tau_t)
+    H, W, I, A, g, taus, _ = case(T=6, seed=9)
+    dH, _ = O.topk_loss_backward(H, W, I, A, None, 1.0, g, tau_rows=taus)
+    dH1, _ = O.topk_kl_backward(H / taus[:, None], W, I, A / taus[:, None], None, 1.0, g)
+    np.testing.assert_allclose(dH, dH1 / taus[:, None], rtol=1e-11, atol=1e-14)
+
+
+# ---------------------------------------------------------------- LM cross-entropy mix
+def test_ce_weight_one_is_torch_cross_entropy():
+    H, W, I, A, g, taus, y = case(T=9, V=40, seed=10)
+    got, _, _ = O.topk_loss_forward(H, W, I, A, None, 1.0, tau_rows=taus, labels=y, ce_weight=1.0)
+    logits = torch.tensor(H @ W) / torch.tensor(taus)[:, None]
+    want = torch.nn.functional.cross_entropy(logits, torch.tensor(y), reduction="none").numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-13)
+
+
+def test_ce_mix_is_the_convex_combination():
+    H, W, I, A, g, _, y = case(T=8, V=36, seed=11)
+    for tau, beta in ((1.0, 0.25), (1.6, 0.5), (0.8, 0.9)):
+        got, lse, _ = O.topk_loss_forward(H, W, I, A, None, tau, labels=y, ce_weight=beta)
+        kd, lse2, _ = O.topk_kl_forward(H, W, I, A, None, tau)
+        ce = torch.nn.functional.cross_entropy(torch.tensor(H @ W / tau), torch.tensor(y),
+                                               reduction="none").numpy()
+        np.testing.assert_allclose(got, (1 - beta) * kd + beta * ce, rtol=1e-12)
+        np.testing.assert_allclose(lse, lse2, rtol=1e-14)
+
+
+def test_ce_gradient_matches_torch_autograd():
+    H, W, I, A, g, _, y = case(T=6, V=30, seed=12)
+    tau, beta = 1.3, 0.4
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    logits = Ht @ Wt / tau
+    ce = torch.nn.functional.cross_entropy(logits, torch.tensor(y), reduction="none")
+    (beta * ce * torch.tensor(g)).sum().backward()
+    dH_ce, dW_ce = Ht.grad.numpy().copy(), Wt.grad.numpy().copy()
+    dH_kd, dW_kd = O.topk_kl_backward(H, W, I, A, None, tau, g)
+    dH, dW = O.topk_loss_backward(H, W, I, A, None, tau, g, labels=y, ce_weight=beta)
+    np.testing.assert_allclose(dH, (1 - beta) * dH_kd + dH_ce, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dW, (1 - beta) * dW_kd + dW_ce, rtol=1e-11, atol=1e-14)
+
+
+# ---------------------------------------------------------------- all options at once
+def test_all_options_finite_differences():
+    H, W, I, A, g, taus, y = case(T=4, d=8, V=32, K=4, seed=13, dup=True)
+    y[0] = I[0, 2]  # a label that is also a cached index
+    tl, _ = teacher_lse_for_mass(A, taus, np.random.default_rng(14))
+    mask = np.array([1, 0, 1, 1], dtype=np.uint8)
+    kw = dict(tau_rows=taus, teacher_lse=tl, labels=y, ce_weight=0.35)
+    dH, dW = O.topk_loss_backward(H, W, I, A, mask, 1.0, g, **kw)
+
+    def loss(Hx, Wx):
+        v, _, _ = O.topk_loss_forward(Hx, Wx, I, A, mask, 1.0, **kw)
+        return float((v * g).sum())
+
+    h = 1e-6
+    rng = np.random.default_rng(15)
+    for _ in range(12):
+        t, j = rng.integers(4), rng.integers(8)
+        Hp, Hm = H.copy(), H.copy()
+        Hp[t, j] += h
+        Hm[t, j] -= h
+        assert (loss(Hp, W) - loss(Hm, W)) / (2 * h) == pytest.approx(dH[t, j], rel=1e-7, abs=1e-9)
+    for _ in range(12):
+        j, v = rng.integers(8), rng.integers(32)
+        Wp, Wm = W.copy(), W.copy()
+        Wp[j, v] += h
+        Wm[j, v] -= h
+        assert (loss(H, Wp) - loss(H, Wm)) / (2 * h) == pytest.approx(dW[j, v], rel=1e-7, abs=1e-9)
+    assert np.all(dH[1] == 0)
+
+
+def test_no_options_is_the_plain_loss():
+    H, W, I, A, g, _, _ = case(T=7, seed=16)
+    a = O.topk_loss_forward(H, W, I, A, None, 1.4)
+    b = O.topk_kl_forward(H, W, I, A, None, 1.4)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(O.topk_loss_backward(H, W, I, A, None, 1.4, g)[1],
+                               O.topk_kl_backward(H, W, I, A, None, 1.4, g)[1], rtol=1e-12, atol=1e-15)
+
+
+def test_masked_rows_ignore_garbage_options():
+    H, W, I, A, g, taus, y = case(T=5, seed=17)
+    tl, _ = teacher_lse_for_mass(A, taus, np.random.default_rng(18))
+    mask = np.array([1, 0, 1, 0, 1], dtype=np.uint8)
+    taus[1], tl[3], y[1], y[3] = np.nan, np.nan, -7, 10 ** 6
+    H[3] = np.nan
+    kw = dict(tau_rows=taus, teacher_lse=tl, labels=y, ce_weight=0.5)
+    v, lse, z = O.topk_loss_forward(H, W, I, A, mask, 1.0, **kw)
+    dH, dW = O.topk_loss_backward(H, W, I, A, mask, 1.0, g, **kw)
+    assert np.all(v[[1, 3]] == 0) and np.all(lse[[1, 3]] == 0) and np.all(dH[[1, 3]] == 0)
+    assert np.all(np.isfinite(v)) and np.all(np.isfinite(dW))
+
+
+def test_rows_helper_matches_full_functions():
+    H, W, I, A, g, taus, y = case(T=9, seed=19)
+    tl, _ = teacher_lse_for_mass(A, taus, np.random.default_rng(20))
+    kw = dict(tau_rows=taus, teacher_lse=tl, labels=y, ce_weight=0.3)
+    v, lse, z = O.topk_loss_forward(H, W, I, A, None, 1.0, **kw)
+    dH, _ = O.topk_loss_backward(H, W, I, A, None, 1.0, g, **kw)
+    rows = [0, 4, 8]
+    rv, rl, rz, rdH = O.topk_loss_rows(H, W, I, A, None, 1.0, g, rows, **kw)
+    np.testing.assert_allclose(rv, v[rows], rtol=1e-14)
+    np.testing.assert_allclose(rdH, dH[rows], rtol=1e-13, atol=1e-16)
