@@ -18,7 +18,8 @@ import torch
 
 from ._binding import (  # noqa: F401
     EXPORTS, KD_BF16, KD_DEFAULT_CHUNK_ROWS, KD_F32, KD_MAX_K, LIB_PATH, KDError, kd_full_kl_bwd, kd_full_kl_fwd,
-    kd_full_kl_fwd_bwd, kd_full_kl_fwd_bwd_workspace_size, kd_full_kl_workspace_size, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd, kd_topk_kl_fwd_bwd_workspace_size,
+    kd_full_kl_fwd_bwd, kd_full_kl_fwd_bwd_workspace_size, kd_full_kl_workspace_size, kd_topk_kl_bwd_ex,
+    kd_topk_kl_fwd_bwd_ex, kd_topk_kl_fwd_ex, topk_opts, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd, kd_topk_kl_fwd_bwd_workspace_size,
     kd_topk_kl_workspace_size, kd_version, lib,
     profile_enable, profile_read, profile_reset,
 )
@@ -28,6 +29,7 @@ __all__ = [
     "full_kl_backward", "full_kl_forward_backward", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_topk_kl_fwd_bwd",
     "kd_full_kl_fwd", "kd_full_kl_bwd", "kd_full_kl_fwd_bwd", "kd_topk_kl_workspace_size",
     "kd_topk_kl_fwd_bwd_workspace_size", "kd_full_kl_workspace_size", "kd_full_kl_fwd_bwd_workspace_size", "KDError",
+    "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex", "topk_opts",
 ]
 
 
@@ -35,8 +37,13 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def topk_kl_forward(H, W, topk_idx, topk_logits, mask=None, tau=1.0, want_z_topk=False, workspace=None):
-    """Per-token KL, log-normaliser and (optionally) the gathered raw logits."""
+# Optional parts of the top-K loss, as keyword arguments of the functions below
+# (kd_topk_opts of kdloss.h): tau_rows [T] float32 per-token temperature,
+# teacher_lse [T] float32 teacher log-normaliser (partial-mass teacher),
+# labels [T] int32 with ce_weight in [0, 1] (loss = (1 - w) KD + w CE).
+def topk_kl_forward(H, W, topk_idx, topk_logits, mask=None, tau=1.0, want_z_topk=False, workspace=None,
+                    **options):
+    """Per-token loss, log-normaliser and (optionally) the gathered raw logits."""
     T, d = H.shape
     V, K = W.shape[1], topk_idx.shape[1]
     kl = torch.empty(T, dtype=torch.float32, device=H.device)
@@ -44,11 +51,12 @@ def topk_kl_forward(H, W, topk_idx, topk_logits, mask=None, tau=1.0, want_z_topk
     z = torch.empty(T, K, dtype=torch.float32, device=H.device) if want_z_topk else None
     if workspace is None:
         workspace = _workspace(kd_topk_kl_workspace_size(T, d, V, K, H.dtype), H.device)
-    kd_topk_kl_fwd(H, W, topk_idx, topk_logits, mask, tau, kl, lse, z, workspace)
+    kd_topk_kl_fwd_ex(H, W, topk_idx, topk_logits, mask, tau, topk_opts(**options), kl, lse, z, workspace)
     return kl, lse, z
 
 
-def topk_kl_backward(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl, chunk_rows=0, workspace=None):
+def topk_kl_backward(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl, chunk_rows=0, workspace=None,
+                     **options):
     """dH (dtype of H) and dW (float32) for the per-token upstream gradient."""
     T, d = H.shape
     V, K = W.shape[1], topk_idx.shape[1]
@@ -56,13 +64,13 @@ def topk_kl_backward(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl, chunk
     dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
     if workspace is None:
         workspace = _workspace(kd_topk_kl_workspace_size(T, d, V, K, H.dtype, chunk_rows), H.device)
-    kd_topk_kl_bwd(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl.float().contiguous(), dH, dW, chunk_rows,
-                   workspace)
+    kd_topk_kl_bwd_ex(H, W, topk_idx, topk_logits, mask, tau, topk_opts(**options), lse,
+                      grad_kl.float().contiguous(), dH, dW, chunk_rows, workspace)
     return dH, dW
 
 
 def topk_kl_forward_backward(H, W, topk_idx, topk_logits, mask, tau, grad_kl, chunk_rows=0, want_z_topk=False,
-                             workspace=None):
+                             workspace=None, **options):
     """kl, lse, z_topk (or None), dH and dW in one call, for a known grad_kl."""
     T, d = H.shape
     V, K = W.shape[1], topk_idx.shape[1]
@@ -73,8 +81,8 @@ def topk_kl_forward_backward(H, W, topk_idx, topk_logits, mask, tau, grad_kl, ch
     dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
     if workspace is None:
         workspace = _workspace(kd_topk_kl_fwd_bwd_workspace_size(T, d, V, K, H.dtype, chunk_rows), H.device)
-    kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logits, mask, tau, grad_kl.float().contiguous(), kl, lse, z, dH, dW,
-                       chunk_rows, workspace)
+    kd_topk_kl_fwd_bwd_ex(H, W, topk_idx, topk_logits, mask, tau, topk_opts(**options),
+                          grad_kl.float().contiguous(), kl, lse, z, dH, dW, chunk_rows, workspace)
     return kl, lse, z, dH, dW
 
 
@@ -120,17 +128,17 @@ def full_kl_forward_backward(H, Ws, Ht, Wt, mask, tau, grad_kl, chunk_rows=0, wo
 
 class _TopkKL(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, W, topk_idx, topk_logits, mask, tau, chunk_rows):
-        kl, lse, _ = topk_kl_forward(H, W, topk_idx, topk_logits, mask, tau)
+    def forward(ctx, H, W, topk_idx, topk_logits, mask, tau, chunk_rows, options):
+        kl, lse, _ = topk_kl_forward(H, W, topk_idx, topk_logits, mask, tau, **options)
         ctx.save_for_backward(H, W, topk_idx, topk_logits, lse)
-        ctx.mask, ctx.tau, ctx.chunk_rows = mask, tau, chunk_rows
+        ctx.mask, ctx.tau, ctx.chunk_rows, ctx.options = mask, tau, chunk_rows, options
         return kl
 
     @staticmethod
     def backward(ctx, g):
         H, W, idx, logits, lse = ctx.saved_tensors
-        dH, dW = topk_kl_backward(H, W, idx, logits, ctx.mask, ctx.tau, lse, g, ctx.chunk_rows)
-        return dH, dW.to(W.dtype), None, None, None, None, None
+        dH, dW = topk_kl_backward(H, W, idx, logits, ctx.mask, ctx.tau, lse, g, ctx.chunk_rows, **ctx.options)
+        return dH, dW.to(W.dtype), None, None, None, None, None, None
 
 
 class _FullKL(torch.autograd.Function):
@@ -148,11 +156,14 @@ class _FullKL(torch.autograd.Function):
         return dH, dW.to(Ws.dtype), None, None, None, None, None
 
 
-def topk_kl(H, W, topk_idx, topk_logits, mask=None, tau=1.0, chunk_rows=0):
-    """Per-token KL(p_teacher || q_student) with a top-K teacher; differentiable
-    in H and W (W's gradient is cast to W's dtype; the float32 one is available
-    from topk_kl_backward)."""
-    return _TopkKL.apply(H, W, topk_idx, topk_logits, mask, float(tau), int(chunk_rows))
+def topk_kl(H, W, topk_idx, topk_logits, mask=None, tau=1.0, chunk_rows=0, tau_rows=None, teacher_lse=None,
+            labels=None, ce_weight=0.0):
+    """Per-token KL(p_teacher || q_student) with a top-K teacher (with the
+    options: the mixed loss of kd_topk_opts); differentiable in H and W (W's
+    gradient is cast to W's dtype; the float32 one is available from
+    topk_kl_backward)."""
+    options = dict(tau_rows=tau_rows, teacher_lse=teacher_lse, labels=labels, ce_weight=float(ce_weight))
+    return _TopkKL.apply(H, W, topk_idx, topk_logits, mask, float(tau), int(chunk_rows), options)
 
 
 def full_kl(H, Ws, Ht, Wt, mask=None, tau=1.0, chunk_rows=0):

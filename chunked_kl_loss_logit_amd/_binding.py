@@ -26,11 +26,18 @@ STATUS = {
 EXPORTS = (
     "kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd",
     "kd_topk_kl_fwd_bwd_workspace_size", "kd_topk_kl_fwd_bwd",
+    "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex",
     "kd_full_kl_workspace_size", "kd_full_kl_fwd", "kd_full_kl_bwd",
     "kd_full_kl_fwd_bwd_workspace_size", "kd_full_kl_fwd_bwd",
     "kd_status_string", "kd_last_error", "kd_version",
     "kd_profile_enable", "kd_profile_count", "kd_profile_get", "kd_profile_reset",
 )
+
+
+class KdTopkOpts(ctypes.Structure):
+    """kd_topk_opts of kdloss.h: device pointers (0 = NULL) and the CE weight."""
+    _fields_ = [("tau_rows", ctypes.c_void_p), ("teacher_lse", ctypes.c_void_p), ("labels", ctypes.c_void_p),
+                ("ce_weight", ctypes.c_float)]
 
 
 class KDError(RuntimeError):
@@ -61,6 +68,12 @@ def lib() -> ctypes.CDLL:
     L.kd_topk_kl_fwd_bwd_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
     L.kd_topk_kl_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp, i64,
                                      vp, sz, vp]
+    op = ctypes.POINTER(KdTopkOpts)
+    L.kd_topk_kl_fwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, op, i64, i64, i64, i64, st, vp, vp, vp, vp, sz, vp]
+    L.kd_topk_kl_bwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, op, i64, i64, i64, i64, st, vp, vp, vp, vp, i64, vp, sz,
+                                    vp]
+    L.kd_topk_kl_fwd_bwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, op, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp,
+                                        i64, vp, sz, vp]
     L.kd_full_kl_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
     L.kd_full_kl_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, sz, vp]
     L.kd_full_kl_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, i64, vp, sz,
@@ -69,7 +82,8 @@ def lib() -> ctypes.CDLL:
     L.kd_full_kl_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp, i64,
                                      vp, sz, vp]
     for f in ("kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_topk_kl_fwd_bwd_workspace_size",
-              "kd_topk_kl_fwd_bwd", "kd_full_kl_workspace_size",
+              "kd_topk_kl_fwd_bwd", "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex",
+              "kd_full_kl_workspace_size",
               "kd_full_kl_fwd", "kd_full_kl_bwd", "kd_full_kl_fwd_bwd_workspace_size", "kd_full_kl_fwd_bwd",
               "kd_profile_enable", "kd_profile_get", "kd_profile_reset"):
         getattr(L, f).restype = st
@@ -172,6 +186,59 @@ def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logits, mask, tau, grad_kl, kl, lse,
                                     _ptr(z_topk), _ptr(dH), _ptr(dW), int(chunk_rows), _ptr(workspace),
                                     workspace.numel() if workspace is not None else 0, _stream(stream)),
            "kd_topk_kl_fwd_bwd")
+
+
+def topk_opts(tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0):
+    """The kd_topk_opts struct for these device tensors (or None when no option is set).  The
+    tensors must stay alive until the call that takes the struct has been enqueued."""
+    if tau_rows is None and teacher_lse is None and labels is None and not ce_weight:
+        return None
+    for name, t, dt in (("tau_rows", tau_rows, torch.float32), ("teacher_lse", teacher_lse, torch.float32),
+                        ("labels", labels, torch.int32)):
+        if t is not None and t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}")
+    return KdTopkOpts(_ptr(tau_rows), _ptr(teacher_lse), _ptr(labels), float(ce_weight))
+
+
+def _opts_ref(opts):
+    return None if opts is None else ctypes.byref(opts)
+
+
+def kd_topk_kl_fwd_ex(H, W, topk_idx, topk_logits, mask, tau, opts, kl, lse, z_topk, workspace, stream=None):
+    """kd_topk_kl_fwd with a kd_topk_opts (topk_opts(...)) or None."""
+    T, d = H.shape
+    V = W.shape[1]
+    K = topk_idx.shape[1]
+    _check(lib().kd_topk_kl_fwd_ex(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask), float(tau),
+                                   _opts_ref(opts), T, d, V, K, _dtype_code(H.dtype), _ptr(kl), _ptr(lse),
+                                   _ptr(z_topk), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                   _stream(stream)), "kd_topk_kl_fwd_ex")
+
+
+def kd_topk_kl_bwd_ex(H, W, topk_idx, topk_logits, mask, tau, opts, lse, grad_kl, dH, dW, chunk_rows, workspace,
+                      stream=None):
+    """kd_topk_kl_bwd with a kd_topk_opts (the forward call's) or None."""
+    T, d = H.shape
+    V = W.shape[1]
+    K = topk_idx.shape[1]
+    _check(lib().kd_topk_kl_bwd_ex(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask), float(tau),
+                                   _opts_ref(opts), T, d, V, K, _dtype_code(H.dtype), _ptr(lse), _ptr(grad_kl),
+                                   _ptr(dH), _ptr(dW), int(chunk_rows), _ptr(workspace),
+                                   workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "kd_topk_kl_bwd_ex")
+
+
+def kd_topk_kl_fwd_bwd_ex(H, W, topk_idx, topk_logits, mask, tau, opts, grad_kl, kl, lse, z_topk, dH, dW,
+                          chunk_rows, workspace, stream=None):
+    """kd_topk_kl_fwd_bwd with a kd_topk_opts or None."""
+    T, d = H.shape
+    V = W.shape[1]
+    K = topk_idx.shape[1]
+    _check(lib().kd_topk_kl_fwd_bwd_ex(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask),
+                                       float(tau), _opts_ref(opts), T, d, V, K, _dtype_code(H.dtype), _ptr(grad_kl),
+                                       _ptr(kl), _ptr(lse), _ptr(z_topk), _ptr(dH), _ptr(dW), int(chunk_rows),
+                                       _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                       _stream(stream)), "kd_topk_kl_fwd_bwd_ex")
 
 
 def kd_full_kl_fwd(H, Ws, Ht, Wt, mask, tau, kl, lse_s, lse_t, workspace, stream=None):

@@ -95,7 +95,7 @@ kd_status check_k(int64_t T, int64_t K, int64_t V) {
   if (K < 1) return fail(KD_ERR_INVALID_ARG, "K must be >= 1");
   if (K > V) return fail(KD_ERR_INVALID_ARG, "K must be <= V");
   if (K > KD_MAX_K) return fail(KD_ERR_UNSUPPORTED, "K above KD_MAX_K");
-  if (T * K >= INT32_MAX) return fail(KD_ERR_UNSUPPORTED, "T * K must be below 2^31");
+  if (T * (K + 1) >= INT32_MAX) return fail(KD_ERR_UNSUPPORTED, "T * (K + 1) must be below 2^31");
   return KD_OK;
 }
 
@@ -176,7 +176,7 @@ ChunkPlan plan_chunk(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_ro
 
 struct TopkPlan {
   int ntiles, nrb, S;
-  size_t o_pair, o_perm, o_ent, o_rows, o_count, o_part;
+  size_t o_pair, o_perm, o_ent, o_rowc, o_rows, o_count, o_part;
   ChunkPlan ch;
   size_t fwd_total, total;  // bytes the forward call needs; bytes both calls need
   // single-call forward + backward: per-chunk partials, the chunk's fp32
@@ -192,9 +192,11 @@ TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t
   p.nrb = (int)cdiv(T, kd::kTileM);
   p.S = splits_for(p.nrb, p.ntiles);
   Carver cv;
-  p.o_pair = cv.take((size_t)T * K * 8);
-  p.o_perm = cv.take((size_t)T * K * 2);
+  // room for K + 1 entries per row: a cross-entropy label is one more
+  p.o_pair = cv.take((size_t)T * (K + 1) * 8);
+  p.o_perm = cv.take((size_t)T * (K + 1) * 2);
   p.o_ent = cv.take((size_t)T * 4);
+  p.o_rowc = cv.take((size_t)T * 16);
   p.o_rows = cv.take((size_t)T * 4);
   p.o_count = cv.take(16);
   Carver fw = cv, bw = cv;  // forward partials and backward chunk buffers overlap
@@ -321,7 +323,7 @@ const char* kd_status_string(kd_status s) {
 
 const char* kd_last_error(void) { return g_err.c_str(); }
 
-int kd_version(void) { return 10200; }
+int kd_version(void) { return 10300; }
 
 kd_status kd_profile_enable(int on) {
   g_prof_on = on != 0;
@@ -353,6 +355,49 @@ kd_status kd_profile_reset(void) {
 }
 
 // ---------------------------------------------------------------- top-K
+}  // extern "C"
+
+namespace {
+
+// The options of a top-K call as the kernels take them; KE is the number of
+// support entries per row (K, or K + 1 with a cross-entropy label).
+struct TopkOpts {
+  kd::TopkPrepOpts prep;
+  int64_t KE;
+};
+
+kd_status resolve_opts(const kd_topk_opts* o, float tau, int64_t K, TopkOpts& r) {
+  r.prep = kd::TopkPrepOpts{};
+  r.prep.c2 = (float)(1.4426950408889634 / (double)tau);
+  r.prep.inv_tau = 1.0f / tau;
+  r.KE = K;
+  if (o == nullptr) return KD_OK;
+  if (!std::isfinite(o->ce_weight) || o->ce_weight < 0.f || o->ce_weight > 1.f)
+    return fail(KD_ERR_INVALID_ARG, "ce_weight must be finite and in [0, 1]");
+  if (o->ce_weight > 0.f && o->labels == nullptr) return fail(KD_ERR_INVALID_ARG, "ce_weight > 0 needs labels");
+  KD_TRY(need_align(o->tau_rows, 4, "tau_rows"));
+  KD_TRY(need_align(o->teacher_lse, 4, "teacher_lse"));
+  KD_TRY(need_align(o->labels, 4, "labels"));
+  r.prep.tau_rows = o->tau_rows;
+  r.prep.teacher_lse = o->teacher_lse;
+  if (o->ce_weight > 0.f) {
+    if (K + 1 > KD_MAX_K) return fail(KD_ERR_UNSUPPORTED, "a CE label needs K < KD_MAX_K");
+    r.prep.labels = o->labels;
+    r.prep.beta = o->ce_weight;
+    r.KE = K + 1;
+  }
+  return KD_OK;
+}
+
+kd::TopkRowData row_data(void* ws, const TopkPlan& p) {
+  return kd::TopkRowData{at<int2>(ws, p.o_pair), at<uint16_t>(ws, p.o_perm), at<float>(ws, p.o_ent),
+                         at<float4>(ws, p.o_rowc)};
+}
+
+}  // namespace
+
+extern "C" {
+
 kd_status kd_topk_kl_workspace_size(int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt, int64_t chunk_rows,
                                     size_t* bytes) {
   g_err.clear();
@@ -367,9 +412,19 @@ kd_status kd_topk_kl_fwd(const void* H, const void* W, const int32_t* topk_idx, 
                          const uint8_t* mask, float tau, int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
                          float* kl, float* lse, float* z_topk, void* workspace, size_t workspace_bytes,
                          void* stream) {
+  return kd_topk_kl_fwd_ex(H, W, topk_idx, topk_logits, mask, tau, nullptr, T, d, V, K, dt, kl, lse, z_topk,
+                           workspace, workspace_bytes, stream);
+}
+
+kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                            const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d,
+                            int64_t V, int64_t K, kd_dtype dt, float* kl, float* lse, float* z_topk,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
   KD_TRY(check_k(T, K, V));
+  TopkOpts op;
+  KD_TRY(resolve_opts(opts, tau, K, op));
   if (T == 0) return KD_OK;
   KD_TRY(need(H, "H"));
   KD_TRY(need(W, "W"));
@@ -390,11 +445,11 @@ kd_status kd_topk_kl_fwd(const void* H, const void* W, const int32_t* topk_idx, 
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
-  kd::TopkRowData rd{at<int2>(workspace, p.o_pair), at<uint16_t>(workspace, p.o_perm), at<float>(workspace, p.o_ent)};
+  const kd::TopkRowData rd = row_data(workspace, p);
   float* part = at<float>(workspace, p.o_part);
 
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
-  KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, tau, rd, z_topk, st));
+  KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, op.KE, op.prep, rd, z_topk, st));
   kd::TopkFwdArgs a{};
   a.H = static_cast<const char*>(H);
   a.W = static_cast<const char*>(W);
@@ -409,14 +464,14 @@ kd_status kd_topk_kl_fwd(const void* H, const void* W, const int32_t* topk_idx, 
   a.T = T;
   a.d = d;
   a.V = V;
-  a.K = K;
+  a.K = op.KE;
+  a.Kz = K;
   a.nrb = p.nrb;
   a.S = p.S;
   a.ntiles = p.ntiles;
   a.group = kRasterGroup;
-  a.c2 = (float)(1.4426950408889634 / (double)tau);
   KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
-  KD_LAUNCH("topk_combine", st, kd::launch_topk_combine(part, p.S, T, c, mask, rd.ent, T, tau, kl, lse, 0, T, true, st));
+  KD_LAUNCH("topk_combine", st, kd::launch_topk_combine(part, p.S, T, c, mask, rd, T, kl, lse, 0, T, true, st));
   return KD_OK;
 }
 
@@ -424,9 +479,19 @@ kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx, 
                          const uint8_t* mask, float tau, int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
                          const float* lse, const float* grad_kl, void* dH, float* dW, int64_t chunk_rows,
                          void* workspace, size_t workspace_bytes, void* stream) {
+  return kd_topk_kl_bwd_ex(H, W, topk_idx, topk_logits, mask, tau, nullptr, T, d, V, K, dt, lse, grad_kl, dH, dW,
+                           chunk_rows, workspace, workspace_bytes, stream);
+}
+
+kd_status kd_topk_kl_bwd_ex(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                            const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d,
+                            int64_t V, int64_t K, kd_dtype dt, const float* lse, const float* grad_kl, void* dH,
+                            float* dW, int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
   KD_TRY(check_k(T, K, V));
+  TopkOpts op;
+  KD_TRY(resolve_opts(opts, tau, K, op));
   KD_TRY(need(dW, "dW"));
   KD_TRY(need_align(dW, 16, "dW"));
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -454,9 +519,9 @@ kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx, 
   KD_TRY(check_workspace(workspace, workspace_bytes, p.total));
 
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
-  kd::TopkRowData rd{at<int2>(workspace, p.o_pair), at<uint16_t>(workspace, p.o_perm), at<float>(workspace, p.o_ent)};
+  const kd::TopkRowData rd = row_data(workspace, p);
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
-  KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, tau, rd, nullptr, st));
+  KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, op.KE, op.prep, rd, nullptr, st));
   KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * elem, dH, st));
 
   const ChunkPlan& ch = p.ch;
@@ -480,13 +545,11 @@ kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx, 
     za.T = T;
     za.d = d;
     za.V = V;
-    za.K = K;
+    za.K = op.KE;
     za.nrb = ch.nrb_c;
     za.ntiles = p.ntiles;
     za.group = kRasterGroup;
     za.S = splits_for(ch.nrb_c, p.ntiles);
-    za.c2 = (float)(1.4426950408889634 / (double)tau);
-    za.inv_tau = 1.0f / tau;
     KD_LAUNCH("topk_dz_tile", st, kd::launch_topk_dz(elem, za, st));
     KD_TRY(grad_chunk(H, W, dH, dW, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
   }
@@ -761,9 +824,20 @@ kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_i
                              const uint8_t* mask, float tau, int64_t T, int64_t d, int64_t V, int64_t K,
                              kd_dtype dt, const float* grad_kl, float* kl, float* lse, float* z_topk, void* dH,
                              float* dW, int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  return kd_topk_kl_fwd_bwd_ex(H, W, topk_idx, topk_logits, mask, tau, nullptr, T, d, V, K, dt, grad_kl, kl, lse,
+                               z_topk, dH, dW, chunk_rows, workspace, workspace_bytes, stream);
+}
+
+kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                                const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d,
+                                int64_t V, int64_t K, kd_dtype dt, const float* grad_kl, float* kl, float* lse,
+                                float* z_topk, void* dH, float* dW, int64_t chunk_rows, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
   KD_TRY(check_k(T, K, V));
+  TopkOpts op;
+  KD_TRY(resolve_opts(opts, tau, K, op));
   KD_TRY(need(dW, "dW"));
   KD_TRY(need_align(dW, 16, "dW"));
   if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
@@ -794,17 +868,16 @@ kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_i
   KD_TRY(check_workspace(workspace, workspace_bytes, p.fused_total));
 
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
-  kd::TopkRowData rd{at<int2>(workspace, p.o_pair), at<uint16_t>(workspace, p.o_perm), at<float>(workspace, p.o_ent)};
+  const kd::TopkRowData rd = row_data(workspace, p);
   float* part = at<float>(workspace, p.o_part_c);
   float* z = at<float>(workspace, p.o_z);
   const ChunkPlan& ch = p.ch_f;
   char* dz = at<char>(workspace, ch.o_dz);
   char* hT = at<char>(workspace, ch.o_hT);
   float* dhp = at<float>(workspace, ch.o_dhp);
-  const float c2 = (float)(1.4426950408889634 / (double)tau);
 
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
-  KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, tau, rd, z_topk, st));
+  KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, op.KE, op.prep, rd, z_topk, st));
   KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * elem, dH, st));
   const int64_t nchunks = cdiv(T, ch.C);
   for (int64_t k = 0; k < nchunks; ++k) {
@@ -826,15 +899,15 @@ kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_i
     a.T = T;
     a.d = d;
     a.V = V;
-    a.K = K;
+    a.K = op.KE;
+    a.Kz = K;
     a.nrb = ch.nrb_c;
     a.S = p.S_c;
     a.ntiles = p.ntiles;
     a.group = kRasterGroup;
-    a.c2 = c2;
     KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
     KD_LAUNCH("topk_combine", st,
-              kd::launch_topk_combine(part, p.S_c, ch.C, c, mask, rd.ent, T, tau, kl, lse, c0, c0 + ch.C, k == 0, st));
+              kd::launch_topk_combine(part, p.S_c, ch.C, c, mask, rd, T, kl, lse, c0, c0 + ch.C, k == 0, st));
     // dZ from the kept logits: no second projection
     kd::TopkDzFromZArgs za{};
     za.z = z;
@@ -844,12 +917,10 @@ kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_i
     za.c0 = c0;
     za.C = ch.C;
     za.V = V;
-    za.K = K;
+    za.K = op.KE;
     za.rd = rd;
     za.lse = lse;
     za.g = grad_kl;
-    za.c2 = c2;
-    za.inv_tau = 1.0f / tau;
     KD_LAUNCH("topk_dz_from_z", st, kd::launch_topk_dz_from_z(elem, za, st));
     KD_TRY(grad_chunk(H, W, dH, dW, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
   }

@@ -15,11 +15,22 @@ constexpr int kTileM = 256;      // token rows per tile
 inline bool fits32(int64_t bytes) { return bytes < (int64_t(1) << 32) - 65536; }
 
 // Per-row teacher data of the top-K loss, written by the prep kernel for
-// every valid row t (row-major [T][K], sorted by vocabulary index).
+// every valid row t (row-major [T][KE], sorted by vocabulary index; KE is K,
+// or K + 1 when the label of a cross-entropy term is one more entry).
 struct TopkRowData {
-  int2* pair;       // (cached index, teacher probability bits), ascending index
-  uint16_t* perm;   // original position k of each sorted entry
-  float* ent;       // [T] sum_k p_k log p_k
+  int2* pair;       // (vocabulary index, weight bits), ascending index
+  uint16_t* perm;   // original position k of each sorted entry (K: the label)
+  float* ent;       // [T] sum_k w_k log p_k (the teacher-entropy term)
+  float4* rowc;     // [T] (log2(e) / tau_t, 1 / tau_t, mass, log2(mass)) of row t
+};
+
+// Optional parts of the top-K loss, as the prep kernel applies them.
+struct TopkPrepOpts {
+  const float* tau_rows;     // nullable [T]: per-row temperature
+  const float* teacher_lse;  // nullable [T]: partial mass, p = exp(A / tau - teacher_lse)
+  const int32_t* labels;     // nullable [T]: labels of the cross-entropy term
+  float beta;                // weight of the cross-entropy term (labels set)
+  float c2, inv_tau;         // log2(e) / tau and 1 / tau of the scalar temperature
 };
 
 struct Compact {
@@ -30,12 +41,12 @@ struct Compact {
 // ---------------------------------------------------------------- small kernels
 hipError_t launch_compact(const uint8_t* mask, int64_t T, Compact c, hipStream_t st);
 hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8_t* mask, int64_t T, int64_t K,
-                            float tau, TopkRowData rd, float* z_topk, hipStream_t st);
+                            int64_t KE, const TopkPrepOpts& o, TopkRowData rd, float* z_topk, hipStream_t st);
 // Merges the split partials of compacted rows [jb, je) (partial row p holds
 // compacted row jb + p) into kl and lse; with zero_masked, also zeroes kl and
 // lse of every masked row.
 hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
-                               const float* ent, int64_t T, float tau, float* kl, float* lse, int64_t jb, int64_t je,
+                               TopkRowData rd, int64_t T, float* kl, float* lse, int64_t jb, int64_t je,
                                bool zero_masked, hipStream_t st);
 hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
                                int64_t T, float* kl, float* lse_s, float* lse_t, int64_t jb, int64_t je,
@@ -62,10 +73,11 @@ struct TopkFwdArgs {
   int64_t c0, C;  // compacted rows [c0, c0 + C) (all rows: 0, T)
   float* zout;    // nullable: the logits of those rows, fp32 [C][ldz]
   int64_t ldz;
-  int64_t T, d, V, K;
+  int64_t T, d, V;
+  int64_t K;      // entries per row of the pair arrays
+  int64_t Kz;     // width of z_topk (the cached entries; a label entry has perm == Kz)
   int nrb, S, ntiles;
   int group;  // row blocks per raster group (grouped_coords)
-  float c2;  // log2(e) / tau
 };
 hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st);
 
@@ -79,26 +91,24 @@ struct TopkDzArgs {
   char* dz;        // [C][ldz] chunk of dZ
   int64_t ldz;     // padded vocabulary (multiple of the tile width)
   int64_t c0, C;   // first compacted row of the chunk, chunk capacity
-  int64_t T, d, V, K;
+  int64_t T, d, V, K;  // K: entries per row of the pair arrays
   int nrb, S, ntiles;
   int group;  // row blocks per raster group (grouped_coords)
-  float c2, inv_tau;
 };
 hipError_t launch_topk_dz(int elem, const TopkDzArgs& a, hipStream_t st);
 
 // dZ of a chunk from its stored fp32 logits (no recompute):
-// dz[i][v] = (g/tau) (2^(z c2 - L2) - sum of p over hits) for the chunk's
-// valid rows i and v < V; zero for the chunk's other rows.
+// dz[i][v] = (g/tau) (mass 2^(z c2 - L2) - sum of w over hits) for the
+// chunk's valid rows i and v < V; zero for the chunk's other rows.
 struct TopkDzFromZArgs {
   const float* z;    // [C][ldz]
   char* dz;          // [C][ldz], element type
   int64_t ldz;
   Compact c;
-  int64_t c0, C, V, K;
+  int64_t c0, C, V, K;  // K: entries per row of the pair arrays
   TopkRowData rd;
   const float* lse;
   const float* g;
-  float c2, inv_tau;
 };
 hipError_t launch_topk_dz_from_z(int elem, const TopkDzFromZArgs& a, hipStream_t st);
 

@@ -93,43 +93,75 @@ hipError_t launch_compact(const uint8_t* mask, int64_t T, Compact c, hipStream_t
 // ------------------------------------------------------------------ teacher prep
 // One workgroup per row.  Dynamic LDS: KP sort keys (64-bit: biased index in
 // the high word, position k in the low word) and K probabilities.
+//
+// Row t's temperature is tau_rows[t] when given (per-token temperature, the
+// adaptive-distillation abstract on the WASD page), else the scalar one.
+// The teacher probabilities are softmax(A_t / tau) over the K cached entries,
+// or, with a teacher log-normaliser, the cached probabilities
+// exp(A_t / tau - teacher_lse[t]) of the full teacher softmax, which keep
+// their partial mass m = sum_k p_k ("Efficient Knowledge Distillation for
+// LLMs ...", §3 "Offline distillation").  A cross-entropy term with weight
+// beta on label y is one more entry (y, beta), the others weigh (1 - beta) p,
+// so the loss keeps the support form sum w log p - sum w s + mass L with
+// mass = (1 - beta) m + beta.
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_prep_kernel(const float* logits, const int32_t* idx, const uint8_t* mask,
-                                                       int K, int KP, float inv_tau, TopkRowData rd, float* z_topk) {
+                                                       int K, int KE, int KP, TopkPrepOpts o, TopkRowData rd,
+                                                       float* z_topk) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   __shared__ float red[NT / 64 > 0 ? NT / 64 : 1];
   uint64_t* key = reinterpret_cast<uint64_t*>(sm);
   float* p = reinterpret_cast<float*>(key + KP);
   const long t = blockIdx.x;
-  const long base = t * K;
+  const long base = t * K, pbase = t * KE;
   if (z_topk)
     for (int k = threadIdx.x; k < K; k += NT) z_topk[base + k] = 0.f;
   if (mask != nullptr && mask[t] == 0) return;
 
-  // p = softmax(A_t / tau) over the K cached entries, and sum p log p
-  float mx = -INFINITY;
-  for (int k = threadIdx.x; k < K; k += NT) {
-    const float a = logits[base + k] * inv_tau;
-    p[k] = a;
-    mx = fmaxf(mx, a);
+  float inv_tau = o.inv_tau, c2 = o.c2;
+  if (o.tau_rows) {
+    const float tt = o.tau_rows[t];
+    inv_tau = 1.0f / tt;
+    c2 = (float)(1.4426950408889634 / (double)tt);
   }
-  mx = block_max<NT>(mx, red);
-  float s = 0.f;
-  for (int k = threadIdx.x; k < K; k += NT) s += expf(p[k] - mx);
-  s = block_sum<NT>(s, red);
-  const float lz = mx + logf(s);
-  float ent = 0.f;
+  // log p = A_t / tau - log-normaliser (of the K entries, or the given one)
+  for (int k = threadIdx.x; k < K; k += NT) p[k] = logits[base + k] * inv_tau;
+  float lz;
+  if (o.teacher_lse) {
+    lz = o.teacher_lse[t];
+    __syncthreads();
+  } else {
+    float mx = -INFINITY;
+    for (int k = threadIdx.x; k < K; k += NT) mx = fmaxf(mx, p[k]);
+    mx = block_max<NT>(mx, red);
+    float s = 0.f;
+    for (int k = threadIdx.x; k < K; k += NT) s += expf(p[k] - mx);
+    s = block_sum<NT>(s, red);
+    lz = mx + logf(s);
+  }
+  float ent = 0.f, m = 0.f;
   for (int k = threadIdx.x; k < K; k += NT) {
     const float lp = p[k] - lz;
     const float pk = expf(lp);
     p[k] = pk;
     ent = fmaf(pk, lp, ent);
+    m += pk;
   }
   ent = block_sum<NT>(ent, red);
+  float mass = 1.f;  // renormalised: exactly one
+  if (o.teacher_lse) mass = block_sum<NT>(m, red);
+  const bool ce = KE > K;
+  const float wk = ce ? 1.f - o.beta : 1.f;
+  if (ce) {
+    ent *= wk;
+    mass = fmaf(wk, mass, o.beta);
+  }
 
   // sort (index, position) pairs by index; ties keep position order
-  for (int j = threadIdx.x; j < KP; j += NT)
-    key[j] = j < K ? ((uint64_t)((uint32_t)idx[base + j] ^ 0x80000000u) << 32) | (uint32_t)j : ~0ull;
+  for (int j = threadIdx.x; j < KP; j += NT) {
+    const int32_t v = j < K ? idx[base + j] : (j < KE ? o.labels[t] : 0);
+    key[j] = j < KE ? ((uint64_t)((uint32_t)v ^ 0x80000000u) << 32) | (uint32_t)j : ~0ull;
+  }
   for (int size = 2; size <= KP; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       __syncthreads();
@@ -146,41 +178,45 @@ __global__ __launch_bounds__(NT) void topk_prep_kernel(const float* logits, cons
     }
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < K; j += NT) {
+  for (int j = threadIdx.x; j < KE; j += NT) {
     const uint64_t kv = key[j];
     const uint32_t k = (uint32_t)(kv & 0xffffffffu);
-    rd.pair[base + j] = make_int2((int32_t)((uint32_t)(kv >> 32) ^ 0x80000000u), __float_as_int(p[k]));
-    rd.perm[base + j] = (uint16_t)k;
+    const float w = k < (uint32_t)K ? (ce ? wk * p[k] : p[k]) : o.beta;
+    rd.pair[pbase + j] = make_int2((int32_t)((uint32_t)(kv >> 32) ^ 0x80000000u), __float_as_int(w));
+    rd.perm[pbase + j] = (uint16_t)k;
   }
-  if (threadIdx.x == 0) rd.ent[t] = ent;
+  if (threadIdx.x == 0) {
+    rd.ent[t] = ent;
+    rd.rowc[t] = make_float4(c2, inv_tau, mass, log2f(mass));
+  }
 }
 
 hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8_t* mask, int64_t T, int64_t K,
-                            float tau, TopkRowData rd, float* z_topk, hipStream_t st) {
+                            int64_t KE, const TopkPrepOpts& o, TopkRowData rd, float* z_topk, hipStream_t st) {
   int KP = 1;
-  while (KP < K) KP <<= 1;
+  while (KP < KE) KP <<= 1;
   const size_t shm = (size_t)KP * 8 + (size_t)K * 4;
-  const float inv_tau = 1.0f / tau;
   const dim3 grid((unsigned)T);
   if (shm > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_prep_kernel<256>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
   }
-  if (K <= 64)
-    hipLaunchKernelGGL(topk_prep_kernel<64>, grid, dim3(64), shm, st, logits, idx, mask, (int)K, KP, inv_tau, rd,
+  if (KE <= 64)
+    hipLaunchKernelGGL(topk_prep_kernel<64>, grid, dim3(64), shm, st, logits, idx, mask, (int)K, (int)KE, KP, o, rd,
                        z_topk);
   else
-    hipLaunchKernelGGL(topk_prep_kernel<256>, grid, dim3(256), shm, st, logits, idx, mask, (int)K, KP, inv_tau, rd,
-                       z_topk);
+    hipLaunchKernelGGL(topk_prep_kernel<256>, grid, dim3(256), shm, st, logits, idx, mask, (int)K, (int)KE, KP, o,
+                       rd, z_topk);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ combines
 // Thread j: (a) zero kl/lse of row j if it is masked, (b) if j is a valid
-// compacted row, merge its S partials (m2, l, x) in split order.
+// compacted row, merge its S partials (m2, l, x) in split order:
+// kl = sum w log p - x / tau + mass L.
 __global__ void topk_combine_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask,
-                                    const float* ent, long T, float inv_tau, float* kl, float* lse, long jb, long je,
+                                    TopkRowData rd, long T, float* kl, float* lse, long jb, long je,
                                     int zero_masked) {
   const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= T) return;
@@ -199,17 +235,18 @@ __global__ void topk_combine_kernel(const float* part, int S, long stride, Compa
     x += q.z;
   }
   const long t = c.rows[j];
+  const float4 rc = rd.rowc[t];
   const float L = (M + log2f(l)) * kLn2;
   lse[t] = L;
-  kl[t] = ent[t] - x * inv_tau + L;
+  kl[t] = rd.ent[t] - x * rc.y + rc.z * L;
 }
 
 hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
-                               const float* ent, int64_t T, float tau, float* kl, float* lse, int64_t jb, int64_t je,
+                               TopkRowData rd, int64_t T, float* kl, float* lse, int64_t jb, int64_t je,
                                bool zero_masked, hipStream_t st) {
   const dim3 grid((unsigned)((T + 255) / 256));
-  hipLaunchKernelGGL(topk_combine_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, ent, (long)T,
-                     1.0f / tau, kl, lse, (long)jb, (long)je, zero_masked ? 1 : 0);
+  hipLaunchKernelGGL(topk_combine_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, rd, (long)T,
+                     kl, lse, (long)jb, (long)je, zero_masked ? 1 : 0);
   return hipGetLastError();
 }
 

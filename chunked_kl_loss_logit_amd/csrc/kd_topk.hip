@@ -16,8 +16,11 @@
 //   forward  : running base-2 max / sum per row, plus the index-match gather.
 //              The row's cached indices are sorted, so one cursor walks them
 //              in step with the column blocks and picks the hits out of LDS.
-//   backward : dZ = (g/tau) (2^(y - L2) - sum of p over hits), written in the
-//              input dtype to the chunk's dZ buffer.
+//   backward : dZ = (g/tau) (mass 2^(y - L2) - sum of w over hits), written in
+//              the input dtype to the chunk's dZ buffer.
+// Each row carries its own constants (log2(e)/tau, 1/tau, mass) from the prep
+// kernel: per-token temperature, a partial-mass teacher and a cross-entropy
+// entry change those and the weights w, not the tiles.
 #include <climits>
 
 #include "kd_gemm.h"
@@ -95,8 +98,9 @@ struct FwdRow {
   Cursor cur;
   const uint16_t* perm;  // uniform bases, indexed by pair position
   float* ztk;            // z_topk (nullable), indexed by row_k + original position
-  long row_k;            // t * K
-  float m2, l, x;
+  long row_k;            // t * Kz
+  int kz;                // cached entries per row (a label entry has perm == kz)
+  float m2, l, x, c2;
   bool rv;
 
   // 32 columns [cb, cb + 32) of this row, staged in st; [clo, chi) are the
@@ -131,14 +135,17 @@ struct FwdRow {
     cur.take_below(cb + hi, [&](int v, float pv, int c) {
       const float z = st_row(st, r)[st_pos(r, v - cb)];
       x = fmaf(pv, z, x);
-      if (ztk) ztk[row_k + perm[c]] = z;
+      if (ztk) {
+        const int k = perm[c];
+        if (k < kz) ztk[row_k + k] = z;
+      }
     });
   }
 };
 
 struct DzRow {
   Cursor cur;
-  float L2, gs;
+  float L2, gs, c2;  // L2: base-2 log Z less log2(mass), so 2^(y - L2) = mass q
   bool rv;
 
   // replace the staged logits of this row by dZ (zero outside the valid rows
@@ -183,7 +190,7 @@ __device__ inline void fwd_round(const Slots& sl, const f32x16_t (&acc)[4][4], i
   const int cb = n0 + H * 128 + NBI * 32;
   stage_half<NBI, 4>(sl.ep, H, acc);
   ring_barrier();
-  R.consume(sl.ep, cb, lo, hi, a.c2);
+  R.consume(sl.ep, cb, lo, hi, R.c2);
   // both only read the staged block: the logits go out as they are
   if (a.zout) store_block<F32>(sl.ep, reinterpret_cast<char*>(a.zout), a.ldz, row0, cb, M, a.ldz, lo);
   ring_barrier();
@@ -195,7 +202,7 @@ __device__ inline void dz_round(const Slots& sl, const f32x16_t (&acc)[4][4], in
   const int cb = n0 + H * 128 + NBI * 32;
   stage_half<NBI, 4>(sl.ep, H, acc);
   ring_barrier();
-  R.consume(sl.ep, cb, lo, hi, a.c2);
+  R.consume(sl.ep, cb, lo, hi, R.c2);
   ring_barrier();
   store_block<E>(sl.ep, a.dz, a.ldz, row0, cb, LONG_MAX, a.ldz, lo);
   ring_barrier();
@@ -241,10 +248,12 @@ __global__ __launch_bounds__(kThreads, 1) void topk_fwd_kernel(TopkFwdArgs a) {
   R.cur.refill();
   R.perm = a.rd.perm;
   R.ztk = a.z_topk;
-  R.row_k = t * a.K;
+  R.row_k = t * a.Kz;
+  R.kz = (int)a.Kz;
   R.m2 = -INFINITY;
   R.l = 0.f;
   R.x = 0.f;
+  R.c2 = R.rv ? a.rd.rowc[t].x : 0.f;
 
   mainloop.run(
       sl, te - tb, [&](int i) { return TileAt{0, tile_n0(tb + i, V)}; },
@@ -299,8 +308,10 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_kernel(TopkDzArgs a) {
   R.cur.end = (int)(t * a.K + (R.rv ? a.K : 0));
   R.cur.c = lower_bound(a.rd.pair, (int)(t * a.K), R.cur.end, (long)tb * kBN);
   R.cur.refill();
-  R.L2 = R.rv ? a.lse[t] * kLog2e : 0.f;
-  R.gs = R.rv ? a.g[t] * a.inv_tau : 0.f;
+  const float4 rc = R.rv ? a.rd.rowc[t] : make_float4(0.f, 0.f, 1.f, 0.f);
+  R.L2 = R.rv ? a.lse[t] * kLog2e - rc.w : 0.f;
+  R.gs = R.rv ? a.g[t] * rc.y : 0.f;
+  R.c2 = rc.x;
 
   mainloop.run(
       sl, te - tb, [&](int i) { return TileAt{0, tile_n0(tb + i, V)}; },
@@ -319,10 +330,11 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_kernel(TopkDzArgs a) {
 }
 
 // ---------------------------------------------------------------- dZ from stored logits
-// One thread: EPT consecutive columns (16 bytes of dZ) of one row.  The row's
-// cached entries are sorted, so the hits of [v0, v0 + EPT) are found with a
-// binary search over the K entries (shared by the block, so L1-resident) and
-// subtracted before the one rounding to the element type.
+// One thread: EPT consecutive columns (16 bytes of dZ) of one row, the same
+// formula as the recomputing tile's epilogue.  The row's entries are sorted,
+// so the hits of [v0, v0 + EPT) are found with a binary search over them
+// (shared by the block, so L1-resident) and subtracted before the one
+// rounding to the element type.
 template <class E>
 __global__ __launch_bounds__(256) void topk_dz_from_z_kernel(TopkDzFromZArgs a) {
   constexpr int EPT = E::kEpc;
@@ -333,15 +345,16 @@ __global__ __launch_bounds__(256) void topk_dz_from_z_kernel(TopkDzFromZArgs a) 
   float o[EPT];
   if (i < M) {
     const long t = a.c.rows[a.c0 + i];
-    const float L2 = a.lse[t] * kLog2e, gs = a.g[t] * a.inv_tau;
+    const float4 rc = a.rd.rowc[t];
+    const float L2 = a.lse[t] * kLog2e - rc.w, gs = a.g[t] * rc.y, c2 = rc.x;
     const float* zr = a.z + i * a.ldz + v0;
 #pragma unroll
     for (int e = 0; e < EPT; e += 4) {
       const float4 z4 = *reinterpret_cast<const float4*>(zr + e);
-      o[e + 0] = gs * fast_exp2(fmaf(z4.x, a.c2, -L2));
-      o[e + 1] = gs * fast_exp2(fmaf(z4.y, a.c2, -L2));
-      o[e + 2] = gs * fast_exp2(fmaf(z4.z, a.c2, -L2));
-      o[e + 3] = gs * fast_exp2(fmaf(z4.w, a.c2, -L2));
+      o[e + 0] = gs * fast_exp2(fmaf(z4.x, c2, -L2));
+      o[e + 1] = gs * fast_exp2(fmaf(z4.y, c2, -L2));
+      o[e + 2] = gs * fast_exp2(fmaf(z4.z, c2, -L2));
+      o[e + 3] = gs * fast_exp2(fmaf(z4.w, c2, -L2));
     }
     const int b = (int)(t * a.K), e = (int)(t * a.K + a.K);
     for (int c = lower_bound(a.rd.pair, b, e, v0); c < e; ++c) {

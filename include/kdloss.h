@@ -41,7 +41,7 @@
  *    float32.  KD_F32: they are float32 and the contraction runs on fp32
  *    matrix cores.  kl, lse, grad_kl, dW are float32 in both cases.
  *  - d, dt and V must be multiples of 8 (bf16) or 4 (fp32); 1 <= K <= V,
- *    K <= KD_MAX_K and T * K < 2^31.  Otherwise the call returns
+ *    K <= KD_MAX_K and T * (K + 1) < 2^31.  Otherwise the call returns
  *    KD_ERR_UNSUPPORTED.
  *  - Pointers to H, W, Ht, Wt, dH, dW must be 16-byte aligned, all other
  *    arrays 4-byte aligned, the workspace 256-byte aligned
@@ -151,6 +151,62 @@ kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_i
                              const float* grad_kl, float* kl, float* lse, float* z_topk,
                              void* dH, float* dW, int64_t chunk_rows,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- top-K options
+ * Optional parts of the top-K loss.  The _ex calls take the same arguments
+ * as the calls above plus `opts`; opts = NULL, or every field zero, is the
+ * plain call.  The backward call must get the same options as the forward
+ * call that produced lse.  With every option, per valid row t:
+ *   tau_t = tau_rows[t] (else tau);  s = z / tau_t;  L_t = logsumexp(s)
+ *   p_k   = exp(A_tk / tau_t - teacher_lse[t])  (else softmax(A_t / tau_t));
+ *   m_t   = sum_k p_k (1 when renormalised)
+ *   KD_t  = sum_k p_k log p_k - sum_k p_k s[I_tk] + m_t L_t
+ *   CE_t  = L_t - s[labels[t]]
+ *   kl_t  = (1 - ce_weight) KD_t + ce_weight CE_t
+ *   dZ_t  = (g_t / tau_t) ((1 - ce_weight)(m_t softmax(s) - scatter_add(I_t, p))
+ *                          + ce_weight (softmax(s) - onehot(labels[t])))
+ * Sources: per-token temperature, the adaptive-distillation abstract on the
+ * WASD page (thelatestinai.com/papers/2610.07706); cached probabilities with
+ * their unnormalised partial mass and the support identity above, §3
+ * "Offline distillation"; the language-modelling loss mixed with the
+ * distillation loss, the teacher-strength abstract
+ * (thelatestinai.com/papers/2605.11513), with CE the one-entry case of the
+ * same loss at the same temperature (tau = 1 gives the plain LM loss).
+ * Only the per-row constants and the weights of the support entries change,
+ * so every option keeps the tiles, workspace size and speed of the plain
+ * call.  Argument errors: ce_weight outside [0, 1] or not finite, or
+ * ce_weight > 0 without labels: KD_ERR_INVALID_ARG; ce_weight > 0 with
+ * K = KD_MAX_K: KD_ERR_UNSUPPORTED (the label is entry K + 1); misaligned
+ * arrays: KD_ERR_ALIGNMENT.  Values are not checked: tau_rows must be
+ * finite and > 0 and labels in [0, V) on valid rows (masked rows are never
+ * read). */
+typedef struct kd_topk_opts {
+  const float* tau_rows;     /* [T] per-token temperature, or NULL */
+  const float* teacher_lse;  /* [T] teacher log-normaliser at tau_t (partial mass), or NULL */
+  const int32_t* labels;     /* [T] next-token labels of the CE term, or NULL */
+  float ce_weight;           /* weight of the CE term in [0, 1]; 0 = distillation only */
+} kd_topk_opts;
+
+kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_idx,
+                            const float* topk_logits, const uint8_t* mask, float tau,
+                            const kd_topk_opts* opts,
+                            int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                            float* kl, float* lse, float* z_topk,
+                            void* workspace, size_t workspace_bytes, void* stream);
+kd_status kd_topk_kl_bwd_ex(const void* H, const void* W, const int32_t* topk_idx,
+                            const float* topk_logits, const uint8_t* mask, float tau,
+                            const kd_topk_opts* opts,
+                            int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                            const float* lse, const float* grad_kl,
+                            void* dH, float* dW, int64_t chunk_rows,
+                            void* workspace, size_t workspace_bytes, void* stream);
+kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* topk_idx,
+                                const float* topk_logits, const uint8_t* mask, float tau,
+                                const kd_topk_opts* opts,
+                                int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                                const float* grad_kl, float* kl, float* lse, float* z_topk,
+                                void* dH, float* dW, int64_t chunk_rows,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- full vocabulary */
 

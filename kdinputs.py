@@ -17,7 +17,8 @@ Conventions:
   * Values are drawn in float32 from NumPy PCG64 streams and rounded to the
     storage dtype (bf16 rounding is round-to-nearest-even, done by torch).
   * Every tensor role has its own seed: H=1, W=2, A (teacher logits)=3,
-    I (indices)=4, mask=5, g (upstream gradient)=6, Ht=7, Wt=8, each plus
+    I (indices)=4, mask=5, g (upstream gradient)=6, Ht=7, Wt=8, per-token
+    temperature=9, cached probabilities=10, labels=11, each plus
     ``100 * preset_number``.
   * Large tensors are filled block by block; block ``b`` of role ``r`` always
     uses ``SeedSequence([seed_r, b])``, so results do not depend on the thread
@@ -33,6 +34,7 @@ import numpy as np
 import torch
 
 ROLE_H, ROLE_W, ROLE_A, ROLE_I, ROLE_MASK, ROLE_G, ROLE_HT, ROLE_WT = 1, 2, 3, 4, 5, 6, 7, 8
+ROLE_TAU, ROLE_MASS, ROLE_Y = 9, 10, 11
 _BLOCK = 1 << 22  # elements per independently seeded block
 
 
@@ -190,6 +192,47 @@ def make_topk(T, d, V, K, dtype, tau=1.0, teacher_var=3.0, mask="none", number=0
     else:
         raise ValueError(g)
     return dict(H=H, W=W, I=I, A=A, mask=M, g=G, tau=float(tau))
+
+
+def add_topk_options(inp, tau_rows=False, partial_mass=False, labels=False, ce_weight=0.0, number=0):
+    """Inputs of the optional parts of the top-K loss, added to a make_topk dict.
+
+    tau_rows: [T] float32 per-token temperatures, uniform in [0.5, 2).
+    partial_mass: the cache holds probabilities of the full teacher softmax.
+      Row t draws a mass m_t uniform in [0.5, 0.99) and K heavy-tailed weights
+      u^4 (u uniform), sorted descending and scaled to sum to m_t; A is
+      replaced by tau_t (log p + c_t) and teacher_lse is c_t ~ N(0, 1), so the
+      cached entries are exactly those probabilities at the row's temperature.
+    labels: [T] int32 next-token labels: the row's first cached index with
+      probability 1/2, else uniform over [0, V); ce_weight is stored with them.
+    """
+    base = 100 * number
+    T, K = inp["I"].shape
+    V = inp["W"].shape[1]
+    out = dict(inp)
+    taus = np.full(T, inp["tau"], dtype=np.float64)
+    if tau_rows:
+        rng = np.random.Generator(np.random.PCG64(ROLE_TAU + base))
+        tr = rng.uniform(0.5, 2.0, T).astype(np.float32)
+        out["tau_rows"] = torch.from_numpy(tr)
+        taus = tr.astype(np.float64)
+    if partial_mass:
+        rng = np.random.Generator(np.random.PCG64(ROLE_MASS + base))
+        m = rng.uniform(0.5, 0.99, T)
+        u = -np.sort(-(rng.random((T, K)) ** 4), axis=1)
+        u = np.maximum(u, 1e-30)
+        p = u * (m / u.sum(axis=1))[:, None]
+        c = rng.standard_normal(T)
+        out["A"] = torch.from_numpy((taus[:, None] * (np.log(p) + c[:, None])).astype(np.float32))
+        out["teacher_lse"] = torch.from_numpy(c.astype(np.float32))
+    if labels:
+        rng = np.random.Generator(np.random.PCG64(ROLE_Y + base))
+        y = rng.integers(0, V, T)
+        top = rng.random(T) < 0.5
+        y[top] = inp["I"].numpy()[top, 0]
+        out["labels"] = torch.from_numpy(y.astype(np.int32))
+        out["ce_weight"] = float(ce_weight)
+    return out
 
 
 def make_full(T, d, dt, V, dtype, tau=1.0, mask="none", number=0, g="mean", n_masked=None):

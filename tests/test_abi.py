@@ -29,7 +29,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), f"{n} declared in kdloss.h but not exported"
     assert sorted(kdl.EXPORTS) == names
@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
 def test_status_strings_and_version(L):
     for code, name in kdl._binding.STATUS.items():
         assert L.kd_status_string(code).decode() == name
-    assert L.kd_version() == 10200
+    assert L.kd_version() == 10300
 
 
 # ---------------------------------------------------------------- workspace sizing
@@ -247,3 +247,46 @@ def test_full_fwd_bwd_workspace_adds_two_fp32_logit_chunks(L):
         two_call = ws_full(T, chunk=chunk)[1]
         extra = 2 * C * 128256 * 4
         assert two_call + extra <= out.value <= two_call + extra + 256 * C * 32 + (1 << 20)
+
+
+# ---------------------------------------------------------------- top-K options
+def fwd_ex(opts, T=8, d=64, V=256, K=4, wsb=0):
+    vp = ctypes.c_void_p
+    L = kdl.lib()
+    ref = None if opts is None else ctypes.byref(opts)
+    return L.kd_topk_kl_fwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), ref, T, d, V, K,
+                               kdl.KD_BF16, vp(FAKE), vp(FAKE), None, vp(FAKE), wsb, None)
+
+
+def opts(tau_rows=0, teacher_lse=0, labels=0, ce_weight=0.0):
+    return kdl._binding.KdTopkOpts(tau_rows or None, teacher_lse or None, labels or None, ce_weight)
+
+
+@pytest.mark.parametrize("o,code", [
+    (opts(ce_weight=0.5), 1),                                     # a CE weight needs labels
+    (opts(labels=FAKE, ce_weight=-0.1), 1), (opts(labels=FAKE, ce_weight=1.5), 1),
+    (opts(labels=FAKE, ce_weight=math.nan), 1), (opts(labels=FAKE, ce_weight=math.inf), 1),
+    (opts(tau_rows=FAKE + 2), 3), (opts(teacher_lse=FAKE + 1), 3), (opts(labels=FAKE + 2, ce_weight=0.5), 3),
+    (opts(tau_rows=FAKE, teacher_lse=FAKE, labels=FAKE, ce_weight=0.5), 4),  # valid: reaches the workspace
+    (None, 4), (opts(), 4), (opts(labels=FAKE), 4),                # labels without a weight are ignored
+])
+def test_topk_options_checks(L, o, code):
+    assert fwd_ex(o) == code
+    assert last_error() != ""
+
+
+def test_topk_options_label_needs_room_for_one_more_entry(L):
+    o = opts(labels=FAKE, ce_weight=0.5)
+    assert fwd_ex(o, V=16384, K=kdl.KD_MAX_K) == 2
+    assert fwd_ex(o, V=16384, K=kdl.KD_MAX_K - 1) == 4
+    assert fwd_ex(None, V=16384, K=kdl.KD_MAX_K) == 4
+
+
+def test_topk_ex_calls_check_their_options_too(L):
+    vp = ctypes.c_void_p
+    bad = ctypes.byref(opts(ce_weight=0.5))
+    assert L.kd_topk_kl_bwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), bad, 8, 64, 256, 4,
+                               kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 0, vp(FAKE), 0, None) == 1
+    assert L.kd_topk_kl_fwd_bwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), bad, 8, 64,
+                                   256, 4, kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), 0,
+                                   vp(FAKE), 0, None) == 1
