@@ -22,6 +22,8 @@ compute.  Sources, cited by page title and section:
          distillation recomputes the teacher logits from the teacher's final
          hidden states through a frozen copy of the teacher's output head.
 
+[KLD]    KL-direction abstract (thelatestinai.com/papers/2606.20005): forward
+         and reverse token-level KL, and their mixture ("KL mixing").
 [AKD]    Adaptive-distillation abstract (on the WASD page,
          thelatestinai.com/papers/2610.07706): the distillation temperature is
          adjusted per token.
@@ -38,6 +40,8 @@ design notes of this repository):
   * The LM cross-entropy term is the K = 1 case of the same loss (one cached
     entry, the label, with p = 1) at the same temperature; the mixed loss is
     (1 - beta) KD + beta CE.
+  * KL mixing (full vocabulary): (1 - r) KL(p || q) + r KL(q || p), both at
+    the row's temperature.
   * Both teacher and student logits are divided by tau; there is no tau^2.
   * The output is per token; the caller reduces.  ``g`` is dLoss/dKL_t.
   * mask[t] == 1 marks a valid row.  Masked rows give KL = 0, lse = 0,
@@ -57,6 +61,7 @@ __all__ = [
     "topk_kl_forward", "topk_kl_backward", "topk_kl_rows",
     "topk_loss_forward", "topk_loss_backward", "topk_loss_rows",
     "full_kl_forward", "full_kl_backward", "full_kl_rows",
+    "full_loss_forward", "full_loss_backward", "full_loss_rows",
 ]
 
 
@@ -387,3 +392,85 @@ def _rows_dh_full(H, Ws, Ht, Wt, mask, tau, g, row_block=64):
         D = (np.exp(s - Ls[:, None]) - np.exp(u - Lt[:, None])) * (g[rb] / tau)[:, None]
         dH[rb] = D @ Ws.T
     return dH, None
+
+
+def _full_block(H, Ws, Ht, Wt, rb, taus):
+    """Both heads' scaled logits of a block of valid rows and their softmaxes."""
+    tau = taus[rb][:, None]
+    s = (H[rb] @ Ws) / tau
+    u = (Ht[rb] @ Wt) / tau
+    Ls, Lt = logsumexp_rows(s), logsumexp_rows(u)
+    q = np.exp(s - Ls[:, None])
+    p = np.exp(u - Lt[:, None])
+    return s, u, Ls, Lt, q, p
+
+
+def full_loss_forward(H, Ws, Ht, Wt, mask, tau, tau_rows=None, rev_weight=0.0, row_block=64):
+    """Full-vocabulary loss with KL mixing ([KLD]) and per-token temperature
+    ([AKD]), teacher logits through the frozen teacher head ([KDFlow]).
+
+    Per valid row t at temperature tau_t, with s = H_t Ws / tau_t, u = Ht_t Wt / tau_t,
+    q = softmax(s), p = softmax(u):
+        KLf = sum_v p_v (u_v - s_v) - logsumexp(u) + logsumexp(s)     KL(p || q)
+        KLr = sum_v q_v (s_v - u_v) - logsumexp(s) + logsumexp(u)     KL(q || p)
+        loss = (1 - r) KLf + r KLr.
+    Returns (loss [T], lse_s [T], lse_t [T], kl_rev [T])."""
+    H, Ws, Ht, Wt = as_f64(H), as_f64(Ws), as_f64(Ht), as_f64(Wt)
+    T = H.shape[0]
+    taus = _row_values(tau_rows, T, tau)
+    r = float(rev_weight)
+    valid = _valid_rows(mask, T)
+    loss, ls, lt, krev = np.zeros(T), np.zeros(T), np.zeros(T), np.zeros(T)
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        s, u, Ls, Lt, q, p = _full_block(H, Ws, Ht, Wt, rb, taus)
+        klf = (p * (u - s)).sum(axis=1) - Lt + Ls
+        klr = (q * (s - u)).sum(axis=1) - Ls + Lt
+        loss[rb] = (1.0 - r) * klf + r * klr
+        ls[rb], lt[rb], krev[rb] = Ls, Lt, klr
+    return loss, ls, lt, krev
+
+
+def _full_loss_dz(s, u, Ls, Lt, q, p, g_rows, tau_rows, r):
+    """dLoss/dz_s: (g/tau) [(1 - r)(q - p) + r q ((s - Ls) - (u - Lt) - KLr)]."""
+    D = (1.0 - r) * (q - p)
+    if r != 0.0:
+        lr = (s - Ls[:, None]) - (u - Lt[:, None])
+        klr = (q * lr).sum(axis=1)
+        D = D + r * q * (lr - klr[:, None])
+    return D * (g_rows / tau_rows)[:, None]
+
+
+def full_loss_backward(H, Ws, Ht, Wt, mask, tau, g, tau_rows=None, rev_weight=0.0, row_block=64, v_panel=16384,
+                       want_dw=True):
+    """Gradients of sum_t g_t loss_t (full_loss_forward) w.r.t. the student's
+    H and Ws only.  Returns (dH [T, d], dWs [d, V] or None)."""
+    H, Ws, Ht, Wt, g = as_f64(H), as_f64(Ws), as_f64(Ht), as_f64(Wt), as_f64(g)
+    T, d = H.shape
+    V = Ws.shape[1]
+    taus = _row_values(tau_rows, T, tau)
+    valid = _valid_rows(mask, T)
+    dH, dW = np.zeros((T, d)), (np.zeros((d, V)) if want_dw else None)
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        s, u, Ls, Lt, q, p = _full_block(H, Ws, Ht, Wt, rb, taus)
+        D = _full_loss_dz(s, u, Ls, Lt, q, p, g[rb], taus[rb], float(rev_weight))
+        dH[rb] = D @ Ws.T
+        if want_dw:
+            for v0 in range(0, V, v_panel):
+                dW[:, v0:v0 + v_panel] += H[rb].T @ D[:, v0:v0 + v_panel]
+    return dH, dW
+
+
+def full_loss_rows(H, Ws, Ht, Wt, mask, tau, g, rows, tau_rows=None, rev_weight=0.0):
+    """loss, lse_s, lse_t, kl_rev and dH of full_loss_* for selected rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    Hr, Htr = as_f64(_take_rows(H, rows)), as_f64(_take_rows(Ht, rows))
+    mr, gr = _take_rows(mask, rows), _take_rows(g, rows)
+    kw = dict(tau_rows=_take_rows(tau_rows, rows), rev_weight=rev_weight)
+    Ws, Wt = as_f64(Ws), as_f64(Wt)
+    out = full_loss_forward(Hr, Ws, Htr, Wt, mr, tau, **kw)
+    dH, _ = full_loss_backward(Hr, Ws, Htr, Wt, mr, tau, gr, want_dw=False, **kw)
+    return out + (dH,)

@@ -27,6 +27,9 @@ PINS = [
     Q.test_per_token_tau_is_row_scaling, Q.test_per_token_tau_gradient_is_row_scaled_plain_gradient,
     Q.test_ce_weight_one_is_torch_cross_entropy, Q.test_ce_mix_is_the_convex_combination,
     Q.test_ce_gradient_matches_torch_autograd, Q.test_all_options_finite_differences,
+    Q.test_full_reverse_kl_is_torch_kl_div_swapped, Q.test_full_kl_mixing_is_the_convex_combination,
+    Q.test_full_per_token_tau_is_row_scaling, Q.test_full_mixed_gradient_matches_torch_autograd,
+    Q.test_full_mixed_finite_differences_and_mask,
 ]
 
 
@@ -175,7 +178,39 @@ def _loss_fwd_ce_sign(*args, labels=None, ce_weight=0.0, **kw):
     return ((1.0 - ce_weight) * kd - ce_weight * ce,) + tuple(mix[1:])
 
 
+_ORIG_FULL_DZ = O._full_loss_dz
+_ORIG_FULL_LOSS = O.full_loss_forward
+
+
+def _full_dz_no_klr(s, u, Ls, Lt, q, p, g_rows, tau_rows, r):
+    D = (1.0 - r) * (q - p)
+    if r != 0.0:
+        D = D + r * q * ((s - Ls[:, None]) - (u - Lt[:, None]))  # the -KLr baseline dropped
+    return D * (g_rows / tau_rows)[:, None]
+
+
+def _full_dz_reverse_sign(s, u, Ls, Lt, q, p, g_rows, tau_rows, r):
+    D = _ORIG_FULL_DZ(s, u, Ls, Lt, q, p, g_rows, tau_rows, 0.0) * (1.0 - r)
+    if r != 0.0:
+        D = D - _ORIG_FULL_DZ(s, u, Ls, Lt, q, p, g_rows, tau_rows, 1.0) * r
+    return D
+
+
+def _full_loss_mix_swapped(*args, rev_weight=0.0, **kw):
+    return _ORIG_FULL_LOSS(*args, rev_weight=1.0 - rev_weight, **kw)
+
+
+def _full_block_scalar_tau(H, Ws, Ht, Wt, rb, taus):
+    return _ORIG_FULL_BLOCK(H, Ws, Ht, Wt, rb, np.full_like(taus, taus.mean()))
+
+
+_ORIG_FULL_BLOCK = O._full_block
+
 MUTATIONS = {
+    "full_dz_reverse_baseline_dropped": ("_full_loss_dz", _full_dz_no_klr),
+    "full_dz_reverse_sign": ("_full_loss_dz", _full_dz_reverse_sign),
+    "full_mix_weights_swapped": ("full_loss_forward", _full_loss_mix_swapped),
+    "full_tau_rows_ignored": ("_full_block", _full_block_scalar_tau),
     "loss_mass_term_unit": ("_loss_block", _loss_block_unit_mass),
     "loss_partial_mass_renormalised": ("_loss_block", _loss_block_renormalised),
     "loss_tau_rows_ignored": ("_row_values", _row_values_ignored),

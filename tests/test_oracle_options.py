@@ -230,3 +230,107 @@ def test_rows_helper_matches_full_functions():
     rv, rl, rz, rdH = O.topk_loss_rows(H, W, I, A, None, 1.0, g, rows, **kw)
     np.testing.assert_allclose(rv, v[rows], rtol=1e-14)
     np.testing.assert_allclose(rdH, dH[rows], rtol=1e-13, atol=1e-16)
+
+
+# ---------------------------------------------------------------- full vocabulary: KL mixing, per-token tau
+def full_case(T=6, d=8, dt=10, V=30, seed=30):
+    rng = np.random.default_rng(seed)
+    H, Ht = rng.standard_normal((T, d)), rng.standard_normal((T, dt))
+    Ws = rng.standard_normal((d, V)) / np.sqrt(d)
+    Wt = rng.standard_normal((dt, V)) * 1.5 / np.sqrt(dt)
+    g = rng.standard_normal(T)
+    taus = rng.uniform(0.6, 2.5, T)
+    return H, Ws, Ht, Wt, g, taus
+
+
+def torch_kl_both(H, Ws, Ht, Wt, taus):
+    """KL(p || q) and KL(q || p) per row with torch's kl_div (log-space inputs)."""
+    tau = torch.tensor(taus)[:, None]
+    logq = torch.log_softmax(torch.tensor(H @ Ws) / tau, dim=1)
+    logp = torch.log_softmax(torch.tensor(Ht @ Wt) / tau, dim=1)
+    fwd = torch.nn.functional.kl_div(logq, logp, log_target=True, reduction="none").sum(1).numpy()
+    rev = torch.nn.functional.kl_div(logp, logq, log_target=True, reduction="none").sum(1).numpy()
+    return fwd, rev
+
+
+def test_full_reverse_kl_is_torch_kl_div_swapped():
+    H, Ws, Ht, Wt, g, taus = full_case(seed=31)
+    got, _, _, krev = O.full_loss_forward(H, Ws, Ht, Wt, None, 1.0, tau_rows=taus, rev_weight=1.0)
+    fwd, rev = torch_kl_both(H, Ws, Ht, Wt, taus)
+    np.testing.assert_allclose(got, rev, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(krev, rev, rtol=1e-12, atol=1e-14)
+    assert np.all(rev >= 0) and np.all(np.abs(rev - fwd) > 1e-6)  # the two directions differ here
+
+
+def test_full_kl_mixing_is_the_convex_combination():
+    H, Ws, Ht, Wt, g, taus = full_case(seed=32)
+    fwd, rev = torch_kl_both(H, Ws, Ht, Wt, np.full(6, 1.3))
+    for r in (0.0, 0.3, 0.8):
+        got, lse_s, lse_t, krev = O.full_loss_forward(H, Ws, Ht, Wt, None, 1.3, rev_weight=r)
+        np.testing.assert_allclose(got, (1 - r) * fwd + r * rev, rtol=1e-12, atol=1e-14)
+        a, b, c = O.full_kl_forward(H, Ws, Ht, Wt, None, 1.3)
+        np.testing.assert_allclose(lse_s, b, rtol=1e-14)
+        np.testing.assert_allclose(lse_t, c, rtol=1e-14)
+
+
+def test_full_per_token_tau_is_row_scaling():
+    H, Ws, Ht, Wt, g, taus = full_case(seed=33)
+    got, ls, lt, _ = O.full_loss_forward(H, Ws, Ht, Wt, None, 1.0, tau_rows=taus)
+    want, ls1, lt1 = O.full_kl_forward(H / taus[:, None], Ws, Ht / taus[:, None], Wt, None, 1.0)
+    np.testing.assert_allclose(got, want, rtol=1e-12)
+    np.testing.assert_allclose(ls, ls1, rtol=1e-13)
+
+
+def test_full_mixed_gradient_matches_torch_autograd():
+    H, Ws, Ht, Wt, g, taus = full_case(T=5, seed=34)
+    for r in (0.0, 0.4, 1.0):
+        Hv = torch.tensor(H, requires_grad=True)
+        Wv = torch.tensor(Ws, requires_grad=True)
+        tau = torch.tensor(taus)[:, None]
+        logq = torch.log_softmax((Hv @ Wv) / tau, dim=1)
+        logp = torch.log_softmax(torch.tensor(Ht @ Wt) / tau, dim=1)
+        fwd = torch.nn.functional.kl_div(logq, logp, log_target=True, reduction="none").sum(1)
+        rev = torch.nn.functional.kl_div(logp, logq, log_target=True, reduction="none").sum(1)
+        (((1 - r) * fwd + r * rev) * torch.tensor(g)).sum().backward()
+        dH, dW = O.full_loss_backward(H, Ws, Ht, Wt, None, 1.0, g, tau_rows=taus, rev_weight=r)
+        np.testing.assert_allclose(dH, Hv.grad.numpy(), rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(dW, Wv.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_full_mixed_finite_differences_and_mask():
+    H, Ws, Ht, Wt, g, taus = full_case(T=4, d=6, dt=5, V=20, seed=35)
+    mask = np.array([1, 1, 0, 1], dtype=np.uint8)
+    kw = dict(tau_rows=taus, rev_weight=0.6)
+    dH, dW = O.full_loss_backward(H, Ws, Ht, Wt, mask, 1.0, g, **kw)
+
+    def loss(Hx, Wx):
+        v = O.full_loss_forward(Hx, Wx, Ht, Wt, mask, 1.0, **kw)[0]
+        return float((v * g).sum())
+
+    h = 1e-6
+    rng = np.random.default_rng(36)
+    for _ in range(10):
+        t, j = rng.integers(4), rng.integers(6)
+        Hp, Hm = H.copy(), H.copy()
+        Hp[t, j] += h
+        Hm[t, j] -= h
+        assert (loss(Hp, Ws) - loss(Hm, Ws)) / (2 * h) == pytest.approx(dH[t, j], rel=1e-7, abs=1e-9)
+    for _ in range(10):
+        j, v = rng.integers(6), rng.integers(20)
+        Wp, Wm = Ws.copy(), Ws.copy()
+        Wp[j, v] += h
+        Wm[j, v] -= h
+        assert (loss(H, Wp) - loss(H, Wm)) / (2 * h) == pytest.approx(dW[j, v], rel=1e-7, abs=1e-9)
+    assert np.all(dH[2] == 0)
+
+
+def test_full_options_defaults_and_equal_heads():
+    H, Ws, Ht, Wt, g, _ = full_case(seed=37)
+    a = O.full_loss_forward(H, Ws, Ht, Wt, None, 0.9)
+    b = O.full_kl_forward(H, Ws, Ht, Wt, None, 0.9)
+    for x, y in zip(a[:3], b):
+        np.testing.assert_allclose(x, y, rtol=1e-13, atol=1e-15)
+    v, _, _, kr = O.full_loss_forward(H, Ws, H, Ws, None, 0.9, rev_weight=0.5)
+    assert np.all(np.abs(v) < 1e-13) and np.all(np.abs(kr) < 1e-13)
+    dH, _ = O.full_loss_backward(H, Ws, H, Ws, None, 0.9, g, rev_weight=0.5)
+    assert np.all(np.abs(dH) < 1e-13)
