@@ -19,7 +19,8 @@ import torch
 from ._binding import (  # noqa: F401
     EXPORTS, KD_BF16, KD_DEFAULT_CHUNK_ROWS, KD_F32, KD_MAX_K, LIB_PATH, KDError, kd_full_kl_bwd, kd_full_kl_fwd,
     kd_full_kl_fwd_bwd, kd_full_kl_fwd_bwd_workspace_size, kd_full_kl_workspace_size, kd_topk_kl_bwd_ex,
-    kd_topk_kl_fwd_bwd_ex, kd_topk_kl_fwd_ex, topk_opts, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd, kd_topk_kl_fwd_bwd_workspace_size,
+    kd_topk_kl_fwd_bwd_ex, kd_topk_kl_fwd_ex, topk_opts, kd_full_kl_fwd_ex, kd_full_kl_bwd_ex, kd_full_kl_fwd_bwd_ex,
+    full_opts, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd, kd_topk_kl_fwd_bwd_workspace_size,
     kd_topk_kl_workspace_size, kd_version, lib,
     profile_enable, profile_read, profile_reset,
 )
@@ -29,7 +30,8 @@ __all__ = [
     "full_kl_backward", "full_kl_forward_backward", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_topk_kl_fwd_bwd",
     "kd_full_kl_fwd", "kd_full_kl_bwd", "kd_full_kl_fwd_bwd", "kd_topk_kl_workspace_size",
     "kd_topk_kl_fwd_bwd_workspace_size", "kd_full_kl_workspace_size", "kd_full_kl_fwd_bwd_workspace_size", "KDError",
-    "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex", "topk_opts",
+    "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex", "topk_opts", "kd_full_kl_fwd_ex",
+    "kd_full_kl_bwd_ex", "kd_full_kl_fwd_bwd_ex", "full_opts",
 ]
 
 
@@ -86,44 +88,55 @@ def topk_kl_forward_backward(H, W, topk_idx, topk_logits, mask, tau, grad_kl, ch
     return kl, lse, z, dH, dW
 
 
-def full_kl_forward(H, Ws, Ht, Wt, mask=None, tau=1.0, workspace=None):
+# Options of the full-vocabulary loss (kd_full_opts of kdloss.h): tau_rows
+# [T] float32 per-token temperature; rev_weight r in [0, 1] mixes in the
+# reverse KL, (1 - r) KL(p||q) + r KL(q||p).  With want_kl_rev the forward
+# also returns KL(q||p) per row, which the backward needs when r > 0.
+def full_kl_forward(H, Ws, Ht, Wt, mask=None, tau=1.0, workspace=None, tau_rows=None, rev_weight=0.0,
+                    want_kl_rev=False):
+    """kl, lse_s, lse_t (and kl_rev with want_kl_rev)."""
     T, d = H.shape
     dt, V = Ht.shape[1], Ws.shape[1]
     kl = torch.empty(T, dtype=torch.float32, device=H.device)
     ls = torch.empty(T, dtype=torch.float32, device=H.device)
     lt = torch.empty(T, dtype=torch.float32, device=H.device)
+    kr = torch.empty(T, dtype=torch.float32, device=H.device) if want_kl_rev else None
     if workspace is None:
         workspace = _workspace(kd_full_kl_workspace_size(T, d, dt, V, H.dtype), H.device)
-    kd_full_kl_fwd(H, Ws, Ht, Wt, mask, tau, kl, ls, lt, workspace)
-    return kl, ls, lt
+    kd_full_kl_fwd_ex(H, Ws, Ht, Wt, mask, tau, full_opts(tau_rows, rev_weight), kl, ls, lt, kr, workspace)
+    return (kl, ls, lt, kr) if want_kl_rev else (kl, ls, lt)
 
 
-def full_kl_backward(H, Ws, Ht, Wt, mask, tau, lse_s, lse_t, grad_kl, chunk_rows=0, workspace=None):
+def full_kl_backward(H, Ws, Ht, Wt, mask, tau, lse_s, lse_t, grad_kl, chunk_rows=0, workspace=None, tau_rows=None,
+                     rev_weight=0.0, kl_rev=None):
+    """dH (dtype of H) and dWs (float32)."""
     T, d = H.shape
     dt, V = Ht.shape[1], Ws.shape[1]
     dH = torch.empty_like(H)
     dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
     if workspace is None:
         workspace = _workspace(kd_full_kl_workspace_size(T, d, dt, V, H.dtype, chunk_rows), H.device)
-    kd_full_kl_bwd(H, Ws, Ht, Wt, mask, tau, lse_s, lse_t, grad_kl.float().contiguous(), dH, dW, chunk_rows,
-                   workspace)
+    kd_full_kl_bwd_ex(H, Ws, Ht, Wt, mask, tau, full_opts(tau_rows, rev_weight), lse_s, lse_t, kl_rev,
+                      grad_kl.float().contiguous(), dH, dW, chunk_rows, workspace)
     return dH, dW
 
 
-def full_kl_forward_backward(H, Ws, Ht, Wt, mask, tau, grad_kl, chunk_rows=0, workspace=None):
-    """kl, lse_s, lse_t, dH and dWs in one call, for a known grad_kl."""
+def full_kl_forward_backward(H, Ws, Ht, Wt, mask, tau, grad_kl, chunk_rows=0, workspace=None, tau_rows=None,
+                             rev_weight=0.0, want_kl_rev=False):
+    """kl, lse_s, lse_t, (kl_rev,) dH and dWs in one call, for a known grad_kl."""
     T, d = H.shape
     dt, V = Ht.shape[1], Ws.shape[1]
     kl = torch.empty(T, dtype=torch.float32, device=H.device)
     ls = torch.empty(T, dtype=torch.float32, device=H.device)
     lt = torch.empty(T, dtype=torch.float32, device=H.device)
+    kr = torch.empty(T, dtype=torch.float32, device=H.device) if want_kl_rev else None
     dH = torch.empty_like(H)
     dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
     if workspace is None:
         workspace = _workspace(kd_full_kl_fwd_bwd_workspace_size(T, d, dt, V, H.dtype, chunk_rows), H.device)
-    kd_full_kl_fwd_bwd(H, Ws, Ht, Wt, mask, tau, grad_kl.float().contiguous(), kl, ls, lt, dH, dW, chunk_rows,
-                       workspace)
-    return kl, ls, lt, dH, dW
+    kd_full_kl_fwd_bwd_ex(H, Ws, Ht, Wt, mask, tau, full_opts(tau_rows, rev_weight), grad_kl.float().contiguous(),
+                          kl, ls, lt, kr, dH, dW, chunk_rows, workspace)
+    return (kl, ls, lt, kr, dH, dW) if want_kl_rev else (kl, ls, lt, dH, dW)
 
 
 class _TopkKL(torch.autograd.Function):
@@ -143,17 +156,20 @@ class _TopkKL(torch.autograd.Function):
 
 class _FullKL(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, H, Ws, Ht, Wt, mask, tau, chunk_rows):
-        kl, ls, lt = full_kl_forward(H, Ws, Ht, Wt, mask, tau)
-        ctx.save_for_backward(H, Ws, Ht, Wt, ls, lt)
+    def forward(ctx, H, Ws, Ht, Wt, mask, tau, chunk_rows, tau_rows, rev_weight):
+        kl, ls, lt, kr = full_kl_forward(H, Ws, Ht, Wt, mask, tau, tau_rows=tau_rows, rev_weight=rev_weight,
+                                         want_kl_rev=True)
+        ctx.save_for_backward(H, Ws, Ht, Wt, ls, lt, kr)
         ctx.mask, ctx.tau, ctx.chunk_rows = mask, tau, chunk_rows
+        ctx.tau_rows, ctx.rev_weight = tau_rows, rev_weight
         return kl
 
     @staticmethod
     def backward(ctx, g):
-        H, Ws, Ht, Wt, ls, lt = ctx.saved_tensors
-        dH, dW = full_kl_backward(H, Ws, Ht, Wt, ctx.mask, ctx.tau, ls, lt, g, ctx.chunk_rows)
-        return dH, dW.to(Ws.dtype), None, None, None, None, None
+        H, Ws, Ht, Wt, ls, lt, kr = ctx.saved_tensors
+        dH, dW = full_kl_backward(H, Ws, Ht, Wt, ctx.mask, ctx.tau, ls, lt, g, ctx.chunk_rows,
+                                  tau_rows=ctx.tau_rows, rev_weight=ctx.rev_weight, kl_rev=kr)
+        return dH, dW.to(Ws.dtype), None, None, None, None, None, None, None
 
 
 def topk_kl(H, W, topk_idx, topk_logits, mask=None, tau=1.0, chunk_rows=0, tau_rows=None, teacher_lse=None,
@@ -166,7 +182,7 @@ def topk_kl(H, W, topk_idx, topk_logits, mask=None, tau=1.0, chunk_rows=0, tau_r
     return _TopkKL.apply(H, W, topk_idx, topk_logits, mask, float(tau), int(chunk_rows), options)
 
 
-def full_kl(H, Ws, Ht, Wt, mask=None, tau=1.0, chunk_rows=0):
-    """Per-token full-vocabulary KL through a frozen teacher head; differentiable
-    in H and Ws only."""
-    return _FullKL.apply(H, Ws, Ht, Wt, mask, float(tau), int(chunk_rows))
+def full_kl(H, Ws, Ht, Wt, mask=None, tau=1.0, chunk_rows=0, tau_rows=None, rev_weight=0.0):
+    """Per-token full-vocabulary KL through a frozen teacher head (with the
+    options: the KL mixture of kd_full_opts); differentiable in H and Ws only."""
+    return _FullKL.apply(H, Ws, Ht, Wt, mask, float(tau), int(chunk_rows), tau_rows, float(rev_weight))

@@ -29,6 +29,7 @@ EXPORTS = (
     "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex",
     "kd_full_kl_workspace_size", "kd_full_kl_fwd", "kd_full_kl_bwd",
     "kd_full_kl_fwd_bwd_workspace_size", "kd_full_kl_fwd_bwd",
+    "kd_full_kl_fwd_ex", "kd_full_kl_bwd_ex", "kd_full_kl_fwd_bwd_ex",
     "kd_status_string", "kd_last_error", "kd_version",
     "kd_profile_enable", "kd_profile_count", "kd_profile_get", "kd_profile_reset",
 )
@@ -38,6 +39,11 @@ class KdTopkOpts(ctypes.Structure):
     """kd_topk_opts of kdloss.h: device pointers (0 = NULL) and the CE weight."""
     _fields_ = [("tau_rows", ctypes.c_void_p), ("teacher_lse", ctypes.c_void_p), ("labels", ctypes.c_void_p),
                 ("ce_weight", ctypes.c_float)]
+
+
+class KdFullOpts(ctypes.Structure):
+    """kd_full_opts of kdloss.h."""
+    _fields_ = [("tau_rows", ctypes.c_void_p), ("rev_weight", ctypes.c_float)]
 
 
 class KDError(RuntimeError):
@@ -74,6 +80,12 @@ def lib() -> ctypes.CDLL:
                                     vp]
     L.kd_topk_kl_fwd_bwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, op, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp,
                                         i64, vp, sz, vp]
+    fo = ctypes.POINTER(KdFullOpts)
+    L.kd_full_kl_fwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, fo, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, sz, vp]
+    L.kd_full_kl_bwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, fo, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp, i64,
+                                    vp, sz, vp]
+    L.kd_full_kl_fwd_bwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, fo, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp,
+                                        vp, i64, vp, sz, vp]
     L.kd_full_kl_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
     L.kd_full_kl_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, sz, vp]
     L.kd_full_kl_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, i64, vp, sz,
@@ -85,6 +97,7 @@ def lib() -> ctypes.CDLL:
               "kd_topk_kl_fwd_bwd", "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex",
               "kd_full_kl_workspace_size",
               "kd_full_kl_fwd", "kd_full_kl_bwd", "kd_full_kl_fwd_bwd_workspace_size", "kd_full_kl_fwd_bwd",
+              "kd_full_kl_fwd_ex", "kd_full_kl_bwd_ex", "kd_full_kl_fwd_bwd_ex",
               "kd_profile_enable", "kd_profile_get", "kd_profile_reset"):
         getattr(L, f).restype = st
     L.kd_status_string.argtypes = [st]
@@ -281,6 +294,49 @@ def kd_full_kl_fwd_bwd(H, Ws, Ht, Wt, mask, tau, grad_kl, kl, lse_s, lse_t, dH, 
                                     _ptr(dH), _ptr(dWs), int(chunk_rows), _ptr(workspace),
                                     workspace.numel() if workspace is not None else 0, _stream(stream)),
            "kd_full_kl_fwd_bwd")
+
+
+def full_opts(tau_rows=None, rev_weight=0.0):
+    """The kd_full_opts struct (or None when no option is set)."""
+    if tau_rows is None and not rev_weight:
+        return None
+    if tau_rows is not None and tau_rows.dtype != torch.float32:
+        raise TypeError("tau_rows must be torch.float32")
+    return KdFullOpts(_ptr(tau_rows), float(rev_weight))
+
+
+def kd_full_kl_fwd_ex(H, Ws, Ht, Wt, mask, tau, opts, kl, lse_s, lse_t, kl_rev, workspace, stream=None):
+    T, d = H.shape
+    dt = Ht.shape[1]
+    V = Ws.shape[1]
+    _check(lib().kd_full_kl_fwd_ex(_ptr(H), _ptr(Ws), _ptr(Ht), _ptr(Wt), _ptr(mask), float(tau), _opts_ref(opts),
+                                   T, d, dt, V, _dtype_code(H.dtype), _ptr(kl), _ptr(lse_s), _ptr(lse_t),
+                                   _ptr(kl_rev), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                   _stream(stream)), "kd_full_kl_fwd_ex")
+
+
+def kd_full_kl_bwd_ex(H, Ws, Ht, Wt, mask, tau, opts, lse_s, lse_t, kl_rev, grad_kl, dH, dWs, chunk_rows, workspace,
+                      stream=None):
+    T, d = H.shape
+    dt = Ht.shape[1]
+    V = Ws.shape[1]
+    _check(lib().kd_full_kl_bwd_ex(_ptr(H), _ptr(Ws), _ptr(Ht), _ptr(Wt), _ptr(mask), float(tau), _opts_ref(opts),
+                                   T, d, dt, V, _dtype_code(H.dtype), _ptr(lse_s), _ptr(lse_t), _ptr(kl_rev),
+                                   _ptr(grad_kl), _ptr(dH), _ptr(dWs), int(chunk_rows), _ptr(workspace),
+                                   workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "kd_full_kl_bwd_ex")
+
+
+def kd_full_kl_fwd_bwd_ex(H, Ws, Ht, Wt, mask, tau, opts, grad_kl, kl, lse_s, lse_t, kl_rev, dH, dWs, chunk_rows,
+                          workspace, stream=None):
+    T, d = H.shape
+    dt = Ht.shape[1]
+    V = Ws.shape[1]
+    _check(lib().kd_full_kl_fwd_bwd_ex(_ptr(H), _ptr(Ws), _ptr(Ht), _ptr(Wt), _ptr(mask), float(tau),
+                                       _opts_ref(opts), T, d, dt, V, _dtype_code(H.dtype), _ptr(grad_kl), _ptr(kl),
+                                       _ptr(lse_s), _ptr(lse_t), _ptr(kl_rev), _ptr(dH), _ptr(dWs), int(chunk_rows),
+                                       _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                       _stream(stream)), "kd_full_kl_fwd_bwd_ex")
 
 
 def kd_version() -> int:

@@ -222,7 +222,7 @@ struct FullPlan {
   // student and teacher logits and the backward chunk buffers
   int S_c;
   ChunkPlan ch_f;
-  size_t o_part_c, o_zs, o_zt, fused_total;
+  size_t o_part_c, o_zs, o_zt, o_krev, fused_total;
 };
 
 FullPlan plan_full(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows) {
@@ -244,6 +244,7 @@ FullPlan plan_full(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows
   p.ch_f = plan_chunk(T, d, V, elem, chunk_rows, fu);
   p.o_zs = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
   p.o_zt = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
+  p.o_krev = fu.take((size_t)T * 4);
   p.fused_total = fu.off;
   return p;
 }
@@ -323,7 +324,7 @@ const char* kd_status_string(kd_status s) {
 
 const char* kd_last_error(void) { return g_err.c_str(); }
 
-int kd_version(void) { return 10300; }
+int kd_version(void) { return 10400; }
 
 kd_status kd_profile_enable(int on) {
   g_prof_on = on != 0;
@@ -386,6 +387,17 @@ kd_status resolve_opts(const kd_topk_opts* o, float tau, int64_t K, TopkOpts& r)
     r.prep.beta = o->ce_weight;
     r.KE = K + 1;
   }
+  return KD_OK;
+}
+
+kd_status resolve_full_opts(const kd_full_opts* o, kd::FullMix& mx) {
+  mx = kd::FullMix{};
+  if (o == nullptr) return KD_OK;
+  if (!std::isfinite(o->rev_weight) || o->rev_weight < 0.f || o->rev_weight > 1.f)
+    return fail(KD_ERR_INVALID_ARG, "rev_weight must be finite and in [0, 1]");
+  KD_TRY(need_align(o->tau_rows, 4, "tau_rows"));
+  mx.tau_rows = o->tau_rows;
+  mx.r = o->rev_weight;
   return KD_OK;
 }
 
@@ -570,9 +582,20 @@ kd_status kd_full_kl_workspace_size(int64_t T, int64_t d, int64_t dt_hidden, int
 kd_status kd_full_kl_fwd(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask, float tau,
                          int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt, float* kl, float* lse_s,
                          float* lse_t, void* workspace, size_t workspace_bytes, void* stream) {
+  return kd_full_kl_fwd_ex(H, Ws, Ht, Wt, mask, tau, nullptr, T, d, dt_hidden, V, dt, kl, lse_s, lse_t, nullptr,
+                           workspace, workspace_bytes, stream);
+}
+
+kd_status kd_full_kl_fwd_ex(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask,
+                            float tau, const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden, int64_t V,
+                            kd_dtype dt, float* kl, float* lse_s, float* lse_t, float* kl_rev, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
   KD_TRY(check_common(T, dt_hidden, V, dt, tau));
+  kd::FullMix mx;
+  KD_TRY(resolve_full_opts(opts, mx));
+  KD_TRY(need_align(kl_rev, 4, "kl_rev"));
   if (T == 0) return KD_OK;
   KD_TRY(need(H, "H"));
   KD_TRY(need(Ws, "Ws"));
@@ -616,8 +639,10 @@ kd_status kd_full_kl_fwd(const void* H, const void* Ws, const void* Ht, const vo
   a.ntiles = p.ntiles;
   a.group = kRasterGroup;
   a.c2 = (float)(1.4426950408889634 / (double)tau);
+  a.tau_rows = mx.tau_rows;
   KD_LAUNCH("full_fwd_tile", st, kd::launch_full_fwd(elem, a, st));
-  KD_LAUNCH("full_combine", st, kd::launch_full_combine(part, p.S, T, c, mask, T, kl, lse_s, lse_t, 0, T, true, st));
+  KD_LAUNCH("full_combine", st,
+            kd::launch_full_combine(part, p.S, T, c, mask, T, mx.r, kl, lse_s, lse_t, kl_rev, 0, T, true, st));
   return KD_OK;
 }
 
@@ -625,9 +650,22 @@ kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const vo
                          int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt, const float* lse_s,
                          const float* lse_t, const float* grad_kl, void* dH, float* dWs, int64_t chunk_rows,
                          void* workspace, size_t workspace_bytes, void* stream) {
+  return kd_full_kl_bwd_ex(H, Ws, Ht, Wt, mask, tau, nullptr, T, d, dt_hidden, V, dt, lse_s, lse_t, nullptr, grad_kl,
+                           dH, dWs, chunk_rows, workspace, workspace_bytes, stream);
+}
+
+kd_status kd_full_kl_bwd_ex(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask,
+                            float tau, const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden, int64_t V,
+                            kd_dtype dt, const float* lse_s, const float* lse_t, const float* kl_rev,
+                            const float* grad_kl, void* dH, float* dWs, int64_t chunk_rows, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
   KD_TRY(check_common(T, dt_hidden, V, dt, tau));
+  kd::FullMix mx;
+  KD_TRY(resolve_full_opts(opts, mx));
+  KD_TRY(need_align(kl_rev, 4, "kl_rev"));
+  mx.kl_rev = kl_rev;
   KD_TRY(need(dWs, "dWs"));
   KD_TRY(need_align(dWs, 16, "dWs"));
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -643,6 +681,7 @@ kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const vo
   KD_TRY(need(lse_t, "lse_t"));
   KD_TRY(need(grad_kl, "grad_kl"));
   KD_TRY(need(dH, "dH"));
+  if (mx.r != 0.f) KD_TRY(need(kl_rev, "kl_rev (rev_weight > 0)"));
   KD_TRY(need_align(H, 16, "H"));
   KD_TRY(need_align(Ws, 16, "Ws"));
   KD_TRY(need_align(Ht, 16, "Ht"));
@@ -690,6 +729,7 @@ kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const vo
     za.S = splits_for(ch.nrb_c, p.ntiles);
     za.c2 = (float)(1.4426950408889634 / (double)tau);
     za.inv_tau = 1.0f / tau;
+    za.mix = mx;
     KD_LAUNCH("full_dz_tile", st, kd::launch_full_dz(elem, za, st));
     KD_TRY(grad_chunk(H, Ws, dH, dWs, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
   }
@@ -712,9 +752,21 @@ kd_status kd_full_kl_fwd_bwd(const void* H, const void* Ws, const void* Ht, cons
                              float tau, int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
                              const float* grad_kl, float* kl, float* lse_s, float* lse_t, void* dH, float* dWs,
                              int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  return kd_full_kl_fwd_bwd_ex(H, Ws, Ht, Wt, mask, tau, nullptr, T, d, dt_hidden, V, dt, grad_kl, kl, lse_s, lse_t,
+                               nullptr, dH, dWs, chunk_rows, workspace, workspace_bytes, stream);
+}
+
+kd_status kd_full_kl_fwd_bwd_ex(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask,
+                                float tau, const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden,
+                                int64_t V, kd_dtype dt, const float* grad_kl, float* kl, float* lse_s, float* lse_t,
+                                float* kl_rev, void* dH, float* dWs, int64_t chunk_rows, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
   KD_TRY(check_common(T, dt_hidden, V, dt, tau));
+  kd::FullMix mx;
+  KD_TRY(resolve_full_opts(opts, mx));
+  KD_TRY(need_align(kl_rev, 4, "kl_rev"));
   KD_TRY(need(dWs, "dWs"));
   KD_TRY(need_align(dWs, 16, "dWs"));
   if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
@@ -749,6 +801,9 @@ kd_status kd_full_kl_fwd_bwd(const void* H, const void* Ws, const void* Ht, cons
   float* part = at<float>(workspace, p.o_part_c);
   float* zs = at<float>(workspace, p.o_zs);
   float* zt = at<float>(workspace, p.o_zt);
+  // the reverse KL of each row feeds its dZ: the caller's array, else the workspace's
+  float* krev = kl_rev ? kl_rev : at<float>(workspace, p.o_krev);
+  mx.kl_rev = krev;
   const ChunkPlan& ch = p.ch_f;
   char* dz = at<char>(workspace, ch.o_dz);
   char* hT = at<char>(workspace, ch.o_hT);
@@ -784,9 +839,11 @@ kd_status kd_full_kl_fwd_bwd(const void* H, const void* Ws, const void* Ht, cons
     a.ntiles = p.ntiles;
     a.group = kRasterGroup;
     a.c2 = c2;
+    a.tau_rows = mx.tau_rows;
     KD_LAUNCH("full_fwd_tile", st, kd::launch_full_fwd(elem, a, st));
     KD_LAUNCH("full_combine", st,
-              kd::launch_full_combine(part, p.S_c, ch.C, c, mask, T, kl, lse_s, lse_t, c0, c0 + ch.C, k == 0, st));
+              kd::launch_full_combine(part, p.S_c, ch.C, c, mask, T, mx.r, kl, lse_s, lse_t, krev, c0, c0 + ch.C,
+                                      k == 0, st));
     // dZ from the kept logits: no second pair of projections
     kd::FullDzFromZArgs za{};
     za.zs = zs;
@@ -802,6 +859,7 @@ kd_status kd_full_kl_fwd_bwd(const void* H, const void* Ws, const void* Ht, cons
     za.g = grad_kl;
     za.c2 = c2;
     za.inv_tau = 1.0f / tau;
+    za.mix = mx;
     KD_LAUNCH("full_dz_from_z", st, kd::launch_full_dz_from_z(elem, za, st));
     KD_TRY(grad_chunk(H, Ws, dH, dWs, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
   }

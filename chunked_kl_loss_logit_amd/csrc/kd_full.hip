@@ -10,11 +10,16 @@
 //
 // Forward, per row and in base 2 (y = z log2(e) / tau): running maxima and
 // sums of 2^(ys - ms) and 2^(yt - mt), plus R = sum 2^(yt - mt) (yt - ys),
-// rescaled whenever mt grows.  This is the one-pass online form of the
-// coupled two-distribution KL (the idea in StreamKL's abstract, on the same
-// page as the KDFlow abstract, here over vocabulary tiles):
-//   KL = ln2 (R / lt - (mt + log2 lt) + (ms + log2 ls)).
-// Backward: dZ = (g / tau) (2^(ys - Ls2) - 2^(yt - Lt2)).
+// rescaled whenever mt grows, and R2 = sum 2^(ys - ms) (ys - yt), rescaled
+// whenever ms grows.  This is the one-pass online form of the coupled
+// two-distribution KL (the idea in StreamKL's abstract, on the same page as
+// the KDFlow abstract, here over vocabulary tiles), in both directions:
+//   KL(p||q) = ln2 (R / lt - (mt + log2 lt) + (ms + log2 ls)),
+//   KL(q||p) = ln2 (R2 / ls - (ms + log2 ls) + (mt + log2 lt)).
+// Backward: dZ = (g / tau) (2^(ys - Ls2) - 2^(yt - Lt2)), or with KL mixing
+// (the KL-direction abstract on the same page) weight r on the reverse KL:
+//   dZ = (g / tau) [(1 - r)(q - p) + r q (ln q - ln p - KL(q||p))].
+// A per-row temperature (tau_rows) gives each row its own log2(e) / tau.
 #include <climits>
 
 #include "kd_gemm.h"
@@ -28,10 +33,10 @@ namespace {
 constexpr int kBN = kTileNFull;
 
 struct FullFwdRow {
-  float ms, ls, mt, lt, R;
+  float ms, ls, mt, lt, R, R2, c2;
   bool rv;
 
-  __device__ inline void consume(StPair ss, StPair su, long cb, long V, float c2) {
+  __device__ inline void consume(StPair ss, StPair su, long cb, long V) {
     if (!rv) return;
     const int nv = (int)max(0L, min(32L, V - cb));
     if (nv == 0) return;
@@ -55,7 +60,9 @@ struct FullFwdRow {
     }
     const float cys = cms * c2, cyt = cmt * c2;
     if (cys > ms) {
-      ls *= fast_exp2(ms - cys);
+      const float f = fast_exp2(ms - cys);
+      ls *= f;
+      R2 *= f;
       ms = cys;
     }
     if (cyt > mt) {
@@ -64,38 +71,75 @@ struct FullFwdRow {
       R *= f;
       mt = cyt;
     }
-    float sum_s = 0.f, sum_t = 0.f, rr = 0.f;
+    float sum_s = 0.f, sum_t = 0.f, rr = 0.f, rr2 = 0.f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       if (j < nv) {
         const float ys = vs[j] * c2, yt = vu[j] * c2;
-        const float et = fast_exp2(yt - mt);
-        sum_s += fast_exp2(ys - ms);
+        const float et = fast_exp2(yt - mt), es = fast_exp2(ys - ms);
+        sum_s += es;
         sum_t += et;
         rr = fmaf(et, yt - ys, rr);
+        rr2 = fmaf(es, ys - yt, rr2);
       }
     }
     ls += sum_s;
     lt += sum_t;
     R += rr;
+    R2 += rr2;
   }
 };
 
+// dZ of one element from its two logits and the row's constants.
+struct FullDzConst {
+  float Ls2, Lt2, gs, c2;
+  float a, b, kr;  // KL mixing: weights of the forward and reverse terms, the row's KL(q||p)
+  bool mix;
+
+  __device__ inline float operator()(float zs, float zt) const {
+    const float ds = fmaf(zs, c2, -Ls2), dt = fmaf(zt, c2, -Lt2);
+    const float qs = fast_exp2(ds), pt = fast_exp2(dt);
+    if (!mix) return gs * (qs - pt);
+    return gs * fmaf(a, qs - pt, b * qs * fmaf(kLn2, ds - dt, -kr));
+  }
+};
+
+// The row's constants for the backward, from the forward's outputs.
+__device__ inline FullDzConst full_dz_const(bool rv, long t, const float* lse_s, const float* lse_t, const float* g,
+                                            float c2, float inv_tau, const FullMix& mx) {
+  FullDzConst k{};
+  if (!rv) return k;
+  if (mx.tau_rows) {
+    const float tt = mx.tau_rows[t];
+    c2 = (float)(1.4426950408889634 / (double)tt);
+    inv_tau = 1.0f / tt;
+  }
+  k.c2 = c2;
+  k.Ls2 = lse_s[t] * kLog2e;
+  k.Lt2 = lse_t[t] * kLog2e;
+  k.gs = g[t] * inv_tau;
+  k.mix = mx.r != 0.f;
+  k.a = 1.f - mx.r;
+  k.b = mx.r;
+  k.kr = k.mix ? mx.kl_rev[t] : 0.f;
+  return k;
+}
+
 struct FullDzRow {
-  float Ls2, Lt2, gs;
+  FullDzConst k;
   bool rv;
 
-  __device__ inline void consume(StPair ss, StPair su, long cb, long V, float c2) {
+  __device__ inline void consume(StPair ss, StPair su, long cb, long V) {
     const int r = threadIdx.x;
     const int nv = rv ? (int)max(0L, min(32L, V - cb)) : 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float4 fs = st_read4(ss, r, j);
       const float4 fu = st_read4(su, r, j);
-      fs.x = 4 * j + 0 < nv ? gs * (fast_exp2(fmaf(fs.x, c2, -Ls2)) - fast_exp2(fmaf(fu.x, c2, -Lt2))) : 0.f;
-      fs.y = 4 * j + 1 < nv ? gs * (fast_exp2(fmaf(fs.y, c2, -Ls2)) - fast_exp2(fmaf(fu.y, c2, -Lt2))) : 0.f;
-      fs.z = 4 * j + 2 < nv ? gs * (fast_exp2(fmaf(fs.z, c2, -Ls2)) - fast_exp2(fmaf(fu.z, c2, -Lt2))) : 0.f;
-      fs.w = 4 * j + 3 < nv ? gs * (fast_exp2(fmaf(fs.w, c2, -Ls2)) - fast_exp2(fmaf(fu.w, c2, -Lt2))) : 0.f;
+      fs.x = 4 * j + 0 < nv ? k(fs.x, fu.x) : 0.f;
+      fs.y = 4 * j + 1 < nv ? k(fs.y, fu.y) : 0.f;
+      fs.z = 4 * j + 2 < nv ? k(fs.z, fu.z) : 0.f;
+      fs.w = 4 * j + 3 < nv ? k(fs.w, fu.w) : 0.f;
       st_write4(ss, r, j, fs);
     }
   }
@@ -113,8 +157,8 @@ __device__ inline void full_fwd_round(const Slots& sl, const f32x16_t (&acc_s)[4
                                       long row0, long M) {
   stage_pair<NBI>(sl, acc_s, acc_t);
   __syncthreads();
-  R.consume(st_pair<0>(sl), st_pair<2>(sl), n0 + NBI * 32, a.V, a.c2);
-  R.consume(st_pair<1>(sl), st_pair<3>(sl), n0 + 64 + NBI * 32, a.V, a.c2);
+  R.consume(st_pair<0>(sl), st_pair<2>(sl), n0 + NBI * 32, a.V);
+  R.consume(st_pair<1>(sl), st_pair<3>(sl), n0 + 64 + NBI * 32, a.V);
   if (a.zs) {  // the consume only read the staged blocks: the logits go out as they are
     char* zs = reinterpret_cast<char*>(a.zs);
     char* zt = reinterpret_cast<char*>(a.zt);
@@ -131,8 +175,8 @@ __device__ inline void full_dz_round(const Slots& sl, const f32x16_t (&acc_s)[4]
                                      long n0, long row0, FullDzRow& R, const FullDzArgs& a) {
   stage_pair<NBI>(sl, acc_s, acc_t);
   __syncthreads();
-  R.consume(st_pair<0>(sl), st_pair<2>(sl), n0 + NBI * 32, a.V, a.c2);
-  R.consume(st_pair<1>(sl), st_pair<3>(sl), n0 + 64 + NBI * 32, a.V, a.c2);
+  R.consume(st_pair<0>(sl), st_pair<2>(sl), n0 + NBI * 32, a.V);
+  R.consume(st_pair<1>(sl), st_pair<3>(sl), n0 + 64 + NBI * 32, a.V);
   __syncthreads();
   store_block<E>(st_pair<0>(sl), a.dz, a.ldz, row0, n0 + NBI * 32, LONG_MAX, a.ldz);
   store_block<E>(st_pair<1>(sl), a.dz, a.ldz, row0, n0 + 64 + NBI * 32, LONG_MAX, a.ldz);
@@ -168,7 +212,8 @@ __global__ __launch_bounds__(kThreads, 1) void full_fwd_kernel(FullFwdArgs a) {
           a.Wt, a.V * E::kElem, a.V, a.dt);
 
   const int ti = row0 + (int)threadIdx.x;
-  FullFwdRow R{-INFINITY, 0.f, -INFINITY, 0.f, 0.f, ti < M};
+  FullFwdRow R{-INFINITY, 0.f, -INFINITY, 0.f, 0.f, 0.f, a.c2, ti < M};
+  if (R.rv && a.tau_rows) R.c2 = (float)(1.4426950408889634 / (double)a.tau_rows[rows[ti]]);
 
   f32x16_t acc_s[4][2], acc_t[4][2];
   for (int vt = tb; vt < te; ++vt) {
@@ -181,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 1) void full_fwd_kernel(FullFwdArgs a) {
   if (R.rv) {
     float4* o = reinterpret_cast<float4*>(a.part) + 2 * ((long)sp * a.part_stride + (a.c0 - a.part_row0) + ti);
     o[0] = make_float4(R.ms, R.ls, R.mt, R.lt);
-    o[1] = make_float4(R.R, 0.f, 0.f, 0.f);
+    o[1] = make_float4(R.R, R.R2, 0.f, 0.f);
   }
 }
 
@@ -212,9 +257,7 @@ __global__ __launch_bounds__(kThreads, 1) void full_dz_kernel(FullDzArgs a) {
   FullDzRow R;
   R.rv = ti < M;
   const long t = R.rv ? rows[ti] : 0;
-  R.Ls2 = R.rv ? a.lse_s[t] * kLog2e : 0.f;
-  R.Lt2 = R.rv ? a.lse_t[t] * kLog2e : 0.f;
-  R.gs = R.rv ? a.g[t] * a.inv_tau : 0.f;
+  R.k = full_dz_const(R.rv, t, a.lse_s, a.lse_t, a.g, a.c2, a.inv_tau, a.mix);
 
   f32x16_t acc_s[4][2], acc_t[4][2];
   for (int vt = tb; vt < te; ++vt) {
@@ -238,17 +281,17 @@ __global__ __launch_bounds__(256) void full_dz_from_z_kernel(FullDzFromZArgs a) 
   float o[EPT];
   if (i < M) {
     const long t = a.c.rows[a.c0 + i];
-    const float Ls2 = a.lse_s[t] * kLog2e, Lt2 = a.lse_t[t] * kLog2e, gs = a.g[t] * a.inv_tau;
+    const FullDzConst k = full_dz_const(true, t, a.lse_s, a.lse_t, a.g, a.c2, a.inv_tau, a.mix);
     const float* sr = a.zs + i * a.ldz + v0;
     const float* ur = a.zt + i * a.ldz + v0;
 #pragma unroll
     for (int e = 0; e < EPT; e += 4) {
       const float4 fs = *reinterpret_cast<const float4*>(sr + e);
       const float4 fu = *reinterpret_cast<const float4*>(ur + e);
-      o[e + 0] = gs * (fast_exp2(fmaf(fs.x, a.c2, -Ls2)) - fast_exp2(fmaf(fu.x, a.c2, -Lt2)));
-      o[e + 1] = gs * (fast_exp2(fmaf(fs.y, a.c2, -Ls2)) - fast_exp2(fmaf(fu.y, a.c2, -Lt2)));
-      o[e + 2] = gs * (fast_exp2(fmaf(fs.z, a.c2, -Ls2)) - fast_exp2(fmaf(fu.z, a.c2, -Lt2)));
-      o[e + 3] = gs * (fast_exp2(fmaf(fs.w, a.c2, -Ls2)) - fast_exp2(fmaf(fu.w, a.c2, -Lt2)));
+      o[e + 0] = k(fs.x, fu.x);
+      o[e + 1] = k(fs.y, fu.y);
+      o[e + 2] = k(fs.z, fu.z);
+      o[e + 3] = k(fs.w, fu.w);
     }
   } else {
 #pragma unroll

@@ -48,9 +48,10 @@ hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8
 hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
                                TopkRowData rd, int64_t T, float* kl, float* lse, int64_t jb, int64_t je,
                                bool zero_masked, hipStream_t st);
+// kl = (1 - r) KL(p||q) + r KL(q||p); kl_rev (nullable) gets KL(q||p).
 hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
-                               int64_t T, float* kl, float* lse_s, float* lse_t, int64_t jb, int64_t je,
-                               bool zero_masked, hipStream_t st);
+                               int64_t T, float r, float* kl, float* lse_s, float* lse_t, float* kl_rev, int64_t jb,
+                               int64_t je, bool zero_masked, hipStream_t st);
 // H^T of one chunk of compacted rows: out[j][i] = H[rows[c0 + i]][j] for
 // i < valid rows of the chunk, 0 up to C.
 hipError_t launch_gather_transpose(const void* H, int elem, int64_t d, Compact c, int64_t c0, int64_t C, void* out,
@@ -128,9 +129,17 @@ struct FullFwdArgs {
   int64_t T, d, dt, V;
   int nrb, S, ntiles;
   int group;  // row blocks per raster group (grouped_coords)
-  float c2;
+  float c2;               // log2(e) / tau
+  const float* tau_rows;  // nullable [T]: per-row temperature, replaces tau
 };
 hipError_t launch_full_fwd(int elem, const FullFwdArgs& a, hipStream_t st);
+
+// Per-row mixing of the backward: dZ = (g/tau) [(1 - r)(q - p) + r q (log q - log p - KLr)].
+struct FullMix {
+  const float* tau_rows;  // nullable [T]
+  const float* kl_rev;    // [T] KL(q||p) of each row (read when r > 0)
+  float r;                // weight of the reverse KL
+};
 
 struct FullDzArgs {
   const char* H;
@@ -147,6 +156,7 @@ struct FullDzArgs {
   int nrb, S, ntiles;
   int group;  // row blocks per raster group (grouped_coords)
   float c2, inv_tau;
+  FullMix mix;
 };
 hipError_t launch_full_dz(int elem, const FullDzArgs& a, hipStream_t st);
 
@@ -164,6 +174,7 @@ struct FullDzFromZArgs {
   const float* lse_t;
   const float* g;
   float c2, inv_tau;
+  FullMix mix;
 };
 hipError_t launch_full_dz_from_z(int elem, const FullDzFromZArgs& a, hipStream_t st);
 

@@ -250,16 +250,19 @@ hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Co
   return hipGetLastError();
 }
 
-// Partials per (split, row): (ms, ls, mt, lt), (R, -, -, -) in base 2; the
+// Partials per (split, row): (ms, ls, mt, lt), (R, R2, -, -) in base 2, with
+// R = sum 2^(yt - mt) (yt - ys) and R2 = sum 2^(ys - ms) (ys - yt); the
 // partial row p holds compacted row jb + p.
 __global__ void full_combine_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask, long T,
-                                    float* kl, float* lse_s, float* lse_t, long jb, long je, int zero_masked) {
+                                    float r, float* kl, float* lse_s, float* lse_t, float* kl_rev, long jb, long je,
+                                    int zero_masked) {
   const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= T) return;
   if (zero_masked && mask != nullptr && mask[j] == 0) {
     kl[j] = 0.f;
     lse_s[j] = 0.f;
     lse_t[j] = 0.f;
+    if (kl_rev) kl_rev[j] = 0.f;
   }
   if (j < jb || j >= je || j >= *c.count) return;
   const float4* pp = reinterpret_cast<const float4*>(part);
@@ -270,28 +273,33 @@ __global__ void full_combine_kernel(const float* part, int S, long stride, Compa
     Ms = fmaxf(Ms, q.x);
     Mt = fmaxf(Mt, q.z);
   }
-  float ls = 0.f, lt = 0.f, R = 0.f;
+  float ls = 0.f, lt = 0.f, R = 0.f, R2 = 0.f;
   for (int s = 0; s < S; ++s) {
     const float4 q = pp[2 * ((long)s * stride + p)];
-    const float r = pp[2 * ((long)s * stride + p) + 1].x;
-    ls += q.y * exp2f(q.x - Ms);
+    const float4 x = pp[2 * ((long)s * stride + p) + 1];
+    const float fs = exp2f(q.x - Ms);
+    ls += q.y * fs;
+    R2 += x.y * fs;
     const float f = exp2f(q.z - Mt);
     lt += q.w * f;
-    R += r * f;
+    R += x.x * f;
   }
   const long t = c.rows[j];
   const float Ls2 = Ms + log2f(ls), Lt2 = Mt + log2f(lt);
   lse_s[t] = Ls2 * kLn2;
   lse_t[t] = Lt2 * kLn2;
-  kl[t] = (R / lt - Lt2 + Ls2) * kLn2;
+  const float fwd = (R / lt - Lt2 + Ls2) * kLn2;
+  const float rev = (R2 / ls - Ls2 + Lt2) * kLn2;
+  kl[t] = r == 0.f ? fwd : (1.f - r) * fwd + r * rev;
+  if (kl_rev) kl_rev[t] = rev;
 }
 
 hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
-                               int64_t T, float* kl, float* lse_s, float* lse_t, int64_t jb, int64_t je,
-                               bool zero_masked, hipStream_t st) {
+                               int64_t T, float r, float* kl, float* lse_s, float* lse_t, float* kl_rev, int64_t jb,
+                               int64_t je, bool zero_masked, hipStream_t st) {
   const dim3 grid((unsigned)((T + 255) / 256));
-  hipLaunchKernelGGL(full_combine_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, (long)T, kl,
-                     lse_s, lse_t, (long)jb, (long)je, zero_masked ? 1 : 0);
+  hipLaunchKernelGGL(full_combine_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, (long)T, r,
+                     kl, lse_s, lse_t, kl_rev, (long)jb, (long)je, zero_masked ? 1 : 0);
   return hipGetLastError();
 }
 

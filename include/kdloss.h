@@ -253,6 +253,47 @@ kd_status kd_full_kl_fwd_bwd(const void* H, const void* Ws, const void* Ht, cons
                              void* dH, float* dWs, int64_t chunk_rows,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- full-vocabulary options
+ * The _ex calls take the arguments of the calls above plus `opts` (NULL or
+ * every field zero = the plain call) and kl_rev [T] float32, the reverse
+ * KL(q || p) of each row: written by the forward calls when not NULL (zero
+ * on masked rows), and read by kd_full_kl_bwd_ex, which needs the forward
+ * call's values when rev_weight > 0 (KD_ERR_INVALID_ARG if NULL then).  The
+ * backward call must get the same options as the forward call.  Per valid
+ * row t, with tau_t = tau_rows[t] (else tau), s = z / tau_t, u = Ht_t.Wt / tau_t,
+ * q = softmax(s), p = softmax(u) and r = rev_weight:
+ *   kl_t = (1 - r) KL(p || q) + r KL(q || p)
+ *   dZ_t = (g_t / tau_t) [(1 - r)(q - p) + r q (log q - log p - KL(q || p))]
+ * (KL mixing of the forward and reverse token-level KL: the KL-direction
+ * abstract, thelatestinai.com/papers/2606.20005; per-token temperature: the
+ * adaptive-distillation abstract on the WASD page).  The forward tiles keep
+ * both running sums, so no option changes the tiles' work.  Argument
+ * errors: rev_weight outside [0, 1] or not finite: KD_ERR_INVALID_ARG;
+ * misaligned tau_rows or kl_rev: KD_ERR_ALIGNMENT.  tau_rows values must be
+ * finite and > 0 on valid rows (not checked). */
+typedef struct kd_full_opts {
+  const float* tau_rows;  /* [T] per-token temperature, or NULL */
+  float rev_weight;       /* weight r of the reverse KL in [0, 1]; 0 = forward KL */
+} kd_full_opts;
+
+kd_status kd_full_kl_fwd_ex(const void* H, const void* Ws, const void* Ht, const void* Wt,
+                            const uint8_t* mask, float tau, const kd_full_opts* opts,
+                            int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                            float* kl, float* lse_s, float* lse_t, float* kl_rev,
+                            void* workspace, size_t workspace_bytes, void* stream);
+kd_status kd_full_kl_bwd_ex(const void* H, const void* Ws, const void* Ht, const void* Wt,
+                            const uint8_t* mask, float tau, const kd_full_opts* opts,
+                            int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                            const float* lse_s, const float* lse_t, const float* kl_rev,
+                            const float* grad_kl, void* dH, float* dWs, int64_t chunk_rows,
+                            void* workspace, size_t workspace_bytes, void* stream);
+kd_status kd_full_kl_fwd_bwd_ex(const void* H, const void* Ws, const void* Ht, const void* Wt,
+                                const uint8_t* mask, float tau, const kd_full_opts* opts,
+                                int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                                const float* grad_kl, float* kl, float* lse_s, float* lse_t,
+                                float* kl_rev, void* dH, float* dWs, int64_t chunk_rows,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- errors, version */
 
 const char* kd_status_string(kd_status s);

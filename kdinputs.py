@@ -235,6 +235,18 @@ def add_topk_options(inp, tau_rows=False, partial_mass=False, labels=False, ce_w
     return out
 
 
+def add_full_options(inp, tau_rows=False, rev_weight=0.0, number=0):
+    """Options of the full-vocabulary loss added to a make_full dict:
+    tau_rows [T] float32 uniform in [0.5, 2) (per-token temperature) and the
+    weight of the reverse KL."""
+    out = dict(inp)
+    if tau_rows:
+        rng = np.random.Generator(np.random.PCG64(ROLE_TAU + 100 * number))
+        out["tau_rows"] = torch.from_numpy(rng.uniform(0.5, 2.0, inp["H"].shape[0]).astype(np.float32))
+    out["rev_weight"] = float(rev_weight)
+    return out
+
+
 def make_full(T, d, dt, V, dtype, tau=1.0, mask="none", number=0, g="mean", n_masked=None):
     """Inputs of the full-vocabulary loss as CPU tensors: H [T,d], Ws [d,V],
     Ht [T,dt], Wt [dt,V], mask, g, tau.  Each head is N(0, 1/its own width)."""

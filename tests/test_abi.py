@@ -29,7 +29,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 20
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), f"{n} declared in kdloss.h but not exported"
     assert sorted(kdl.EXPORTS) == names
@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
 def test_status_strings_and_version(L):
     for code, name in kdl._binding.STATUS.items():
         assert L.kd_status_string(code).decode() == name
-    assert L.kd_version() == 10300
+    assert L.kd_version() == 10400
 
 
 # ---------------------------------------------------------------- workspace sizing
@@ -290,3 +290,41 @@ def test_topk_ex_calls_check_their_options_too(L):
     assert L.kd_topk_kl_fwd_bwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), bad, 8, 64,
                                    256, 4, kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(FAKE), None, vp(FAKE), vp(FAKE), 0,
                                    vp(FAKE), 0, None) == 1
+
+
+# ---------------------------------------------------------------- full-vocabulary options
+def full_fwd_ex(o, kl_rev=FAKE, wsb=0):
+    vp = ctypes.c_void_p
+    ref = None if o is None else ctypes.byref(o)
+    return kdl.lib().kd_full_kl_fwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), ref, 8, 64,
+                                       64, 256, kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(FAKE),
+                                       vp(kl_rev) if kl_rev else None, vp(FAKE), wsb, None)
+
+
+def full_bwd_ex(o, kl_rev=FAKE):
+    vp = ctypes.c_void_p
+    ref = None if o is None else ctypes.byref(o)
+    return kdl.lib().kd_full_kl_bwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), ref, 8, 64,
+                                       64, 256, kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(kl_rev) if kl_rev else None,
+                                       vp(FAKE), vp(FAKE), vp(FAKE), 0, vp(FAKE), 0, None)
+
+
+def fopts(tau_rows=0, rev_weight=0.0):
+    return kdl._binding.KdFullOpts(tau_rows or None, rev_weight)
+
+
+@pytest.mark.parametrize("o,kr,code", [
+    (fopts(rev_weight=-0.5), FAKE, 1), (fopts(rev_weight=1.01), FAKE, 1), (fopts(rev_weight=math.nan), FAKE, 1),
+    (fopts(tau_rows=FAKE + 2), FAKE, 3), (fopts(), FAKE + 2, 3),
+    (fopts(rev_weight=0.5), 0, 4), (fopts(tau_rows=FAKE, rev_weight=1.0), FAKE, 4), (None, 0, 4),
+])
+def test_full_options_checks(L, o, kr, code):
+    assert full_fwd_ex(o, kl_rev=kr) == code
+    assert last_error() != ""
+
+
+def test_full_backward_needs_kl_rev_when_mixing(L):
+    assert full_bwd_ex(fopts(rev_weight=0.5), kl_rev=0) == 1
+    assert "kl_rev" in last_error()
+    assert full_bwd_ex(fopts(rev_weight=0.5)) == 4
+    assert full_bwd_ex(fopts(), kl_rev=0) == 4
