@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the packed and full-vocabulary workloads")
     ap.add_argument("--one-call", action="store_true",
                     help="full-vocabulary workload: time the single forward + backward call")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--sweep", action="store_true", help="T in 4096, 16384, 65536, 262144: one line each")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 4 times (calibrates HBM byte counters)")
