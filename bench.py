@@ -32,7 +32,8 @@ if ROOT not in sys.path:
 
 METRIC = "fused KL fwd+bwd tokens/s (d=3072,V=128256) + % bf16 MFMA peak; peak extra HBM"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
-TILE_KERNELS = ("topk_fwd_tile", "topk_dz_tile", "full_fwd_tile", "full_dz_tile", "dh_tile", "dw_tile")
+TILE_KERNELS = ("topk_fwd_tile", "topk_dz_tile", "full_fwd_tile", "full_dz_tile", "full_teacher_tile", "full_student_tile",
+                "dh_tile", "dw_tile")
 
 
 def parse():
@@ -281,6 +282,7 @@ def run_full(p, steps: int, warmup: int, chunk_rows: int, one_call: bool = False
     peak_extra = torch.cuda.max_memory_allocated() - base + (0 if one_call else 2 * T * 4)  # + saved lse_s, lse_t
     ms, prof = timed(step, steps, warmup)
     fl = {"full_fwd_tile": 2.0 * T * (d + dt) * V, "full_dz_tile": 2.0 * T * (d + dt) * V,
+          "full_teacher_tile": 2.0 * T * dt * V, "full_student_tile": 2.0 * T * d * V,
           "dh_tile": 2.0 * T * d * V, "dw_tile": 2.0 * T * d * V}
     dom, achieved = dominant(prof, fl, steps)
     credited = (2.0 * (d + dt) + 4.0 * d) * V * T

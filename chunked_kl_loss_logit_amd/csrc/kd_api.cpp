@@ -218,11 +218,13 @@ struct FullPlan {
   size_t o_rows, o_count, o_part;
   ChunkPlan ch;
   size_t fwd_total, total;
-  // single-call forward + backward: per-chunk partials, the chunk's fp32
-  // student and teacher logits and the backward chunk buffers
-  int S_c;
+  // single-call forward + backward: each head through the 256-wide top-K
+  // tiles (per-chunk split partials of both, per-row constants, a dummy
+  // entry list), the chunk's fp32 logits of both heads, the elementwise
+  // pass's per-row terms, per-row reverse KL, and the backward chunk buffers
+  int S_c, nblk;
   ChunkPlan ch_f;
-  size_t o_part_c, o_zs, o_zt, o_krev, fused_total;
+  size_t o_part_s, o_part_t, o_rowc, o_pair0, o_zs, o_zt, o_terms, o_krev, fused_total;
 };
 
 FullPlan plan_full(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows) {
@@ -239,11 +241,17 @@ FullPlan plan_full(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows
   p.fwd_total = fw.off;
   p.total = std::max(fw.off, bw.off);
   Carver fu = cv;
-  p.S_c = splits_for(cdiv(chunk_of(T, chunk_rows), kd::kTileM), p.ntiles);
-  p.o_part_c = fu.take((size_t)p.S_c * chunk_of(T, chunk_rows) * 32);
+  const int64_t C = chunk_of(T, chunk_rows);
+  p.S_c = splits_for(cdiv(C, kd::kTileM), cdiv(V, kd::kTileN));
+  p.nblk = kd::full_from_z_blocks(elem, V);
+  p.o_part_s = fu.take((size_t)p.S_c * C * 16);
+  p.o_part_t = fu.take((size_t)p.S_c * C * 16);
+  p.o_rowc = fu.take((size_t)T * 16);
+  p.o_pair0 = fu.take(16);
   p.ch_f = plan_chunk(T, d, V, elem, chunk_rows, fu);
   p.o_zs = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
   p.o_zt = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
+  p.o_terms = fu.take((size_t)C * p.nblk * 8);
   p.o_krev = fu.take((size_t)T * 4);
   p.fused_total = fu.off;
   return p;
@@ -798,10 +806,12 @@ kd_status kd_full_kl_fwd_bwd_ex(const void* H, const void* Ws, const void* Ht, c
   KD_TRY(check_workspace(workspace, workspace_bytes, p.fused_total));
 
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
-  float* part = at<float>(workspace, p.o_part_c);
+  float* part_s = at<float>(workspace, p.o_part_s);
+  float* part_t = at<float>(workspace, p.o_part_t);
   float* zs = at<float>(workspace, p.o_zs);
   float* zt = at<float>(workspace, p.o_zt);
-  // the reverse KL of each row feeds its dZ: the caller's array, else the workspace's
+  float2* terms = at<float2>(workspace, p.o_terms);
+  // the reverse KL of each row feeds its dZ when mixing: the caller's array, else the workspace's
   float* krev = kl_rev ? kl_rev : at<float>(workspace, p.o_krev);
   mx.kl_rev = krev;
   const ChunkPlan& ch = p.ch_f;
@@ -809,47 +819,54 @@ kd_status kd_full_kl_fwd_bwd_ex(const void* H, const void* Ws, const void* Ht, c
   char* hT = at<char>(workspace, ch.o_hT);
   float* dhp = at<float>(workspace, ch.o_dhp);
   const float c2 = (float)(1.4426950408889634 / (double)tau);
+  // each head goes through the top-K forward tiles with no cached entries:
+  // the per-row constants are the temperatures', the entry list is empty
+  const kd::TopkRowData rd{at<int2>(workspace, p.o_pair0), nullptr, nullptr, at<float4>(workspace, p.o_rowc)};
 
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
   KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * elem, dH, st));
+  KD_LAUNCH("fill_zero", st, kd::launch_fill_zero(rd.pair, 16, st));
+  KD_LAUNCH("full_rowc", st, kd::launch_full_rowc(c, T, mx.tau_rows, c2, 1.0f / tau, rd.rowc, st));
   const int64_t nchunks = cdiv(T, ch.C);
   for (int64_t k = 0; k < nchunks; ++k) {
     const int64_t c0 = k * ch.C;
-    // both heads' logits of the chunk: the coupled partials, kept in fp32
-    kd::FullFwdArgs a{};
-    a.H = static_cast<const char*>(H);
-    a.Ws = static_cast<const char*>(Ws);
-    a.Ht = static_cast<const char*>(Ht);
-    a.Wt = static_cast<const char*>(Wt);
-    a.c = c;
-    a.part = part;
-    a.part_stride = ch.C;
-    a.part_row0 = c0;
-    a.c0 = c0;
-    a.C = ch.C;
-    a.zs = zs;
-    a.zt = zt;
-    a.ldz = ch.ldz;
-    a.T = T;
-    a.d = d;
-    a.dt = dt_hidden;
-    a.V = V;
-    a.nrb = ch.nrb_c;
-    a.S = p.S_c;
-    a.ntiles = p.ntiles;
-    a.group = kRasterGroup;
-    a.c2 = c2;
-    a.tau_rows = mx.tau_rows;
-    KD_LAUNCH("full_fwd_tile", st, kd::launch_full_fwd(elem, a, st));
-    KD_LAUNCH("full_combine", st,
-              kd::launch_full_combine(part, p.S_c, ch.C, c, mask, T, mx.r, kl, lse_s, lse_t, krev, c0, c0 + ch.C,
-                                      k == 0, st));
-    // dZ from the kept logits: no second pair of projections
-    kd::FullDzFromZArgs za{};
+    // the chunk's logits of each head, kept in fp32, and each head's log Z partials
+    for (int head = 0; head < 2; ++head) {
+      kd::TopkFwdArgs a{};
+      a.H = static_cast<const char*>(head ? Ht : H);
+      a.W = static_cast<const char*>(head ? Wt : Ws);
+      a.c = c;
+      a.rd = rd;
+      a.part = head ? part_t : part_s;
+      a.part_stride = ch.C;
+      a.part_row0 = c0;
+      a.c0 = c0;
+      a.C = ch.C;
+      a.zout = head ? zt : zs;
+      a.ldz = ch.ldz;
+      a.T = T;
+      a.d = head ? dt_hidden : d;
+      a.V = V;
+      a.K = 0;
+      a.Kz = 0;
+      a.nrb = ch.nrb_c;
+      a.S = p.S_c;
+      a.ntiles = (int)cdiv(V, kd::kTileN);
+      a.group = kRasterGroup;
+      KD_LAUNCH(head ? "full_teacher_tile" : "full_student_tile", st, kd::launch_topk_fwd(elem, a, st));
+    }
+    KD_LAUNCH("full_lse_combine", st,
+              kd::launch_full_lse_combine(part_s, part_t, p.S_c, ch.C, c, mask, T, kl, lse_s, lse_t, kl_rev, c0,
+                                          c0 + ch.C, k == 0, st));
+    // one pass over the kept logits: both KL terms with the final
+    // normalisers and dZ (no second pair of projections); with the reverse
+    // KL in the mix, dZ needs the row's reverse KL first, so the terms come
+    // from a pass of their own
+    kd::FullFromZArgs za{};
     za.zs = zs;
     za.zt = zt;
-    za.dz = dz;
     za.ldz = ch.ldz;
+    za.nblk = p.nblk;
     za.c = c;
     za.c0 = c0;
     za.C = ch.C;
@@ -860,7 +877,16 @@ kd_status kd_full_kl_fwd_bwd_ex(const void* H, const void* Ws, const void* Ht, c
     za.c2 = c2;
     za.inv_tau = 1.0f / tau;
     za.mix = mx;
-    KD_LAUNCH("full_dz_from_z", st, kd::launch_full_dz_from_z(elem, za, st));
+    za.terms = terms;
+    za.dz = mx.r != 0.f ? nullptr : dz;
+    KD_LAUNCH("full_from_z", st, kd::launch_full_from_z(elem, za, st));
+    KD_LAUNCH("full_kl_from_terms", st,
+              kd::launch_full_kl_from_terms(terms, p.nblk, c, lse_s, lse_t, mx.r, kl, krev, c0, c0 + ch.C, st));
+    if (mx.r != 0.f) {
+      za.terms = nullptr;
+      za.dz = dz;
+      KD_LAUNCH("full_from_z", st, kd::launch_full_from_z(elem, za, st));
+    }
     KD_TRY(grad_chunk(H, Ws, dH, dWs, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
   }
   return KD_OK;

@@ -153,20 +153,11 @@ __device__ inline void stage_pair(const Slots& sl, const f32x16_t (&acc_s)[4][2]
 
 template <int NBI>
 __device__ inline void full_fwd_round(const Slots& sl, const f32x16_t (&acc_s)[4][2],
-                                      const f32x16_t (&acc_t)[4][2], long n0, FullFwdRow& R, const FullFwdArgs& a,
-                                      long row0, long M) {
+                                      const f32x16_t (&acc_t)[4][2], long n0, FullFwdRow& R, const FullFwdArgs& a) {
   stage_pair<NBI>(sl, acc_s, acc_t);
   __syncthreads();
   R.consume(st_pair<0>(sl), st_pair<2>(sl), n0 + NBI * 32, a.V);
   R.consume(st_pair<1>(sl), st_pair<3>(sl), n0 + 64 + NBI * 32, a.V);
-  if (a.zs) {  // the consume only read the staged blocks: the logits go out as they are
-    char* zs = reinterpret_cast<char*>(a.zs);
-    char* zt = reinterpret_cast<char*>(a.zt);
-    store_block<F32>(st_pair<0>(sl), zs, a.ldz, row0, n0 + NBI * 32, M, a.ldz);
-    store_block<F32>(st_pair<1>(sl), zs, a.ldz, row0, n0 + 64 + NBI * 32, M, a.ldz);
-    store_block<F32>(st_pair<2>(sl), zt, a.ldz, row0, n0 + NBI * 32, M, a.ldz);
-    store_block<F32>(st_pair<3>(sl), zt, a.ldz, row0, n0 + 64 + NBI * 32, M, a.ldz);
-  }
   __syncthreads();
 }
 
@@ -186,8 +177,7 @@ __device__ inline void full_dz_round(const Slots& sl, const f32x16_t (&acc_s)[4]
 }  // namespace
 
 // Rows: the compacted valid rows [c0, c0 + C) (the plain forward takes them
-// all); partials are indexed by compacted position, and with zs set both
-// tiles' logits are also written out, fp32, one row per compacted row.
+// all); partials are indexed by compacted position.
 template <class Main, class E>
 __global__ __launch_bounds__(kThreads, 1) void full_fwd_kernel(FullFwdArgs a) {
   KD_DECLARE_SLOTS(sl);
@@ -220,8 +210,8 @@ __global__ __launch_bounds__(kThreads, 1) void full_fwd_kernel(FullFwdArgs a) {
     const long n0 = (long)vt * kBN;
     mt.tile(sl, n0, acc_t);
     ms.tile(sl, n0, acc_s);
-    full_fwd_round<0>(sl, acc_s, acc_t, n0, R, a, row0, M);
-    full_fwd_round<1>(sl, acc_s, acc_t, n0, R, a, row0, M);
+    full_fwd_round<0>(sl, acc_s, acc_t, n0, R, a);
+    full_fwd_round<1>(sl, acc_s, acc_t, n0, R, a);
   }
   if (R.rv) {
     float4* o = reinterpret_cast<float4*>(a.part) + 2 * ((long)sp * a.part_stride + (a.c0 - a.part_row0) + ti);
@@ -269,17 +259,40 @@ __global__ __launch_bounds__(kThreads, 1) void full_dz_kernel(FullDzArgs a) {
   }
 }
 
-// One thread: EPT consecutive columns (16 bytes of dZ) of one row, the same
-// formula as the recomputing tile's epilogue.
+// ---------------------------------------------------------------- single call
+__global__ void full_rowc_kernel(Compact c, long T, const float* tau_rows, float c2, float inv_tau, float4* rowc) {
+  const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= T || j >= *c.count) return;
+  const long t = c.rows[j];
+  if (tau_rows) {
+    const float tt = tau_rows[t];
+    c2 = (float)(1.4426950408889634 / (double)tt);
+    inv_tau = 1.0f / tt;
+  }
+  rowc[t] = make_float4(c2, inv_tau, 1.f, 0.f);
+}
+
+hipError_t launch_full_rowc(Compact c, int64_t T, const float* tau_rows, float c2, float inv_tau, float4* rowc,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(full_rowc_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, c, (long)T, tau_rows, c2,
+                     inv_tau, rowc);
+  return hipGetLastError();
+}
+
+// One thread: EPT consecutive columns (16 bytes of dZ) of one row; the block
+// (256 threads, one row) also sums the row's two KL terms over its columns,
+// in a fixed order, for the terms array.
 template <class E>
-__global__ __launch_bounds__(256) void full_dz_from_z_kernel(FullDzFromZArgs a) {
+__global__ __launch_bounds__(256) void full_from_z_kernel(FullFromZArgs a) {
   constexpr int EPT = E::kEpc;
+  __shared__ float2 red[4];
   const long i = blockIdx.y;  // row of the chunk
   const long v0 = ((long)blockIdx.x * 256 + threadIdx.x) * EPT;
-  if (v0 >= a.V) return;
   const long M = min(a.C, (long)*a.c.count - a.c0);
+  const bool in = v0 < a.V;
   float o[EPT];
-  if (i < M) {
+  float tp = 0.f, tq = 0.f;  // sum p (yt - ys), sum q (ys - yt), base 2
+  if (i < M && in) {
     const long t = a.c.rows[a.c0 + i];
     const FullDzConst k = full_dz_const(true, t, a.lse_s, a.lse_t, a.g, a.c2, a.inv_tau, a.mix);
     const float* sr = a.zs + i * a.ldz + v0;
@@ -288,32 +301,59 @@ __global__ __launch_bounds__(256) void full_dz_from_z_kernel(FullDzFromZArgs a) 
     for (int e = 0; e < EPT; e += 4) {
       const float4 fs = *reinterpret_cast<const float4*>(sr + e);
       const float4 fu = *reinterpret_cast<const float4*>(ur + e);
-      o[e + 0] = k(fs.x, fu.x);
-      o[e + 1] = k(fs.y, fu.y);
-      o[e + 2] = k(fs.z, fu.z);
-      o[e + 3] = k(fs.w, fu.w);
+      const float s4[4] = {fs.x, fs.y, fs.z, fs.w}, u4[4] = {fu.x, fu.y, fu.z, fu.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        o[e + q] = k(s4[q], u4[q]);
+        const float ds = fmaf(s4[q], k.c2, -k.Ls2), dt = fmaf(u4[q], k.c2, -k.Lt2);
+        const float dy = (u4[q] - s4[q]) * k.c2;  // yt - ys
+        tp = fmaf(fast_exp2(dt), dy, tp);
+        tq = fmaf(fast_exp2(ds), -dy, tq);
+      }
     }
   } else {
 #pragma unroll
     for (int q = 0; q < EPT; ++q) o[q] = 0.f;
   }
-  char* dst = a.dz + (i * a.ldz + v0) * E::kElem;
-  if constexpr (EPT == 8) {
-    const u32x4_t w{Bf16::pack2(o[0], o[1]), Bf16::pack2(o[2], o[3]), Bf16::pack2(o[4], o[5]),
-                    Bf16::pack2(o[6], o[7])};
-    *reinterpret_cast<u32x4_t*>(dst) = w;
-  } else {
-    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+  if (a.dz && in) {
+    char* dst = a.dz + (i * a.ldz + v0) * E::kElem;
+    if constexpr (EPT == 8) {
+      const u32x4_t w{Bf16::pack2(o[0], o[1]), Bf16::pack2(o[2], o[3]), Bf16::pack2(o[4], o[5]),
+                      Bf16::pack2(o[6], o[7])};
+      *reinterpret_cast<u32x4_t*>(dst) = w;
+    } else {
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  if (a.terms == nullptr || i >= M) return;  // uniform over the block
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    tp += __shfl_xor(tp, off);
+    tq += __shfl_xor(tq, off);
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(tp, tq);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float2 r = red[0];
+    for (int w = 1; w < 4; ++w) {
+      r.x += red[w].x;
+      r.y += red[w].y;
+    }
+    a.terms[i * a.nblk + blockIdx.x] = r;
   }
 }
 
-hipError_t launch_full_dz_from_z(int elem, const FullDzFromZArgs& a, hipStream_t st) {
+int full_from_z_blocks(int elem, int64_t V) {
   const int ept = elem == 2 ? Bf16::kEpc : F32::kEpc;
-  const dim3 grid((unsigned)((a.V + 256L * ept - 1) / (256L * ept)), (unsigned)a.C), block(256);
+  return (int)((V + 256L * ept - 1) / (256L * ept));
+}
+
+hipError_t launch_full_from_z(int elem, const FullFromZArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)full_from_z_blocks(elem, a.V), (unsigned)a.C), block(256);
   if (elem == 2)
-    hipLaunchKernelGGL(full_dz_from_z_kernel<Bf16>, grid, block, 0, st, a);
+    hipLaunchKernelGGL(full_from_z_kernel<Bf16>, grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(full_dz_from_z_kernel<F32>, grid, block, 0, st, a);
+    hipLaunchKernelGGL(full_from_z_kernel<F32>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

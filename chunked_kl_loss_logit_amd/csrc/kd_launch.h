@@ -123,9 +123,6 @@ struct FullFwdArgs {
   float* part;     // [S][part_stride][8], row p of a split is compacted row part_row0 + p
   int64_t part_stride, part_row0;
   int64_t c0, C;   // compacted rows [c0, c0 + C) (all rows: 0, T)
-  float* zs;       // nullable: student logits of those rows, fp32 [C][ldz]
-  float* zt;       // teacher logits, same layout (set together with zs)
-  int64_t ldz;
   int64_t T, d, dt, V;
   int nrb, S, ntiles;
   int group;  // row blocks per raster group (grouped_coords)
@@ -160,14 +157,32 @@ struct FullDzArgs {
 };
 hipError_t launch_full_dz(int elem, const FullDzArgs& a, hipStream_t st);
 
-// dZ of a chunk from its stored fp32 student and teacher logits:
-// dz[i][v] = (g/tau) (2^(zs c2 - Ls2) - 2^(zt c2 - Lt2)) for the chunk's
-// valid rows i and v < V; zero for the chunk's other rows.
-struct FullDzFromZArgs {
+// ---------------------------------------------------------------- full vocabulary, single call
+// The single call runs each head through the top-K forward tiles (no cached
+// entries, logits kept) and then one elementwise pass over the chunk's two
+// stored logit arrays.  Per-row constants of those tiles: rowc[t] =
+// (log2(e) / tau_t, 1 / tau_t, 1, 0) for every valid row.
+hipError_t launch_full_rowc(Compact c, int64_t T, const float* tau_rows, float c2, float inv_tau, float4* rowc,
+                            hipStream_t st);
+// lse_s, lse_t of compacted rows [jb, je) from the student's and teacher's
+// split partials (m2, l, -, -), partial row p = compacted row jb + p; with
+// zero_masked, also zeroes kl, lse_s, lse_t and kl_rev (nullable) of masked rows.
+hipError_t launch_full_lse_combine(const float* part_s, const float* part_t, int S, int64_t part_stride, Compact c,
+                                   const uint8_t* mask, int64_t T, float* kl, float* lse_s, float* lse_t,
+                                   float* kl_rev, int64_t jb, int64_t je, bool zero_masked, hipStream_t st);
+
+// Elementwise pass over a chunk's stored fp32 logits (both heads): per chunk
+// row i and block b of 256 * EPT columns, terms[i][b] = (sum p (yt - ys),
+// sum q (ys - yt)) in base 2 with the final log-normalisers, and (dz set) dZ
+// as the recomputing tile's epilogue writes it; dZ is zero on rows past the
+// chunk's valid rows.
+struct FullFromZArgs {
   const float* zs;   // [C][ldz]
   const float* zt;   // [C][ldz]
-  char* dz;          // [C][ldz], element type
   int64_t ldz;
+  char* dz;          // nullable: [C][ldz], element type
+  float2* terms;     // nullable: [C][nblk]
+  int nblk;
   Compact c;
   int64_t c0, C, V;
   const float* lse_s;
@@ -176,7 +191,12 @@ struct FullDzFromZArgs {
   float c2, inv_tau;
   FullMix mix;
 };
-hipError_t launch_full_dz_from_z(int elem, const FullDzFromZArgs& a, hipStream_t st);
+int full_from_z_blocks(int elem, int64_t V);
+hipError_t launch_full_from_z(int elem, const FullFromZArgs& a, hipStream_t st);
+// kl (and kl_rev, nullable) of compacted rows [jb, je) from the pass's terms.
+hipError_t launch_full_kl_from_terms(const float2* terms, int nblk, Compact c, const float* lse_s,
+                                     const float* lse_t, float r, float* kl, float* kl_rev, int64_t jb, int64_t je,
+                                     hipStream_t st);
 
 // ---------------------------------------------------------------- gradient contractions
 // part[s][i][j] = sum over the s-th vocabulary range of dz[i][v] * W[j][v]

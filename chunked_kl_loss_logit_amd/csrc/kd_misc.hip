@@ -303,6 +303,75 @@ hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Co
   return hipGetLastError();
 }
 
+// Single call, full vocabulary: the two heads' log-normalisers from the
+// top-K tiles' split partials (m2, l, -, -) of each head.
+__global__ void full_lse_combine_kernel(const float* part_s, const float* part_t, int S, long stride, Compact c,
+                                        const uint8_t* mask, long T, float* kl, float* lse_s, float* lse_t,
+                                        float* kl_rev, long jb, long je, int zero_masked) {
+  const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= T) return;
+  if (zero_masked && mask != nullptr && mask[j] == 0) {
+    kl[j] = 0.f;
+    lse_s[j] = 0.f;
+    lse_t[j] = 0.f;
+    if (kl_rev) kl_rev[j] = 0.f;
+  }
+  if (j < jb || j >= je || j >= *c.count) return;
+  const float4* ps = reinterpret_cast<const float4*>(part_s) + (j - jb);
+  const float4* pt = reinterpret_cast<const float4*>(part_t) + (j - jb);
+  float Ms = -INFINITY, Mt = -INFINITY;
+  for (int s = 0; s < S; ++s) {
+    Ms = fmaxf(Ms, ps[(long)s * stride].x);
+    Mt = fmaxf(Mt, pt[(long)s * stride].x);
+  }
+  float ls = 0.f, lt = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float4 a = ps[(long)s * stride], b = pt[(long)s * stride];
+    ls += a.y * exp2f(a.x - Ms);
+    lt += b.y * exp2f(b.x - Mt);
+  }
+  const long t = c.rows[j];
+  lse_s[t] = (Ms + log2f(ls)) * kLn2;
+  lse_t[t] = (Mt + log2f(lt)) * kLn2;
+}
+
+hipError_t launch_full_lse_combine(const float* part_s, const float* part_t, int S, int64_t part_stride, Compact c,
+                                   const uint8_t* mask, int64_t T, float* kl, float* lse_s, float* lse_t,
+                                   float* kl_rev, int64_t jb, int64_t je, bool zero_masked, hipStream_t st) {
+  hipLaunchKernelGGL(full_lse_combine_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, part_s, part_t, S,
+                     (long)part_stride, c, mask, (long)T, kl, lse_s, lse_t, kl_rev, (long)jb, (long)je,
+                     zero_masked ? 1 : 0);
+  return hipGetLastError();
+}
+
+// KL(p||q) = ln2 sum p (yt - ys) - Lt + Ls and KL(q||p) = ln2 sum q (ys - yt) - Ls + Lt
+// per valid row, the sums taken over the terms' column blocks in order.
+__global__ void full_kl_from_terms_kernel(const float2* terms, int nblk, Compact c, const float* lse_s,
+                                          const float* lse_t, float r, float* kl, float* kl_rev, long jb, long je) {
+  const long j = jb + (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= je || j >= *c.count) return;
+  const float2* tr = terms + (j - jb) * nblk;
+  float a = 0.f, b = 0.f;
+  for (int k = 0; k < nblk; ++k) {
+    a += tr[k].x;
+    b += tr[k].y;
+  }
+  const long t = c.rows[j];
+  const float d = lse_s[t] - lse_t[t];
+  const float fwd = a * kLn2 + d, rev = b * kLn2 - d;
+  kl[t] = r == 0.f ? fwd : (1.f - r) * fwd + r * rev;
+  if (kl_rev) kl_rev[t] = rev;
+}
+
+hipError_t launch_full_kl_from_terms(const float2* terms, int nblk, Compact c, const float* lse_s,
+                                     const float* lse_t, float r, float* kl, float* kl_rev, int64_t jb, int64_t je,
+                                     hipStream_t st) {
+  const int64_t n = je - jb;
+  hipLaunchKernelGGL(full_kl_from_terms_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, terms, nblk, c,
+                     lse_s, lse_t, r, kl, kl_rev, (long)jb, (long)je);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ chunk plumbing
 // out[j][i] = H[rows[c0 + i]][j] for i < M (valid rows of the chunk), 0 for
 // M <= i < C.  64 x 64 tiles through LDS.

@@ -238,12 +238,14 @@ kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const vo
 
 /* Forward and backward in one call, when grad_kl is known up front.  Same
  * arguments and outputs as kd_full_kl_fwd followed by kd_full_kl_bwd with
- * the same chunk_rows, and the same bits: each chunk's forward keeps both
- * heads' logits (fp32, in the workspace), so dZ comes from them instead of
- * from recomputing both projections (the trade of §3 "Fused chunked KL",
- * made the other way).  That costs 2 * C * roundup(V, 256) * 4 more
- * workspace bytes for a chunk of C rows; kd_full_kl_fwd_bwd_workspace_size
- * gives the size.  T = 0 sets dWs to zero and touches nothing else. */
+ * the same chunk_rows, equal up to rounding: each chunk's two projections
+ * run one head at a time through the 256-column top-K tiles, which keep the
+ * logits (fp32, in the workspace); one elementwise pass over them then gives
+ * both KL terms with the final log-normalisers and dZ, instead of
+ * recomputing both projections (the trade of §3 "Fused chunked KL", made the
+ * other way).  That costs 2 * C * roundup(V, 256) * 4 more workspace bytes
+ * for a chunk of C rows; kd_full_kl_fwd_bwd_workspace_size gives the size.
+ * T = 0 sets dWs to zero and touches nothing else. */
 kd_status kd_full_kl_fwd_bwd_workspace_size(int64_t T, int64_t d, int64_t dt_hidden, int64_t V,
                                             kd_dtype dt, int64_t chunk_rows, size_t* bytes);
 kd_status kd_full_kl_fwd_bwd(const void* H, const void* Ws, const void* Ht, const void* Wt,

@@ -2,11 +2,13 @@
 kd_full_kl_fwd_bwd).
 
 Each computes what its forward call followed by its backward call computes,
-from the chunk's kept fp32 logits instead of a second projection.  When one
-chunk holds every row, the vocabulary splits and every formula are the same
-as in the two-call path, so the outputs must be bit-identical to it; with
-several chunks the split count per chunk differs and the outputs are checked
-against the fp64 oracle instead.
+from the chunk's kept fp32 logits instead of a second projection.  Top-K:
+when one chunk holds every row, the vocabulary splits and every formula are
+the same as in the two-call path, so the outputs must be bit-identical to it;
+with several chunks the split count per chunk differs and the outputs are
+checked against the fp64 oracle instead.  Full vocabulary: the single call
+takes each head through its own 256-column tiles, so it is checked against
+the oracle (and the two-call path) within the tolerances.
 """
 import numpy as np
 import pytest
@@ -92,19 +94,46 @@ def run_full_fused(inp, chunk_rows=0):
                 dH=dH.cpu().double().numpy(), dW=dW.cpu().double().numpy())
 
 
+def check_full(got, inp, dtype):
+    kl, lse_s, lse_t = O.full_kl_forward(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], inp["mask"], inp["tau"])
+    dH, dW = O.full_kl_backward(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], inp["mask"], inp["tau"], inp["g"])
+    T = kl.shape[0]
+    v = np.ones(T, bool) if inp["mask"] is None else inp["mask"].numpy() != 0
+    assert_kl(got["kl"], kl, dtype, v)
+    assert_lse(got["lse_s"], lse_s, dtype, v)
+    assert_lse(got["lse_t"], lse_t, dtype, v)
+    for k in ("kl", "lse_s", "lse_t", "dH"):
+        assert np.all(got[k][~v] == 0), k
+    assert_grad(got["dH"], dH, dtype, "dH")
+    assert_grad(got["dW"], dW, dtype, "dWs")
+
+
+# The single call takes each head through the 256-column top-K tiles and the
+# KL terms from the exact normalisers, so it matches the two-call path (and
+# the oracle) within rounding, not bit for bit.
 @pytest.mark.parametrize("dtype,T,d,dt,V,tau,mask", [
     (torch.bfloat16, 512, 3072, 4096, 128256, 1.0, "none"),   # the heads of the full-vocabulary workload
     (torch.bfloat16, 700, 384, 256, 1288, 1.3, "random10"),   # direct-load, ragged last vocabulary tile, masked
     (torch.bfloat16, 300, 136, 72, 1032, 1.0, "none"),        # general mainloop, ragged everything
     (torch.float32, 513, 64, 128, 520, 0.8, "random10"),      # fp32 matrix cores
 ])
-def test_full_single_chunk_matches_two_calls_bitwise(dtype, T, d, dt, V, tau, mask):
+def test_full_single_chunk_matches_the_oracle_and_two_calls(dtype, T, d, dt, V, tau, mask):
     inp = G.make_full(T, d, dt, V, dtype, tau=tau, mask=mask, number=26, g="normal")
-    say(f"full fused vs two calls T={T} d={d} dt={dt} V={V} {dtype}")
-    two = run_full(inp)
+    say(f"full fused vs oracle and two calls T={T} d={d} dt={dt} V={V} {dtype}")
     one = run_full_fused(inp)
-    for k in ("kl", "lse_s", "lse_t", "dH", "dW"):
-        np.testing.assert_array_equal(one[k], two[k], err_msg=k)
+    check_full(one, inp, dtype)
+    two = run_full(inp)
+    v = np.ones(T, bool) if inp["mask"] is None else inp["mask"].numpy() != 0
+    assert_kl(one["kl"], two["kl"], dtype, v)
+    assert_grad(one["dW"], two["dW"], dtype, "dWs vs two calls")
+
+
+def test_full_single_call_is_deterministic():
+    inp = G.make_full(600, 256, 384, 2056, torch.bfloat16, mask="random10", number=29, g="normal")
+    say("full fused determinism")
+    a, b = run_full_fused(inp, chunk_rows=256), run_full_fused(inp, chunk_rows=256)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 
 
 @pytest.mark.parametrize("dtype,T,d,dt,V,chunk,mask", [
@@ -115,17 +144,7 @@ def test_full_single_chunk_matches_two_calls_bitwise(dtype, T, d, dt, V, tau, ma
 def test_full_several_chunks_match_the_oracle(dtype, T, d, dt, V, chunk, mask):
     inp = G.make_full(T, d, dt, V, dtype, tau=1.4, mask=mask, number=27, g="normal")
     say(f"full fused chunks={chunk} T={T} d={d} dt={dt} V={V} {dtype}")
-    got = run_full_fused(inp, chunk_rows=chunk)
-    kl, ls, lt = O.full_kl_forward(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], inp["mask"], inp["tau"])
-    dH, dW = O.full_kl_backward(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], inp["mask"], inp["tau"], inp["g"])
-    v = np.ones(T, bool) if inp["mask"] is None else inp["mask"].numpy() != 0
-    assert_kl(got["kl"], kl, dtype, v)
-    assert_lse(got["lse_s"], ls, dtype, v)
-    assert_lse(got["lse_t"], lt, dtype, v)
-    for k in ("kl", "lse_s", "lse_t", "dH"):
-        assert np.all(got[k][~v] == 0), k
-    assert_grad(got["dH"], dH, dtype, "dH")
-    assert_grad(got["dW"], dW, dtype, "dWs")
+    check_full(run_full_fused(inp, chunk_rows=chunk), inp, dtype)
 
 
 def test_full_all_rows_masked_and_empty_batch():
