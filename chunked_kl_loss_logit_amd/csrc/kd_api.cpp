@@ -135,10 +135,20 @@ int splits_for(int64_t nrb, int64_t ntiles) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, ntiles));
 }
 
-int64_t chunk_of(int64_t T, int64_t chunk_rows) {
+// Rows per backward chunk: the request (or the default) rounded up to whole
+// 256-row tiles, at most the rows present, and for bf16 at most what keeps
+// the chunk's dZ buffer within the 32-bit offsets of the direct-to-LDS loads
+// that dH and dW read it with (16640 rows at V = 128256).
+int64_t chunk_of(int64_t T, int64_t V, int elem, int64_t chunk_rows) {
   int64_t C = chunk_rows <= 0 ? KD_DEFAULT_CHUNK_ROWS : chunk_rows;
   C = (int64_t)up((size_t)C, 256);
-  return std::min<int64_t>(C, (int64_t)up((size_t)std::max<int64_t>(T, 1), 256));
+  C = std::min<int64_t>(C, (int64_t)up((size_t)std::max<int64_t>(T, 1), 256));
+  if (elem == 2) {
+    const int64_t ldz = cdiv(V, kd::kTileN) * kd::kTileN;
+    int64_t cmax = ((int64_t(1) << 32) - 65537) / (ldz * 2) / 256 * 256;
+    C = std::min<int64_t>(C, std::max<int64_t>(cmax, 256));
+  }
+  return C;
 }
 
 struct Carver {
@@ -159,7 +169,7 @@ struct ChunkPlan {
 
 ChunkPlan plan_chunk(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows, Carver& cv) {
   ChunkPlan p{};
-  p.C = chunk_of(T, chunk_rows);
+  p.C = chunk_of(T, V, elem, chunk_rows);
   p.ldz = cdiv(V, kd::kTileN) * kd::kTileN;
   p.nrb_c = (int)(p.C / kd::kTileM);
   p.nrb_dh = p.nrb_c;
@@ -205,8 +215,8 @@ TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t
   p.fwd_total = fw.off;
   p.total = std::max(fw.off, bw.off);
   Carver fu = cv;
-  p.S_c = splits_for(cdiv(chunk_of(T, chunk_rows), kd::kTileM), p.ntiles);
-  p.o_part_c = fu.take((size_t)p.S_c * chunk_of(T, chunk_rows) * 16);
+  p.S_c = splits_for(cdiv(chunk_of(T, V, elem, chunk_rows), kd::kTileM), p.ntiles);
+  p.o_part_c = fu.take((size_t)p.S_c * chunk_of(T, V, elem, chunk_rows) * 16);
   p.ch_f = plan_chunk(T, d, V, elem, chunk_rows, fu);
   p.o_z = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
   p.fused_total = fu.off;
@@ -241,7 +251,7 @@ FullPlan plan_full(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows
   p.fwd_total = fw.off;
   p.total = std::max(fw.off, bw.off);
   Carver fu = cv;
-  const int64_t C = chunk_of(T, chunk_rows);
+  const int64_t C = chunk_of(T, V, elem, chunk_rows);
   p.S_c = splits_for(cdiv(C, kd::kTileM), cdiv(V, kd::kTileN));
   p.nblk = kd::full_from_z_blocks(elem, V);
   p.o_part_s = fu.take((size_t)p.S_c * C * 16);

@@ -98,8 +98,13 @@ typedef enum kd_dtype { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
 /* Workspace bytes that both kd_topk_kl_fwd and kd_topk_kl_bwd need for this
  * shape (one size serves both calls).  chunk_rows: token rows per backward
  * chunk (0 = KD_DEFAULT_CHUNK_ROWS; rounded up to a multiple of 256; clamped
- * to the rows present).  The size is affine in T for a fixed chunk size: the
- * per-row part is about 10*K + 32 bytes, the rest does not depend on T.
+ * to the rows present; for bf16 also clamped so that the chunk's dZ buffer,
+ * chunk * roundup(V, 256) * 2 bytes, stays under 4 GiB, the reach of the
+ * direct-to-LDS loads that read it: 16640 rows at V = 128256).  Every call
+ * taking chunk_rows applies the same rule.  Larger chunks trade workspace
+ * for speed at long context (fewer read-modify-writes of dW).  The size is
+ * affine in T for a fixed chunk size: the per-row part is about 10*K + 44
+ * bytes, the rest does not depend on T.
  * Returns KD_OK and writes *bytes, or an argument error. */
 kd_status kd_topk_kl_workspace_size(int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
                                     int64_t chunk_rows, size_t* bytes);
