@@ -8,11 +8,12 @@ A step of the top-K workloads is one kd_topk_kl_fwd plus one kd_topk_kl_bwd
 over one batch of synthetic rows (inputs already in HBM): the output
 projection, online log Z, top-K gather, per-token KL, and the chunked backward
 (recomputed projection, dZ, dH, dW).  A step of the full-vocabulary workload
-is kd_full_kl_fwd plus kd_full_kl_bwd.  The default run prints ONE JSON line
-for the output-head workload (T=4096, d=3072, V=128256, K=64); the same
-workload through the single-call kd_topk_kl_fwd_bwd (no recompute), the packed
-long-context and the full-vocabulary workloads ride along in its "extra"
-object.
+is kd_full_kl_fwd plus kd_full_kl_bwd (or, with --one-call, one
+kd_full_kl_fwd_bwd).  The default run prints ONE JSON line for the
+output-head workload (T=4096, d=3072, V=128256, K=64); the same workload
+through the single-call kd_topk_kl_fwd_bwd (no recompute), the packed
+long-context workload and the full-vocabulary workload (two calls and single
+call) ride along in its "extra" object.
 
 The loss-only benchmark of "Efficient Knowledge Distillation for LLMs: Offline
 Top-K Logits and a Fused Chunked KL Loss" (App. B) times the same path: output
