@@ -18,7 +18,10 @@
  * logit tiles live on chip only, the full [T, V] logit tensor is never
  * written, and the backward pass recomputes the projection chunk by chunk of
  * token rows (one extra projection per chunk, as in output-head gradient
- * checkpointing).
+ * checkpointing).  Each variant also has a single forward + backward call
+ * that keeps one chunk's logits instead of recomputing them, and _ex calls
+ * with optional parts of the loss (per-token temperature, a partial-mass
+ * teacher, an LM cross-entropy term, KL mixing); see their sections.
  *
  * Definitions, per valid row t (s = z / tau with z = H_t . W, L_t = logsumexp(s)):
  *   top-K:  p = softmax(A_t / tau) over the K entries;
