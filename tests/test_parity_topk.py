@@ -240,3 +240,31 @@ def test_head_t32768_packed_sampled_rows():
     check_sampled(got, inp, rows, torch.bfloat16)
     m = inp["mask"].numpy() == 0
     assert np.all(got["kl"][m] == 0) and np.all(got["dH"][m] == 0)
+
+
+def test_out_of_range_index_in_a_valid_row_is_left_out_of_the_gather():
+    # documented behaviour: an index outside [0, V) in a valid row never matches a
+    # vocabulary column, so its entry drops out of the cross term (its z_topk stays
+    # 0) while its probability still counts in the teacher terms
+    inp = G.make_topk(300, 64, 520, 8, torch.bfloat16, tau=1.3, number=17, g="normal")
+    bad = {(3, 2): 520 + 5, (10, 5): -3, (299, 0): 1 << 20}
+    I = inp["I"].clone()
+    for (t, k), v in bad.items():
+        I[t, k] = v
+    say("out-of-range indices in valid rows")
+    got = run_topk(dict(inp, I=I))
+    # the oracle on the in-range indices (the bad ones moved to column 0), then the
+    # cross term of the moved entries taken back out
+    I0 = I.clone()
+    for (t, k) in bad:
+        I0[t, k] = 0
+    kl, lse, z = O.topk_kl_forward(inp["H"], inp["W"], I0, inp["A"], None, inp["tau"])
+    logp = O.teacher_log_probs(O.as_f64(inp["A"]), inp["tau"])
+    for (t, k) in bad:
+        kl[t] += np.exp(logp[t, k]) * z[t, k] / inp["tau"]
+        z[t, k] = 0.0
+    assert_kl(got["kl"], kl, torch.bfloat16)
+    assert_lse(got["lse"], lse, torch.bfloat16)
+    np.testing.assert_allclose(got["z"], z, rtol=1e-4, atol=1e-5)
+    for (t, k) in bad:
+        assert got["z"][t, k] == 0
