@@ -236,7 +236,11 @@ __device__ inline void store_block(StPair st, char* dst, long ld, long row0, lon
   const int q = tid % CPR;
   const long col = col0 + (long)q * E::kEpc;
   if (col >= ncols || col < clo) return;
-  for (int r = tid / CPR; r < kBM; r += RPP) {
+  // unrolled, so the LDS reads of all of a thread's rows go out before the
+  // first store waits on them
+#pragma unroll
+  for (int k = 0; k < kBM / RPP; ++k) {
+    const int r = tid / CPR + k * RPP;
     if (row0 + r >= nrows) break;
     u32x4_t o;
     if constexpr (E::kEpc == 8) {

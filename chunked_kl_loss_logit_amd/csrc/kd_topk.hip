@@ -94,10 +94,15 @@ __device__ inline void block_range(int cb, int clo, int chi, int& lo, int& hi) {
   hi = max(0, min(32, chi - cb));
 }
 
+// kZ: the caller asked for z_topk.  Without it the gather keeps no output
+// state, which leaves the epilogue enough registers that nothing spills (a
+// spilled cursor word reloaded in the hit path made every round wait for all
+// vector memory, the next tile's operand loads and earlier stores included).
+template <bool kZ>
 struct FwdRow {
   Cursor cur;
   const uint16_t* perm;  // uniform bases, indexed by pair position
-  float* ztk;            // z_topk (nullable), indexed by row_k + original position
+  float* ztk;            // z_topk, indexed by row_k + original position (kZ)
   long row_k;            // t * Kz
   int kz;                // cached entries per row (a label entry has perm == kz)
   float m2, l, x, c2;
@@ -135,7 +140,7 @@ struct FwdRow {
     cur.take_below(cb + hi, [&](int v, float pv, int c) {
       const float z = st_row(st, r)[st_pos(r, v - cb)];
       x = fmaf(pv, z, x);
-      if (ztk) {
+      if constexpr (kZ) {
         const int k = perm[c];
         if (k < kz) ztk[row_k + k] = z;
       }
@@ -184,8 +189,8 @@ __device__ inline int tile_n0(int vt, int V) { return V >= kBN ? min(vt * kBN, V
 // The epilogue walks the 256 x 256 tile in eight rounds of one 32-column
 // block (wave column half h, block NBI) staged in the epilogue array, in
 // ascending column order: half 0 blocks 0..3, then half 1.
-template <int H, int NBI>
-__device__ inline void fwd_round(const Slots& sl, const f32x16_t (&acc)[4][4], int n0, int lo, int hi, FwdRow& R,
+template <int H, int NBI, class Row>
+__device__ inline void fwd_round(const Slots& sl, const f32x16_t (&acc)[4][4], int n0, int lo, int hi, Row& R,
                                  const TopkFwdArgs& a, long row0, long M) {
   const int cb = n0 + H * 128 + NBI * 32;
   stage_half<NBI, 4>(sl.ep, H, acc);
@@ -213,7 +218,7 @@ __device__ inline void dz_round(const Slots& sl, const f32x16_t (&acc)[4][4], in
 // Rows: the compacted valid rows [c0, c0 + C) (the plain forward takes them
 // all); partials are indexed by compacted position, and with zout set the
 // tile's logits are also written out, fp32, one row per compacted row.
-template <class Main, class E>
+template <class Main, class E, bool kZ>
 __global__ __launch_bounds__(kThreads, 1) void topk_fwd_kernel(TopkFwdArgs a) {
   KD_DECLARE_SLOTS(sl);
 
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_fwd_kernel(TopkFwdArgs a) {
       a.W, a.V * E::kElem, a.V, a.d);
 
   const int ti = row0 + (int)threadIdx.x;
-  FwdRow R;
+  FwdRow<kZ> R;
   R.rv = ti < M;
   const long t = R.rv ? rows[ti] : 0;
   R.cur.pair = a.rd.pair;
@@ -389,14 +394,22 @@ hipError_t launch_topk_dz_from_z(int elem, const TopkDzFromZArgs& a, hipStream_t
 
 // The direct-load ring needs bf16, a hidden width that is a multiple of 128
 // and at least one whole 256-column tile of vocabulary.
-hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st) {
+template <bool kZ>
+static void launch_topk_fwd_z(int elem, const TopkFwdArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
   if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.T * a.d * 2) && fits32(a.d * a.V * 2))
-    hipLaunchKernelGGL((topk_fwd_kernel<DmaNN<kBN>, Bf16>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((topk_fwd_kernel<DmaNN<kBN>, Bf16, kZ>), grid, block, 0, st, a);
   else if (elem == 2)
-    hipLaunchKernelGGL((topk_fwd_kernel<GenNN<Bf16, kBN>, Bf16>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((topk_fwd_kernel<GenNN<Bf16, kBN>, Bf16, kZ>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((topk_fwd_kernel<GenNN<F32, kBN>, F32>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((topk_fwd_kernel<GenNN<F32, kBN>, F32, kZ>), grid, block, 0, st, a);
+}
+
+hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st) {
+  if (a.z_topk)
+    launch_topk_fwd_z<true>(elem, a, st);
+  else
+    launch_topk_fwd_z<false>(elem, a, st);
   return hipGetLastError();
 }
 
