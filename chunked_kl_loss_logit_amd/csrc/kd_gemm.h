@@ -253,7 +253,10 @@ __device__ inline void store_block(StPair st, char* dst, long ld, long row0, lon
       const float4 a = st_read4(st, r, q);
       o = u32x4_t{__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w)};
     }
-    *reinterpret_cast<u32x4_t*>(dst + ((row0 + r) * ld + col) * E::kElem) = o;
+    // streaming (non-temporal) store: the block is read back only by a later
+    // kernel, and evict-first lines leave L2 to the operands the other
+    // workgroups of the XCD are still reusing
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(dst + ((row0 + r) * ld + col) * E::kElem));
   }
 }
 
