@@ -41,12 +41,21 @@ struct FullFwdRow {
     const int nv = (int)max(0L, min(32L, V - cb));
     if (nv == 0) return;
     const int r = threadIdx.x;
-    float vs[32], vu[32];
+    // two online updates of 16 columns each: half the live temporaries of one
+    // 32-column update, so the epilogue needs no scratch
+    half<0>(ss, su, r, nv);
+    if (nv > 16) half<4>(ss, su, r, nv);
+  }
+
+  // columns [4 J0, 4 J0 + 16) of the staged blocks, those below nv valid
+  template <int J0>
+  __device__ inline void half(StPair ss, StPair su, int r, int nv) {
+    float vs[16], vu[16];
     float cms = -INFINITY, cmt = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float4 fs = st_read4(ss, r, j), fu = st_read4(su, r, j);
-      const bool ok = 4 * j < nv;
+    for (int j = 0; j < 4; ++j) {
+      const float4 fs = st_read4(ss, r, J0 + j), fu = st_read4(su, r, J0 + j);
+      const bool ok = 4 * (J0 + j) < nv;
       vs[4 * j + 0] = ok ? fs.x : -INFINITY;
       vs[4 * j + 1] = ok ? fs.y : -INFINITY;
       vs[4 * j + 2] = ok ? fs.z : -INFINITY;
@@ -73,8 +82,8 @@ struct FullFwdRow {
     }
     float sum_s = 0.f, sum_t = 0.f, rr = 0.f, rr2 = 0.f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if (j < nv) {
+    for (int j = 0; j < 16; ++j) {
+      if (4 * J0 + j < nv) {
         const float ys = vs[j] * c2, yt = vu[j] * c2;
         const float et = fast_exp2(yt - mt), es = fast_exp2(ys - ms);
         sum_s += es;
