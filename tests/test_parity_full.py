@@ -72,6 +72,34 @@ def test_full_t16384_sampled_rows():
     assert np.all(np.isfinite(got["dW"]))
 
 
+
+def test_full_largest_direct_load_chunk_sampled_rows():
+    # chunk_rows past the direct-load reach is capped at 16640 rows at V = 128256:
+    # a chunk of 16640 rows (offsets past 2^31 in dH and dW) and one of 360
+    p = G.PRESETS["full_vocab_t16384"]
+    T = 17000
+    inp = G.make_full(T, p.d, p.dt_hidden, p.V, p.dtype, tau=1.0, number=19, g="normal")
+    say("full T=17000, chunk_rows=32768 (capped at 16640)")
+    got = run_full(inp, chunk_rows=32768)
+    rng = np.random.default_rng(9)
+    rows = np.array(sorted(set(rng.choice(T, 24, replace=False).tolist()) | {0, 8400, 16639, 16640, T - 1}))
+    kl, ls, lt, dH = O.full_kl_rows(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], None, 1.0, inp["g"], rows)
+    assert_kl(got["kl"][rows], kl, torch.bfloat16)
+    assert_lse(got["lse_s"][rows], ls, torch.bfloat16)
+    assert_lse(got["lse_t"][rows], lt, torch.bfloat16)
+    assert_grad(got["dH"][rows], dH, torch.bfloat16, "dH rows")
+    # q - p sums to zero over V in every row, so each row of dW (d x V) does too,
+    # up to the bf16 rounding of dZ
+    dW = got["dW"]
+    assert np.all(np.isfinite(dW))
+    assert np.all(np.abs(dW.sum(axis=1)) <= 2e-2 * np.linalg.norm(dW, axis=1))
+    say("full T=17000, chunk_rows=4096")
+    ref = run_full(inp, chunk_rows=4096)
+    np.testing.assert_array_equal(got["kl"], ref["kl"])
+    assert np.linalg.norm(got["dH"] - ref["dH"]) <= 1e-3 * np.linalg.norm(ref["dH"])
+    assert np.linalg.norm(got["dW"] - ref["dW"]) <= 1e-5 * np.linalg.norm(ref["dW"])
+
+
 @pytest.mark.parametrize("T,d,dt,V,tau,mask,chunk", [
     (700, 384, 256, 1288, 1.0, "none", 256),       # last vocabulary tile shifted back, ragged row tile
     (900, 256, 640, 2568, 1.6, "random10", 512),   # teacher wider than student, masked rows

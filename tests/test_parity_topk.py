@@ -268,3 +268,33 @@ def test_out_of_range_index_in_a_valid_row_is_left_out_of_the_gather():
     np.testing.assert_allclose(got["z"], z, rtol=1e-4, atol=1e-5)
     for (t, k) in bad:
         assert got["z"][t, k] == 0
+
+
+
+def test_largest_direct_load_chunk_sampled_rows():
+    # chunk_rows past the direct-load reach is capped at 16640 rows at V = 128256:
+    # a chunk of 16640 rows (a 4.27 GB dZ buffer, so offsets past 2^31 in dH and
+    # dW) and one of 360 whose dW is added to the first's in place
+    p = G.PRESETS["head_topk_t4096"]
+    T = 17000
+    inp = G.make_topk(T, p.d, p.V, p.K, p.dtype, tau=1.0, number=18, g="normal")
+    say("head T=17000, chunk_rows=32768 (capped at 16640)")
+    got = run_topk(inp, want_z=False, chunk_rows=32768)
+    rng = np.random.default_rng(8)
+    rows = np.array(sorted(set(rng.choice(T, 24, replace=False).tolist()) | {0, 8400, 16383, 16639, 16640, T - 1}))
+    kl, lse, _, dH = O.topk_kl_rows(inp["H"], inp["W"], inp["I"], inp["A"], None, 1.0, inp["g"], rows)
+    assert_kl(got["kl"][rows], kl, torch.bfloat16)
+    assert_lse(got["lse"][rows], lse, torch.bfloat16)
+    assert_grad(got["dH"][rows], dH, torch.bfloat16, "dH rows")
+    # every row of dZ sums to zero (mass 1), so each row of dW (d x V) sums to
+    # zero over V up to the bf16 rounding of dZ, about 2^-9 of its norm
+    dW = got["dW"]
+    assert np.all(np.isfinite(dW))
+    assert np.all(np.abs(dW.sum(axis=1)) <= 2e-2 * np.linalg.norm(dW, axis=1))
+    # 4096-row chunks give the same gradients up to the fp32 order of the sums
+    # (dH's split over V and dW's sum over chunks both depend on the chunk)
+    say("head T=17000, chunk_rows=4096")
+    ref = run_topk(inp, want_z=False, chunk_rows=4096)
+    np.testing.assert_array_equal(got["kl"], ref["kl"])
+    assert np.linalg.norm(got["dH"] - ref["dH"]) <= 1e-3 * np.linalg.norm(ref["dH"])
+    assert np.linalg.norm(got["dW"] - ref["dW"]) <= 1e-5 * np.linalg.norm(ref["dW"])
