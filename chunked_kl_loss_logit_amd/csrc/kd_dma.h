@@ -22,6 +22,13 @@
 // loads still landing in the other three and does not wait for them; the ring
 // waits on its own loads with explicit vmcnt counts.
 //
+// Operands come in two layouts.  Row-major: row r at r * ld bytes.  Panels
+// (the library's own workspace buffers): a matrix of R rows is cut into
+// 64-byte pieces along its rows, and piece p of row r sits at (p R + r) * 64,
+// so the 64-byte pieces of one stage of consecutive rows are contiguous: a
+// stage of a 256-row operand is one 16 KB run instead of 256 pieces of 64
+// bytes in 256 cache lines, which halves the cache-line requests of its loads.
+//
 // Requirements (the launchers fall back to the general path otherwise): bf16
 // and a contraction length that is a multiple of 128 (whole ring turns)
 // whose data is readable (real data or zero padding).  Rows or columns outside the operand are
@@ -64,12 +71,15 @@ __device__ inline u32x4_t ld_lds16(const char* slot, int off) {
 
 // k-contiguous operand with NR rows: NR / 16 direct loads per stage, NR / 64
 // per wave.  Lane L of load q covers row 16 q + L / 4 at chunk position L % 4.
+// row_ptr gives the address of a row's first stage; stage s is s * sst bytes
+// further (row-major: 64; panels of R rows: 64 R).
 template <int NR>
 struct DmaRows {
   static constexpr int kPer = NR / 64;
   static constexpr int kBytes = NR * kRowB;  // per stage
   __amdgpu_buffer_rsrc_t rs;
   uint32_t off[kPer];  // this lane's row offset from the operand base, plus its swizzled chunk
+  uint32_t sst;        // bytes from one stage of a row to the next
 
   __device__ inline static int row_of(int i) {
     const int q = wave_id() * kPer + i;
@@ -77,8 +87,9 @@ struct DmaRows {
   }
   // row_ptr(i) for i < kPer: address of row row_of(i) (clamped to a valid row)
   template <class RowAddr>
-  __device__ inline void init(const char* b, RowAddr&& row_ptr) {
+  __device__ inline void init(const char* b, RowAddr&& row_ptr, uint32_t stage_stride = kRowB) {
     rs = make_rsrc(b);
+    sst = stage_stride;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int m = row_of(i);
@@ -89,14 +100,15 @@ struct DmaRows {
   // another row block of the same operand)
   __device__ inline void issue(long s, long extra, char* dst) const {
     const int w = wave_id();
-    const uint32_t soff = (uint32_t)(s * kRowB + extra);
+    const uint32_t soff = (uint32_t)(s * sst + extra);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) dma16(rs, off[i], soff, dst + (w * kPer + i) * 1024);
   }
   __device__ inline void issue(long s, char* dst) const { issue(s, 0L, dst); }
 };
 
-// n-contiguous operand ([K][N] row-major), BN columns per tile.
+// n-contiguous operand ([K][N]), BN columns per tile, row-major or in panels
+// of K rows (each 64-byte piece of a k-row is one 16-byte-chunk group).
 template <int BN>
 struct DmaCols {
   static constexpr int kRowBytes = BN * 2;
@@ -106,29 +118,52 @@ struct DmaCols {
   static constexpr int kPer = kLoads / 4;                // per wave
   static constexpr int kBytes = kDmaKs * kRowBytes;      // per stage
   __amdgpu_buffer_rsrc_t rs;
-  long ld;  // global row stride, bytes
+  long ld;       // row-major: global row stride, bytes
+  uint32_t sst;  // bytes from one stage to the next
   uint32_t off[kPer];
 
-  // panel at b (element (0, n0)), ncols valid columns from it (clamped beyond)
+  // this lane's k-row and column of load i; columns at or past ncols are
+  // clamped to the last whole chunk
+  __device__ inline static void lane_pos(int i, long ncols, int& k, long& col) {
+    const int w = wave_id(), L = threadIdx.x & 63;
+    const int q = w * kPer + i;
+    k = q * kRowsPerLoad + L / kChunks;
+    col = 8L * ((L % kChunks) ^ (4 * (k & 3)));
+    if (col + 8 > ncols) col = ncols - 8;
+  }
+
+  // row-major panel at b (element (0, n0)), ncols valid columns from it
   __device__ inline void init(const char* b, long ncols) {
     rs = make_rsrc(b);
-    const int w = wave_id(), L = threadIdx.x & 63;
+    sst = (uint32_t)(kDmaKs * ld);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int q = w * kPer + i;
-      const int k = q * kRowsPerLoad + L / kChunks;
-      const int c = (L % kChunks) ^ (4 * (k & 3));
-      long col = 8L * c;
-      if (col + 8 > ncols) col = ncols - 8;
+      int k;
+      long col;
+      lane_pos(i, ncols, k, col);
       off[i] = (uint32_t)(k * ld + col * 2);
+    }
+  }
+  // columns [n0, n0 + BN) of a matrix at b stored in panels of prows rows,
+  // ncols valid columns from n0
+  __device__ inline void init_panels(const char* b, long n0, long ncols, long prows) {
+    rs = make_rsrc(b);
+    sst = (uint32_t)(kDmaKs * kRowB);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int k;
+      long col;
+      lane_pos(i, ncols, k, col);
+      off[i] = (uint32_t)panel_off(prows, k, (n0 + col) * 2);
     }
   }
   __device__ inline void issue(long s, char* dst) const {
     const int w = wave_id();
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) dma16(rs, off[i], (uint32_t)(s * kDmaKs * ld), dst + (w * kPer + i) * 1024);
+    for (int i = 0; i < kPer; ++i) dma16(rs, off[i], (uint32_t)(s * sst), dst + (w * kPer + i) * 1024);
   }
   // stage s of the panel that starts col0 columns after the one init() saw
+  // (row-major only)
   __device__ inline void issue(long s, long col0, char* dst) const {
     const int w = wave_id();
     const uint32_t soff = (uint32_t)(s * kDmaKs * ld + col0 * 2);

@@ -178,8 +178,8 @@ __device__ inline void full_dz_round(const Slots& sl, const f32x16_t (&acc_s)[4]
   R.consume(st_pair<0>(sl), st_pair<2>(sl), n0 + NBI * 32, a.V);
   R.consume(st_pair<1>(sl), st_pair<3>(sl), n0 + 64 + NBI * 32, a.V);
   __syncthreads();
-  store_block<E>(st_pair<0>(sl), a.dz, a.ldz, row0, n0 + NBI * 32, LONG_MAX, a.ldz);
-  store_block<E>(st_pair<1>(sl), a.dz, a.ldz, row0, n0 + 64 + NBI * 32, LONG_MAX, a.ldz);
+  store_block<E>(st_pair<0>(sl), a.dz, a.ldz, row0, n0 + NBI * 32, LONG_MAX, a.ldz, 0, a.C);
+  store_block<E>(st_pair<1>(sl), a.dz, a.ldz, row0, n0 + 64 + NBI * 32, LONG_MAX, a.ldz, 0, a.C);
   __syncthreads();
 }
 
@@ -288,77 +288,70 @@ hipError_t launch_full_rowc(Compact c, int64_t T, const float* tau_rows, float c
   return hipGetLastError();
 }
 
-// One thread: EPT consecutive columns (16 bytes of dZ) of one row; the block
-// (256 threads, one row) also sums the row's two KL terms over its columns,
-// in a fixed order, for the terms array.
+// Block geometry as kEwRows / kEwRanges say: a thread handles EPT consecutive
+// columns (16 bytes of dZ) of its row in each piece of the block's range, and
+// sums the row's two KL terms over them; the four threads of a row then add
+// theirs, in a fixed order, for the terms array.
 template <class E>
 __global__ __launch_bounds__(256) void full_from_z_kernel(FullFromZArgs a) {
   constexpr int EPT = E::kEpc;
-  __shared__ float2 red[4];
-  const long i = blockIdx.y;  // row of the chunk
-  const long v0 = ((long)blockIdx.x * 256 + threadIdx.x) * EPT;
+  constexpr int PC = kRowB / E::kElem;  // columns per piece
+  const long i = (long)blockIdx.y * kEwRows + (threadIdx.x >> 2);  // row of the chunk
+  const int sub = threadIdx.x & 3;
+  const long np = (a.V * E::kElem + kRowB - 1) / kRowB;
+  const long pb = np * blockIdx.x / gridDim.x, pe = np * (blockIdx.x + 1) / gridDim.x;
   const long M = min(a.C, (long)*a.c.count - a.c0);
-  const bool in = v0 < a.V;
-  float o[EPT];
+  const bool rv = i < M;
+  const long t = rv ? a.c.rows[a.c0 + i] : 0;
+  const FullDzConst k = full_dz_const(rv, t, a.lse_s, a.lse_t, a.g, a.c2, a.inv_tau, a.mix);
+  const float* sr = a.zs + i * a.ldz;
+  const float* ur = a.zt + i * a.ldz;
   float tp = 0.f, tq = 0.f;  // sum p (yt - ys), sum q (ys - yt), base 2
-  if (i < M && in) {
-    const long t = a.c.rows[a.c0 + i];
-    const FullDzConst k = full_dz_const(true, t, a.lse_s, a.lse_t, a.g, a.c2, a.inv_tau, a.mix);
-    const float* sr = a.zs + i * a.ldz + v0;
-    const float* ur = a.zt + i * a.ldz + v0;
+  for (long p = pb; p < pe; ++p) {
+    const long v0 = p * PC + sub * EPT;
+    if (v0 >= a.V) break;
+    float o[EPT];
+    if (rv) {
 #pragma unroll
-    for (int e = 0; e < EPT; e += 4) {
-      const float4 fs = *reinterpret_cast<const float4*>(sr + e);
-      const float4 fu = *reinterpret_cast<const float4*>(ur + e);
-      const float s4[4] = {fs.x, fs.y, fs.z, fs.w}, u4[4] = {fu.x, fu.y, fu.z, fu.w};
+      for (int e = 0; e < EPT; e += 4) {
+        const float4 fs = *reinterpret_cast<const float4*>(sr + v0 + e);
+        const float4 fu = *reinterpret_cast<const float4*>(ur + v0 + e);
+        const float s4[4] = {fs.x, fs.y, fs.z, fs.w}, u4[4] = {fu.x, fu.y, fu.z, fu.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        o[e + q] = k(s4[q], u4[q]);
-        const float ds = fmaf(s4[q], k.c2, -k.Ls2), dt = fmaf(u4[q], k.c2, -k.Lt2);
-        const float dy = (u4[q] - s4[q]) * k.c2;  // yt - ys
-        tp = fmaf(fast_exp2(dt), dy, tp);
-        tq = fmaf(fast_exp2(ds), -dy, tq);
+        for (int q = 0; q < 4; ++q) {
+          o[e + q] = k(s4[q], u4[q]);
+          const float ds = fmaf(s4[q], k.c2, -k.Ls2), dt = fmaf(u4[q], k.c2, -k.Lt2);
+          const float dy = (u4[q] - s4[q]) * k.c2;  // yt - ys
+          tp = fmaf(fast_exp2(dt), dy, tp);
+          tq = fmaf(fast_exp2(ds), -dy, tq);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) o[q] = 0.f;
+    }
+    if (a.dz) {
+      char* dst = a.dz + panel_off(a.C, i, v0 * E::kElem);
+      if constexpr (EPT == 8) {
+        const u32x4_t w{Bf16::pack2(o[0], o[1]), Bf16::pack2(o[2], o[3]), Bf16::pack2(o[4], o[5]),
+                        Bf16::pack2(o[6], o[7])};
+        *reinterpret_cast<u32x4_t*>(dst) = w;
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
       }
     }
-  } else {
-#pragma unroll
-    for (int q = 0; q < EPT; ++q) o[q] = 0.f;
   }
-  if (a.dz && in) {
-    char* dst = a.dz + (i * a.ldz + v0) * E::kElem;
-    if constexpr (EPT == 8) {
-      const u32x4_t w{Bf16::pack2(o[0], o[1]), Bf16::pack2(o[2], o[3]), Bf16::pack2(o[4], o[5]),
-                      Bf16::pack2(o[6], o[7])};
-      *reinterpret_cast<u32x4_t*>(dst) = w;
-    } else {
-      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-    }
-  }
-  if (a.terms == nullptr || i >= M) return;  // uniform over the block
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    tp += __shfl_xor(tp, off);
-    tq += __shfl_xor(tq, off);
-  }
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(tp, tq);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float2 r = red[0];
-    for (int w = 1; w < 4; ++w) {
-      r.x += red[w].x;
-      r.y += red[w].y;
-    }
-    a.terms[i * a.nblk + blockIdx.x] = r;
-  }
+  tp += __shfl_xor(tp, 1);
+  tq += __shfl_xor(tq, 1);
+  tp += __shfl_xor(tp, 2);
+  tq += __shfl_xor(tq, 2);
+  if (a.terms && rv && sub == 0) a.terms[i * a.nblk + blockIdx.x] = make_float2(tp, tq);
 }
 
-int full_from_z_blocks(int elem, int64_t V) {
-  const int ept = elem == 2 ? Bf16::kEpc : F32::kEpc;
-  return (int)((V + 256L * ept - 1) / (256L * ept));
-}
+int full_from_z_blocks(int elem, int64_t V) { return ew_ranges(elem, V); }
 
 hipError_t launch_full_from_z(int elem, const FullFromZArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)full_from_z_blocks(elem, a.V), (unsigned)a.C), block(256);
+  const dim3 grid((unsigned)full_from_z_blocks(elem, a.V), (unsigned)(a.C / kEwRows)), block(256);
   if (elem == 2)
     hipLaunchKernelGGL(full_from_z_kernel<Bf16>, grid, block, 0, st, a);
   else

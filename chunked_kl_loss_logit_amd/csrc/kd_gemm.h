@@ -223,13 +223,20 @@ __device__ inline void stage_half(StPair st, int h, const f32x16_t (&acc)[4][NB]
     }
 }
 
-// Store a staged [256][32] float block as the element type into a row-major
-// destination (`ld` elements per row): rows [row0, row0 + 256) clipped to
-// nrows, columns [col0, col0 + 32) clipped to [clo, ncols) (both multiples
-// of 4/8).
+// Panels: a matrix of prows rows cut into 64-byte pieces along its rows,
+// piece p of row r at (p prows + r) * 64 bytes.  Offset of byte `byte` of
+// row `row`:
+__device__ inline long panel_off(long prows, long row, long byte) {
+  return ((byte >> 6) * prows + row) * kRowB + (byte & 63);
+}
+
+// Store a staged [256][32] float block as the element type: rows [row0,
+// row0 + 256) clipped to nrows, columns [col0, col0 + 32) clipped to
+// [clo, ncols) (both multiples of 4/8).  The destination is row-major (`ld`
+// elements per row) or, with prows set, in panels of prows rows.
 template <class E>
 __device__ inline void store_block(StPair st, char* dst, long ld, long row0, long col0, long nrows,
-                                   long ncols, long clo = 0) {
+                                   long ncols, long clo = 0, long prows = 0) {
   constexpr int CPR = 32 * E::kElem / 16;  // 16-byte chunks per row
   constexpr int RPP = kThreads / CPR;
   const int tid = opaque((int)threadIdx.x);
@@ -256,7 +263,9 @@ __device__ inline void store_block(StPair st, char* dst, long ld, long row0, lon
     // streaming (non-temporal) store: the block is read back only by a later
     // kernel, and evict-first lines leave L2 to the operands the other
     // workgroups of the XCD are still reusing
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(dst + ((row0 + r) * ld + col) * E::kElem));
+    const long byte = col * E::kElem;
+    char* p = dst + (prows ? panel_off(prows, row0 + r, byte) : (row0 + r) * ld * E::kElem + byte);
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(p));
   }
 }
 

@@ -60,9 +60,10 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
 
   // contraction over the first V columns of both operands, split in S ranges
   Main mainloop;
-  mainloop.init(a.dz, [&](int r) -> const char* { return row0 + r < M ? a.dz + (row0 + r) * a.ldz * E::kElem : nullptr; },
+  // dz in panels of C rows, W row-major
+  mainloop.init(a.dz, [&](int r) -> const char* { return row0 + r < M ? a.dz + (row0 + r) * kRowB : nullptr; },
                 a.W, [&](int r) -> const char* { return n0 + r < a.d ? a.W + (n0 + r) * a.V * E::kElem : nullptr; },
-                a.V);
+                a.V, a.C * kRowB);
   // split boundaries on whole groups of Main::kStageGroup stages
   const long ng = mainloop.nst / Main::kStageGroup;
   const long s0 = ng * sp / a.S * Main::kStageGroup, s1 = ng * (sp + 1) / a.S * Main::kStageGroup;
@@ -88,8 +89,9 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   // 256-row tile
   const long K = (M + Main::kKMult - 1) / Main::kKMult * Main::kKMult;
   Main mainloop;
-  mainloop.init(a.hT, [&](int r) -> const char* { return row0 + r < a.d ? a.hT + (row0 + r) * a.C * E::kElem : nullptr; },
-                a.dz, a.ldz * E::kElem, a.V, K);
+  // hT in panels of d rows, dz in panels of C rows
+  mainloop.init(a.hT, [&](int r) -> const char* { return row0 + r < a.d ? a.hT + (row0 + r) * kRowB : nullptr; },
+                a.dz, 0, a.V, K, a.d * kRowB, a.C);
   f32x16_t acc[4][BN / 64];
   mainloop.tile(sl, n0, acc);
   store_tile_f32(sl, acc, a.dW, a.V, row0, n0, a.d, a.V, a.accumulate != 0);

@@ -38,6 +38,17 @@ struct Compact {
   int32_t* count;  // [1] number of valid rows
 };
 
+// Elementwise passes that write a dZ chunk: a block of 256 threads covers 64
+// rows and one of at most kEwRanges ranges of the 64-byte pieces of those
+// rows (4 threads per piece, so a wave writes 16 consecutive rows of a piece:
+// one contiguous kilobyte of the panel layout).
+constexpr int kEwRows = 64;
+constexpr int kEwRanges = 64;
+inline int ew_ranges(int elem, int64_t V) {
+  const int64_t pieces = (V * elem + 63) / 64;
+  return (int)(pieces < kEwRanges ? pieces : kEwRanges);
+}
+
 // ---------------------------------------------------------------- small kernels
 hipError_t launch_compact(const uint8_t* mask, int64_t T, Compact c, hipStream_t st);
 hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8_t* mask, int64_t T, int64_t K,
@@ -53,7 +64,8 @@ hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Co
                                int64_t T, float r, float* kl, float* lse_s, float* lse_t, float* kl_rev, int64_t jb,
                                int64_t je, bool zero_masked, hipStream_t st);
 // H^T of one chunk of compacted rows: out[j][i] = H[rows[c0 + i]][j] for
-// i < valid rows of the chunk, 0 up to C.
+// i < valid rows of the chunk, 0 up to C; out is [d][C] in panels of d rows
+// (piece p of row j at (p d + j) * 64 bytes).
 hipError_t launch_gather_transpose(const void* H, int elem, int64_t d, Compact c, int64_t c0, int64_t C, void* out,
                                    hipStream_t st);
 // dH[rows[c0 + i]] = sum_s part[s][i] (converted to the element type)
@@ -89,7 +101,7 @@ struct TopkDzArgs {
   TopkRowData rd;
   const float* lse;
   const float* g;
-  char* dz;        // [C][ldz] chunk of dZ
+  char* dz;        // [C][ldz] chunk of dZ, in panels of C rows (panel_off)
   int64_t ldz;     // padded vocabulary (multiple of the tile width)
   int64_t c0, C;   // first compacted row of the chunk, chunk capacity
   int64_t T, d, V, K;  // K: entries per row of the pair arrays
@@ -103,7 +115,7 @@ hipError_t launch_topk_dz(int elem, const TopkDzArgs& a, hipStream_t st);
 // chunk's valid rows i and v < V; zero for the chunk's other rows.
 struct TopkDzFromZArgs {
   const float* z;    // [C][ldz]
-  char* dz;          // [C][ldz], element type
+  char* dz;          // [C][ldz], element type, in panels of C rows
   int64_t ldz;
   Compact c;
   int64_t c0, C, V, K;  // K: entries per row of the pair arrays
@@ -147,7 +159,7 @@ struct FullDzArgs {
   const float* lse_s;
   const float* lse_t;
   const float* g;
-  char* dz;
+  char* dz;  // [C][ldz] chunk of dZ, in panels of C rows
   int64_t ldz, c0, C;
   int64_t T, d, dt, V;
   int nrb, S, ntiles;
@@ -172,7 +184,7 @@ hipError_t launch_full_lse_combine(const float* part_s, const float* part_t, int
                                    float* kl_rev, int64_t jb, int64_t je, bool zero_masked, hipStream_t st);
 
 // Elementwise pass over a chunk's stored fp32 logits (both heads): per chunk
-// row i and block b of 256 * EPT columns, terms[i][b] = (sum p (yt - ys),
+// row i and column range b (ew_ranges), terms[i][b] = (sum p (yt - ys),
 // sum q (ys - yt)) in base 2 with the final log-normalisers, and (dz set) dZ
 // as the recomputing tile's epilogue writes it; dZ is zero on rows past the
 // chunk's valid rows.
@@ -180,7 +192,7 @@ struct FullFromZArgs {
   const float* zs;   // [C][ldz]
   const float* zt;   // [C][ldz]
   int64_t ldz;
-  char* dz;          // nullable: [C][ldz], element type
+  char* dz;          // nullable: [C][ldz], element type, in panels of C rows
   float2* terms;     // nullable: [C][nblk]
   int nblk;
   Compact c;
@@ -201,7 +213,7 @@ hipError_t launch_full_kl_from_terms(const float2* terms, int nblk, Compact c, c
 // ---------------------------------------------------------------- gradient contractions
 // part[s][i][j] = sum over the s-th vocabulary range of dz[i][v] * W[j][v]
 struct DhArgs {
-  const char* dz;  // [C][ldz]
+  const char* dz;  // [C][ldz] in panels of C rows
   const char* W;   // [d][V]
   float* part;     // [S][C][d]
   const int32_t* count;
@@ -213,8 +225,8 @@ hipError_t launch_dh(int elem, const DhArgs& a, hipStream_t st);
 
 // dW[j][v] (+)= sum_i hT[j][i] * dz[i][v]
 struct DwArgs {
-  const char* hT;  // [d][C]
-  const char* dz;  // [C][ldz]
+  const char* hT;  // [d][C] in panels of d rows
+  const char* dz;  // [C][ldz] in panels of C rows
   float* dW;       // [d][V]
   const int32_t* count;
   int64_t c0, C, ldz, d, V;

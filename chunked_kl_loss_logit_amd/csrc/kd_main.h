@@ -53,17 +53,22 @@ __device__ inline void mma_stage_rows(const char* As, const char* Bs, f32x16_t (
 // ------------------------------------------------------------------ register-staged loaders
 // k-contiguous operand with NR rows; thread t loads chunk t % 4 of rows
 // t / 4 + 64 j.  Rows without a pointer and bytes past kbytes read as zero.
+// rp[j] is the address of a row's first stage; stage s is s * sst bytes
+// further (row-major: 64; panels of R rows: 64 R).
 template <int NR>
 struct GRows {
   static constexpr int kPer = NR / 64;
   const char* rp[kPer];
   u32x4_t r[kPer];
+  long sst;
   __device__ inline static int row_of(int j) { return (threadIdx.x >> 2) + 64 * j; }
+  // kbyte0: the stage's first byte along the rows, a multiple of 64
   __device__ inline void load(long kbyte0, long kbytes, long extra = 0) {
     const long off = kbyte0 + 16 * (threadIdx.x & 3);
+    const long pos = kbyte0 / kRowB * sst + 16 * (threadIdx.x & 3);
     const bool kv = off < kbytes;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) r[j] = (kv && rp[j]) ? ld16(rp[j] + extra + off) : zero4();
+    for (int j = 0; j < kPer; ++j) r[j] = (kv && rp[j]) ? ld16(rp[j] + extra + pos) : zero4();
   }
   __device__ inline void store(char* dst) const {
 #pragma unroll
@@ -72,9 +77,10 @@ struct GRows {
   }
 };
 
-// n-contiguous operand ([K][N] row-major) stored as BN k-contiguous rows:
-// each thread loads an EPC x EPC block (EPC k-rows of one 16-byte column
-// chunk), transposes it in registers and writes EPC 16-byte row chunks.
+// n-contiguous operand ([K][N], row-major or in panels of prows rows) stored
+// as BN k-contiguous rows: each thread loads an EPC x EPC block (EPC k-rows of
+// one 16-byte column chunk), transposes it in registers and writes EPC
+// 16-byte row chunks.
 template <class E, int BN>
 struct GCols {
   static constexpr int kKs = kRowB / E::kElem;  // k-rows per stage
@@ -83,8 +89,10 @@ struct GCols {
   static constexpr int kNblk = kNkb * kNnc;
   static constexpr int kPer = (kNblk + kThreads - 1) / kThreads;
   u32x4_t r[kPer][E::kEpc];
+  const char* mat;   // element (0, 0)
   const char* base;  // element (0, n0)
-  long ld;           // row stride, bytes
+  long ld;           // row-major: row stride, bytes
+  long prows;        // panels: rows per panel (0: row-major)
   long N, n0, K;
 
   __device__ inline void load(long k0) {
@@ -96,7 +104,9 @@ struct GCols {
 #pragma unroll
       for (int e = 0; e < E::kEpc; ++e) {
         const long k = k0 + kb * E::kEpc + e;
-        r[i][e] = (nv && k < K) ? ld16(base + k * ld + (long)nc * 16) : zero4();
+        const long byte = (n0 + (long)nc * E::kEpc) * E::kElem;
+        const char* p = prows ? mat + panel_off(prows, k, byte) : base + k * ld + (long)nc * 16;
+        r[i][e] = (nv && k < K) ? ld16(p) : zero4();
       }
     }
   }
@@ -154,11 +164,17 @@ struct GenNN {
   const char* B;
   long kbytes, nst;
 
+  // a_sst: stage stride of A (see GRows); b_prows: B in panels of that many
+  // rows (0: row-major with stride ldb)
   template <class RowPtr>
-  __device__ inline void init(const char*, RowPtr&& row_ptr, const char* Bm, long ldb, long N, long K) {
+  __device__ inline void init(const char*, RowPtr&& row_ptr, const char* Bm, long ldb, long N, long K,
+                              long a_sst = kRowB, long b_prows = 0) {
 #pragma unroll
     for (int j = 0; j < GRows<kBM>::kPer; ++j) al.rp[j] = row_ptr(GRows<kBM>::row_of(j));
+    al.sst = a_sst;
     B = Bm;
+    bl.mat = Bm;
+    bl.prows = b_prows;
     bl.ld = ldb;
     bl.N = N;
     bl.K = K;
@@ -208,16 +224,24 @@ struct DmaNN {
   FragReader<BN> rd;
   const char* B;
   long N;
+  long b_prows;
   int nst;
 
+  // a_sst: stage stride of A (see DmaRows); b_prows: B in panels of that many
+  // rows (0: row-major with stride ldb; run() takes row-major B only)
   template <class RowPtr>
-  __device__ inline void init(const char* abase, RowPtr&& row_ptr, const char* Bm, long ldb, long Nn, long K) {
+  __device__ inline void init(const char* abase, RowPtr&& row_ptr, const char* Bm, long ldb, long Nn, long K,
+                              uint32_t a_sst = kRowB, long bp = 0) {
     const char* safe = row_ptr(0);  // row 0 of a launched tile is always inside the operand
-    a.init(abase, [&](int i) {
-      const char* p = row_ptr(DmaRows<kBM>::row_of(i));
-      return p ? p : safe;
-    });
+    a.init(
+        abase,
+        [&](int i) {
+          const char* p = row_ptr(DmaRows<kBM>::row_of(i));
+          return p ? p : safe;
+        },
+        a_sst);
     B = Bm;
+    b_prows = bp;
     b.ld = ldb;
     N = Nn;
     nst = (int)(K / kDmaKs);
@@ -248,7 +272,10 @@ struct DmaNN {
   }
 
   __device__ inline void tile(const Slots& sl, long n0, f32x16_t (&acc)[4][BN / 64]) {
-    b.init(B + n0 * 2, N - n0);
+    if (b_prows)
+      b.init_panels(B, n0, N - n0, b_prows);
+    else
+      b.init(B + n0 * 2, N - n0);
     zero_acc<BN / 64>(acc);
     ring_contract<kLpw, FragsNN<BN>>(
         sl, nst,
@@ -269,12 +296,16 @@ struct GenNT {
   GRows<BN> bl;
   long kbytes, nst;
 
+  // a_sst, b_sst: stage strides of the operands (see GRows)
   template <class RowPtrA, class RowPtrB>
-  __device__ inline void init(const char*, RowPtrA&& row_a, const char*, RowPtrB&& row_b, long K) {
+  __device__ inline void init(const char*, RowPtrA&& row_a, const char*, RowPtrB&& row_b, long K, long a_sst = kRowB,
+                              long b_sst = kRowB) {
 #pragma unroll
     for (int j = 0; j < GRows<kBM>::kPer; ++j) al.rp[j] = row_a(GRows<kBM>::row_of(j));
 #pragma unroll
     for (int j = 0; j < GRows<BN>::kPer; ++j) bl.rp[j] = row_b(GRows<BN>::row_of(j));
+    al.sst = a_sst;
+    bl.sst = b_sst;
     kbytes = K * E::kElem;
     nst = (kbytes + kRowB - 1) / kRowB;
   }
@@ -306,18 +337,26 @@ struct DmaNT {
   FragReader<BN> rd;
   long nst;
 
+  // a_sst, b_sst: stage strides of the operands (see DmaRows)
   template <class RowPtrA, class RowPtrB>
-  __device__ inline void init(const char* abase, RowPtrA&& row_a, const char* bbase, RowPtrB&& row_b, long K) {
+  __device__ inline void init(const char* abase, RowPtrA&& row_a, const char* bbase, RowPtrB&& row_b, long K,
+                              uint32_t a_sst = kRowB, uint32_t b_sst = kRowB) {
     const char* sa = row_a(0);
     const char* sb = row_b(0);
-    a.init(abase, [&](int i) {
-      const char* p = row_a(DmaRows<kBM>::row_of(i));
-      return p ? p : sa;
-    });
-    b.init(bbase, [&](int i) {
-      const char* p = row_b(DmaRows<BN>::row_of(i));
-      return p ? p : sb;
-    });
+    a.init(
+        abase,
+        [&](int i) {
+          const char* p = row_a(DmaRows<kBM>::row_of(i));
+          return p ? p : sa;
+        },
+        a_sst);
+    b.init(
+        bbase,
+        [&](int i) {
+          const char* p = row_b(DmaRows<BN>::row_of(i));
+          return p ? p : sb;
+        },
+        b_sst);
     nst = K / kDmaKs;
     rd.init_rows();
   }

@@ -391,7 +391,7 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(const U* H, long 
   __syncthreads();
   for (int jj = ty; jj < 64; jj += 4) {
     const long j = j0 + jj, i = i0 + tx;
-    if (j < d && i < C) out[j * C + i] = tile[tx][jj];
+    if (j < d && i < C) *reinterpret_cast<U*>(reinterpret_cast<char*>(out) + panel_off(d, j, i * (long)sizeof(U))) = tile[tx][jj];
   }
 }
 

@@ -209,7 +209,7 @@ __device__ inline void dz_round(const Slots& sl, const f32x16_t (&acc)[4][4], in
   ring_barrier();
   R.consume(sl.ep, cb, lo, hi, R.c2);
   ring_barrier();
-  store_block<E>(sl.ep, a.dz, a.ldz, row0, cb, LONG_MAX, a.ldz, lo);
+  store_block<E>(sl.ep, a.dz, a.ldz, row0, cb, LONG_MAX, a.ldz, lo, a.C);
   ring_barrier();
 }
 
@@ -335,56 +335,70 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_kernel(TopkDzArgs a) {
 }
 
 // ---------------------------------------------------------------- dZ from stored logits
-// One thread: EPT consecutive columns (16 bytes of dZ) of one row, the same
-// formula as the recomputing tile's epilogue.  The row's entries are sorted,
-// so the hits of [v0, v0 + EPT) are found with a binary search over them
-// (shared by the block, so L1-resident) and subtracted before the one
-// rounding to the element type.
+// Block geometry as kEwRows / kEwRanges say: a thread handles EPT consecutive
+// columns (16 bytes of dZ) of its row in each piece of the block's range, with
+// the recomputing tile's epilogue formula.  The row's entries are sorted and
+// the thread's columns ascend, so one cursor walks the hits in order; they are
+// subtracted before the one rounding to the element type.
 template <class E>
 __global__ __launch_bounds__(256) void topk_dz_from_z_kernel(TopkDzFromZArgs a) {
   constexpr int EPT = E::kEpc;
-  const long i = blockIdx.y;  // row of the chunk
-  const long v0 = ((long)blockIdx.x * 256 + threadIdx.x) * EPT;
-  if (v0 >= a.V) return;
+  constexpr int PC = kRowB / E::kElem;  // columns per piece
+  const long i = (long)blockIdx.y * kEwRows + (threadIdx.x >> 2);  // row of the chunk
+  const int sub = threadIdx.x & 3;
+  const long np = (a.V * E::kElem + kRowB - 1) / kRowB;
+  const long pb = np * blockIdx.x / gridDim.x, pe = np * (blockIdx.x + 1) / gridDim.x;
   const long M = min(a.C, (long)*a.c.count - a.c0);
-  float o[EPT];
-  if (i < M) {
+  const bool rv = i < M;
+  float L2 = 0.f, gs = 0.f, c2 = 0.f;
+  int c = 0, ce = 0;
+  if (rv) {
     const long t = a.c.rows[a.c0 + i];
     const float4 rc = a.rd.rowc[t];
-    const float L2 = a.lse[t] * kLog2e - rc.w, gs = a.g[t] * rc.y, c2 = rc.x;
-    const float* zr = a.z + i * a.ldz + v0;
-#pragma unroll
-    for (int e = 0; e < EPT; e += 4) {
-      const float4 z4 = *reinterpret_cast<const float4*>(zr + e);
-      o[e + 0] = gs * fast_exp2(fmaf(z4.x, c2, -L2));
-      o[e + 1] = gs * fast_exp2(fmaf(z4.y, c2, -L2));
-      o[e + 2] = gs * fast_exp2(fmaf(z4.z, c2, -L2));
-      o[e + 3] = gs * fast_exp2(fmaf(z4.w, c2, -L2));
-    }
-    const int b = (int)(t * a.K), e = (int)(t * a.K + a.K);
-    for (int c = lower_bound(a.rd.pair, b, e, v0); c < e; ++c) {
-      const int2 pr = a.rd.pair[c];
-      if ((long)pr.x >= v0 + EPT) break;
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) o[q] = (long)pr.x == v0 + q ? o[q] - gs * __int_as_float(pr.y) : o[q];
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < EPT; ++q) o[q] = 0.f;
+    L2 = a.lse[t] * kLog2e - rc.w;
+    gs = a.g[t] * rc.y;
+    c2 = rc.x;
+    ce = (int)(t * a.K + a.K);
+    c = lower_bound(a.rd.pair, (int)(t * a.K), ce, pb * PC);
   }
-  char* dst = a.dz + (i * a.ldz + v0) * E::kElem;
-  if constexpr (EPT == 8) {
-    const u32x4_t w{Bf16::pack2(o[0], o[1]), Bf16::pack2(o[2], o[3]), Bf16::pack2(o[4], o[5]),
-                    Bf16::pack2(o[6], o[7])};
-    *reinterpret_cast<u32x4_t*>(dst) = w;
-  } else {
-    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+  const float* zr = a.z + i * a.ldz;
+  for (long p = pb; p < pe; ++p) {
+    const long v0 = p * PC + sub * EPT;
+    if (v0 >= a.V) break;
+    float o[EPT];
+    if (rv) {
+#pragma unroll
+      for (int e = 0; e < EPT; e += 4) {
+        const float4 z4 = *reinterpret_cast<const float4*>(zr + v0 + e);
+        o[e + 0] = gs * fast_exp2(fmaf(z4.x, c2, -L2));
+        o[e + 1] = gs * fast_exp2(fmaf(z4.y, c2, -L2));
+        o[e + 2] = gs * fast_exp2(fmaf(z4.z, c2, -L2));
+        o[e + 3] = gs * fast_exp2(fmaf(z4.w, c2, -L2));
+      }
+      for (; c < ce; ++c) {
+        const int2 pr = a.rd.pair[c];
+        if ((long)pr.x >= v0 + EPT) break;
+        if ((long)pr.x < v0) continue;  // another thread's columns
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) o[q] = (long)pr.x == v0 + q ? o[q] - gs * __int_as_float(pr.y) : o[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) o[q] = 0.f;
+    }
+    char* dst = a.dz + panel_off(a.C, i, v0 * E::kElem);
+    if constexpr (EPT == 8) {
+      const u32x4_t w{Bf16::pack2(o[0], o[1]), Bf16::pack2(o[2], o[3]), Bf16::pack2(o[4], o[5]),
+                      Bf16::pack2(o[6], o[7])};
+      *reinterpret_cast<u32x4_t*>(dst) = w;
+    } else {
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+    }
   }
 }
 
 hipError_t launch_topk_dz_from_z(int elem, const TopkDzFromZArgs& a, hipStream_t st) {
-  const int ept = elem == 2 ? Bf16::kEpc : F32::kEpc;
-  const dim3 grid((unsigned)((a.V + 256L * ept - 1) / (256L * ept)), (unsigned)a.C), block(256);
+  const dim3 grid((unsigned)ew_ranges(elem, a.V), (unsigned)(a.C / kEwRows)), block(256);
   if (elem == 2)
     hipLaunchKernelGGL(topk_dz_from_z_kernel<Bf16>, grid, block, 0, st, a);
   else
