@@ -160,11 +160,15 @@ struct Carver {
   }
 };
 
+// Bytes of `rows` rows of row_bytes each in 64-byte panels (a last partial
+// piece takes a whole slot).
+size_t panel_bytes(int64_t rows, int64_t row_bytes) { return (size_t)rows * (size_t)cdiv(row_bytes, 64) * 64; }
+
 // Backward chunk buffers shared by both variants.
 struct ChunkPlan {
   int64_t C, ldz;
   int nrb_c, nrb_dh, ncb_dh, S_dh, nrb_dw, ncb_dw;
-  size_t o_dz, o_hT, o_dhp;
+  size_t o_dz, o_hT, o_dhp, o_hp;  // o_hp: the chunk's rows of H in panels
 };
 
 ChunkPlan plan_chunk(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows, Carver& cv) {
@@ -181,12 +185,17 @@ ChunkPlan plan_chunk(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_ro
   p.o_dz = cv.take((size_t)p.C * p.ldz * elem);
   p.o_hT = cv.take((size_t)d * p.C * elem);
   p.o_dhp = cv.take((size_t)p.S_dh * p.C * d * 4);
+  p.o_hp = cv.take(panel_bytes(p.C, d * elem));
   return p;
 }
 
 struct TopkPlan {
+  // the forward call: chunks of Cf rows (the default chunk size, whatever the
+  // backward's), nrb row blocks and S vocabulary splits per launch, partials
+  // of every row, the chunk's rows of H in panels
   int ntiles, nrb, S;
-  size_t o_pair, o_perm, o_ent, o_rowc, o_rows, o_count, o_part;
+  int64_t Cf;
+  size_t o_pair, o_perm, o_ent, o_rowc, o_rows, o_count, o_part, o_hp_f;
   ChunkPlan ch;
   size_t fwd_total, total;  // bytes the forward call needs; bytes both calls need
   // single-call forward + backward: per-chunk partials, the chunk's fp32
@@ -199,7 +208,8 @@ struct TopkPlan {
 TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t chunk_rows) {
   TopkPlan p{};
   p.ntiles = (int)cdiv(V, kd::kTileN);
-  p.nrb = (int)cdiv(T, kd::kTileM);
+  p.Cf = chunk_of(T, V, elem, 0);
+  p.nrb = (int)cdiv(p.Cf, kd::kTileM);
   p.S = splits_for(p.nrb, p.ntiles);
   Carver cv;
   // room for K + 1 entries per row: a cross-entropy label is one more
@@ -211,6 +221,7 @@ TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t
   p.o_count = cv.take(16);
   Carver fw = cv, bw = cv;  // forward partials and backward chunk buffers overlap
   p.o_part = fw.take((size_t)p.S * T * 16);
+  p.o_hp_f = fw.take(panel_bytes(p.Cf, d * elem));
   p.ch = plan_chunk(T, d, V, elem, chunk_rows, bw);
   p.fwd_total = fw.off;
   p.total = std::max(fw.off, bw.off);
@@ -224,8 +235,12 @@ TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t
 }
 
 struct FullPlan {
+  // the forward call as the top-K one, with the chunk's rows of both H and Ht
+  // in panels; the backward and the single call add Ht's panels to their
+  // chunk buffers
   int ntiles, nrb, S;
-  size_t o_rows, o_count, o_part;
+  int64_t Cf;
+  size_t o_rows, o_count, o_part, o_hp_f, o_htp_f, o_htp_b, o_htp_u;
   ChunkPlan ch;
   size_t fwd_total, total;
   // single-call forward + backward: each head through the 256-wide top-K
@@ -237,17 +252,21 @@ struct FullPlan {
   size_t o_part_s, o_part_t, o_rowc, o_pair0, o_zs, o_zt, o_terms, o_krev, fused_total;
 };
 
-FullPlan plan_full(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows) {
+FullPlan plan_full(int64_t T, int64_t d, int64_t dt, int64_t V, int elem, int64_t chunk_rows) {
   FullPlan p{};
   p.ntiles = (int)cdiv(V, kd::kTileNFull);
-  p.nrb = (int)cdiv(T, kd::kTileM);
+  p.Cf = chunk_of(T, V, elem, 0);
+  p.nrb = (int)cdiv(p.Cf, kd::kTileM);
   p.S = splits_for(p.nrb, p.ntiles);
   Carver cv;
   p.o_rows = cv.take((size_t)T * 4);
   p.o_count = cv.take(16);
   Carver fw = cv, bw = cv;
   p.o_part = fw.take((size_t)p.S * T * 32);
+  p.o_hp_f = fw.take(panel_bytes(p.Cf, d * elem));
+  p.o_htp_f = fw.take(panel_bytes(p.Cf, dt * elem));
   p.ch = plan_chunk(T, d, V, elem, chunk_rows, bw);
+  p.o_htp_b = bw.take(panel_bytes(p.ch.C, dt * elem));
   p.fwd_total = fw.off;
   p.total = std::max(fw.off, bw.off);
   Carver fu = cv;
@@ -259,6 +278,7 @@ FullPlan plan_full(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_rows
   p.o_rowc = fu.take((size_t)T * 16);
   p.o_pair0 = fu.take(16);
   p.ch_f = plan_chunk(T, d, V, elem, chunk_rows, fu);
+  p.o_htp_u = fu.take(panel_bytes(p.ch.C, dt * elem));
   p.o_zs = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
   p.o_zt = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
   p.o_terms = fu.take((size_t)C * p.nblk * 8);
@@ -480,8 +500,9 @@ kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_id
 
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
   KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, op.KE, op.prep, rd, z_topk, st));
+  char* hp = at<char>(workspace, p.o_hp_f);
   kd::TopkFwdArgs a{};
-  a.H = static_cast<const char*>(H);
+  a.Hp = hp;
   a.W = static_cast<const char*>(W);
   a.c = c;
   a.rd = rd;
@@ -489,8 +510,7 @@ kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_id
   a.part = part;
   a.part_stride = T;
   a.part_row0 = 0;
-  a.c0 = 0;
-  a.C = T;
+  a.C = p.Cf;
   a.T = T;
   a.d = d;
   a.V = V;
@@ -500,7 +520,11 @@ kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_id
   a.S = p.S;
   a.ntiles = p.ntiles;
   a.group = kRasterGroup;
-  KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
+  for (int64_t c0 = 0; c0 < T; c0 += p.Cf) {
+    KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(H, d * elem, c, c0, p.Cf, hp, st));
+    a.c0 = c0;
+    KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
+  }
   KD_LAUNCH("topk_combine", st, kd::launch_topk_combine(part, p.S, T, c, mask, rd, T, kl, lse, 0, T, true, st));
   return KD_OK;
 }
@@ -561,8 +585,10 @@ kd_status kd_topk_kl_bwd_ex(const void* H, const void* W, const int32_t* topk_id
   const int64_t nchunks = cdiv(T, ch.C);
   for (int64_t k = 0; k < nchunks; ++k) {
     const int64_t c0 = k * ch.C;
+    char* hp = at<char>(workspace, ch.o_hp);
+    KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(H, d * elem, c, c0, ch.C, hp, st));
     kd::TopkDzArgs za{};
-    za.H = static_cast<const char*>(H);
+    za.Hp = hp;
     za.W = static_cast<const char*>(W);
     za.c = c;
     za.rd = rd;
@@ -593,7 +619,7 @@ kd_status kd_full_kl_workspace_size(int64_t T, int64_t d, int64_t dt_hidden, int
   KD_TRY(need(bytes, "bytes"));
   KD_TRY(check_common(T, d, V, dt, 1.0f));
   KD_TRY(check_common(T, dt_hidden, V, dt, 1.0f));
-  *bytes = T == 0 ? 0 : plan_full(T, d, V, elem_of(dt), chunk_rows).total;
+  *bytes = T == 0 ? 0 : plan_full(T, d, dt_hidden, V, elem_of(dt), chunk_rows).total;
   return KD_OK;
 }
 
@@ -630,24 +656,25 @@ kd_status kd_full_kl_fwd_ex(const void* H, const void* Ws, const void* Ht, const
   KD_TRY(need_align(lse_s, 4, "lse_s"));
   KD_TRY(need_align(lse_t, 4, "lse_t"));
   const int elem = elem_of(dt);
-  const FullPlan p = plan_full(T, d, V, elem, 0);
+  const FullPlan p = plan_full(T, d, dt_hidden, V, elem, 0);
   KD_TRY(check_workspace(workspace, workspace_bytes, p.fwd_total));
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
   float* part = at<float>(workspace, p.o_part);
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
+  char* hp = at<char>(workspace, p.o_hp_f);
+  char* htp = at<char>(workspace, p.o_htp_f);
   kd::FullFwdArgs a{};
-  a.H = static_cast<const char*>(H);
+  a.Hp = hp;
   a.Ws = static_cast<const char*>(Ws);
-  a.Ht = static_cast<const char*>(Ht);
+  a.Htp = htp;
   a.Wt = static_cast<const char*>(Wt);
   a.c = c;
   a.part = part;
   a.part_stride = T;
   a.part_row0 = 0;
-  a.c0 = 0;
-  a.C = T;
+  a.C = p.Cf;
   a.T = T;
   a.d = d;
   a.dt = dt_hidden;
@@ -658,7 +685,12 @@ kd_status kd_full_kl_fwd_ex(const void* H, const void* Ws, const void* Ht, const
   a.group = kRasterGroup;
   a.c2 = (float)(1.4426950408889634 / (double)tau);
   a.tau_rows = mx.tau_rows;
-  KD_LAUNCH("full_fwd_tile", st, kd::launch_full_fwd(elem, a, st));
+  for (int64_t c0 = 0; c0 < T; c0 += p.Cf) {
+    KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(H, d * elem, c, c0, p.Cf, hp, st));
+    KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(Ht, dt_hidden * elem, c, c0, p.Cf, htp, st));
+    a.c0 = c0;
+    KD_LAUNCH("full_fwd_tile", st, kd::launch_full_fwd(elem, a, st));
+  }
   KD_LAUNCH("full_combine", st,
             kd::launch_full_combine(part, p.S, T, c, mask, T, mx.r, kl, lse_s, lse_t, kl_rev, 0, T, true, st));
   return KD_OK;
@@ -710,7 +742,7 @@ kd_status kd_full_kl_bwd_ex(const void* H, const void* Ws, const void* Ht, const
   KD_TRY(need_align(grad_kl, 4, "grad_kl"));
   if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
   const int elem = elem_of(dt);
-  const FullPlan p = plan_full(T, d, V, elem, chunk_rows);
+  const FullPlan p = plan_full(T, d, dt_hidden, V, elem, chunk_rows);
   KD_TRY(check_workspace(workspace, workspace_bytes, p.total));
 
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
@@ -724,10 +756,14 @@ kd_status kd_full_kl_bwd_ex(const void* H, const void* Ws, const void* Ht, const
   const int64_t nchunks = cdiv(T, ch.C);
   for (int64_t k = 0; k < nchunks; ++k) {
     const int64_t c0 = k * ch.C;
+    char* hp = at<char>(workspace, ch.o_hp);
+    char* htp = at<char>(workspace, p.o_htp_b);
+    KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(H, d * elem, c, c0, ch.C, hp, st));
+    KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(Ht, dt_hidden * elem, c, c0, ch.C, htp, st));
     kd::FullDzArgs za{};
-    za.H = static_cast<const char*>(H);
+    za.Hp = hp;
     za.Ws = static_cast<const char*>(Ws);
-    za.Ht = static_cast<const char*>(Ht);
+    za.Htp = htp;
     za.Wt = static_cast<const char*>(Wt);
     za.c = c;
     za.lse_s = lse_s;
@@ -762,7 +798,7 @@ kd_status kd_full_kl_fwd_bwd_workspace_size(int64_t T, int64_t d, int64_t dt_hid
   KD_TRY(check_common(T, d, V, dt, 1.0f));
   KD_TRY(check_common(T, dt_hidden, V, dt, 1.0f));
   if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
-  *bytes = T == 0 ? 0 : plan_full(T, d, V, elem_of(dt), chunk_rows).fused_total;
+  *bytes = T == 0 ? 0 : plan_full(T, d, dt_hidden, V, elem_of(dt), chunk_rows).fused_total;
   return KD_OK;
 }
 
@@ -812,7 +848,7 @@ kd_status kd_full_kl_fwd_bwd_ex(const void* H, const void* Ws, const void* Ht, c
   KD_TRY(need_align(lse_s, 4, "lse_s"));
   KD_TRY(need_align(lse_t, 4, "lse_t"));
   const int elem = elem_of(dt);
-  const FullPlan p = plan_full(T, d, V, elem, chunk_rows);
+  const FullPlan p = plan_full(T, d, dt_hidden, V, elem, chunk_rows);
   KD_TRY(check_workspace(workspace, workspace_bytes, p.fused_total));
 
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
@@ -841,9 +877,13 @@ kd_status kd_full_kl_fwd_bwd_ex(const void* H, const void* Ws, const void* Ht, c
   for (int64_t k = 0; k < nchunks; ++k) {
     const int64_t c0 = k * ch.C;
     // the chunk's logits of each head, kept in fp32, and each head's log Z partials
+    char* hp = at<char>(workspace, ch.o_hp);
+    char* htp = at<char>(workspace, p.o_htp_u);
+    KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(H, d * elem, c, c0, ch.C, hp, st));
+    KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(Ht, dt_hidden * elem, c, c0, ch.C, htp, st));
     for (int head = 0; head < 2; ++head) {
       kd::TopkFwdArgs a{};
-      a.H = static_cast<const char*>(head ? Ht : H);
+      a.Hp = head ? htp : hp;
       a.W = static_cast<const char*>(head ? Wt : Ws);
       a.c = c;
       a.rd = rd;
@@ -977,8 +1017,10 @@ kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* top
   for (int64_t k = 0; k < nchunks; ++k) {
     const int64_t c0 = k * ch.C;
     // the chunk's logits: log Z partials, the top-K gather, and z kept in fp32
+    char* hp = at<char>(workspace, ch.o_hp);
+    KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(H, d * elem, c, c0, ch.C, hp, st));
     kd::TopkFwdArgs a{};
-    a.H = static_cast<const char*>(H);
+    a.Hp = hp;
     a.W = static_cast<const char*>(W);
     a.c = c;
     a.rd = rd;

@@ -203,12 +203,12 @@ __global__ __launch_bounds__(kThreads, 1) void full_fwd_kernel(FullFwdArgs a) {
   const int32_t* rows = a.c.rows + a.c0;
 
   Main ms, mt;
-  ms.init(a.H,
-          [&](int r) -> const char* { return row0 + r < M ? a.H + (long)rows[row0 + r] * a.d * E::kElem : nullptr; },
-          a.Ws, a.V * E::kElem, a.V, a.d);
-  mt.init(a.Ht,
-          [&](int r) -> const char* { return row0 + r < M ? a.Ht + (long)rows[row0 + r] * a.dt * E::kElem : nullptr; },
-          a.Wt, a.V * E::kElem, a.V, a.dt);
+  // rows past the valid ones read the last valid row: they only feed
+  // accumulator rows that the epilogue discards
+  ms.init(a.Hp, [&](int r) -> const char* { return a.Hp + min((long)row0 + r, M - 1) * kRowB; }, a.Ws,
+          a.V * E::kElem, a.V, a.d, a.C * kRowB);
+  mt.init(a.Htp, [&](int r) -> const char* { return a.Htp + min((long)row0 + r, M - 1) * kRowB; }, a.Wt,
+          a.V * E::kElem, a.V, a.dt, a.C * kRowB);
 
   const int ti = row0 + (int)threadIdx.x;
   FullFwdRow R{-INFINITY, 0.f, -INFINITY, 0.f, 0.f, 0.f, a.c2, ti < M};
@@ -245,12 +245,12 @@ __global__ __launch_bounds__(kThreads, 1) void full_dz_kernel(FullDzArgs a) {
   const int32_t* rows = a.c.rows + a.c0;
 
   Main ms, mt;
-  ms.init(a.H,
-          [&](int r) -> const char* { return row0 + r < M ? a.H + (long)rows[row0 + r] * a.d * E::kElem : nullptr; },
-          a.Ws, a.V * E::kElem, a.V, a.d);
-  mt.init(a.Ht,
-          [&](int r) -> const char* { return row0 + r < M ? a.Ht + (long)rows[row0 + r] * a.dt * E::kElem : nullptr; },
-          a.Wt, a.V * E::kElem, a.V, a.dt);
+  // rows past the valid ones read the last valid row: they only feed
+  // accumulator rows that the epilogue discards
+  ms.init(a.Hp, [&](int r) -> const char* { return a.Hp + min((long)row0 + r, M - 1) * kRowB; }, a.Ws,
+          a.V * E::kElem, a.V, a.d, a.C * kRowB);
+  mt.init(a.Htp, [&](int r) -> const char* { return a.Htp + min((long)row0 + r, M - 1) * kRowB; }, a.Wt,
+          a.V * E::kElem, a.V, a.dt, a.C * kRowB);
 
   const int ti = row0 + (int)threadIdx.x;
   FullDzRow R;
@@ -360,14 +360,15 @@ hipError_t launch_full_from_z(int elem, const FullFromZArgs& a, hipStream_t st) 
 }
 
 // The direct-load ring needs bf16 and both hidden widths multiples of 128.
-static bool full_dma_ok(int64_t T, int64_t d, int64_t dt, int64_t V) {
-  return d % kDmaKMult == 0 && dt % kDmaKMult == 0 && fits32(T * d * 2) && fits32(T * dt * 2) && fits32(d * V * 2) &&
+// C: rows of the launch's panel buffers
+static bool full_dma_ok(int64_t C, int64_t d, int64_t dt, int64_t V) {
+  return d % kDmaKMult == 0 && dt % kDmaKMult == 0 && fits32(C * d * 2) && fits32(C * dt * 2) && fits32(d * V * 2) &&
          fits32(dt * V * 2);
 }
 
 hipError_t launch_full_fwd(int elem, const FullFwdArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
-  if (elem == 2 && full_dma_ok(a.T, a.d, a.dt, a.V))
+  if (elem == 2 && full_dma_ok(a.C, a.d, a.dt, a.V))
     hipLaunchKernelGGL((full_fwd_kernel<DmaNN<kBN>, Bf16>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((full_fwd_kernel<GenNN<Bf16, kBN>, Bf16>), grid, block, 0, st, a);
@@ -378,7 +379,7 @@ hipError_t launch_full_fwd(int elem, const FullFwdArgs& a, hipStream_t st) {
 
 hipError_t launch_full_dz(int elem, const FullDzArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
-  if (elem == 2 && full_dma_ok(a.T, a.d, a.dt, a.V))
+  if (elem == 2 && full_dma_ok(a.C, a.d, a.dt, a.V))
     hipLaunchKernelGGL((full_dz_kernel<DmaNN<kBN>, Bf16>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((full_dz_kernel<GenNN<Bf16, kBN>, Bf16>), grid, block, 0, st, a);

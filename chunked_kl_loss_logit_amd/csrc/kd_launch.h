@@ -68,6 +68,12 @@ hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Co
 // (piece p of row j at (p d + j) * 64 bytes).
 hipError_t launch_gather_transpose(const void* H, int elem, int64_t d, Compact c, int64_t c0, int64_t C, void* out,
                                    hipStream_t st);
+// The rows of one chunk of compacted rows (row_bytes each, a multiple of 16)
+// in panels of C rows: byte b of row rows[c0 + i] at (b / 64 * C + i) * 64 +
+// b % 64, for i < valid rows of the chunk.  The tiles read their
+// k-contiguous operand from these panels.
+hipError_t launch_gather_panels(const void* H, int64_t row_bytes, Compact c, int64_t c0, int64_t C, void* out,
+                                hipStream_t st);
 // dH[rows[c0 + i]] = sum_s part[s][i] (converted to the element type)
 hipError_t launch_reduce_dh(const float* part, int S, int64_t C, int64_t d, Compact c, int64_t c0, void* dH,
                             int elem, hipStream_t st);
@@ -76,7 +82,7 @@ hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);
 
 // ---------------------------------------------------------------- top-K tiles
 struct TopkFwdArgs {
-  const char* H;  // [T][d]
+  const char* Hp;  // rows [c0, c0 + C) of H in panels of C rows (launch_gather_panels)
   const char* W;  // [d][V]
   Compact c;
   TopkRowData rd;
@@ -95,7 +101,7 @@ struct TopkFwdArgs {
 hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st);
 
 struct TopkDzArgs {
-  const char* H;
+  const char* Hp;  // rows [c0, c0 + C) of H in panels of C rows
   const char* W;
   Compact c;
   TopkRowData rd;
@@ -127,9 +133,9 @@ hipError_t launch_topk_dz_from_z(int elem, const TopkDzFromZArgs& a, hipStream_t
 
 // ---------------------------------------------------------------- full-vocabulary tiles
 struct FullFwdArgs {
-  const char* H;   // [T][d]
-  const char* Ws;  // [d][V]
-  const char* Ht;  // [T][dt]
+  const char* Hp;   // rows [c0, c0 + C) of H in panels of C rows
+  const char* Ws;   // [d][V]
+  const char* Htp;  // rows [c0, c0 + C) of Ht in panels of C rows
   const char* Wt;  // [dt][V]
   Compact c;
   float* part;     // [S][part_stride][8], row p of a split is compacted row part_row0 + p
@@ -151,9 +157,9 @@ struct FullMix {
 };
 
 struct FullDzArgs {
-  const char* H;
+  const char* Hp;   // rows [c0, c0 + C) of H in panels of C rows
   const char* Ws;
-  const char* Ht;
+  const char* Htp;  // rows [c0, c0 + C) of Ht in panels of C rows
   const char* Wt;
   Compact c;
   const float* lse_s;

@@ -407,6 +407,29 @@ hipError_t launch_gather_transpose(const void* H, int elem, int64_t d, Compact c
   return hipGetLastError();
 }
 
+// Rows of one chunk of compacted rows in panels of C rows: byte b of H row
+// rows[c0 + i] goes to panel_off(C, i, b).  A block covers 64 rows of one
+// 64-byte piece, four threads per piece, so a wave writes 16 consecutive
+// rows of the piece: one contiguous kilobyte.  Rows past the chunk's valid
+// rows are not written (the tiles never read them).
+__global__ __launch_bounds__(256) void gather_panels_kernel(const char* H, long rowb, Compact c, long c0, long C,
+                                                            char* out) {
+  const long M = min(C, (long)*c.count - c0);
+  const long i = (long)blockIdx.y * 64 + (threadIdx.x >> 2);
+  const long b = (long)blockIdx.x * kRowB + 16 * (threadIdx.x & 3);
+  if (i >= M || b >= rowb) return;
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(H + (long)c.rows[c0 + i] * rowb + b);
+  *reinterpret_cast<u32x4_t*>(out + panel_off(C, i, b)) = v;
+}
+
+hipError_t launch_gather_panels(const void* H, int64_t row_bytes, Compact c, int64_t c0, int64_t C, void* out,
+                                hipStream_t st) {
+  const dim3 grid((unsigned)((row_bytes + kRowB - 1) / kRowB), (unsigned)((C + 63) / 64));
+  hipLaunchKernelGGL(gather_panels_kernel, grid, dim3(256), 0, st, static_cast<const char*>(H), (long)row_bytes, c,
+                     (long)c0, (long)C, static_cast<char*>(out));
+  return hipGetLastError();
+}
+
 // dH[rows[c0 + i]][j..j+3] = sum over s of part[s][i][j..j+3], in split order.
 template <int ELEM>
 __global__ void reduce_dh_kernel(const float* part, int S, long C, long d, Compact c, long c0, void* dH) {

@@ -236,12 +236,8 @@ __global__ __launch_bounds__(kThreads, 1) void topk_fwd_kernel(TopkFwdArgs a) {
 
   Main mainloop;
   mainloop.init(
-      a.H,
-      [&](int r) -> const char* {
-        const long i = row0 + r;
-        return i < M ? a.H + (long)rows[i] * a.d * E::kElem : nullptr;
-      },
-      a.W, a.V * E::kElem, a.V, a.d);
+      a.Hp, [&](int r) -> const char* { return row0 + r < M ? a.Hp + (row0 + r) * kRowB : nullptr; }, a.W,
+      a.V * E::kElem, a.V, a.d, a.C * kRowB);
 
   const int ti = row0 + (int)threadIdx.x;
   FwdRow<kZ> R;
@@ -298,12 +294,8 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_kernel(TopkDzArgs a) {
 
   Main mainloop;
   mainloop.init(
-      a.H,
-      [&](int r) -> const char* {
-        const long i = row0 + r;
-        return i < M ? a.H + (long)rows[i] * a.d * E::kElem : nullptr;
-      },
-      a.W, a.V * E::kElem, a.V, a.d);
+      a.Hp, [&](int r) -> const char* { return row0 + r < M ? a.Hp + (row0 + r) * kRowB : nullptr; }, a.W,
+      a.V * E::kElem, a.V, a.d, a.C * kRowB);
 
   const int ti = row0 + (int)threadIdx.x;
   DzRow R;
@@ -411,7 +403,7 @@ hipError_t launch_topk_dz_from_z(int elem, const TopkDzFromZArgs& a, hipStream_t
 template <bool kZ>
 static void launch_topk_fwd_z(int elem, const TopkFwdArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
-  if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.T * a.d * 2) && fits32(a.d * a.V * 2))
+  if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.C * a.d * 2) && fits32(a.d * a.V * 2))
     hipLaunchKernelGGL((topk_fwd_kernel<DmaNN<kBN>, Bf16, kZ>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((topk_fwd_kernel<GenNN<Bf16, kBN>, Bf16, kZ>), grid, block, 0, st, a);
@@ -429,7 +421,7 @@ hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st) {
 
 hipError_t launch_topk_dz(int elem, const TopkDzArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
-  if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.T * a.d * 2) && fits32(a.d * a.V * 2))
+  if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.C * a.d * 2) && fits32(a.d * a.V * 2))
     hipLaunchKernelGGL((topk_dz_kernel<DmaNN<kBN>, Bf16>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((topk_dz_kernel<GenNN<Bf16, kBN>, Bf16>), grid, block, 0, st, a);
