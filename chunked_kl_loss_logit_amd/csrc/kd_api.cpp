@@ -130,10 +130,42 @@ constexpr int kRasterGroup = 4;
 // Vocabulary splits of the tile kernels: enough workgroups to fill the CUs,
 // and at least 8 so that at large T the workgroups running together read
 // several W panels instead of all hammering one.
-int splits_for(int64_t nrb, int64_t ntiles) {
-  int64_t s = std::max<int64_t>(cdiv(256, std::max<int64_t>(1, nrb)), 8);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(s, ntiles));
+// Splits of `work` units (vocabulary tiles or stage groups) for `units`
+// independent tile rows, at most max_s: the tile kernels run one workgroup
+// per CU, so the launch takes ceil(units * S / 256) rounds of ceil(work / S)
+// units each, plus about two units per workgroup of fixed cost (ring fill,
+// partials); the S with the lowest total wins, ties going to fewer splits.  A
+// rule such as ceil(256 / units) overshoots 256 workgroups by a few whenever
+// units does not divide 256 (15 row blocks: 270 workgroups, a second round
+// for 14 of them).
+int balanced_splits(int64_t units, int64_t work, int64_t max_s) {
+  units = std::max<int64_t>(1, units);
+  int best = 1;
+  int64_t cost = INT64_MAX;
+  for (int64_t s = 1; s <= std::max<int64_t>(1, std::min(max_s, work)); ++s) {
+    const int64_t c = cdiv(units * s, 256) * (cdiv(work, s) + 2);
+    if (c < cost) {
+      cost = c;
+      best = (int)s;
+    }
+  }
+  return best;
 }
+
+int splits_for(int64_t nrb, int64_t ntiles) { return balanced_splits(nrb, ntiles, ntiles); }
+
+// Launch shape of the tile kernels for the chunk of C rows at c0: row blocks
+// of the rows it can hold (a last partial chunk gets fewer, and more splits),
+// and the splits that fill the GPU with them.  S never exceeds
+// max_splits(ntiles), which sizes the per-chunk partial buffers.
+struct ChunkShape {
+  int nrb, S;
+};
+ChunkShape chunk_shape(int64_t T, int64_t c0, int64_t C, int64_t ntiles) {
+  const int nrb = (int)cdiv(std::min(C, T - c0), kd::kTileM);
+  return {nrb, splits_for(nrb, ntiles)};
+}
+int64_t max_splits(int64_t ntiles) { return splits_for(1, ntiles); }
 
 // Rows per backward chunk: the request (or the default) rounded up to whole
 // 256-row tiles, at most the rows present, and for bf16 at most what keeps
@@ -178,8 +210,10 @@ ChunkPlan plan_chunk(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_ro
   p.nrb_c = (int)(p.C / kd::kTileM);
   p.nrb_dh = p.nrb_c;
   p.ncb_dh = (int)cdiv(d, 256);
-  const int64_t nstv = cdiv(V * elem, 128);
-  p.S_dh = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(768, (int64_t)p.nrb_dh * p.ncb_dh), nstv));
+  // dH splits the vocabulary (whole groups of four 64-byte stages); at most
+  // enough splits for four rounds, which bounds the fp32 partials
+  const int64_t units = (int64_t)p.nrb_dh * p.ncb_dh;
+  p.S_dh = balanced_splits(units, cdiv(V * elem, 256), std::max<int64_t>(1, cdiv(1024, units)));
   p.nrb_dw = (int)cdiv(d, 256);
   p.ncb_dw = (int)cdiv(V, 256);
   p.o_dz = cv.take((size_t)p.C * p.ldz * elem);
@@ -191,16 +225,15 @@ ChunkPlan plan_chunk(int64_t T, int64_t d, int64_t V, int elem, int64_t chunk_ro
 
 struct TopkPlan {
   // the forward call: chunks of Cf rows (the default chunk size, whatever the
-  // backward's), nrb row blocks and S vocabulary splits per launch, partials
-  // of every row, the chunk's rows of H in panels
-  int ntiles, nrb, S;
+  // backward's), each with its own launch shape and combine, so the partials
+  // hold one chunk; the chunk's rows of H in panels
+  int ntiles;
   int64_t Cf;
   size_t o_pair, o_perm, o_ent, o_rowc, o_rows, o_count, o_part, o_hp_f;
   ChunkPlan ch;
   size_t fwd_total, total;  // bytes the forward call needs; bytes both calls need
   // single-call forward + backward: per-chunk partials, the chunk's fp32
   // logits and the backward chunk buffers all live at once
-  int S_c;
   ChunkPlan ch_f;
   size_t o_part_c, o_z, fused_total;
 };
@@ -209,8 +242,6 @@ TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t
   TopkPlan p{};
   p.ntiles = (int)cdiv(V, kd::kTileN);
   p.Cf = chunk_of(T, V, elem, 0);
-  p.nrb = (int)cdiv(p.Cf, kd::kTileM);
-  p.S = splits_for(p.nrb, p.ntiles);
   Carver cv;
   // room for K + 1 entries per row: a cross-entropy label is one more
   p.o_pair = cv.take((size_t)T * (K + 1) * 8);
@@ -220,14 +251,13 @@ TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t
   p.o_rows = cv.take((size_t)T * 4);
   p.o_count = cv.take(16);
   Carver fw = cv, bw = cv;  // forward partials and backward chunk buffers overlap
-  p.o_part = fw.take((size_t)p.S * T * 16);
+  p.o_part = fw.take((size_t)max_splits(p.ntiles) * p.Cf * 16);
   p.o_hp_f = fw.take(panel_bytes(p.Cf, d * elem));
   p.ch = plan_chunk(T, d, V, elem, chunk_rows, bw);
   p.fwd_total = fw.off;
   p.total = std::max(fw.off, bw.off);
   Carver fu = cv;
-  p.S_c = splits_for(cdiv(chunk_of(T, V, elem, chunk_rows), kd::kTileM), p.ntiles);
-  p.o_part_c = fu.take((size_t)p.S_c * chunk_of(T, V, elem, chunk_rows) * 16);
+  p.o_part_c = fu.take((size_t)max_splits(p.ntiles) * chunk_of(T, V, elem, chunk_rows) * 16);
   p.ch_f = plan_chunk(T, d, V, elem, chunk_rows, fu);
   p.o_z = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
   p.fused_total = fu.off;
@@ -238,7 +268,7 @@ struct FullPlan {
   // the forward call as the top-K one, with the chunk's rows of both H and Ht
   // in panels; the backward and the single call add Ht's panels to their
   // chunk buffers
-  int ntiles, nrb, S;
+  int ntiles;
   int64_t Cf;
   size_t o_rows, o_count, o_part, o_hp_f, o_htp_f, o_htp_b, o_htp_u;
   ChunkPlan ch;
@@ -247,7 +277,7 @@ struct FullPlan {
   // tiles (per-chunk split partials of both, per-row constants, a dummy
   // entry list), the chunk's fp32 logits of both heads, the elementwise
   // pass's per-row terms, per-row reverse KL, and the backward chunk buffers
-  int S_c, nblk;
+  int nblk;
   ChunkPlan ch_f;
   size_t o_part_s, o_part_t, o_rowc, o_pair0, o_zs, o_zt, o_terms, o_krev, fused_total;
 };
@@ -256,13 +286,11 @@ FullPlan plan_full(int64_t T, int64_t d, int64_t dt, int64_t V, int elem, int64_
   FullPlan p{};
   p.ntiles = (int)cdiv(V, kd::kTileNFull);
   p.Cf = chunk_of(T, V, elem, 0);
-  p.nrb = (int)cdiv(p.Cf, kd::kTileM);
-  p.S = splits_for(p.nrb, p.ntiles);
   Carver cv;
   p.o_rows = cv.take((size_t)T * 4);
   p.o_count = cv.take(16);
   Carver fw = cv, bw = cv;
-  p.o_part = fw.take((size_t)p.S * T * 32);
+  p.o_part = fw.take((size_t)max_splits(p.ntiles) * p.Cf * 32);
   p.o_hp_f = fw.take(panel_bytes(p.Cf, d * elem));
   p.o_htp_f = fw.take(panel_bytes(p.Cf, dt * elem));
   p.ch = plan_chunk(T, d, V, elem, chunk_rows, bw);
@@ -271,10 +299,9 @@ FullPlan plan_full(int64_t T, int64_t d, int64_t dt, int64_t V, int elem, int64_
   p.total = std::max(fw.off, bw.off);
   Carver fu = cv;
   const int64_t C = chunk_of(T, V, elem, chunk_rows);
-  p.S_c = splits_for(cdiv(C, kd::kTileM), cdiv(V, kd::kTileN));
   p.nblk = kd::full_from_z_blocks(elem, V);
-  p.o_part_s = fu.take((size_t)p.S_c * C * 16);
-  p.o_part_t = fu.take((size_t)p.S_c * C * 16);
+  p.o_part_s = fu.take((size_t)max_splits(cdiv(V, kd::kTileN)) * C * 16);
+  p.o_part_t = fu.take((size_t)max_splits(cdiv(V, kd::kTileN)) * C * 16);
   p.o_rowc = fu.take((size_t)T * 16);
   p.o_pair0 = fu.take(16);
   p.ch_f = plan_chunk(T, d, V, elem, chunk_rows, fu);
@@ -508,24 +535,25 @@ kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_id
   a.rd = rd;
   a.z_topk = z_topk;
   a.part = part;
-  a.part_stride = T;
-  a.part_row0 = 0;
+  a.part_stride = p.Cf;
   a.C = p.Cf;
   a.T = T;
   a.d = d;
   a.V = V;
   a.K = op.KE;
   a.Kz = K;
-  a.nrb = p.nrb;
-  a.S = p.S;
   a.ntiles = p.ntiles;
   a.group = kRasterGroup;
   for (int64_t c0 = 0; c0 < T; c0 += p.Cf) {
+    const ChunkShape sh = chunk_shape(T, c0, p.Cf, p.ntiles);
     KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(H, d * elem, c, c0, p.Cf, hp, st));
-    a.c0 = c0;
+    a.c0 = a.part_row0 = c0;
+    a.nrb = sh.nrb;
+    a.S = sh.S;
     KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
+    KD_LAUNCH("topk_combine", st,
+              kd::launch_topk_combine(part, sh.S, p.Cf, c, mask, rd, T, kl, lse, c0, c0 + p.Cf, c0 == 0, st));
   }
-  KD_LAUNCH("topk_combine", st, kd::launch_topk_combine(part, p.S, T, c, mask, rd, T, kl, lse, 0, T, true, st));
   return KD_OK;
 }
 
@@ -602,10 +630,11 @@ kd_status kd_topk_kl_bwd_ex(const void* H, const void* W, const int32_t* topk_id
     za.d = d;
     za.V = V;
     za.K = op.KE;
-    za.nrb = ch.nrb_c;
+    const ChunkShape sh = chunk_shape(T, c0, ch.C, p.ntiles);
+    za.nrb = sh.nrb;
     za.ntiles = p.ntiles;
     za.group = kRasterGroup;
-    za.S = splits_for(ch.nrb_c, p.ntiles);
+    za.S = sh.S;
     KD_LAUNCH("topk_dz_tile", st, kd::launch_topk_dz(elem, za, st));
     KD_TRY(grad_chunk(H, W, dH, dW, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
   }
@@ -672,27 +701,28 @@ kd_status kd_full_kl_fwd_ex(const void* H, const void* Ws, const void* Ht, const
   a.Wt = static_cast<const char*>(Wt);
   a.c = c;
   a.part = part;
-  a.part_stride = T;
-  a.part_row0 = 0;
+  a.part_stride = p.Cf;
   a.C = p.Cf;
   a.T = T;
   a.d = d;
   a.dt = dt_hidden;
   a.V = V;
-  a.nrb = p.nrb;
-  a.S = p.S;
   a.ntiles = p.ntiles;
   a.group = kRasterGroup;
   a.c2 = (float)(1.4426950408889634 / (double)tau);
   a.tau_rows = mx.tau_rows;
   for (int64_t c0 = 0; c0 < T; c0 += p.Cf) {
+    const ChunkShape sh = chunk_shape(T, c0, p.Cf, p.ntiles);
     KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(H, d * elem, c, c0, p.Cf, hp, st));
     KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(Ht, dt_hidden * elem, c, c0, p.Cf, htp, st));
-    a.c0 = c0;
+    a.c0 = a.part_row0 = c0;
+    a.nrb = sh.nrb;
+    a.S = sh.S;
     KD_LAUNCH("full_fwd_tile", st, kd::launch_full_fwd(elem, a, st));
+    KD_LAUNCH("full_combine", st,
+              kd::launch_full_combine(part, sh.S, p.Cf, c, mask, T, mx.r, kl, lse_s, lse_t, kl_rev, c0, c0 + p.Cf,
+                                      c0 == 0, st));
   }
-  KD_LAUNCH("full_combine", st,
-            kd::launch_full_combine(part, p.S, T, c, mask, T, mx.r, kl, lse_s, lse_t, kl_rev, 0, T, true, st));
   return KD_OK;
 }
 
@@ -777,10 +807,11 @@ kd_status kd_full_kl_bwd_ex(const void* H, const void* Ws, const void* Ht, const
     za.d = d;
     za.dt = dt_hidden;
     za.V = V;
-    za.nrb = ch.nrb_c;
+    const ChunkShape sh = chunk_shape(T, c0, ch.C, p.ntiles);
+    za.nrb = sh.nrb;
     za.ntiles = p.ntiles;
     za.group = kRasterGroup;
-    za.S = splits_for(ch.nrb_c, p.ntiles);
+    za.S = sh.S;
     za.c2 = (float)(1.4426950408889634 / (double)tau);
     za.inv_tau = 1.0f / tau;
     za.mix = mx;
@@ -881,6 +912,7 @@ kd_status kd_full_kl_fwd_bwd_ex(const void* H, const void* Ws, const void* Ht, c
     char* htp = at<char>(workspace, p.o_htp_u);
     KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(H, d * elem, c, c0, ch.C, hp, st));
     KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(Ht, dt_hidden * elem, c, c0, ch.C, htp, st));
+    const ChunkShape sh = chunk_shape(T, c0, ch.C, cdiv(V, kd::kTileN));
     for (int head = 0; head < 2; ++head) {
       kd::TopkFwdArgs a{};
       a.Hp = head ? htp : hp;
@@ -899,14 +931,14 @@ kd_status kd_full_kl_fwd_bwd_ex(const void* H, const void* Ws, const void* Ht, c
       a.V = V;
       a.K = 0;
       a.Kz = 0;
-      a.nrb = ch.nrb_c;
-      a.S = p.S_c;
+      a.nrb = sh.nrb;
+      a.S = sh.S;
       a.ntiles = (int)cdiv(V, kd::kTileN);
       a.group = kRasterGroup;
       KD_LAUNCH(head ? "full_teacher_tile" : "full_student_tile", st, kd::launch_topk_fwd(elem, a, st));
     }
     KD_LAUNCH("full_lse_combine", st,
-              kd::launch_full_lse_combine(part_s, part_t, p.S_c, ch.C, c, mask, T, kl, lse_s, lse_t, kl_rev, c0,
+              kd::launch_full_lse_combine(part_s, part_t, sh.S, ch.C, c, mask, T, kl, lse_s, lse_t, kl_rev, c0,
                                           c0 + ch.C, k == 0, st));
     // one pass over the kept logits: both KL terms with the final
     // normalisers and dZ (no second pair of projections); with the reverse
@@ -1019,6 +1051,7 @@ kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* top
     // the chunk's logits: log Z partials, the top-K gather, and z kept in fp32
     char* hp = at<char>(workspace, ch.o_hp);
     KD_LAUNCH("gather_panels", st, kd::launch_gather_panels(H, d * elem, c, c0, ch.C, hp, st));
+    const ChunkShape sh = chunk_shape(T, c0, ch.C, p.ntiles);
     kd::TopkFwdArgs a{};
     a.Hp = hp;
     a.W = static_cast<const char*>(W);
@@ -1037,13 +1070,13 @@ kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* top
     a.V = V;
     a.K = op.KE;
     a.Kz = K;
-    a.nrb = ch.nrb_c;
-    a.S = p.S_c;
+    a.nrb = sh.nrb;
+    a.S = sh.S;
     a.ntiles = p.ntiles;
     a.group = kRasterGroup;
     KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
     KD_LAUNCH("topk_combine", st,
-              kd::launch_topk_combine(part, p.S_c, ch.C, c, mask, rd, T, kl, lse, c0, c0 + ch.C, k == 0, st));
+              kd::launch_topk_combine(part, sh.S, ch.C, c, mask, rd, T, kl, lse, c0, c0 + ch.C, k == 0, st));
     // dZ from the kept logits: no second projection
     kd::TopkDzFromZArgs za{};
     za.z = z;

@@ -288,64 +288,77 @@ hipError_t launch_full_rowc(Compact c, int64_t T, const float* tau_rows, float c
   return hipGetLastError();
 }
 
-// Block geometry as kEwRows / kEwRanges say: a thread handles EPT consecutive
-// columns (16 bytes of dZ) of its row in each piece of the block's range, and
-// sums the row's two KL terms over them; the four threads of a row then add
-// theirs, in a fixed order, for the terms array.
+// Block geometry as kEwRows / kEwRanges say.  A lane handles EPT consecutive
+// columns (16 bytes of dZ) of each of its wave's 4 rows per tile, and sums the
+// rows' two KL terms over them; at the end each row's sums are added over the
+// wave's lanes in a fixed order, for the terms array.  Without dz (the terms
+// pass of the KL mixture) nothing goes through LDS.
 template <class E>
 __global__ __launch_bounds__(256) void full_from_z_kernel(FullFromZArgs a) {
   constexpr int EPT = E::kEpc;
-  constexpr int PC = kRowB / E::kElem;  // columns per piece
-  const long i = (long)blockIdx.y * kEwRows + (threadIdx.x >> 2);  // row of the chunk
-  const int sub = threadIdx.x & 3;
-  const long np = (a.V * E::kElem + kRowB - 1) / kRowB;
-  const long pb = np * blockIdx.x / gridDim.x, pe = np * (blockIdx.x + 1) / gridDim.x;
+  constexpr int NT = 64 * EPT;   // columns per tile
+  constexpr int RS = 1024 + 16;  // LDS row stride, bytes
+  __shared__ __attribute__((aligned(16))) char tile[kEwRows * RS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long M = min(a.C, (long)*a.c.count - a.c0);
-  const bool rv = i < M;
-  const long t = rv ? a.c.rows[a.c0 + i] : 0;
-  const FullDzConst k = full_dz_const(rv, t, a.lse_s, a.lse_t, a.g, a.c2, a.inv_tau, a.mix);
-  const float* sr = a.zs + i * a.ldz;
-  const float* ur = a.zt + i * a.ldz;
-  float tp = 0.f, tq = 0.f;  // sum p (yt - ys), sum q (ys - yt), base 2
-  for (long p = pb; p < pe; ++p) {
-    const long v0 = p * PC + sub * EPT;
-    if (v0 >= a.V) break;
-    float o[EPT];
-    if (rv) {
+  const long i0 = (long)blockIdx.y * kEwRows;
+  const long nt = (a.V + NT - 1) / NT;
+  const long jb = nt * blockIdx.x / gridDim.x, je = nt * (blockIdx.x + 1) / gridDim.x;
+  FullDzConst k[4];
+  bool rv[4];
+  float tp[4], tq[4];  // sum p (yt - ys), sum q (ys - yt), base 2
 #pragma unroll
-      for (int e = 0; e < EPT; e += 4) {
-        const float4 fs = *reinterpret_cast<const float4*>(sr + v0 + e);
-        const float4 fu = *reinterpret_cast<const float4*>(ur + v0 + e);
-        const float s4[4] = {fs.x, fs.y, fs.z, fs.w}, u4[4] = {fu.x, fu.y, fu.z, fu.w};
+  for (int r = 0; r < 4; ++r) {
+    const long i = i0 + 4 * w + r;
+    rv[r] = i < M;
+    k[r] = full_dz_const(rv[r], rv[r] ? a.c.rows[a.c0 + i] : 0, a.lse_s, a.lse_t, a.g, a.c2, a.inv_tau, a.mix);
+    tp[r] = tq[r] = 0.f;
+  }
+  for (long j = jb; j < je; ++j) {
+    const long v0 = j * NT + lane * EPT;
+    const bool in = v0 < a.V;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o[e + q] = k(s4[q], u4[q]);
-          const float ds = fmaf(s4[q], k.c2, -k.Ls2), dt = fmaf(u4[q], k.c2, -k.Lt2);
-          const float dy = (u4[q] - s4[q]) * k.c2;  // yt - ys
-          tp = fmaf(fast_exp2(dt), dy, tp);
-          tq = fmaf(fast_exp2(ds), -dy, tq);
+    for (int r = 0; r < 4; ++r) {
+      float o[EPT];
+      if (rv[r] && in) {
+        const float* sr = a.zs + (i0 + 4 * w + r) * a.ldz + v0;
+        const float* ur = a.zt + (i0 + 4 * w + r) * a.ldz + v0;
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+          const float4 fs = *reinterpret_cast<const float4*>(sr + e);
+          const float4 fu = *reinterpret_cast<const float4*>(ur + e);
+          const float s4[4] = {fs.x, fs.y, fs.z, fs.w}, u4[4] = {fu.x, fu.y, fu.z, fu.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            o[e + q] = k[r](s4[q], u4[q]);
+            const float ds = fmaf(s4[q], k[r].c2, -k[r].Ls2), dt = fmaf(u4[q], k[r].c2, -k[r].Lt2);
+            const float dy = (u4[q] - s4[q]) * k[r].c2;  // yt - ys
+            tp[r] = fmaf(fast_exp2(dt), dy, tp[r]);
+            tq[r] = fmaf(fast_exp2(ds), -dy, tq[r]);
+          }
         }
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) o[q] = 0.f;
-    }
-    if (a.dz) {
-      char* dst = a.dz + panel_off(a.C, i, v0 * E::kElem);
-      if constexpr (EPT == 8) {
-        const u32x4_t w{Bf16::pack2(o[0], o[1]), Bf16::pack2(o[2], o[3]), Bf16::pack2(o[4], o[5]),
-                        Bf16::pack2(o[6], o[7])};
-        *reinterpret_cast<u32x4_t*>(dst) = w;
       } else {
-        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) o[q] = 0.f;
       }
+      if (a.dz) *reinterpret_cast<u32x4_t*>(tile + (4 * w + r) * RS + lane * 16) = pack16<E>(o);
+    }
+    if (a.dz) {  // uniform
+      __syncthreads();
+      ew_store_tile(tile, RS, a.dz, a.C, i0, j * 1024, a.V * E::kElem);
+      __syncthreads();
     }
   }
-  tp += __shfl_xor(tp, 1);
-  tq += __shfl_xor(tq, 1);
-  tp += __shfl_xor(tp, 2);
-  tq += __shfl_xor(tq, 2);
-  if (a.terms && rv && sub == 0) a.terms[i * a.nblk + blockIdx.x] = make_float2(tp, tq);
+  if (a.terms == nullptr) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      tp[r] += __shfl_xor(tp[r], off);
+      tq[r] += __shfl_xor(tq[r], off);
+    }
+    if (lane == 0 && rv[r]) a.terms[(i0 + 4 * w + r) * a.nblk + blockIdx.x] = make_float2(tp[r], tq[r]);
+  }
 }
 
 int full_from_z_blocks(int elem, int64_t V) { return ew_ranges(elem, V); }

@@ -230,6 +230,32 @@ __device__ inline long panel_off(long prows, long row, long byte) {
   return ((byte >> 6) * prows + row) * kRowB + (byte & 63);
 }
 
+// ------------------------------------------------------------------ elementwise dZ passes
+// Pack EPT floats as 16 bytes of the element type.
+template <class E>
+__device__ inline u32x4_t pack16(const float* o) {
+  if constexpr (E::kEpc == 8)
+    return u32x4_t{Bf16::pack2(o[0], o[1]), Bf16::pack2(o[2], o[3]), Bf16::pack2(o[4], o[5]), Bf16::pack2(o[6], o[7])};
+  else
+    return u32x4_t{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+}
+
+// Write a staged [16][1 KB] tile of dZ (LDS row stride rs) to the panels
+// of C rows: wave w writes pieces 4w .. 4w + 3, lane l row l / 4 and 16-byte
+// chunk l % 4 of the piece.  byte0: the tile's first byte along the rows.
+__device__ inline void ew_store_tile(const char* tile, int rs, char* dz, long C, long i0, long byte0, long rowbytes) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = lane >> 2, sub = lane & 3;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int pc = 4 * w + q;
+    const long byte = byte0 + pc * kRowB + 16 * sub;
+    if (byte < rowbytes)
+      *reinterpret_cast<u32x4_t*>(dz + panel_off(C, i0 + row, byte)) =
+          *reinterpret_cast<const u32x4_t*>(tile + row * rs + pc * kRowB + 16 * sub);
+  }
+}
+
 // Store a staged [256][32] float block as the element type: rows [row0,
 // row0 + 256) clipped to nrows, columns [col0, col0 + 32) clipped to
 // [clo, ncols) (both multiples of 4/8).  The destination is row-major (`ld`

@@ -38,15 +38,17 @@ struct Compact {
   int32_t* count;  // [1] number of valid rows
 };
 
-// Elementwise passes that write a dZ chunk: a block of 256 threads covers 64
-// rows and one of at most kEwRanges ranges of the 64-byte pieces of those
-// rows (4 threads per piece, so a wave writes 16 consecutive rows of a piece:
-// one contiguous kilobyte of the panel layout).
-constexpr int kEwRows = 64;
-constexpr int kEwRanges = 64;
+// Elementwise passes that write a dZ chunk: a block of 256 threads covers
+// kEwRows rows and one of at most kEwRanges ranges of the rows' column tiles,
+// a tile being 1 KB of dZ per row (512 bf16 or 256 fp32 columns).  Each wave
+// reads 4 of the rows, 16 bytes of dZ's columns per lane (one coalesced access
+// per row and operand); the tile goes through LDS so that each wave then
+// writes 16 rows of one 64-byte piece: a contiguous kilobyte of the panels.
+constexpr int kEwRows = 16;
+constexpr int kEwRanges = 16;
 inline int ew_ranges(int elem, int64_t V) {
-  const int64_t pieces = (V * elem + 63) / 64;
-  return (int)(pieces < kEwRanges ? pieces : kEwRanges);
+  const int64_t tiles = (V * elem + 1023) / 1024;
+  return (int)(tiles < kEwRanges ? tiles : kEwRanges);
 }
 
 // ---------------------------------------------------------------- small kernels
