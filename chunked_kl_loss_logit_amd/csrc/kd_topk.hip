@@ -327,78 +327,71 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_kernel(TopkDzArgs a) {
 }
 
 // ---------------------------------------------------------------- dZ from stored logits
-// Block geometry as kEwRows / kEwRanges say.  A lane handles EPT consecutive
-// columns (16 bytes of dZ) of each of its wave's 4 rows per tile, with the
-// recomputing tile's epilogue formula; the row's entries are sorted and the
-// lane's columns ascend, so one cursor per row walks the hits in order, and
-// they are subtracted before the one rounding to the element type.
+constexpr int kDzzRows = 64;    // rows per block of the top-K elementwise dZ pass
+constexpr int kDzzRanges = 64;  // column ranges per block row
+
+// A block covers kDzzRows rows and one of at most kDzzRanges ranges of the
+// rows' 64-byte dZ pieces, four threads per piece, so each wave writes 16
+// consecutive rows of a piece: a contiguous kilobyte of the panels (staging
+// through LDS, as the full pass does, measured slower here).  A thread handles
+// EPT consecutive columns (16 bytes of dZ) of its row in each piece of the
+// block's range, with the recomputing tile's epilogue formula.  The row's
+// entries are sorted and the thread's columns ascend, so one cursor walks the
+// hits in order; they are subtracted before the one rounding to the element
+// type.
 template <class E>
 __global__ __launch_bounds__(256) void topk_dz_from_z_kernel(TopkDzFromZArgs a) {
   constexpr int EPT = E::kEpc;
-  constexpr int NT = 64 * EPT;  // columns per tile
-  constexpr int RS = 1024 + 16;  // LDS row stride, bytes
-  __shared__ __attribute__((aligned(16))) char tile[kEwRows * RS];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int PC = kRowB / E::kElem;  // columns per piece
+  const long i = (long)blockIdx.y * kDzzRows + (threadIdx.x >> 2);  // row of the chunk
+  const int sub = threadIdx.x & 3;
+  const long np = (a.V * E::kElem + kRowB - 1) / kRowB;
+  const long pb = np * blockIdx.x / gridDim.x, pe = np * (blockIdx.x + 1) / gridDim.x;
   const long M = min(a.C, (long)*a.c.count - a.c0);
-  const long i0 = (long)blockIdx.y * kEwRows;
-  const long nt = (a.V + NT - 1) / NT;
-  const long jb = nt * blockIdx.x / gridDim.x, je = nt * (blockIdx.x + 1) / gridDim.x;
-  float L2[4], gs[4], c2[4];
-  int cur[4], ce[4];
-  bool rv[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const long i = i0 + 4 * w + r;
-    rv[r] = i < M;
-    L2[r] = gs[r] = c2[r] = 0.f;
-    cur[r] = ce[r] = 0;
-    if (rv[r]) {
-      const long t = a.c.rows[a.c0 + i];
-      const float4 rc = a.rd.rowc[t];
-      L2[r] = a.lse[t] * kLog2e - rc.w;
-      gs[r] = a.g[t] * rc.y;
-      c2[r] = rc.x;
-      ce[r] = (int)(t * a.K + a.K);
-      cur[r] = lower_bound(a.rd.pair, (int)(t * a.K), ce[r], jb * NT);
-    }
+  const bool rv = i < M;
+  float L2 = 0.f, gs = 0.f, c2 = 0.f;
+  int c = 0, ce = 0;
+  if (rv) {
+    const long t = a.c.rows[a.c0 + i];
+    const float4 rc = a.rd.rowc[t];
+    L2 = a.lse[t] * kLog2e - rc.w;
+    gs = a.g[t] * rc.y;
+    c2 = rc.x;
+    ce = (int)(t * a.K + a.K);
+    c = lower_bound(a.rd.pair, (int)(t * a.K), ce, pb * PC);
   }
-  for (long j = jb; j < je; ++j) {
-    const long v0 = j * NT + lane * EPT;
-    const bool in = v0 < a.V;
+  const float* zr = a.z + i * a.ldz;
+  for (long p = pb; p < pe; ++p) {
+    const long v0 = p * PC + sub * EPT;
+    if (v0 >= a.V) break;
+    float o[EPT];
+    if (rv) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float o[EPT];
-      if (rv[r] && in) {
-        const float* zr = a.z + (i0 + 4 * w + r) * a.ldz + v0;
-#pragma unroll
-        for (int e = 0; e < EPT; e += 4) {
-          const float4 z4 = *reinterpret_cast<const float4*>(zr + e);
-          o[e + 0] = gs[r] * fast_exp2(fmaf(z4.x, c2[r], -L2[r]));
-          o[e + 1] = gs[r] * fast_exp2(fmaf(z4.y, c2[r], -L2[r]));
-          o[e + 2] = gs[r] * fast_exp2(fmaf(z4.z, c2[r], -L2[r]));
-          o[e + 3] = gs[r] * fast_exp2(fmaf(z4.w, c2[r], -L2[r]));
-        }
-        for (; cur[r] < ce[r]; ++cur[r]) {
-          const int2 pr = a.rd.pair[cur[r]];
-          if ((long)pr.x >= v0 + EPT) break;
-          if ((long)pr.x < v0) continue;  // another lane's columns
-#pragma unroll
-          for (int q = 0; q < EPT; ++q) o[q] = (long)pr.x == v0 + q ? o[q] - gs[r] * __int_as_float(pr.y) : o[q];
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < EPT; ++q) o[q] = 0.f;
+      for (int e = 0; e < EPT; e += 4) {
+        const float4 z4 = *reinterpret_cast<const float4*>(zr + v0 + e);
+        o[e + 0] = gs * fast_exp2(fmaf(z4.x, c2, -L2));
+        o[e + 1] = gs * fast_exp2(fmaf(z4.y, c2, -L2));
+        o[e + 2] = gs * fast_exp2(fmaf(z4.z, c2, -L2));
+        o[e + 3] = gs * fast_exp2(fmaf(z4.w, c2, -L2));
       }
-      *reinterpret_cast<u32x4_t*>(tile + (4 * w + r) * RS + lane * 16) = pack16<E>(o);
+      for (; c < ce; ++c) {
+        const int2 pr = a.rd.pair[c];
+        if ((long)pr.x >= v0 + EPT) break;
+        if ((long)pr.x < v0) continue;  // another thread's columns
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) o[q] = (long)pr.x == v0 + q ? o[q] - gs * __int_as_float(pr.y) : o[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) o[q] = 0.f;
     }
-    __syncthreads();
-    ew_store_tile(tile, RS, a.dz, a.C, i0, j * 1024, a.V * E::kElem);
-    __syncthreads();
+    *reinterpret_cast<u32x4_t*>(a.dz + panel_off(a.C, i, v0 * E::kElem)) = pack16<E>(o);
   }
 }
 
 hipError_t launch_topk_dz_from_z(int elem, const TopkDzFromZArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)ew_ranges(elem, a.V), (unsigned)(a.C / kEwRows)), block(256);
+  const int64_t pieces = (a.V * elem + kRowB - 1) / kRowB;
+  const dim3 grid((unsigned)std::min<int64_t>(kDzzRanges, pieces), (unsigned)(a.C / kDzzRows)), block(256);
   if (elem == 2)
     hipLaunchKernelGGL(topk_dz_from_z_kernel<Bf16>, grid, block, 0, st, a);
   else
