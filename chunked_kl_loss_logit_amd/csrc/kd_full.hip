@@ -288,41 +288,44 @@ hipError_t launch_full_rowc(Compact c, int64_t T, const float* tau_rows, float c
   return hipGetLastError();
 }
 
-// Block geometry as kEwRows / kEwRanges say.  A lane handles EPT consecutive
-// columns (16 bytes of dZ) of each of its wave's 4 rows per tile, and sums the
-// rows' two KL terms over them; at the end each row's sums are added over the
-// wave's lanes in a fixed order, for the terms array.  Without dz (the terms
-// pass of the KL mixture) nothing goes through LDS.
+// Block geometry as kEwRows / kEwRanges say, with 8 waves of 2 rows each.  A
+// lane handles EPT consecutive columns (16 bytes of dZ) of its wave's 2 rows
+// per tile and sums the rows' two KL terms over them; at the end each row's
+// sums are added over the wave's lanes in a fixed order, for the terms array.
+// Without dz (the terms pass of the KL mixture) nothing is staged.  The rows'
+// constants sit in LDS and a wave has two rows, which keeps the kernel's
+// registers low: it is bound by HBM and needs the occupancy.
 template <class E>
-__global__ __launch_bounds__(256) void full_from_z_kernel(FullFromZArgs a) {
+__global__ __launch_bounds__(512) void full_from_z_kernel(FullFromZArgs a) {
   constexpr int EPT = E::kEpc;
   constexpr int NT = 64 * EPT;   // columns per tile
   constexpr int RS = 1024 + 16;  // LDS row stride, bytes
   __shared__ __attribute__((aligned(16))) char tile[kEwRows * RS];
+  __shared__ FullDzConst kc[kEwRows];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long M = min(a.C, (long)*a.c.count - a.c0);
   const long i0 = (long)blockIdx.y * kEwRows;
   const long nt = (a.V + NT - 1) / NT;
   const long jb = nt * blockIdx.x / gridDim.x, je = nt * (blockIdx.x + 1) / gridDim.x;
-  FullDzConst k[4];
-  bool rv[4];
-  float tp[4], tq[4];  // sum p (yt - ys), sum q (ys - yt), base 2
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const long i = i0 + 4 * w + r;
-    rv[r] = i < M;
-    k[r] = full_dz_const(rv[r], rv[r] ? a.c.rows[a.c0 + i] : 0, a.lse_s, a.lse_t, a.g, a.c2, a.inv_tau, a.mix);
-    tp[r] = tq[r] = 0.f;
+  if (threadIdx.x < kEwRows) {
+    const long i = i0 + threadIdx.x;
+    const bool v = i < M;
+    kc[threadIdx.x] = full_dz_const(v, v ? a.c.rows[a.c0 + i] : 0, a.lse_s, a.lse_t, a.g, a.c2, a.inv_tau, a.mix);
   }
+  __syncthreads();
+  float tp[2] = {0.f, 0.f}, tq[2] = {0.f, 0.f};  // sum p (yt - ys), sum q (ys - yt), base 2
   for (long j = jb; j < je; ++j) {
     const long v0 = j * NT + lane * EPT;
     const bool in = v0 < a.V;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 2; ++r) {
+      const int row = 2 * w + r;
+      const long i = i0 + row;
       float o[EPT];
-      if (rv[r] && in) {
-        const float* sr = a.zs + (i0 + 4 * w + r) * a.ldz + v0;
-        const float* ur = a.zt + (i0 + 4 * w + r) * a.ldz + v0;
+      if (i < M && in) {
+        const FullDzConst k = kc[row];
+        const float* sr = a.zs + i * a.ldz + v0;
+        const float* ur = a.zt + i * a.ldz + v0;
 #pragma unroll
         for (int e = 0; e < EPT; e += 4) {
           const float4 fs = *reinterpret_cast<const float4*>(sr + e);
@@ -330,9 +333,9 @@ __global__ __launch_bounds__(256) void full_from_z_kernel(FullFromZArgs a) {
           const float s4[4] = {fs.x, fs.y, fs.z, fs.w}, u4[4] = {fu.x, fu.y, fu.z, fu.w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            o[e + q] = k[r](s4[q], u4[q]);
-            const float ds = fmaf(s4[q], k[r].c2, -k[r].Ls2), dt = fmaf(u4[q], k[r].c2, -k[r].Lt2);
-            const float dy = (u4[q] - s4[q]) * k[r].c2;  // yt - ys
+            o[e + q] = k(s4[q], u4[q]);
+            const float ds = fmaf(s4[q], k.c2, -k.Ls2), dt = fmaf(u4[q], k.c2, -k.Lt2);
+            const float dy = (u4[q] - s4[q]) * k.c2;  // yt - ys
             tp[r] = fmaf(fast_exp2(dt), dy, tp[r]);
             tq[r] = fmaf(fast_exp2(ds), -dy, tq[r]);
           }
@@ -341,30 +344,30 @@ __global__ __launch_bounds__(256) void full_from_z_kernel(FullFromZArgs a) {
 #pragma unroll
         for (int q = 0; q < EPT; ++q) o[q] = 0.f;
       }
-      if (a.dz) *reinterpret_cast<u32x4_t*>(tile + (4 * w + r) * RS + lane * 16) = pack16<E>(o);
+      if (a.dz) *reinterpret_cast<u32x4_t*>(tile + row * RS + lane * 16) = pack16<E>(o);
     }
     if (a.dz) {  // uniform
       __syncthreads();
-      ew_store_tile(tile, RS, a.dz, a.C, i0, j * 1024, a.V * E::kElem);
+      ew_store_tile<8>(tile, RS, a.dz, a.C, i0, j * 1024, a.V * E::kElem);
       __syncthreads();
     }
   }
   if (a.terms == nullptr) return;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < 2; ++r) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       tp[r] += __shfl_xor(tp[r], off);
       tq[r] += __shfl_xor(tq[r], off);
     }
-    if (lane == 0 && rv[r]) a.terms[(i0 + 4 * w + r) * a.nblk + blockIdx.x] = make_float2(tp[r], tq[r]);
+    if (lane == 0 && i0 + 2 * w + r < M) a.terms[(i0 + 2 * w + r) * a.nblk + blockIdx.x] = make_float2(tp[r], tq[r]);
   }
 }
 
 int full_from_z_blocks(int elem, int64_t V) { return ew_ranges(elem, V); }
 
 hipError_t launch_full_from_z(int elem, const FullFromZArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)full_from_z_blocks(elem, a.V), (unsigned)(a.C / kEwRows)), block(256);
+  const dim3 grid((unsigned)full_from_z_blocks(elem, a.V), (unsigned)(a.C / kEwRows)), block(512);
   if (elem == 2)
     hipLaunchKernelGGL(full_from_z_kernel<Bf16>, grid, block, 0, st, a);
   else

@@ -241,14 +241,17 @@ __device__ inline u32x4_t pack16(const float* o) {
 }
 
 // Write a staged [16][1 KB] tile of dZ (LDS row stride rs) to the panels
-// of C rows: wave w writes pieces 4w .. 4w + 3, lane l row l / 4 and 16-byte
-// chunk l % 4 of the piece.  byte0: the tile's first byte along the rows.
+// of C rows with NW waves: wave w writes 16 / NW consecutive 64-byte pieces,
+// lane l row l / 4 and 16-byte chunk l % 4 of each, so every store of a wave
+// is a contiguous kilobyte.  byte0: the tile's first byte along the rows.
+template <int NW>
 __device__ inline void ew_store_tile(const char* tile, int rs, char* dz, long C, long i0, long byte0, long rowbytes) {
+  constexpr int PPW = 16 / NW;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int row = lane >> 2, sub = lane & 3;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int pc = 4 * w + q;
+  for (int q = 0; q < PPW; ++q) {
+    const int pc = PPW * w + q;
     const long byte = byte0 + pc * kRowB + 16 * sub;
     if (byte < rowbytes)
       *reinterpret_cast<u32x4_t*>(dz + panel_off(C, i0 + row, byte)) =
