@@ -190,20 +190,47 @@ __device__ inline void st_write4(StPair st, int r, int c4, float4 v) {
   *reinterpret_cast<float4*>(st + r * 32 + ((c4 ^ ((r >> 1) & 7)) << 2)) = v;
 }
 
+// Where a wave's accumulators go in a staged [256][32] block: element i of
+// row block mb of a lane belongs to row wm 128 + 32 mb + 8 (i / 4) + 4 (lane
+// / 32) + i % 4 and column lane % 32, i.e. float row * 32 + st_pos(row, col).
+// The swizzle key (row / 2) % 8 is the lane's bit (lane / 32) at position 1
+// plus compile-time bits of i, so the offset is one of four per-lane values
+// plus a constant: o[q(i)] + 1024 mb + 256 (i / 4) + 32 (i % 4), with
+// q(i) = (i % 4) / 2 + 2 ((i / 4) % 2).  Each write is then one LDS store with
+// an immediate offset instead of a rebuilt address.
+struct StageOff {
+  int o[4];
+};
+__device__ inline StageOff stage_offsets(int wm, int lane) {
+  const int h = lane >> 5, col = lane & 31;
+  const int base = wm * 4096 + h * 128 + (col & 3);
+  const int g = ((col >> 2) ^ (h << 1)) << 2;
+  return StageOff{{base + g, base + (g ^ 4), base + (g ^ 16), base + (g ^ 20)}};
+}
+// Each block passes through an empty asm statement that takes and returns it
+// in accumulator registers, so no copy of it can be made before its round:
+// otherwise the compiler copies later rounds' accumulators out early, spills
+// them, and the reloads wait on all vector memory (the next tile's operand
+// loads included).
+template <int NBI, int NB>
+__device__ inline void stage_acc(float* st, const StageOff& so, const f32x16_t (&acc)[4][NB]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    f32x16_t v = acc[mb][NBI];
+    asm volatile("" : "+a"(v));
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      st[so.o[((i & 3) >> 1) + 2 * ((i >> 2) & 1)] + mb * 1024 + (i >> 2) * 256 + (i & 3) * 32] = v[i];
+  }
+}
+
 // Block NBI (0 .. NB-1) of the waves of column half 0 goes to st0, of column
 // half 1 to st1.
 template <int NBI, int NB>
 __device__ inline void stage_block(StPair st0, StPair st1, const f32x16_t (&acc)[4][NB]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  float* st = wn ? st1 : st0;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = wm * 128 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      st[row * 32 + st_pos(row, lane & 31)] = acc[mb][NBI][i];
-    }
+  const int w = wave_id();
+  const int lane = opaque((int)threadIdx.x) & 63;
+  stage_acc<NBI, NB>((w & 1) ? st1 : st0, stage_offsets(w >> 1, lane), acc);
 }
 
 // Block NBI of the waves of column half h (wave index & 1 == h) into st; the
@@ -211,16 +238,9 @@ __device__ inline void stage_block(StPair st0, StPair st1, const f32x16_t (&acc)
 template <int NBI, int NB>
 __device__ inline void stage_half(StPair st, int h, const f32x16_t (&acc)[4][NB]) {
   const int w = wave_id();
-  const int wm = w >> 1, wn = w & 1;
-  if (wn != h) return;
+  if ((w & 1) != h) return;
   const int lane = opaque((int)threadIdx.x) & 63;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = wm * 128 + mb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      st[row * 32 + st_pos(row, lane & 31)] = acc[mb][NBI][i];
-    }
+  stage_acc<NBI, NB>(st, stage_offsets(w >> 1, lane), acc);
 }
 
 // Panels: a matrix of prows rows cut into 64-byte pieces along its rows,
