@@ -170,7 +170,9 @@ int64_t max_splits(int64_t ntiles) { return splits_for(1, ntiles); }
 // Rows per backward chunk: the request (or the default) rounded up to whole
 // 256-row tiles, at most the rows present, and for bf16 at most what keeps
 // the chunk's dZ buffer within the 32-bit offsets of the direct-to-LDS loads
-// that dH and dW read it with (16640 rows at V = 128256).
+// that dH and dW read it with, rounded down to a multiple of the default
+// chunk when that is possible (16384 rows at V = 128256: a cap of 65 row
+// blocks would launch the tiles in poorly filled rounds).
 int64_t chunk_of(int64_t T, int64_t V, int elem, int64_t chunk_rows) {
   int64_t C = chunk_rows <= 0 ? KD_DEFAULT_CHUNK_ROWS : chunk_rows;
   C = (int64_t)up((size_t)C, 256);
@@ -178,6 +180,7 @@ int64_t chunk_of(int64_t T, int64_t V, int elem, int64_t chunk_rows) {
   if (elem == 2) {
     const int64_t ldz = cdiv(V, kd::kTileN) * kd::kTileN;
     int64_t cmax = ((int64_t(1) << 32) - 65537) / (ldz * 2) / 256 * 256;
+    if (cmax >= KD_DEFAULT_CHUNK_ROWS) cmax = cmax / KD_DEFAULT_CHUNK_ROWS * KD_DEFAULT_CHUNK_ROWS;
     C = std::min<int64_t>(C, std::max<int64_t>(cmax, 256));
   }
   return C;

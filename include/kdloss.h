@@ -103,7 +103,9 @@ typedef enum kd_dtype { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
  * chunk (0 = KD_DEFAULT_CHUNK_ROWS; rounded up to a multiple of 256; clamped
  * to the rows present; for bf16 also clamped so that the chunk's dZ buffer,
  * chunk * roundup(V, 256) * 2 bytes, stays under 4 GiB, the reach of the
- * direct-to-LDS loads that read it: 16640 rows at V = 128256).  Every call
+ * direct-to-LDS loads that read it, that cap being rounded down to a
+ * multiple of KD_DEFAULT_CHUNK_ROWS when it is at least that: 16384 rows at
+ * V = 128256).  Every call
  * taking chunk_rows applies the same rule.  Larger chunks trade workspace
  * for speed at long context (fewer read-modify-writes of dW).  The size is
  * affine in T for a fixed chunk size: the per-row part is about 10*K + 44

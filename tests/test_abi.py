@@ -331,9 +331,10 @@ def test_full_backward_needs_kl_rev_when_mixing(L):
 
 
 def test_bf16_chunks_stay_within_the_direct_load_reach(L):
-    # a chunk's bf16 dZ buffer must stay under 4 GiB: 16640 rows at V = 128256
+    # a chunk's bf16 dZ buffer must stay under 4 GiB (16640 rows at V = 128256),
+    # and the cap is rounded down to a multiple of the default chunk: 16384
     big = ws_topk(65536, chunk=32768)[1]
-    assert big == ws_topk(65536, chunk=16640)[1] and big == ws_topk(65536, chunk=20000)[1]
-    assert ws_topk(65536, chunk=16384)[1] < big
+    assert big == ws_topk(65536, chunk=16384)[1] == ws_topk(65536, chunk=16640)[1] == ws_topk(65536, chunk=20000)[1]
+    assert ws_topk(65536, chunk=16128)[1] < big
     # fp32 has no such limit (its mainloop is not the direct-load one)
     assert ws_topk(65536, chunk=32768, dt=kdl.KD_F32)[1] > ws_topk(65536, chunk=16640, dt=kdl.KD_F32)[1]

@@ -74,15 +74,15 @@ def test_full_t16384_sampled_rows():
 
 
 def test_full_largest_direct_load_chunk_sampled_rows():
-    # chunk_rows past the direct-load reach is capped at 16640 rows at V = 128256:
-    # a chunk of 16640 rows (offsets past 2^31 in dH and dW) and one of 360
+    # chunk_rows past the direct-load reach is capped at 16384 rows at V = 128256:
+    # a chunk of 16384 rows (offsets past 2^31 in dH and dW) and one of 616
     p = G.PRESETS["full_vocab_t16384"]
     T = 17000
     inp = G.make_full(T, p.d, p.dt_hidden, p.V, p.dtype, tau=1.0, number=19, g="normal")
-    say("full T=17000, chunk_rows=32768 (capped at 16640)")
+    say("full T=17000, chunk_rows=32768 (capped at 16384)")
     got = run_full(inp, chunk_rows=32768)
     rng = np.random.default_rng(9)
-    rows = np.array(sorted(set(rng.choice(T, 24, replace=False).tolist()) | {0, 8400, 16639, 16640, T - 1}))
+    rows = np.array(sorted(set(rng.choice(T, 24, replace=False).tolist()) | {0, 8400, 16383, 16384, 16639, T - 1}))
     kl, ls, lt, dH = O.full_kl_rows(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], None, 1.0, inp["g"], rows)
     assert_kl(got["kl"][rows], kl, torch.bfloat16)
     assert_lse(got["lse_s"][rows], ls, torch.bfloat16)

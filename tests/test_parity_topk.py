@@ -272,16 +272,16 @@ def test_out_of_range_index_in_a_valid_row_is_left_out_of_the_gather():
 
 
 def test_largest_direct_load_chunk_sampled_rows():
-    # chunk_rows past the direct-load reach is capped at 16640 rows at V = 128256:
-    # a chunk of 16640 rows (a 4.27 GB dZ buffer, so offsets past 2^31 in dH and
-    # dW) and one of 360 whose dW is added to the first's in place
+    # chunk_rows past the direct-load reach is capped at 16384 rows at V = 128256:
+    # a chunk of 16384 rows (a 4.2 GB dZ buffer, so offsets past 2^31 in dH and
+    # dW) and one of 616 whose dW is added to the first's in place
     p = G.PRESETS["head_topk_t4096"]
     T = 17000
     inp = G.make_topk(T, p.d, p.V, p.K, p.dtype, tau=1.0, number=18, g="normal")
-    say("head T=17000, chunk_rows=32768 (capped at 16640)")
+    say("head T=17000, chunk_rows=32768 (capped at 16384)")
     got = run_topk(inp, want_z=False, chunk_rows=32768)
     rng = np.random.default_rng(8)
-    rows = np.array(sorted(set(rng.choice(T, 24, replace=False).tolist()) | {0, 8400, 16383, 16639, 16640, T - 1}))
+    rows = np.array(sorted(set(rng.choice(T, 24, replace=False).tolist()) | {0, 8400, 16383, 16384, 16639, T - 1}))
     kl, lse, _, dH = O.topk_kl_rows(inp["H"], inp["W"], inp["I"], inp["A"], None, 1.0, inp["g"], rows)
     assert_kl(got["kl"][rows], kl, torch.bfloat16)
     assert_lse(got["lse"][rows], lse, torch.bfloat16)
