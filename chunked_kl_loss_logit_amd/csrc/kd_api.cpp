@@ -125,10 +125,9 @@ kd_status need_align(const void* p, size_t a, const char* name) {
 // Row blocks per raster group of the tile kernels: consecutive workgroups of
 // one XCD share a row block's operand across this many row blocks (grouped_coords).
 // Sweeping 1..16 at the 4096 x 3072 x 128256 head moved each kernel by under 4%.
-// dW takes all its row blocks (d / 256, 12 at d = 3072) in one group, so that
-// consecutive workgroups read the same dZ columns: 4% faster there.
+// (dW over all its row blocks in one group ran 1% faster but fetched 60% more
+// from HBM, 10.8 instead of 6.8 GB per launch.)
 constexpr int kRasterGroup = 4;
-constexpr int kRasterGroupDw = 64;
 
 // Vocabulary splits of the tile kernels: enough workgroups to fill the CUs,
 // and at least 8 so that at large T the workgroups running together read
@@ -369,7 +368,7 @@ kd_status grad_chunk(const void* H, const void* W, void* dH, float* dW, int elem
   wa.V = V;
   wa.nrb = ch.nrb_dw;
   wa.ncb = ch.ncb_dw;
-  wa.group = kRasterGroupDw;
+  wa.group = kRasterGroup;
   wa.accumulate = accumulate;
   KD_LAUNCH("dw_tile", st, kd::launch_dw(elem, wa, st));
   return KD_OK;
