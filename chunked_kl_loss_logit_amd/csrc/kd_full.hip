@@ -4,7 +4,8 @@
 // a frozen copy of its output head (KDFlow abstract,
 // thelatestinai.com/papers/2606.20005), so every vocabulary tile needs two
 // contractions: u = Ht . Wt (teacher, width dt) and s = H . Ws (student,
-// width d).  Both accumulator sets stay in registers (a 256 x 128 tile each);
+// width d), with H and Ht read from the chunk's panel copies.  Both
+// accumulator sets stay in registers (a 256 x 128 tile each);
 // each of two epilogue rounds stages one 32-column block of each wave column
 // half of both sets (all four LDS slots) and reads it back one row per thread.
 //

@@ -1,15 +1,17 @@
 // Gradient contractions of one backward chunk (the dZ chunk is written by the
 // top-K or full-vocabulary dZ kernel):
 //   dH_chunk = dZ . W^T   [C, V] x [V, d]: both operands are contiguous along
-//                         the vocabulary, which is the contraction; the
-//                         vocabulary is split S ways and each split writes
-//                         its own float32 partial (summed in a fixed order by
-//                         the reduce kernel, so results are deterministic).
+//                         the vocabulary, which is the contraction (dZ in
+//                         panels of C rows, W row-major); the vocabulary is
+//                         split S ways and each split writes its own float32
+//                         partial (summed in a fixed order by the reduce
+//                         kernel, so results are deterministic).
 //   dW      += H^T . dZ   [d, C] x [C, V]: H^T of the chunk is a gathered,
-//                         transposed copy (contiguous along the chunk's rows);
-//                         dZ is [rows][V], n-contiguous.  The first chunk
-//                         stores, later chunks add in place, so chunks act as
-//                         a fixed-order split over tokens.
+//                         transposed copy in panels of d rows (contiguous along
+//                         the chunk's rows); dZ is n-contiguous here, read
+//                         from its panels.  The first chunk stores, later
+//                         chunks add in place, so chunks act as a fixed-order
+//                         split over tokens.
 // "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and a Fused
 // Chunked KL Loss", §3 "Fused chunked KL": per chunk, the backward pass costs
 // the recomputed projection plus these two products.

@@ -2,16 +2,18 @@
 // f32x16_t acc[4][BN / 64] per wave.  All of them stage operands in the LDS
 // slot layout of kd_gemm.h and leave the slots free when tile() returns.
 //
-//   NN (B is n-contiguous: W as [d][V], dZ as [rows][V])
-//     DmaNN<BN>      bf16, contraction a multiple of 32: direct-load ring,
+//   NN (B is n-contiguous: W as [d][V], or the dZ chunk in panels)
+//     DmaNN<BN>      bf16, contraction a multiple of 128: direct-load ring,
 //                    transposing LDS reads for B
 //     GenNN<E, BN>   any shape or dtype: register-staged loads, B transposed
 //                    in registers, double buffer in slots 0 and 1
 //   NT (B is k-contiguous: W as [d][V] when V is the contraction)
 //     DmaNT<BN>, GenNT<E, BN>
 //
-// init(row_ptr, ...) takes row_ptr(r) -> address of A row r of the tile, or
-// nullptr outside the operand; NT policies take a second one for B rows.
+// init(row_ptr, ...) takes row_ptr(r) -> address of the first stage of A row
+// r of the tile (row-major: the row itself; panels: the row's first 64-byte
+// piece), or nullptr outside the operand, and the stage stride that leads to
+// the row's next stage; NT policies take the same for B rows.
 #pragma once
 
 #include <climits>

@@ -7,17 +7,18 @@
 // of the loss, logit tiles are discarded after use, and the backward pass
 // recomputes them.
 //
-// Grid: (valid-row block of 256) x (vocabulary split).  A workgroup walks the
-// 256-wide vocabulary tiles of its split in ascending order; each tile is
-// Z = H_rows . W[:, tile] on matrix cores, and the operand loads of the next
-// tile run while the epilogue of this one works.  The epilogue stages the
+// Grid: (valid-row block of 256) x (vocabulary split), per chunk of rows.  A
+// workgroup walks the 256-wide vocabulary tiles of its split in ascending
+// order; each tile is Z = H_rows . W[:, tile] on matrix cores, with H_rows
+// read from the chunk's panel copy (launch_gather_panels), and the operand
+// loads of the next tile run while the epilogue of this one works.  The epilogue stages the
 // tile through LDS one 256 x 32 block at a time and reads it back one row per
 // thread:
 //   forward  : running base-2 max / sum per row, plus the index-match gather.
 //              The row's cached indices are sorted, so one cursor walks them
 //              in step with the column blocks and picks the hits out of LDS.
 //   backward : dZ = (g/tau) (mass 2^(y - L2) - sum of w over hits), written in
-//              the input dtype to the chunk's dZ buffer.
+//              the input dtype to the chunk's dZ buffer (panels of C rows).
 // Each row carries its own constants (log2(e)/tau, 1/tau, mass) from the prep
 // kernel: per-token temperature, a partial-mass teacher and a cross-entropy
 // entry change those and the weights w, not the tiles.
