@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     full_opts, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd, kd_topk_kl_fwd_bwd_workspace_size,
     kd_topk_kl_workspace_size, kd_version, lib,
     profile_enable, profile_read, profile_reset,
+    kd_topk_kl_shard_workspace_size, kd_topk_kl_fwd_shard, kd_topk_kl_shard_combine, kd_topk_kl_bwd_shard,
 )
 
 __all__ = [
@@ -32,6 +33,8 @@ __all__ = [
     "kd_topk_kl_fwd_bwd_workspace_size", "kd_full_kl_workspace_size", "kd_full_kl_fwd_bwd_workspace_size", "KDError",
     "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex", "topk_opts", "kd_full_kl_fwd_ex",
     "kd_full_kl_bwd_ex", "kd_full_kl_fwd_bwd_ex", "full_opts",
+    "topk_kl_shard_forward", "topk_kl_shard_combine", "topk_kl_shard_backward", "kd_topk_kl_shard_workspace_size",
+    "kd_topk_kl_fwd_shard", "kd_topk_kl_shard_combine", "kd_topk_kl_bwd_shard",
 ]
 
 
@@ -86,6 +89,49 @@ def topk_kl_forward_backward(H, W, topk_idx, topk_logits, mask, tau, grad_kl, ch
     kd_topk_kl_fwd_bwd_ex(H, W, topk_idx, topk_logits, mask, tau, topk_opts(**options),
                           grad_kl.float().contiguous(), kl, lse, z, dH, dW, chunk_rows, workspace)
     return kl, lse, z, dH, dW
+
+
+# One vocabulary shard of the top-K loss: W_shard holds columns
+# [v0, v0 + W_shard.shape[1]) of the head; the caller all-gathers the ranks'
+# records before the combine and sums the ranks' dH partials after the
+# backward (kdloss.h, "top-K, one vocabulary shard").
+def topk_kl_shard_forward(H, W_shard, v0, topk_idx, topk_logits, mask=None, tau=1.0, want_z_topk=False,
+                          workspace=None, **options):
+    """This shard's row records rec [T,4], teacher terms trow [T,2] and (optionally) its hits' raw logits."""
+    T, d = H.shape
+    V, K = W_shard.shape[1], topk_idx.shape[1]
+    rec = torch.empty(T, 4, dtype=torch.float32, device=H.device)
+    trow = torch.empty(T, 2, dtype=torch.float32, device=H.device)
+    z = torch.empty(T, K, dtype=torch.float32, device=H.device) if want_z_topk else None
+    if workspace is None:
+        workspace = _workspace(kd_topk_kl_shard_workspace_size(T, d, V, v0, K, H.dtype), H.device)
+    kd_topk_kl_fwd_shard(H, W_shard, v0, topk_idx, topk_logits, mask, tau, topk_opts(**options), rec, trow, z,
+                         workspace)
+    return rec, trow, z
+
+
+def topk_kl_shard_combine(recs, trow, mask=None):
+    """kl and the whole head's lse from the shards' records (a list in rank order, or one [R,T,4] tensor)."""
+    rec = recs if isinstance(recs, torch.Tensor) else torch.stack(list(recs))
+    T = rec.shape[1]
+    kl = torch.empty(T, dtype=torch.float32, device=rec.device)
+    lse = torch.empty(T, dtype=torch.float32, device=rec.device)
+    kd_topk_kl_shard_combine(rec.contiguous(), trow, mask, kl, lse)
+    return kl, lse
+
+
+def topk_kl_shard_backward(H, W_shard, v0, topk_idx, topk_logits, mask, tau, lse, grad_kl, chunk_rows=0,
+                           workspace=None, **options):
+    """This shard's dH partial [T,d] float32 and its columns of dW [d,V_shard] float32."""
+    T, d = H.shape
+    V, K = W_shard.shape[1], topk_idx.shape[1]
+    dH = torch.empty(T, d, dtype=torch.float32, device=H.device)
+    dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
+    if workspace is None:
+        workspace = _workspace(kd_topk_kl_shard_workspace_size(T, d, V, v0, K, H.dtype, chunk_rows), H.device)
+    kd_topk_kl_bwd_shard(H, W_shard, v0, topk_idx, topk_logits, mask, tau, topk_opts(**options), lse,
+                         grad_kl.float().contiguous(), dH, dW, chunk_rows, workspace)
+    return dH, dW
 
 
 # Options of the full-vocabulary loss (kd_full_opts of kdloss.h): tau_rows

@@ -27,6 +27,7 @@ EXPORTS = (
     "kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd",
     "kd_topk_kl_fwd_bwd_workspace_size", "kd_topk_kl_fwd_bwd",
     "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex",
+    "kd_topk_kl_shard_workspace_size", "kd_topk_kl_fwd_shard", "kd_topk_kl_shard_combine", "kd_topk_kl_bwd_shard",
     "kd_full_kl_workspace_size", "kd_full_kl_fwd", "kd_full_kl_bwd",
     "kd_full_kl_fwd_bwd_workspace_size", "kd_full_kl_fwd_bwd",
     "kd_full_kl_fwd_ex", "kd_full_kl_bwd_ex", "kd_full_kl_fwd_bwd_ex",
@@ -81,6 +82,12 @@ def lib() -> ctypes.CDLL:
     L.kd_topk_kl_fwd_bwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, op, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp,
                                         i64, vp, sz, vp]
     fo = ctypes.POINTER(KdFullOpts)
+    L.kd_topk_kl_shard_workspace_size.argtypes = [i64, i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
+    L.kd_topk_kl_fwd_shard.argtypes = [vp, vp, vp, vp, vp, f32, op, i64, i64, i64, i64, i64, st, vp, vp, vp, vp, sz,
+                                       vp]
+    L.kd_topk_kl_shard_combine.argtypes = [vp, i64, vp, vp, i64, vp, vp, vp]
+    L.kd_topk_kl_bwd_shard.argtypes = [vp, vp, vp, vp, vp, f32, op, i64, i64, i64, i64, i64, st, vp, vp, vp, vp, i64,
+                                       vp, sz, vp]
     L.kd_full_kl_fwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, fo, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, sz, vp]
     L.kd_full_kl_bwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, fo, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp, i64,
                                     vp, sz, vp]
@@ -252,6 +259,48 @@ def kd_topk_kl_fwd_bwd_ex(H, W, topk_idx, topk_logits, mask, tau, opts, grad_kl,
                                        _ptr(kl), _ptr(lse), _ptr(z_topk), _ptr(dH), _ptr(dW), int(chunk_rows),
                                        _ptr(workspace), workspace.numel() if workspace is not None else 0,
                                        _stream(stream)), "kd_topk_kl_fwd_bwd_ex")
+
+
+def kd_topk_kl_shard_workspace_size(T, d, V, v0, K, dtype, chunk_rows=0) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().kd_topk_kl_shard_workspace_size(T, d, V, v0, K, _dtype_code(dtype), int(chunk_rows),
+                                                 ctypes.byref(out)), "kd_topk_kl_shard_workspace_size")
+    return out.value
+
+
+def kd_topk_kl_fwd_shard(H, W, v0, topk_idx, topk_logits, mask, tau, opts, rec, trow, z_topk, workspace,
+                         stream=None):
+    """One vocabulary shard's forward: W holds columns [v0, v0 + W.shape[1]) of the head; rec [T,4] and
+    trow [T,2] float32 out."""
+    T, d = H.shape
+    V = W.shape[1]
+    K = topk_idx.shape[1]
+    _check(lib().kd_topk_kl_fwd_shard(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask), float(tau),
+                                      _opts_ref(opts), T, d, V, int(v0), K, _dtype_code(H.dtype), _ptr(rec),
+                                      _ptr(trow), _ptr(z_topk), _ptr(workspace),
+                                      workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "kd_topk_kl_fwd_shard")
+
+
+def kd_topk_kl_shard_combine(rec, trow, mask, kl, lse, stream=None):
+    """rec [R,T,4] (the shards' records in rank order), trow [T,2] -> kl [T], lse [T]."""
+    R, T = rec.shape[0], rec.shape[1]
+    _check(lib().kd_topk_kl_shard_combine(_ptr(rec), R, _ptr(trow), _ptr(mask), T, _ptr(kl), _ptr(lse),
+                                          _stream(stream)), "kd_topk_kl_shard_combine")
+
+
+def kd_topk_kl_bwd_shard(H, W, v0, topk_idx, topk_logits, mask, tau, opts, lse, grad_kl, dH, dW, chunk_rows,
+                         workspace, stream=None):
+    """One vocabulary shard's backward with the whole head's lse: dH [T,d] float32 (a partial) and
+    dW [d,V] float32 (the shard's columns)."""
+    T, d = H.shape
+    V = W.shape[1]
+    K = topk_idx.shape[1]
+    _check(lib().kd_topk_kl_bwd_shard(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask), float(tau),
+                                      _opts_ref(opts), T, d, V, int(v0), K, _dtype_code(H.dtype), _ptr(lse),
+                                      _ptr(grad_kl), _ptr(dH), _ptr(dW), int(chunk_rows), _ptr(workspace),
+                                      workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "kd_topk_kl_bwd_shard")
 
 
 def kd_full_kl_fwd(H, Ws, Ht, Wt, mask, tau, kl, lse_s, lse_t, workspace, stream=None):

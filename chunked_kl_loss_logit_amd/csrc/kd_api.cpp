@@ -91,9 +91,9 @@ kd_status check_common(int64_t T, int64_t d, int64_t V, kd_dtype dt, float tau) 
   return KD_OK;
 }
 
-kd_status check_k(int64_t T, int64_t K, int64_t V) {
+kd_status check_k(int64_t T, int64_t K, int64_t V, bool k_le_v = true) {
   if (K < 1) return fail(KD_ERR_INVALID_ARG, "K must be >= 1");
-  if (K > V) return fail(KD_ERR_INVALID_ARG, "K must be <= V");
+  if (k_le_v && K > V) return fail(KD_ERR_INVALID_ARG, "K must be <= V");
   if (K > KD_MAX_K) return fail(KD_ERR_UNSUPPORTED, "K above KD_MAX_K");
   if (T * (K + 1) >= INT32_MAX) return fail(KD_ERR_UNSUPPORTED, "T * (K + 1) must be below 2^31");
   return KD_OK;
@@ -335,10 +335,11 @@ kd_status check_workspace(const void* ws, size_t have, size_t want) {
 
 // dH and dW of one backward chunk whose dZ sits in the chunk buffer:
 // H^T of the chunk's rows, dH split over the vocabulary and reduced in a
-// fixed order, dW stored (first chunk) or added in place.
+// fixed order (into dH's element size dh_elem, 0 = the inputs'), dW stored
+// (first chunk) or added in place.
 kd_status grad_chunk(const void* H, const void* W, void* dH, float* dW, int elem, int64_t d, int64_t V,
                      const kd::Compact& c, const ChunkPlan& ch, char* dz, char* hT, float* dhp, int64_t c0,
-                     bool accumulate, hipStream_t st) {
+                     bool accumulate, hipStream_t st, int dh_elem = 0) {
   KD_LAUNCH("gather_transpose", st, kd::launch_gather_transpose(H, elem, d, c, c0, ch.C, hT, st));
   kd::DhArgs ha{};
   ha.dz = dz;
@@ -355,7 +356,7 @@ kd_status grad_chunk(const void* H, const void* W, void* dH, float* dW, int elem
   ha.group = kRasterGroup;
   ha.S = ch.S_dh;
   KD_LAUNCH("dh_tile", st, kd::launch_dh(elem, ha, st));
-  KD_LAUNCH("reduce_dh", st, kd::launch_reduce_dh(dhp, ch.S_dh, ch.C, d, c, c0, dH, elem, st));
+  KD_LAUNCH("reduce_dh", st, kd::launch_reduce_dh(dhp, ch.S_dh, ch.C, d, c, c0, dH, dh_elem ? dh_elem : elem, st));
   kd::DwArgs wa{};
   wa.hT = hT;
   wa.dz = dz;
@@ -476,6 +477,23 @@ kd::TopkRowData row_data(void* ws, const TopkPlan& p) {
                          at<float4>(ws, p.o_rowc)};
 }
 
+// A vocabulary shard of the head: W holds its columns [v0, v0 + V).  The
+// forward then writes each row's record (rec [T,4]) and teacher terms
+// (trow [T,2]) in place of kl and lse; the backward takes the whole head's
+// lse and writes an fp32 partial of dH.
+struct Shard {
+  int64_t v0;
+  float* rec;
+  float* trow;
+};
+
+kd_status check_shard(int64_t T, int64_t K, int64_t V, int64_t v0) {
+  KD_TRY(check_k(T, K, V, false));
+  if (v0 < 0) return fail(KD_ERR_INVALID_ARG, "v0 must be >= 0");
+  if (v0 + V > INT32_MAX / 2) return fail(KD_ERR_UNSUPPORTED, "v0 + V must be below 2^30");
+  return KD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -498,28 +516,44 @@ kd_status kd_topk_kl_fwd(const void* H, const void* W, const int32_t* topk_idx, 
                            workspace, workspace_bytes, stream);
 }
 
-kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
-                            const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d,
-                            int64_t V, int64_t K, kd_dtype dt, float* kl, float* lse, float* z_topk,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The top-K forward; with a shard, the row records replace kl and lse.
+kd_status topk_fwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                   const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d, int64_t V,
+                   int64_t K, kd_dtype dt, float* kl, float* lse, float* z_topk, const Shard* shard, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
-  KD_TRY(check_k(T, K, V));
+  KD_TRY(shard ? check_shard(T, K, V, shard->v0) : check_k(T, K, V));
   TopkOpts op;
   KD_TRY(resolve_opts(opts, tau, K, op));
+  if (shard) {
+    op.prep.v0 = (int32_t)shard->v0;
+    op.prep.vs = (int32_t)V;
+  }
   if (T == 0) return KD_OK;
   KD_TRY(need(H, "H"));
   KD_TRY(need(W, "W"));
   KD_TRY(need(topk_idx, "topk_idx"));
   KD_TRY(need(topk_logits, "topk_logits"));
-  KD_TRY(need(kl, "kl"));
-  KD_TRY(need(lse, "lse"));
+  if (shard) {
+    KD_TRY(need(shard->rec, "rec"));
+    KD_TRY(need(shard->trow, "trow"));
+    KD_TRY(need_align(shard->rec, 16, "rec"));
+    KD_TRY(need_align(shard->trow, 8, "trow"));
+  } else {
+    KD_TRY(need(kl, "kl"));
+    KD_TRY(need(lse, "lse"));
+    KD_TRY(need_align(kl, 4, "kl"));
+    KD_TRY(need_align(lse, 4, "lse"));
+  }
   KD_TRY(need_align(H, 16, "H"));
   KD_TRY(need_align(W, 16, "W"));
   KD_TRY(need_align(topk_idx, 4, "topk_idx"));
   KD_TRY(need_align(topk_logits, 4, "topk_logits"));
-  KD_TRY(need_align(kl, 4, "kl"));
-  KD_TRY(need_align(lse, 4, "lse"));
   KD_TRY(need_align(z_topk, 4, "z_topk"));
   const int elem = elem_of(dt);
   const TopkPlan p = plan_topk(T, d, V, K, elem, 0);
@@ -556,10 +590,27 @@ kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_id
     a.nrb = sh.nrb;
     a.S = sh.S;
     KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
-    KD_LAUNCH("topk_combine", st,
-              kd::launch_topk_combine(part, sh.S, p.Cf, c, mask, rd, T, kl, lse, c0, c0 + p.Cf, c0 == 0, st));
+    if (shard)
+      KD_LAUNCH("topk_shard_record", st,
+                kd::launch_topk_shard_record(part, sh.S, p.Cf, c, mask, rd, T, reinterpret_cast<float4*>(shard->rec),
+                                             reinterpret_cast<float2*>(shard->trow), c0, c0 + p.Cf, c0 == 0, st));
+    else
+      KD_LAUNCH("topk_combine", st,
+                kd::launch_topk_combine(part, sh.S, p.Cf, c, mask, rd, T, kl, lse, c0, c0 + p.Cf, c0 == 0, st));
   }
   return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                            const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d,
+                            int64_t V, int64_t K, kd_dtype dt, float* kl, float* lse, float* z_topk,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return topk_fwd(H, W, topk_idx, topk_logits, mask, tau, opts, T, d, V, K, dt, kl, lse, z_topk, nullptr, workspace,
+                  workspace_bytes, stream);
 }
 
 kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
@@ -570,15 +621,24 @@ kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx, 
                            chunk_rows, workspace, workspace_bytes, stream);
 }
 
-kd_status kd_topk_kl_bwd_ex(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
-                            const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d,
-                            int64_t V, int64_t K, kd_dtype dt, const float* lse, const float* grad_kl, void* dH,
-                            float* dW, int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The top-K backward; with a shard (v0 used), dH is an fp32 partial.
+kd_status topk_bwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                   const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d, int64_t V,
+                   int64_t K, kd_dtype dt, const float* lse, const float* grad_kl, void* dH, float* dW,
+                   int64_t chunk_rows, const Shard* shard, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
-  KD_TRY(check_k(T, K, V));
+  KD_TRY(shard ? check_shard(T, K, V, shard->v0) : check_k(T, K, V));
   TopkOpts op;
   KD_TRY(resolve_opts(opts, tau, K, op));
+  if (shard) {
+    op.prep.v0 = (int32_t)shard->v0;
+    op.prep.vs = (int32_t)V;
+  }
   KD_TRY(need(dW, "dW"));
   KD_TRY(need_align(dW, 16, "dW"));
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -609,7 +669,8 @@ kd_status kd_topk_kl_bwd_ex(const void* H, const void* W, const int32_t* topk_id
   const kd::TopkRowData rd = row_data(workspace, p);
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
   KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, op.KE, op.prep, rd, nullptr, st));
-  KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * elem, dH, st));
+  const int dh_elem = shard ? 4 : elem;
+  KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * dh_elem, dH, st));
 
   const ChunkPlan& ch = p.ch;
   char* dz = at<char>(workspace, ch.o_dz);
@@ -641,10 +702,75 @@ kd_status kd_topk_kl_bwd_ex(const void* H, const void* W, const int32_t* topk_id
     za.group = kRasterGroup;
     za.S = sh.S;
     KD_LAUNCH("topk_dz_tile", st, kd::launch_topk_dz(elem, za, st));
-    KD_TRY(grad_chunk(H, W, dH, dW, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
+    KD_TRY(grad_chunk(H, W, dH, dW, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st, dh_elem));
   }
   return KD_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+kd_status kd_topk_kl_bwd_ex(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                            const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d,
+                            int64_t V, int64_t K, kd_dtype dt, const float* lse, const float* grad_kl, void* dH,
+                            float* dW, int64_t chunk_rows, void* workspace, size_t workspace_bytes, void* stream) {
+  return topk_bwd(H, W, topk_idx, topk_logits, mask, tau, opts, T, d, V, K, dt, lse, grad_kl, dH, dW, chunk_rows,
+                  nullptr, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- top-K, one vocabulary shard
+kd_status kd_topk_kl_shard_workspace_size(int64_t T, int64_t d, int64_t V, int64_t v0, int64_t K, kd_dtype dt,
+                                          int64_t chunk_rows, size_t* bytes) {
+  g_err.clear();
+  KD_TRY(need(bytes, "bytes"));
+  KD_TRY(check_common(T, d, V, dt, 1.0f));
+  KD_TRY(check_shard(T, K, V, v0));
+  *bytes = T == 0 ? 0 : plan_topk(T, d, V, K, elem_of(dt), chunk_rows).total;
+  return KD_OK;
+}
+
+kd_status kd_topk_kl_fwd_shard(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                               const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d,
+                               int64_t V, int64_t v0, int64_t K, kd_dtype dt, float* rec, float* trow,
+                               float* z_topk, void* workspace, size_t workspace_bytes, void* stream) {
+  const Shard sh{v0, rec, trow};
+  return topk_fwd(H, W, topk_idx, topk_logits, mask, tau, opts, T, d, V, K, dt, nullptr, nullptr, z_topk, &sh,
+                  workspace, workspace_bytes, stream);
+}
+
+kd_status kd_topk_kl_shard_combine(const float* rec, int64_t R, const float* trow, const uint8_t* mask, int64_t T,
+                                   float* kl, float* lse, void* stream) {
+  g_err.clear();
+  if (T < 0) return fail(KD_ERR_INVALID_ARG, "T must be >= 0");
+  if (R < 1) return fail(KD_ERR_INVALID_ARG, "R must be >= 1");
+  if (T > INT32_MAX / 2 || R * T > INT32_MAX) return fail(KD_ERR_UNSUPPORTED, "R * T must be below 2^31");
+  if (T == 0) return KD_OK;
+  KD_TRY(need(rec, "rec"));
+  KD_TRY(need(trow, "trow"));
+  KD_TRY(need(kl, "kl"));
+  KD_TRY(need(lse, "lse"));
+  KD_TRY(need_align(rec, 16, "rec"));
+  KD_TRY(need_align(trow, 8, "trow"));
+  KD_TRY(need_align(kl, 4, "kl"));
+  KD_TRY(need_align(lse, 4, "lse"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  KD_LAUNCH("topk_shard_combine", st,
+            kd::launch_topk_shard_combine(reinterpret_cast<const float4*>(rec), (int)R, T,
+                                          reinterpret_cast<const float2*>(trow), mask, kl, lse, st));
+  return KD_OK;
+}
+
+kd_status kd_topk_kl_bwd_shard(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                               const uint8_t* mask, float tau, const kd_topk_opts* opts, int64_t T, int64_t d,
+                               int64_t V, int64_t v0, int64_t K, kd_dtype dt, const float* lse, const float* grad_kl,
+                               float* dH, float* dW, int64_t chunk_rows, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const Shard sh{v0, nullptr, nullptr};
+  return topk_bwd(H, W, topk_idx, topk_logits, mask, tau, opts, T, d, V, K, dt, lse, grad_kl, dH, dW, chunk_rows,
+                  &sh, workspace, workspace_bytes, stream);
+}
+
 
 // ---------------------------------------------------------------- full vocabulary
 kd_status kd_full_kl_workspace_size(int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,

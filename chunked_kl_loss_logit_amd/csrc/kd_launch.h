@@ -31,6 +31,7 @@ struct TopkPrepOpts {
   const int32_t* labels;     // nullable [T]: labels of the cross-entropy term
   float beta;                // weight of the cross-entropy term (labels set)
   float c2, inv_tau;         // log2(e) / tau and 1 / tau of the scalar temperature
+  int32_t v0, vs;            // columns [v0, v0 + vs) of a vocabulary shard of W (vs = 0: the whole head)
 };
 
 struct Compact {
@@ -61,6 +62,17 @@ hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8
 hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
                                TopkRowData rd, int64_t T, float* kl, float* lse, int64_t jb, int64_t je,
                                bool zero_masked, hipStream_t st);
+// A vocabulary shard's forward: merges the split partials like
+// launch_topk_combine but writes the row's exchange record instead of kl and
+// lse: rec[t] = (m2, l, x / tau_t, 0) (base-2 max and sum over the shard's
+// columns, the shard's cross term) and trow[t] = (entropy term, mass); with
+// zero_masked, both are zero on masked rows.
+hipError_t launch_topk_shard_record(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
+                                    TopkRowData rd, int64_t T, float4* rec, float2* trow, int64_t jb, int64_t je,
+                                    bool zero_masked, hipStream_t st);
+// kl and lse of every row from R shards' records rec [R][T] and trow [T].
+hipError_t launch_topk_shard_combine(const float4* rec, int R, int64_t T, const float2* trow, const uint8_t* mask,
+                                     float* kl, float* lse, hipStream_t st);
 // kl = (1 - r) KL(p||q) + r KL(q||p); kl_rev (nullable) gets KL(q||p).
 hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
                                int64_t T, float r, float* kl, float* lse_s, float* lse_t, float* kl_rev, int64_t jb,

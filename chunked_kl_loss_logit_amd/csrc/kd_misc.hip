@@ -10,6 +10,11 @@
 //                  index so the tile epilogue can gather with one cursor.
 //   *_combine      merge the per-split running max / sum partials into the
 //                  row's log Z and KL (§3: each row keeps a scalar log Z)
+//   topk_shard_*   the same merge for a vocabulary shard of W: a row record
+//                  (max, sum, cross term) per shard, then one merge of the
+//                  shards' records (the timing at the largest tensor-parallel
+//                  rank of App. B; sharding the head by vocabulary columns is
+//                  the usual tensor-parallel layout of an output head)
 //   gather_transpose, reduce_dh, zero_masked_rows, fill_zero: chunk plumbing
 //                  of the backward pass
 #include <stdint.h>
@@ -104,6 +109,11 @@ hipError_t launch_compact(const uint8_t* mask, int64_t T, Compact c, hipStream_t
 // beta on label y is one more entry (y, beta), the others weigh (1 - beta) p,
 // so the loss keeps the support form sum w log p - sum w s + mass L with
 // mass = (1 - beta) m + beta.
+//
+// For a shard holding columns [v0, v0 + vs) of W, indices (the label too) are
+// shifted to the shard's columns and those outside it become INT32_MAX, which
+// sorts after every column and is never matched; the teacher terms stay those
+// of all K entries.
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_prep_kernel(const float* logits, const int32_t* idx, const uint8_t* mask,
                                                        int K, int KE, int KP, TopkPrepOpts o, TopkRowData rd,
@@ -159,7 +169,11 @@ __global__ __launch_bounds__(NT) void topk_prep_kernel(const float* logits, cons
 
   // sort (index, position) pairs by index; ties keep position order
   for (int j = threadIdx.x; j < KP; j += NT) {
-    const int32_t v = j < K ? idx[base + j] : (j < KE ? o.labels[t] : 0);
+    int32_t v = j < K ? idx[base + j] : (j < KE ? o.labels[t] : 0);
+    if (o.vs > 0) {  // a vocabulary shard: local column, or a sentinel past every column
+      v -= o.v0;
+      v = (uint32_t)v < (uint32_t)o.vs ? v : INT32_MAX;
+    }
     key[j] = j < KE ? ((uint64_t)((uint32_t)v ^ 0x80000000u) << 32) | (uint32_t)j : ~0ull;
   }
   for (int size = 2; size <= KP; size <<= 1) {
@@ -215,6 +229,19 @@ hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8
 // Thread j: (a) zero kl/lse of row j if it is masked, (b) if j is a valid
 // compacted row, merge its S partials (m2, l, x) in split order:
 // kl = sum w log p - x / tau + mass L.
+// (m2, l, x) of S partials at stride `stride` (float4 units), in split order
+__device__ inline float3 merge_splits(const float4* pp, int S, long stride) {
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, pp[(long)s * stride].x);
+  float l = 0.f, x = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float4 q = pp[(long)s * stride];
+    l += q.y * exp2f(q.x - M);
+    x += q.z;
+  }
+  return make_float3(M, l, x);
+}
+
 __global__ void topk_combine_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask,
                                     TopkRowData rd, long T, float* kl, float* lse, long jb, long je,
                                     int zero_masked) {
@@ -225,15 +252,8 @@ __global__ void topk_combine_kernel(const float* part, int S, long stride, Compa
     lse[j] = 0.f;
   }
   if (j < jb || j >= je || j >= *c.count) return;
-  const float4* pp = reinterpret_cast<const float4*>(part) + (j - jb);
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, pp[(long)s * stride].x);
-  float l = 0.f, x = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float4 q = pp[(long)s * stride];
-    l += q.y * exp2f(q.x - M);
-    x += q.z;
-  }
+  const float3 q = merge_splits(reinterpret_cast<const float4*>(part) + (j - jb), S, stride);
+  const float M = q.x, l = q.y, x = q.z;
   const long t = c.rows[j];
   const float4 rc = rd.rowc[t];
   const float L = (M + log2f(l)) * kLn2;
@@ -247,6 +267,57 @@ hipError_t launch_topk_combine(const float* part, int S, int64_t part_stride, Co
   const dim3 grid((unsigned)((T + 255) / 256));
   hipLaunchKernelGGL(topk_combine_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, rd, (long)T,
                      kl, lse, (long)jb, (long)je, zero_masked ? 1 : 0);
+  return hipGetLastError();
+}
+
+__global__ void topk_shard_record_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask,
+                                         TopkRowData rd, long T, float4* rec, float2* trow, long jb, long je,
+                                         int zero_masked) {
+  const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= T) return;
+  if (zero_masked && mask != nullptr && mask[j] == 0) {
+    rec[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    trow[j] = make_float2(0.f, 0.f);
+  }
+  if (j < jb || j >= je || j >= *c.count) return;
+  const float3 q = merge_splits(reinterpret_cast<const float4*>(part) + (j - jb), S, stride);
+  const long t = c.rows[j];
+  const float4 rc = rd.rowc[t];
+  rec[t] = make_float4(q.x, q.y, q.z * rc.y, 0.f);
+  trow[t] = make_float2(rd.ent[t], rc.z);
+}
+
+hipError_t launch_topk_shard_record(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
+                                    TopkRowData rd, int64_t T, float4* rec, float2* trow, int64_t jb, int64_t je,
+                                    bool zero_masked, hipStream_t st) {
+  const dim3 grid((unsigned)((T + 255) / 256));
+  hipLaunchKernelGGL(topk_shard_record_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, rd,
+                     (long)T, rec, trow, (long)jb, (long)je, zero_masked ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Row t: the R shards' (m2, l) give the log-normaliser over all columns,
+// their cross terms add: kl = entropy term - sum of cross terms + mass L.
+__global__ void topk_shard_combine_kernel(const float4* rec, int R, long T, const float2* trow,
+                                          const uint8_t* mask, float* kl, float* lse) {
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  if (mask != nullptr && mask[t] == 0) {
+    kl[t] = 0.f;
+    lse[t] = 0.f;
+    return;
+  }
+  const float3 q = merge_splits(rec + t, R, T);
+  const float2 tr = trow[t];
+  const float L = (q.x + log2f(q.y)) * kLn2;
+  lse[t] = L;
+  kl[t] = tr.x - q.z + tr.y * L;
+}
+
+hipError_t launch_topk_shard_combine(const float4* rec, int R, int64_t T, const float2* trow, const uint8_t* mask,
+                                     float* kl, float* lse, hipStream_t st) {
+  const dim3 grid((unsigned)((T + 255) / 256));
+  hipLaunchKernelGGL(topk_shard_combine_kernel, grid, dim3(256), 0, st, rec, R, (long)T, trow, mask, kl, lse);
   return hipGetLastError();
 }
 

@@ -218,6 +218,66 @@ kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* top
                                 void* dH, float* dW, int64_t chunk_rows,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- top-K, one vocabulary shard
+ * The top-K loss with the output head split by vocabulary columns over R
+ * ranks, the tensor-parallel layout of an output head (the loss-only
+ * benchmark reports time and memory at the largest tensor-parallel rank,
+ * App. B).  Rank r holds W_r = columns [v0, v0 + V) of the head, [d,V]
+ * row-major (V here is the shard's width), and every rank holds all of H,
+ * topk_idx (indices into the whole head), topk_logits, mask and the options.
+ * One step:
+ *   1. each rank: kd_topk_kl_fwd_shard -> rec_r [T,4], trow [T,2]
+ *   2. all-gather rec over the ranks into rec [R,T,4] (rank order)
+ *   3. each rank: kd_topk_kl_shard_combine -> kl [T] and lse [T], the
+ *      log-normaliser over the whole head (the same on every rank)
+ *   4. each rank: kd_topk_kl_bwd_shard with that lse -> dH_r [T,d] float32,
+ *      a partial of dH, and dW_r [d,V] float32, the shard's columns of dW
+ *   5. sum dH_r over the ranks (all-reduce); dW stays sharded.
+ * The library does none of the exchanges; the caller's collectives move
+ * 16 bytes per row in step 2 and d float32 per row in step 5.  The results
+ * are those of the unsharded calls up to rounding (the shard records merge
+ * like the kernels' own split partials).  The single call has no shard form:
+ * its backward needs the whole head's lse before the exchange.
+ *
+ * Records, per valid row t (s = z / tau_t over the shard's columns, hits =
+ * the cached entries whose index lies in [v0, v0 + V)):
+ *   rec[t]  = (m, l, c, 0) with m + log2(l) = log2(sum over the shard of
+ *             exp(s)) (m a base-2 maximum, l a scaled sum) and
+ *             c = sum over hits of w_k s[I_tk] (w: the entries' weights,
+ *             p_k, or with a CE term (1 - ce_weight) p_k and ce_weight at the
+ *             label); masked rows: all zero
+ *   trow[t] = (sum_k w_k log p_k, mass), the teacher terms over all K entries
+ *             (the same on every rank; masked rows: zero)
+ *   the combine: L_t = ln 2 * log2(sum_r l_r 2^(m_r - M)) + ln 2 * M with
+ *   M = max_r m_r; kl_t = trow.x - sum_r c_r + trow.y * L_t.
+ * Argument rules are those of the _ex calls, except that K may exceed the
+ * shard's width V, v0 must be >= 0 (KD_ERR_INVALID_ARG) and v0 + V below
+ * 2^30 (KD_ERR_UNSUPPORTED).  rec must be 16-byte and trow 8-byte aligned;
+ * dH here is always float32 (the partial is summed before any rounding). */
+/* Workspace bytes for a shard's forward and backward (one size serves
+ * both; the rules of kd_topk_kl_workspace_size at the shard's width V). */
+kd_status kd_topk_kl_shard_workspace_size(int64_t T, int64_t d, int64_t V, int64_t v0, int64_t K,
+                                          kd_dtype dt, int64_t chunk_rows, size_t* bytes);
+/* z_topk, when given, holds the logits of the shard's hits and 0 elsewhere,
+ * so the ranks' arrays add up to the unsharded one. */
+kd_status kd_topk_kl_fwd_shard(const void* H, const void* W, const int32_t* topk_idx,
+                               const float* topk_logits, const uint8_t* mask, float tau,
+                               const kd_topk_opts* opts,
+                               int64_t T, int64_t d, int64_t V, int64_t v0, int64_t K, kd_dtype dt,
+                               float* rec, float* trow, float* z_topk,
+                               void* workspace, size_t workspace_bytes, void* stream);
+/* rec [R,T,4] (R records in rank order), trow [T,2] -> kl [T], lse [T];
+ * masked rows get 0.  R >= 1 and R * T < 2^31.  No workspace. */
+kd_status kd_topk_kl_shard_combine(const float* rec, int64_t R, const float* trow, const uint8_t* mask,
+                                   int64_t T, float* kl, float* lse, void* stream);
+kd_status kd_topk_kl_bwd_shard(const void* H, const void* W, const int32_t* topk_idx,
+                               const float* topk_logits, const uint8_t* mask, float tau,
+                               const kd_topk_opts* opts,
+                               int64_t T, int64_t d, int64_t V, int64_t v0, int64_t K, kd_dtype dt,
+                               const float* lse, const float* grad_kl,
+                               float* dH, float* dW, int64_t chunk_rows,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- full vocabulary */
 
 /* Workspace bytes for kd_full_kl_fwd and kd_full_kl_bwd (one size serves

@@ -60,6 +60,7 @@ __all__ = [
     "as_f64", "logsumexp_rows", "teacher_log_probs",
     "topk_kl_forward", "topk_kl_backward", "topk_kl_rows",
     "topk_loss_forward", "topk_loss_backward", "topk_loss_rows",
+    "topk_shard_terms", "topk_shard_backward",
     "full_kl_forward", "full_kl_backward", "full_kl_rows",
     "full_loss_forward", "full_loss_backward", "full_loss_rows",
 ]
@@ -321,6 +322,79 @@ def topk_loss_rows(H, W, I, A, mask, tau, g, rows, tau_rows=None, teacher_lse=No
     loss, lse, ztk = topk_loss_forward(Hr, W, Ir, Ar, mr, tau, **kw)
     dH, _ = topk_loss_backward(Hr, W, Ir, Ar, mr, tau, gr, want_dw=False, **kw)
     return loss, lse, ztk, dH
+
+
+def topk_shard_terms(H, W_shard, v0, I, A, mask, tau, tau_rows=None, teacher_lse=None, labels=None,
+                     ce_weight=0.0):
+    """The terms of topk_loss_forward that one vocabulary shard of the head
+    holds, W_shard being columns [v0, v0 + Vs) of W (the head split by
+    vocabulary columns across tensor-parallel ranks; [EKD] App. B reports the
+    loss benchmark at the largest tensor-parallel rank).  Per valid row t, with
+    s = (H_t W_shard) / tau_t and the support weights w (p_k, times 1 - beta
+    with a CE label, which weighs beta):
+        lse_shard_t = logsumexp over the shard's columns of s
+        cross_t     = sum of w_k s[I_tk - v0] over the entries inside the shard
+        ent_t       = sum of w_k log p_k over all K entries
+        mass_t      = m_t, or (1 - beta) m_t + beta with a label
+    so that over a partition of the vocabulary into shards
+        L_t = logsumexp_shards(lse_shard_t),
+        loss_t = ent_t - sum_shards(cross_t) + mass_t L_t.
+    Masked rows give zeros.  Returns (lse_shard, cross, ent, mass), each [T]."""
+    H, W_shard, A = as_f64(H), as_f64(W_shard), as_f64(A)
+    I = np.asarray(I.cpu().numpy() if hasattr(I, "cpu") else I, dtype=np.int64)
+    T, K = I.shape
+    Vs = W_shard.shape[1]
+    taus = _row_values(tau_rows, T, tau)
+    tlse = None if teacher_lse is None else _row_values(teacher_lse, T, 0.0)
+    y = None if labels is None else np.asarray(labels.cpu().numpy() if hasattr(labels, "cpu") else labels,
+                                               dtype=np.int64)
+    beta = float(ce_weight) if y is not None else 0.0
+    valid = _valid_rows(mask, T)
+    out = [np.zeros(T) for _ in range(4)]
+    for t in np.nonzero(valid)[0]:
+        _, s, Ls, p, logp, m = _loss_block(H, W_shard, A, np.array([t]), taus, tlse)
+        s, p, logp = s[0], p[0], logp[0]
+        wk = 1.0 - beta
+        cross = 0.0
+        for k in range(K):
+            j = I[t, k] - v0
+            if 0 <= j < Vs:
+                cross += wk * p[k] * s[j]
+        if beta != 0.0 and 0 <= y[t] - v0 < Vs:
+            cross += beta * s[y[t] - v0]
+        out[0][t] = Ls[0]
+        out[1][t] = cross
+        out[2][t] = wk * float((p * logp).sum())
+        out[3][t] = wk * float(m[0]) + beta
+    return tuple(out)
+
+
+def topk_shard_backward(H, W, v0, Vs, I, A, mask, tau, g, tau_rows=None, teacher_lse=None, labels=None,
+                        ce_weight=0.0, row_block=64):
+    """One vocabulary shard's part of topk_loss_backward: with dZ the whole
+    head's gradient (_loss_dz, whose softmax needs every column of W) and
+    columns c = [v0, v0 + Vs), the shard's dH partial dZ[:, c] W[:, c]^T and
+    its columns of dW, H^T dZ[:, c].  Summed over a partition of the columns,
+    the partials give dH.  Returns (dH_partial [T, d], dW_shard [d, Vs])."""
+    H, W, A, g = as_f64(H), as_f64(W), as_f64(A), as_f64(g)
+    I = np.asarray(I.cpu().numpy() if hasattr(I, "cpu") else I, dtype=np.int64)
+    T, d = H.shape
+    taus = _row_values(tau_rows, T, tau)
+    tlse = None if teacher_lse is None else _row_values(teacher_lse, T, 0.0)
+    y = None if labels is None else np.asarray(labels.cpu().numpy() if hasattr(labels, "cpu") else labels,
+                                               dtype=np.int64)
+    beta = float(ce_weight)
+    valid = _valid_rows(mask, T)
+    dH, dW = np.zeros((T, d)), np.zeros((d, Vs))
+    Wc = W[:, v0:v0 + Vs]
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        _, s, L, p, _, m = _loss_block(H, W, A, rb, taus, tlse)
+        D = _loss_dz(s, L, I[rb], p, m, None if y is None else y[rb], beta, g[rb], taus[rb])[:, v0:v0 + Vs]
+        dH[rb] = D @ Wc.T
+        dW += H[rb].T @ D
+    return dH, dW
 
 
 def full_kl_forward(H, Ws, Ht, Wt, mask, tau, row_block=64):

@@ -29,7 +29,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 23
+    assert len(names) == 27
     for n in names:
         assert hasattr(L, n), f"{n} declared in kdloss.h but not exported"
     assert sorted(kdl.EXPORTS) == names
@@ -338,3 +338,57 @@ def test_bf16_chunks_stay_within_the_direct_load_reach(L):
     assert ws_topk(65536, chunk=16128)[1] < big
     # fp32 has no such limit (its mainloop is not the direct-load one)
     assert ws_topk(65536, chunk=32768, dt=kdl.KD_F32)[1] > ws_topk(65536, chunk=16640, dt=kdl.KD_F32)[1]
+
+
+# ---------------------------------------------------------------- one vocabulary shard
+def fwd_shard(T=8, d=64, V=256, v0=512, K=4, dt=kdl.KD_BF16, tau=1.0, rec=FAKE, trow=FAKE, wsb=0):
+    vp = ctypes.c_void_p
+    return kdl.lib().kd_topk_kl_fwd_shard(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(tau), None,
+                                          T, d, V, v0, K, dt, vp(rec) if rec else None,
+                                          vp(trow) if trow else None, None, vp(FAKE), wsb, None)
+
+
+def bwd_shard(T=8, d=64, V=256, v0=512, K=4, dH=FAKE, dW=FAKE, wsb=0):
+    vp = ctypes.c_void_p
+    return kdl.lib().kd_topk_kl_bwd_shard(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), None,
+                                          T, d, V, v0, K, kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(dH) if dH else None,
+                                          vp(dW) if dW else None, 0, vp(FAKE), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v0=-1), 1), (dict(rec=0), 1), (dict(trow=0), 1), (dict(K=0), 1),
+    (dict(v0=(1 << 30) - 100), 2), (dict(K=kdl.KD_MAX_K + 1), 2),
+    (dict(rec=FAKE + 8), 3), (dict(trow=FAKE + 4), 3),
+    (dict(wsb=16), 4), (dict(K=300, wsb=16), 4),  # K may exceed the shard's width
+])
+def test_topk_fwd_shard_rejects(L, kw, code):
+    assert fwd_shard(**kw) == code
+    assert last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v0=-1), 1), (dict(dH=0), 1), (dict(dW=0), 1), (dict(dH=FAKE + 8), 3), (dict(wsb=16), 4),
+    (dict(K=300, wsb=16), 4),
+])
+def test_topk_bwd_shard_rejects(L, kw, code):
+    assert bwd_shard(**kw) == code
+
+
+def test_shard_combine_checks(L):
+    vp = ctypes.c_void_p
+    comb = kdl.lib().kd_topk_kl_shard_combine
+    assert comb(vp(FAKE), 8, vp(FAKE), None, 0, None, None, None) == 0  # T = 0: nothing to do
+    assert comb(vp(FAKE), 0, vp(FAKE), None, 16, vp(FAKE), vp(FAKE), None) == 1
+    assert comb(vp(FAKE), 8, vp(FAKE), None, -1, vp(FAKE), vp(FAKE), None) == 1
+    assert comb(None, 8, vp(FAKE), None, 16, vp(FAKE), vp(FAKE), None) == 1
+    assert comb(vp(FAKE + 8), 8, vp(FAKE), None, 16, vp(FAKE), vp(FAKE), None) == 3
+    assert comb(vp(FAKE), 8, vp(FAKE + 4), None, 16, vp(FAKE), vp(FAKE), None) == 3
+    assert comb(vp(FAKE), 1 << 20, vp(FAKE), None, 1 << 12, vp(FAKE), vp(FAKE), None) == 2
+
+
+def test_shard_workspace_is_the_plain_size_at_the_shard_width(L):
+    for T, d, V, K, chunk in ((4096, 3072, 16032, 64, 0), (300, 256, 168, 16, 256)):
+        assert (kdl.kd_topk_kl_shard_workspace_size(T, d, V, 3 * V, K, kdl.torch.bfloat16, chunk)
+                == kdl.kd_topk_kl_workspace_size(T, d, V, K, kdl.torch.bfloat16, chunk))
+    # more cached entries than the shard has columns
+    assert kdl.kd_topk_kl_shard_workspace_size(64, 64, 8, 0, 16, kdl.torch.bfloat16) > 0
