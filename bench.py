@@ -300,8 +300,64 @@ def run_full(p, steps: int, warmup: int, chunk_rows: int, one_call: bool = False
     return out
 
 
+def run_topk_shard(p, T: int, R: int, steps: int, warmup: int, chunk_rows: int):
+    """Time one rank's step of the top-K loss with the head split by vocabulary
+    over R ranks (rank 0: columns [0, V/R)): its forward, the combine of R
+    records and its backward.  The other ranks' records are copies of its own,
+    made once before timing (the exchange between GPUs is not part of one
+    GPU's work; the combine does the same arithmetic on any records)."""
+    import torch
+    import chunked_kl_loss_logit_amd as kd
+    import kdinputs as G
+
+    inp = G.make_topk(T, p.d, p.V, p.K, p.dtype, tau=p.tau, teacher_var=p.teacher_var, mask=p.mask,
+                      number=p.number, seq_len=p.seq_len, n_pad=p.n_pad, g="mean")
+    dev = torch.device("cuda:0")
+    Vs = p.V // R
+    H, I, A, g = (inp[k].to(dev) for k in ("H", "I", "A", "g"))
+    W = inp["W"][:, :Vs].contiguous().to(dev)
+    M = None if inp["mask"] is None else inp["mask"].to(dev)
+    n_valid = T if inp["mask"] is None else int(inp["mask"].sum())
+    del inp
+    d, K, tau = p.d, p.K, p.tau
+    rec = torch.empty(R, T, 4, device=dev)
+    trow = torch.empty(T, 2, device=dev)
+    kl = torch.empty(T, device=dev)
+    lse = torch.empty(T, device=dev)
+    dH = torch.empty(T, d, device=dev)
+    dW = torch.empty(d, Vs, device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    ws = torch.empty(kd.kd_topk_kl_shard_workspace_size(T, d, Vs, 0, K, p.dtype, chunk_rows), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        kd.kd_topk_kl_fwd_shard(H, W, 0, I, A, M, tau, None, rec[0], trow, None, ws)
+        kd.kd_topk_kl_shard_combine(rec, trow, M, kl, lse)
+        kd.kd_topk_kl_bwd_shard(H, W, 0, I, A, M, tau, None, lse, g, dH, dW, chunk_rows, ws)
+
+    kd.kd_topk_kl_fwd_shard(H, W, 0, I, A, M, tau, None, rec[0], trow, None, ws)
+    rec[1:].copy_(rec[0].expand(R - 1, T, 4))
+    step()
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated() - base + (rec.numel() + trow.numel() + lse.numel()) * 4
+    ms, prof = timed(step, steps, warmup)
+    fl = {k: 2.0 * n_valid * d * Vs for k in ("topk_fwd_tile", "topk_dz_tile", "dh_tile", "dw_tile")}
+    dom, achieved = dominant(prof, fl, steps)
+    cred = 6.0 * n_valid * d * Vs / (ms * 1e-3) / 1e12
+    out = {"workload": f"{p.name}_vshard{R}", "T": T, "V_shard": Vs, "valid_rows": n_valid, "ms_per_step": ms,
+           "tokens_per_s": T / (ms * 1e-3), "valid_tokens_per_s": n_valid / (ms * 1e-3), "credited_tflops": cred,
+           "mfma_frac_credited": cred / PEAK_BF16_TFLOPS, "mfma_frac_executed": cred / PEAK_BF16_TFLOPS * 8.0 / 6.0,
+           "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
+           "kernels": kernel_table(prof, ms, steps), "steps_timed": steps}
+    del H, W, I, A, g, M, rec, trow, kl, lse, dH, dW, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def brief(r):
-    keep = ("workload", "T", "valid_rows", "ms_per_step", "tokens_per_s", "valid_tokens_per_s", "credited_tflops",
+    keep = ("workload", "T", "V_shard", "valid_rows", "ms_per_step", "tokens_per_s", "valid_tokens_per_s", "credited_tflops",
             "mfma_frac_credited", "mfma_frac_executed", "peak_extra_hbm_bytes", "dominant", "dominant_tflops")
     out = {k: r[k] for k in keep if k in r}
     out["kernel_ms"] = {k: round(v["avg_ms"] * v["launches"] / r["steps_timed"], 4) for k, v in r["kernels"].items()} \
@@ -381,6 +437,8 @@ def main():
                         pk.name: brief(run_topk(pk, pk.T, 3, 1, a.chunk_rows)[0]),
                         fv.name: brief(run_full(fv, 3, 1, a.chunk_rows)),
                         fv.name + "_one_call": brief(run_full(fv, 3, 1, a.chunk_rows, one_call=True))}
+        sh = run_topk_shard(p, T, 8, a.steps, a.warmup, a.chunk_rows)
+        out["extra"][sh["workload"]] = brief(sh)
     print(json.dumps(out))
 
 

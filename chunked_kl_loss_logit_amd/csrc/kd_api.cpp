@@ -341,6 +341,9 @@ kd_status grad_chunk(const void* H, const void* W, void* dH, float* dW, int elem
                      const kd::Compact& c, const ChunkPlan& ch, char* dz, char* hT, float* dhp, int64_t c0,
                      bool accumulate, hipStream_t st, int dh_elem = 0) {
   KD_LAUNCH("gather_transpose", st, kd::launch_gather_transpose(H, elem, d, c, c0, ch.C, hT, st));
+  if (c0 == 0 && kd::dh_direct(elem, V) && V % 128 != 0)  // the dH ring reads the chunk's columns up to ldz
+    KD_LAUNCH("fill_zero", st,
+              kd::launch_fill_zero(dz + kd::dz_tail_offset(ch.C, V), kd::dz_tail_bytes(ch.C, V, ch.ldz), st));
   kd::DhArgs ha{};
   ha.dz = dz;
   ha.W = static_cast<const char*>(W);

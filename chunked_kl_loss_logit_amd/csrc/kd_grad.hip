@@ -60,7 +60,9 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   const long row0 = (long)rb * kBM, n0 = (long)cb * BN;
   if (row0 >= M) return;
 
-  // contraction over the first V columns of both operands, split in S ranges
+  // contraction over the first V columns of both operands, split in S
+  // ranges (the direct-load ring rounds it up to whole turns: the dZ chunk
+  // holds zeros from V to ldz)
   Main mainloop;
   // dz in panels of C rows, W row-major
   mainloop.init(a.dz, [&](int r) -> const char* { return row0 + r < M ? a.dz + (row0 + r) * kRowB : nullptr; },
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
 
 hipError_t launch_dh(int elem, const DhArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.ncb * a.S), block(kThreads);
-  if (elem == 2 && a.V % kDmaKMult == 0 && fits32(a.C * a.ldz * 2) && fits32(a.d * a.V * 2))
+  if (dh_direct(elem, a.V) && fits32(a.C * a.ldz * 2) && fits32(a.d * a.V * 2))
     hipLaunchKernelGGL((dh_kernel<DmaNT<256>, Bf16>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((dh_kernel<GenNT<Bf16, 256>, Bf16>), grid, block, 0, st, a);

@@ -89,6 +89,14 @@ hipError_t launch_gather_transpose(const void* H, int elem, int64_t d, Compact c
 hipError_t launch_gather_panels(const void* H, int64_t row_bytes, Compact c, int64_t c0, int64_t C, void* out,
                                 hipStream_t st);
 // dH[rows[c0 + i]] = sum_s part[s][i] (converted to the element type)
+// dH's vocabulary contraction takes the direct-load ring for bf16 when V is a
+// multiple of 32 (whole 64-byte stages of W's rows); for V not a multiple of
+// 128 the ring runs over V rounded up to 128, so the dZ chunk's columns from V
+// to ldz must hold zeros (dz_tail_bytes of them, in whole panel pieces, at
+// dz_tail_offset).
+inline bool dh_direct(int elem, int64_t V) { return elem == 2 && V % 32 == 0; }
+inline int64_t dz_tail_offset(int64_t C, int64_t V) { return V / 32 * C * 64; }
+inline int64_t dz_tail_bytes(int64_t C, int64_t V, int64_t ldz) { return (ldz - V) / 32 * C * 64; }
 hipError_t launch_reduce_dh(const float* part, int S, int64_t C, int64_t d, Compact c, int64_t c0, void* dH,
                             int elem, hipStream_t st);
 hipError_t launch_zero_masked_rows(const uint8_t* mask, int64_t T, int64_t row_bytes, void* out, hipStream_t st);

@@ -8,7 +8,11 @@
 //     GenNN<E, BN>   any shape or dtype: register-staged loads, B transposed
 //                    in registers, double buffer in slots 0 and 1
 //   NT (B is k-contiguous: W as [d][V] when V is the contraction)
-//     DmaNT<BN>, GenNT<E, BN>
+//     DmaNT<BN>      bf16, contraction K a multiple of 32, run over K rounded
+//                    up to 128 (whole ring turns): A must hold readable zeros
+//                    in the rounding, and B's stages past K re-read its last
+//                    one (finite data times those zeros adds nothing)
+//     GenNT<E, BN>   any shape or dtype
 //
 // init(row_ptr, ...) takes row_ptr(r) -> address of the first stage of A row
 // r of the tile (row-major: the row itself; panels: the row's first 64-byte
@@ -337,7 +341,7 @@ struct DmaNT {
   DmaRows<kBM> a;
   DmaRows<BN> b;
   FragReader<BN> rd;
-  long nst;
+  long nst, b_last;  // stages contracted; B's last stage
 
   // a_sst, b_sst: stage strides of the operands (see DmaRows)
   template <class RowPtrA, class RowPtrB>
@@ -359,7 +363,8 @@ struct DmaNT {
           return p ? p : sb;
         },
         b_sst);
-    nst = K / kDmaKs;
+    nst = (K + kDmaKMult - 1) / kDmaKMult * kRing;
+    b_last = K / kDmaKs - 1;
     rd.init_rows();
   }
 
@@ -369,7 +374,7 @@ struct DmaNT {
         sl, (int)(s1 - s0),
         [&](long s, char* da, char* db) {
           a.issue(s0 + s, da);
-          b.issue(s0 + s, db);
+          b.issue(min(s0 + s, b_last), db);
         },
         [&](const char* slot, FragsRows<BN>& f) { rd.read_rows(slot, f); },
         [&](const FragsRows<BN>& f) { mma_frags(f, acc); });
