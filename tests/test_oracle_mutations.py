@@ -11,6 +11,7 @@ import pytest
 from oracle import kd_oracle as O
 from tests import test_oracle as P
 from tests import test_oracle_options as Q
+from tests import test_oracle_shard as S
 
 PINS = [
     P.test_lse_constant_rows_closed_form, P.test_lse_matches_scipy, P.test_teacher_equal_logits,
@@ -30,6 +31,10 @@ PINS = [
     Q.test_full_reverse_kl_is_torch_kl_div_swapped, Q.test_full_kl_mixing_is_the_convex_combination,
     Q.test_full_per_token_tau_is_row_scaling, Q.test_full_mixed_gradient_matches_torch_autograd,
     Q.test_full_mixed_finite_differences_and_mask,
+    lambda: S.test_partition_gives_the_unsharded_loss("plain", False),
+    lambda: S.test_partition_gives_the_unsharded_loss("every", True),
+    S.test_whole_head_as_one_shard, S.test_terms_against_scipy_and_the_dense_teacher,
+    lambda: S.test_backward_partials_make_up_the_gradient("every"),
 ]
 
 
@@ -205,8 +210,33 @@ def _full_block_scalar_tau(H, Ws, Ht, Wt, rb, taus):
 
 
 _ORIG_FULL_BLOCK = O._full_block
+_ORIG_SHARD_TERMS = O.topk_shard_terms
+_ORIG_SHARD_BWD = O.topk_shard_backward
+
+
+def _shard_terms_unshifted(H, W_shard, v0, *args, **kw):
+    return _ORIG_SHARD_TERMS(H, W_shard, 0, *args, **kw)  # global indices taken as the shard's columns
+
+
+def _shard_terms_ce_ignored(*args, labels=None, ce_weight=0.0, **kw):
+    return _ORIG_SHARD_TERMS(*args, **kw)
+
+
+def _shard_terms_entropy_unweighted(*args, labels=None, ce_weight=0.0, **kw):
+    ls, cross, ent, mass = _ORIG_SHARD_TERMS(*args, labels=labels, ce_weight=ce_weight, **kw)
+    if labels is not None and ce_weight:
+        ent = ent / (1.0 - ce_weight)
+    return ls, cross, ent, mass
+
+
+def _shard_bwd_first_columns(H, W, v0, Vs, *args, **kw):
+    return _ORIG_SHARD_BWD(H, W, 0, Vs, *args, **kw)
 
 MUTATIONS = {
+    "shard_indices_not_shifted": ("topk_shard_terms", _shard_terms_unshifted),
+    "shard_ce_term_ignored": ("topk_shard_terms", _shard_terms_ce_ignored),
+    "shard_entropy_unweighted": ("topk_shard_terms", _shard_terms_entropy_unweighted),
+    "shard_backward_wrong_columns": ("topk_shard_backward", _shard_bwd_first_columns),
     "full_dz_reverse_baseline_dropped": ("_full_loss_dz", _full_dz_no_klr),
     "full_dz_reverse_sign": ("_full_loss_dz", _full_dz_reverse_sign),
     "full_mix_weights_swapped": ("full_loss_forward", _full_loss_mix_swapped),
