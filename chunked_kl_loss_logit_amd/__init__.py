@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     kd_topk_kl_workspace_size, kd_version, lib,
     profile_enable, profile_read, profile_reset,
     kd_topk_kl_shard_workspace_size, kd_topk_kl_fwd_shard, kd_topk_kl_shard_combine, kd_topk_kl_bwd_shard,
+    kd_full_kl_fwd_shard, kd_full_kl_shard_combine, kd_full_kl_bwd_shard,
 )
 
 __all__ = [
@@ -35,6 +36,8 @@ __all__ = [
     "kd_full_kl_bwd_ex", "kd_full_kl_fwd_bwd_ex", "full_opts",
     "topk_kl_shard_forward", "topk_kl_shard_combine", "topk_kl_shard_backward", "kd_topk_kl_shard_workspace_size",
     "kd_topk_kl_fwd_shard", "kd_topk_kl_shard_combine", "kd_topk_kl_bwd_shard",
+    "full_kl_shard_forward", "full_kl_shard_combine", "full_kl_shard_backward", "kd_full_kl_fwd_shard",
+    "kd_full_kl_shard_combine", "kd_full_kl_bwd_shard",
 ]
 
 
@@ -131,6 +134,45 @@ def topk_kl_shard_backward(H, W_shard, v0, topk_idx, topk_logits, mask, tau, lse
         workspace = _workspace(kd_topk_kl_shard_workspace_size(T, d, V, v0, K, H.dtype, chunk_rows), H.device)
     kd_topk_kl_bwd_shard(H, W_shard, v0, topk_idx, topk_logits, mask, tau, topk_opts(**options), lse,
                          grad_kl.float().contiguous(), dH, dW, chunk_rows, workspace)
+    return dH, dW
+
+
+# One vocabulary shard of the full-vocabulary loss: Ws_shard and Wt_shard hold
+# the same columns of the two heads (kdloss.h, "full vocabulary, one
+# vocabulary shard"); the caller all-gathers the records and sums dH.
+def full_kl_shard_forward(H, Ws_shard, Ht, Wt_shard, mask=None, tau=1.0, workspace=None, tau_rows=None):
+    """This shard's row records rec [T,8] float32."""
+    T, d = H.shape
+    dt, V = Ht.shape[1], Ws_shard.shape[1]
+    rec = torch.empty(T, 8, dtype=torch.float32, device=H.device)
+    if workspace is None:
+        workspace = _workspace(kd_full_kl_workspace_size(T, d, dt, V, H.dtype), H.device)
+    kd_full_kl_fwd_shard(H, Ws_shard, Ht, Wt_shard, mask, tau, full_opts(tau_rows=tau_rows), rec, workspace)
+    return rec
+
+
+def full_kl_shard_combine(recs, mask=None, rev_weight=0.0, want_kl_rev=False):
+    """kl, lse_s, lse_t (and kl_rev, or None) of the whole heads from the shards' records (a list in rank
+    order, or one [R,T,8] tensor)."""
+    rec = recs if isinstance(recs, torch.Tensor) else torch.stack(list(recs))
+    T = rec.shape[1]
+    kl, lse_s, lse_t = (torch.empty(T, dtype=torch.float32, device=rec.device) for _ in range(3))
+    kl_rev = torch.empty(T, dtype=torch.float32, device=rec.device) if want_kl_rev or rev_weight else None
+    kd_full_kl_shard_combine(rec.contiguous(), mask, rev_weight, kl, lse_s, lse_t, kl_rev)
+    return kl, lse_s, lse_t, kl_rev
+
+
+def full_kl_shard_backward(H, Ws_shard, Ht, Wt_shard, mask, tau, lse_s, lse_t, grad_kl, chunk_rows=0,
+                           workspace=None, tau_rows=None, rev_weight=0.0, kl_rev=None):
+    """This shard's dH partial [T,d] float32 and its columns of dWs [d,V_shard] float32."""
+    T, d = H.shape
+    dt, V = Ht.shape[1], Ws_shard.shape[1]
+    dH = torch.empty(T, d, dtype=torch.float32, device=H.device)
+    dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
+    if workspace is None:
+        workspace = _workspace(kd_full_kl_workspace_size(T, d, dt, V, H.dtype, chunk_rows), H.device)
+    kd_full_kl_bwd_shard(H, Ws_shard, Ht, Wt_shard, mask, tau, full_opts(tau_rows=tau_rows, rev_weight=rev_weight),
+                         lse_s, lse_t, kl_rev, grad_kl.float().contiguous(), dH, dW, chunk_rows, workspace)
     return dH, dW
 
 

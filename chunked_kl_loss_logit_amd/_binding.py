@@ -28,6 +28,7 @@ EXPORTS = (
     "kd_topk_kl_fwd_bwd_workspace_size", "kd_topk_kl_fwd_bwd",
     "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex",
     "kd_topk_kl_shard_workspace_size", "kd_topk_kl_fwd_shard", "kd_topk_kl_shard_combine", "kd_topk_kl_bwd_shard",
+    "kd_full_kl_fwd_shard", "kd_full_kl_shard_combine", "kd_full_kl_bwd_shard",
     "kd_full_kl_workspace_size", "kd_full_kl_fwd", "kd_full_kl_bwd",
     "kd_full_kl_fwd_bwd_workspace_size", "kd_full_kl_fwd_bwd",
     "kd_full_kl_fwd_ex", "kd_full_kl_bwd_ex", "kd_full_kl_fwd_bwd_ex",
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
                                     vp, sz, vp]
     L.kd_full_kl_fwd_bwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, fo, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp,
                                         vp, i64, vp, sz, vp]
+    L.kd_full_kl_fwd_shard.argtypes = [vp, vp, vp, vp, vp, f32, fo, i64, i64, i64, i64, st, vp, vp, sz, vp]
+    L.kd_full_kl_shard_combine.argtypes = [vp, i64, vp, i64, f32, vp, vp, vp, vp, vp]
+    L.kd_full_kl_bwd_shard.argtypes = [vp, vp, vp, vp, vp, f32, fo, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp,
+                                       i64, vp, sz, vp]
     L.kd_full_kl_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
     L.kd_full_kl_fwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, sz, vp]
     L.kd_full_kl_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, i64, vp, sz,
@@ -386,6 +391,39 @@ def kd_full_kl_fwd_bwd_ex(H, Ws, Ht, Wt, mask, tau, opts, grad_kl, kl, lse_s, ls
                                        _ptr(lse_s), _ptr(lse_t), _ptr(kl_rev), _ptr(dH), _ptr(dWs), int(chunk_rows),
                                        _ptr(workspace), workspace.numel() if workspace is not None else 0,
                                        _stream(stream)), "kd_full_kl_fwd_bwd_ex")
+
+
+def kd_full_kl_fwd_shard(H, Ws, Ht, Wt, mask, tau, opts, rec, workspace, stream=None):
+    """One vocabulary shard's full-vocabulary forward: Ws and Wt hold the same columns of both heads;
+    rec [T,8] float32 out."""
+    T, d = H.shape
+    dt = Ht.shape[1]
+    V = Ws.shape[1]
+    _check(lib().kd_full_kl_fwd_shard(_ptr(H), _ptr(Ws), _ptr(Ht), _ptr(Wt), _ptr(mask), float(tau),
+                                      _opts_ref(opts), T, d, dt, V, _dtype_code(H.dtype), _ptr(rec), _ptr(workspace),
+                                      workspace.numel() if workspace is not None else 0, _stream(stream)),
+           "kd_full_kl_fwd_shard")
+
+
+def kd_full_kl_shard_combine(rec, mask, rev_weight, kl, lse_s, lse_t, kl_rev, stream=None):
+    """rec [R,T,8] (the shards' records in rank order) -> kl, lse_s, lse_t [T] and kl_rev [T] or None."""
+    R, T = rec.shape[0], rec.shape[1]
+    _check(lib().kd_full_kl_shard_combine(_ptr(rec), R, _ptr(mask), T, float(rev_weight), _ptr(kl), _ptr(lse_s),
+                                          _ptr(lse_t), _ptr(kl_rev), _stream(stream)), "kd_full_kl_shard_combine")
+
+
+def kd_full_kl_bwd_shard(H, Ws, Ht, Wt, mask, tau, opts, lse_s, lse_t, kl_rev, grad_kl, dH, dWs, chunk_rows,
+                         workspace, stream=None):
+    """One vocabulary shard's full-vocabulary backward with the whole heads' log-normalisers: dH [T,d] float32
+    (a partial) and dWs [d,V] float32 (the shard's columns)."""
+    T, d = H.shape
+    dt = Ht.shape[1]
+    V = Ws.shape[1]
+    _check(lib().kd_full_kl_bwd_shard(_ptr(H), _ptr(Ws), _ptr(Ht), _ptr(Wt), _ptr(mask), float(tau),
+                                      _opts_ref(opts), T, d, dt, V, _dtype_code(H.dtype), _ptr(lse_s), _ptr(lse_t),
+                                      _ptr(kl_rev), _ptr(grad_kl), _ptr(dH), _ptr(dWs), int(chunk_rows),
+                                      _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                      _stream(stream)), "kd_full_kl_bwd_shard")
 
 
 def kd_version() -> int:

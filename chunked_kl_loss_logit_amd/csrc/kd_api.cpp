@@ -793,10 +793,16 @@ kd_status kd_full_kl_fwd(const void* H, const void* Ws, const void* Ht, const vo
                            workspace, workspace_bytes, stream);
 }
 
-kd_status kd_full_kl_fwd_ex(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask,
-                            float tau, const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden, int64_t V,
-                            kd_dtype dt, float* kl, float* lse_s, float* lse_t, float* kl_rev, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The full-vocabulary forward; with rec (a vocabulary shard's record [T,8])
+// the merged partials replace kl and the log-normalisers.
+kd_status full_fwd(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask, float tau,
+                   const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                   float* kl, float* lse_s, float* lse_t, float* kl_rev, float* rec, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
   KD_TRY(check_common(T, dt_hidden, V, dt, tau));
@@ -808,16 +814,20 @@ kd_status kd_full_kl_fwd_ex(const void* H, const void* Ws, const void* Ht, const
   KD_TRY(need(Ws, "Ws"));
   KD_TRY(need(Ht, "Ht"));
   KD_TRY(need(Wt, "Wt"));
-  KD_TRY(need(kl, "kl"));
-  KD_TRY(need(lse_s, "lse_s"));
-  KD_TRY(need(lse_t, "lse_t"));
+  if (rec) {
+    KD_TRY(need_align(rec, 16, "rec"));
+  } else {
+    KD_TRY(need(kl, "kl"));
+    KD_TRY(need(lse_s, "lse_s"));
+    KD_TRY(need(lse_t, "lse_t"));
+    KD_TRY(need_align(kl, 4, "kl"));
+    KD_TRY(need_align(lse_s, 4, "lse_s"));
+    KD_TRY(need_align(lse_t, 4, "lse_t"));
+  }
   KD_TRY(need_align(H, 16, "H"));
   KD_TRY(need_align(Ws, 16, "Ws"));
   KD_TRY(need_align(Ht, 16, "Ht"));
   KD_TRY(need_align(Wt, 16, "Wt"));
-  KD_TRY(need_align(kl, 4, "kl"));
-  KD_TRY(need_align(lse_s, 4, "lse_s"));
-  KD_TRY(need_align(lse_t, 4, "lse_t"));
   const int elem = elem_of(dt);
   const FullPlan p = plan_full(T, d, dt_hidden, V, elem, 0);
   KD_TRY(check_workspace(workspace, workspace_bytes, p.fwd_total));
@@ -853,11 +863,28 @@ kd_status kd_full_kl_fwd_ex(const void* H, const void* Ws, const void* Ht, const
     a.nrb = sh.nrb;
     a.S = sh.S;
     KD_LAUNCH("full_fwd_tile", st, kd::launch_full_fwd(elem, a, st));
-    KD_LAUNCH("full_combine", st,
-              kd::launch_full_combine(part, sh.S, p.Cf, c, mask, T, mx.r, kl, lse_s, lse_t, kl_rev, c0, c0 + p.Cf,
-                                      c0 == 0, st));
+    if (rec)
+      KD_LAUNCH("full_shard_record", st,
+                kd::launch_full_shard_record(part, sh.S, p.Cf, c, mask, T, reinterpret_cast<float4*>(rec), c0,
+                                             c0 + p.Cf, c0 == 0, st));
+    else
+      KD_LAUNCH("full_combine", st,
+                kd::launch_full_combine(part, sh.S, p.Cf, c, mask, T, mx.r, kl, lse_s, lse_t, kl_rev, c0, c0 + p.Cf,
+                                        c0 == 0, st));
   }
   return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kd_status kd_full_kl_fwd_ex(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask,
+                            float tau, const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden, int64_t V,
+                            kd_dtype dt, float* kl, float* lse_s, float* lse_t, float* kl_rev, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return full_fwd(H, Ws, Ht, Wt, mask, tau, opts, T, d, dt_hidden, V, dt, kl, lse_s, lse_t, kl_rev, nullptr,
+                  workspace, workspace_bytes, stream);
 }
 
 kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask, float tau,
@@ -868,11 +895,16 @@ kd_status kd_full_kl_bwd(const void* H, const void* Ws, const void* Ht, const vo
                            dH, dWs, chunk_rows, workspace, workspace_bytes, stream);
 }
 
-kd_status kd_full_kl_bwd_ex(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask,
-                            float tau, const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden, int64_t V,
-                            kd_dtype dt, const float* lse_s, const float* lse_t, const float* kl_rev,
-                            const float* grad_kl, void* dH, float* dWs, int64_t chunk_rows, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The full-vocabulary backward; dh_elem 4 gives an fp32 dH (a shard's partial).
+kd_status full_bwd(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask, float tau,
+                   const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                   const float* lse_s, const float* lse_t, const float* kl_rev, const float* grad_kl, void* dH,
+                   float* dWs, int64_t chunk_rows, int dh_elem, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
   KD_TRY(check_common(T, dt_hidden, V, dt, tau));
@@ -911,7 +943,8 @@ kd_status kd_full_kl_bwd_ex(const void* H, const void* Ws, const void* Ht, const
 
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
-  KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * elem, dH, st));
+  if (dh_elem == 0) dh_elem = elem;
+  KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * dh_elem, dH, st));
 
   const ChunkPlan& ch = p.ch;
   char* dz = at<char>(workspace, ch.o_dz);
@@ -950,10 +983,71 @@ kd_status kd_full_kl_bwd_ex(const void* H, const void* Ws, const void* Ht, const
     za.inv_tau = 1.0f / tau;
     za.mix = mx;
     KD_LAUNCH("full_dz_tile", st, kd::launch_full_dz(elem, za, st));
-    KD_TRY(grad_chunk(H, Ws, dH, dWs, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st));
+    KD_TRY(grad_chunk(H, Ws, dH, dWs, elem, d, V, c, ch, dz, hT, dhp, c0, k > 0, st, dh_elem));
   }
   return KD_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+kd_status kd_full_kl_bwd_ex(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask,
+                            float tau, const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden, int64_t V,
+                            kd_dtype dt, const float* lse_s, const float* lse_t, const float* kl_rev,
+                            const float* grad_kl, void* dH, float* dWs, int64_t chunk_rows, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return full_bwd(H, Ws, Ht, Wt, mask, tau, opts, T, d, dt_hidden, V, dt, lse_s, lse_t, kl_rev, grad_kl, dH, dWs,
+                  chunk_rows, 0, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- full vocabulary, one vocabulary shard
+kd_status kd_full_kl_fwd_shard(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask,
+                               float tau, const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden,
+                               int64_t V, kd_dtype dt, float* rec, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (T > 0 && rec == nullptr) {
+    g_err.clear();
+    return fail(KD_ERR_INVALID_ARG, "rec is NULL");
+  }
+  return full_fwd(H, Ws, Ht, Wt, mask, tau, opts, T, d, dt_hidden, V, dt, nullptr, nullptr, nullptr, nullptr, rec,
+                  workspace, workspace_bytes, stream);
+}
+
+kd_status kd_full_kl_shard_combine(const float* rec, int64_t R, const uint8_t* mask, int64_t T, float rev_weight,
+                                   float* kl, float* lse_s, float* lse_t, float* kl_rev, void* stream) {
+  g_err.clear();
+  if (T < 0) return fail(KD_ERR_INVALID_ARG, "T must be >= 0");
+  if (R < 1) return fail(KD_ERR_INVALID_ARG, "R must be >= 1");
+  if (!std::isfinite(rev_weight) || rev_weight < 0.f || rev_weight > 1.f)
+    return fail(KD_ERR_INVALID_ARG, "rev_weight must be finite and in [0, 1]");
+  if (T > INT32_MAX / 2 || R * T > INT32_MAX / 2) return fail(KD_ERR_UNSUPPORTED, "R * T must be below 2^30");
+  if (T == 0) return KD_OK;
+  KD_TRY(need(rec, "rec"));
+  KD_TRY(need(kl, "kl"));
+  KD_TRY(need(lse_s, "lse_s"));
+  KD_TRY(need(lse_t, "lse_t"));
+  KD_TRY(need_align(rec, 16, "rec"));
+  KD_TRY(need_align(kl, 4, "kl"));
+  KD_TRY(need_align(lse_s, 4, "lse_s"));
+  KD_TRY(need_align(lse_t, 4, "lse_t"));
+  KD_TRY(need_align(kl_rev, 4, "kl_rev"));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  KD_LAUNCH("full_shard_combine", st,
+            kd::launch_full_shard_combine(reinterpret_cast<const float4*>(rec), (int)R, T, mask, rev_weight, kl,
+                                          lse_s, lse_t, kl_rev, st));
+  return KD_OK;
+}
+
+kd_status kd_full_kl_bwd_shard(const void* H, const void* Ws, const void* Ht, const void* Wt, const uint8_t* mask,
+                               float tau, const kd_full_opts* opts, int64_t T, int64_t d, int64_t dt_hidden,
+                               int64_t V, kd_dtype dt, const float* lse_s, const float* lse_t, const float* kl_rev,
+                               const float* grad_kl, float* dH, float* dWs, int64_t chunk_rows, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return full_bwd(H, Ws, Ht, Wt, mask, tau, opts, T, d, dt_hidden, V, dt, lse_s, lse_t, kl_rev, grad_kl, dH, dWs,
+                  chunk_rows, 4, workspace, workspace_bytes, stream);
+}
+
 
 // ---------------------------------------------------------------- full vocabulary, forward and backward in one call
 kd_status kd_full_kl_fwd_bwd_workspace_size(int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,

@@ -73,6 +73,15 @@ hipError_t launch_topk_shard_record(const float* part, int S, int64_t part_strid
 // kl and lse of every row from R shards' records rec [R][T] and trow [T].
 hipError_t launch_topk_shard_combine(const float4* rec, int R, int64_t T, const float2* trow, const uint8_t* mask,
                                      float* kl, float* lse, hipStream_t st);
+// A full-vocabulary shard's forward: row t's split partials merged into its
+// record rec[2t], rec[2t + 1] = (ms, ls, mt, lt), (R, R2, 0, 0).
+hipError_t launch_full_shard_record(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
+                                    int64_t T, float4* rec, int64_t jb, int64_t je, bool zero_masked,
+                                    hipStream_t st);
+// kl, both log-normalisers and kl_rev of every row from R shards' records
+// rec [R][T][2] (float4 pairs).
+hipError_t launch_full_shard_combine(const float4* rec, int R, int64_t T, const uint8_t* mask, float r, float* kl,
+                                     float* lse_s, float* lse_t, float* kl_rev, hipStream_t st);
 // kl = (1 - r) KL(p||q) + r KL(q||p); kl_rev (nullable) gets KL(q||p).
 hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
                                int64_t T, float r, float* kl, float* lse_s, float* lse_t, float* kl_rev, int64_t jb,

@@ -324,20 +324,13 @@ hipError_t launch_topk_shard_combine(const float4* rec, int R, int64_t T, const 
 // Partials per (split, row): (ms, ls, mt, lt), (R, R2, -, -) in base 2, with
 // R = sum 2^(yt - mt) (yt - ys) and R2 = sum 2^(ys - ms) (ys - yt); the
 // partial row p holds compacted row jb + p.
-__global__ void full_combine_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask, long T,
-                                    float r, float* kl, float* lse_s, float* lse_t, float* kl_rev, long jb, long je,
-                                    int zero_masked) {
-  const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= T) return;
-  if (zero_masked && mask != nullptr && mask[j] == 0) {
-    kl[j] = 0.f;
-    lse_s[j] = 0.f;
-    lse_t[j] = 0.f;
-    if (kl_rev) kl_rev[j] = 0.f;
-  }
-  if (j < jb || j >= je || j >= *c.count) return;
-  const float4* pp = reinterpret_cast<const float4*>(part);
-  const long p = j - jb;  // partial row
+// The pair of float4 (ms, ls, mt, lt), (R, R2, -, -) of row p merged over S
+// partials at stride `stride` rows, in order.
+struct FullMerged {
+  float4 q, x;
+};
+
+__device__ inline FullMerged merge_full(const float4* pp, int S, long stride, long p) {
   float Ms = -INFINITY, Mt = -INFINITY;
   for (int s = 0; s < S; ++s) {
     const float4 q = pp[2 * ((long)s * stride + p)];
@@ -355,14 +348,83 @@ __global__ void full_combine_kernel(const float* part, int S, long stride, Compa
     lt += q.w * f;
     R += x.x * f;
   }
-  const long t = c.rows[j];
-  const float Ls2 = Ms + log2f(ls), Lt2 = Mt + log2f(lt);
+  return FullMerged{make_float4(Ms, ls, Mt, lt), make_float4(R, R2, 0.f, 0.f)};
+}
+
+// Row t's outputs from its merged partials.
+__device__ inline void full_finish(const FullMerged& m, long t, float r, float* kl, float* lse_s, float* lse_t,
+                                   float* kl_rev) {
+  const float Ls2 = m.q.x + log2f(m.q.y), Lt2 = m.q.z + log2f(m.q.w);
   lse_s[t] = Ls2 * kLn2;
   lse_t[t] = Lt2 * kLn2;
-  const float fwd = (R / lt - Lt2 + Ls2) * kLn2;
-  const float rev = (R2 / ls - Ls2 + Lt2) * kLn2;
+  const float fwd = (m.x.x / m.q.w - Lt2 + Ls2) * kLn2;
+  const float rev = (m.x.y / m.q.y - Ls2 + Lt2) * kLn2;
   kl[t] = r == 0.f ? fwd : (1.f - r) * fwd + r * rev;
   if (kl_rev) kl_rev[t] = rev;
+}
+
+__device__ inline void full_zero(long t, float* kl, float* lse_s, float* lse_t, float* kl_rev) {
+  kl[t] = 0.f;
+  lse_s[t] = 0.f;
+  lse_t[t] = 0.f;
+  if (kl_rev) kl_rev[t] = 0.f;
+}
+
+__global__ void full_combine_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask, long T,
+                                    float r, float* kl, float* lse_s, float* lse_t, float* kl_rev, long jb, long je,
+                                    int zero_masked) {
+  const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= T) return;
+  if (zero_masked && mask != nullptr && mask[j] == 0) full_zero(j, kl, lse_s, lse_t, kl_rev);
+  if (j < jb || j >= je || j >= *c.count) return;
+  const FullMerged m = merge_full(reinterpret_cast<const float4*>(part), S, stride, j - jb);
+  full_finish(m, c.rows[j], r, kl, lse_s, lse_t, kl_rev);
+}
+
+// A vocabulary shard's forward: row t's merged partials are its record,
+// rec[t] = the pair above (zero on masked rows with zero_masked).
+__global__ void full_shard_record_kernel(const float* part, int S, long stride, Compact c, const uint8_t* mask,
+                                         long T, float4* rec, long jb, long je, int zero_masked) {
+  const long j = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= T) return;
+  if (zero_masked && mask != nullptr && mask[j] == 0) {
+    rec[2 * j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    rec[2 * j + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (j < jb || j >= je || j >= *c.count) return;
+  const FullMerged m = merge_full(reinterpret_cast<const float4*>(part), S, stride, j - jb);
+  const long t = c.rows[j];
+  rec[2 * t] = m.q;
+  rec[2 * t + 1] = m.x;
+}
+
+hipError_t launch_full_shard_record(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,
+                                    int64_t T, float4* rec, int64_t jb, int64_t je, bool zero_masked,
+                                    hipStream_t st) {
+  const dim3 grid((unsigned)((T + 255) / 256));
+  hipLaunchKernelGGL(full_shard_record_kernel, grid, dim3(256), 0, st, part, S, (long)part_stride, c, mask, (long)T,
+                     rec, (long)jb, (long)je, zero_masked ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Row t from the R shards' records rec [R][T] (pairs of float4).
+__global__ void full_shard_combine_kernel(const float4* rec, int R, long T, const uint8_t* mask, float r, float* kl,
+                                          float* lse_s, float* lse_t, float* kl_rev) {
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  if (mask != nullptr && mask[t] == 0) {
+    full_zero(t, kl, lse_s, lse_t, kl_rev);
+    return;
+  }
+  full_finish(merge_full(rec, R, T, t), t, r, kl, lse_s, lse_t, kl_rev);
+}
+
+hipError_t launch_full_shard_combine(const float4* rec, int R, int64_t T, const uint8_t* mask, float r, float* kl,
+                                     float* lse_s, float* lse_t, float* kl_rev, hipStream_t st) {
+  const dim3 grid((unsigned)((T + 255) / 256));
+  hipLaunchKernelGGL(full_shard_combine_kernel, grid, dim3(256), 0, st, rec, R, (long)T, mask, r, kl, lse_s, lse_t,
+                     kl_rev);
+  return hipGetLastError();
 }
 
 hipError_t launch_full_combine(const float* part, int S, int64_t part_stride, Compact c, const uint8_t* mask,

@@ -366,6 +366,45 @@ kd_status kd_full_kl_fwd_bwd_ex(const void* H, const void* Ws, const void* Ht, c
                                 float* kl_rev, void* dH, float* dWs, int64_t chunk_rows,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- full vocabulary, one vocabulary shard
+ * The full-vocabulary loss with both heads split by the same vocabulary
+ * columns over R ranks (the tensor-parallel layout of the top-K shard
+ * section above).  Rank r holds Ws_r and Wt_r, columns [v0, v0 + V) of the
+ * student's and the teacher's heads ([d,V] and [dt,V] row-major, V the
+ * shard's width), and all of H, Ht, mask and the options.  One step:
+ *   1. each rank: kd_full_kl_fwd_shard -> rec_r [T,8]
+ *   2. all-gather rec over the ranks into rec [R,T,8] (rank order)
+ *   3. each rank: kd_full_kl_shard_combine -> kl, lse_s, lse_t (and kl_rev),
+ *      those of the whole heads
+ *   4. each rank: kd_full_kl_bwd_shard with them -> dH_r [T,d] float32, a
+ *      partial of dH, and dWs_r [d,V] float32, the shard's columns of dWs
+ *   5. sum dH_r over the ranks; dWs stays sharded.
+ * Record, per valid row t, over the shard's columns (y = x log2(e) / tau_t
+ * for the student's logits ys and the teacher's yt):
+ *   rec[t] = (ms, ls, mt, lt, R, R2, 0, 0) with ms + log2(ls) and
+ *   mt + log2(lt) the base-2 log-normalisers of ys and yt over the shard,
+ *   R = sum 2^(yt - mt) (yt - ys), R2 = sum 2^(ys - ms) (ys - yt);
+ *   masked rows: all zero.  Records merge like the forward's own split
+ *   partials.  The workspace is kd_full_kl_workspace_size at the shard's
+ *   width; rec must be 16-byte aligned.  The combine takes the rev_weight
+ *   of the options (the record does not depend on it); the backward needs
+ *   the same options as the forward and, when rev_weight > 0, kl_rev. */
+kd_status kd_full_kl_fwd_shard(const void* H, const void* Ws, const void* Ht, const void* Wt,
+                               const uint8_t* mask, float tau, const kd_full_opts* opts,
+                               int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                               float* rec, void* workspace, size_t workspace_bytes, void* stream);
+/* rec [R,T,8] -> kl, lse_s, lse_t [T] and kl_rev [T] (nullable); masked rows
+ * get 0.  R >= 1, R * T < 2^30, rev_weight in [0, 1].  No workspace. */
+kd_status kd_full_kl_shard_combine(const float* rec, int64_t R, const uint8_t* mask, int64_t T,
+                                   float rev_weight, float* kl, float* lse_s, float* lse_t,
+                                   float* kl_rev, void* stream);
+kd_status kd_full_kl_bwd_shard(const void* H, const void* Ws, const void* Ht, const void* Wt,
+                               const uint8_t* mask, float tau, const kd_full_opts* opts,
+                               int64_t T, int64_t d, int64_t dt_hidden, int64_t V, kd_dtype dt,
+                               const float* lse_s, const float* lse_t, const float* kl_rev,
+                               const float* grad_kl, float* dH, float* dWs, int64_t chunk_rows,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- errors, version */
 
 const char* kd_status_string(kd_status s);

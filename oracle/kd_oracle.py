@@ -60,7 +60,7 @@ __all__ = [
     "as_f64", "logsumexp_rows", "teacher_log_probs",
     "topk_kl_forward", "topk_kl_backward", "topk_kl_rows",
     "topk_loss_forward", "topk_loss_backward", "topk_loss_rows",
-    "topk_shard_terms", "topk_shard_backward",
+    "topk_shard_terms", "topk_shard_backward", "full_shard_terms", "full_shard_backward",
     "full_kl_forward", "full_kl_backward", "full_kl_rows",
     "full_loss_forward", "full_loss_backward", "full_loss_rows",
 ]
@@ -535,6 +535,54 @@ def full_loss_backward(H, Ws, Ht, Wt, mask, tau, g, tau_rows=None, rev_weight=0.
         if want_dw:
             for v0 in range(0, V, v_panel):
                 dW[:, v0:v0 + v_panel] += H[rb].T @ D[:, v0:v0 + v_panel]
+    return dH, dW
+
+
+def full_shard_terms(H, Ws_shard, Ht, Wt_shard, mask, tau, tau_rows=None):
+    """What one vocabulary shard of both heads holds of full_loss_forward
+    (columns c of both heads; [EKD] App. B: tensor-parallel ranks).  Per
+    valid row t, with s and u the student's and teacher's scaled logits over
+    c and P, Q their softmaxes restricted to c:
+        lse_s_t, lse_t_t = logsumexp over c of s, of u
+        e_fwd_t = sum over c of P (u - s),  e_rev_t = sum over c of Q (s - u)
+    so that over a partition of the vocabulary, with L = logsumexp of the
+    shards' lse and w_r = exp(lse_r - L) the shards' shares of the mass,
+        KL(p||q) = sum_r w_t,r e_fwd_r - Lt + Ls,
+        KL(q||p) = sum_r w_s,r e_rev_r - Ls + Lt.
+    Masked rows give zeros.  Returns (lse_s, lse_t, e_fwd, e_rev), each [T]."""
+    H, Ws_shard, Ht, Wt_shard = as_f64(H), as_f64(Ws_shard), as_f64(Ht), as_f64(Wt_shard)
+    T = H.shape[0]
+    taus = _row_values(tau_rows, T, tau)
+    valid = _valid_rows(mask, T)
+    out = [np.zeros(T) for _ in range(4)]
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, 64):
+        rb = rows[r0:r0 + 64]
+        s, u, Ls, Lt, Q, P = _full_block(H, Ws_shard, Ht, Wt_shard, rb, taus)
+        out[0][rb], out[1][rb] = Ls, Lt
+        out[2][rb] = (P * (u - s)).sum(axis=1)
+        out[3][rb] = (Q * (s - u)).sum(axis=1)
+    return tuple(out)
+
+
+def full_shard_backward(H, Ws, Ht, Wt, v0, Vs, mask, tau, g, tau_rows=None, rev_weight=0.0, row_block=64):
+    """One vocabulary shard's part of full_loss_backward: with dZ the whole
+    heads' gradient (_full_loss_dz, whose softmaxes need every column) and
+    columns c = [v0, v0 + Vs), the dH partial dZ[:, c] Ws[:, c]^T and the
+    columns c of dWs, H^T dZ[:, c].  Returns (dH_partial [T, d], dWs [d, Vs])."""
+    H, Ws, Ht, Wt, g = as_f64(H), as_f64(Ws), as_f64(Ht), as_f64(Wt), as_f64(g)
+    T, d = H.shape
+    taus = _row_values(tau_rows, T, tau)
+    valid = _valid_rows(mask, T)
+    dH, dW = np.zeros((T, d)), np.zeros((d, Vs))
+    Wc = Ws[:, v0:v0 + Vs]
+    rows = np.nonzero(valid)[0]
+    for r0 in range(0, rows.size, row_block):
+        rb = rows[r0:r0 + row_block]
+        s, u, Ls, Lt, q, p = _full_block(H, Ws, Ht, Wt, rb, taus)
+        D = _full_loss_dz(s, u, Ls, Lt, q, p, g[rb], taus[rb], float(rev_weight))[:, v0:v0 + Vs]
+        dH[rb] = D @ Wc.T
+        dW += H[rb].T @ D
     return dH, dW
 
 

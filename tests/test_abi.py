@@ -29,7 +29,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 27
+    assert len(names) == 30
     for n in names:
         assert hasattr(L, n), f"{n} declared in kdloss.h but not exported"
     assert sorted(kdl.EXPORTS) == names
@@ -392,3 +392,23 @@ def test_shard_workspace_is_the_plain_size_at_the_shard_width(L):
                 == kdl.kd_topk_kl_workspace_size(T, d, V, K, kdl.torch.bfloat16, chunk))
     # more cached entries than the shard has columns
     assert kdl.kd_topk_kl_shard_workspace_size(64, 64, 8, 0, 16, kdl.torch.bfloat16) > 0
+
+
+def test_full_shard_checks(L):
+    vp = ctypes.c_void_p
+    f = kdl.lib()
+    fwd = lambda rec=FAKE, T=8: f.kd_full_kl_fwd_shard(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None,
+                                                        ctypes.c_float(1.0), None, T, 64, 64, 256, kdl.KD_BF16,
+                                                        vp(rec) if rec else None, vp(FAKE), 16, None)
+    assert fwd(rec=0) == 1 and fwd(rec=FAKE + 8) == 3 and fwd() == 4  # reaches the workspace check
+    assert fwd(rec=0, T=0) == 0
+    comb = lambda R=8, T=16, r=0.0, rec=FAKE, kr=None: f.kd_full_kl_shard_combine(
+        vp(rec) if rec else None, R, None, T, ctypes.c_float(r), vp(FAKE), vp(FAKE), vp(FAKE), kr, None)
+    assert comb(R=0) == 1 and comb(T=-1) == 1 and comb(r=1.5) == 1 and comb(r=math.nan) == 1
+    assert comb(rec=0) == 1 and comb(rec=FAKE + 8) == 3 and comb(kr=vp(FAKE + 2)) == 3
+    assert comb(R=1 << 20, T=1 << 12) == 2
+    assert comb(T=0) == 0
+    bwd = lambda dH=FAKE: f.kd_full_kl_bwd_shard(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0),
+                                                 None, 8, 64, 64, 256, kdl.KD_BF16, vp(FAKE), vp(FAKE), None,
+                                                 vp(FAKE), vp(dH) if dH else None, vp(FAKE), 0, vp(FAKE), 16, None)
+    assert bwd(dH=0) == 1 and bwd(dH=FAKE + 8) == 3 and bwd() == 4

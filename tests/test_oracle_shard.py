@@ -1,5 +1,5 @@
-"""Pins of the oracle's vocabulary-shard terms (``topk_shard_terms``,
-``topk_shard_backward``): the output head split by vocabulary columns across
+"""Pins of the oracle's vocabulary-shard terms (``topk_shard_*``,
+``full_shard_*``): the output head split by vocabulary columns across
 tensor-parallel ranks ("Efficient Knowledge Distillation for LLMs: Offline
 Top-K Logits and a Fused Chunked KL Loss", App. B: the loss benchmark reports
 the largest tensor-parallel rank).  CPU only.
@@ -8,8 +8,9 @@ Each pin ties the shard terms to something other than their own formula: the
 already pinned unsharded oracle through the partition identities (the shards'
 log-normalisers log-sum-exp to L, the cross terms add, the loss comes back
 from the teacher terms; the dH partials add to dH and the dW slices make up
-dW), scipy's logsumexp over the shard's columns, and the dense
-reconstruction of the support weights (§3 "Offline implementations").
+dW), scipy's logsumexp over the shard's columns, the dense reconstruction of
+the support weights (§3 "Offline implementations"), and scipy's relative
+entropy of the two heads' softmaxes restricted to the shard.
 """
 import numpy as np
 import pytest
@@ -101,3 +102,61 @@ def test_backward_partials_make_up_the_gradient(opt):
     np.testing.assert_allclose(sum(p[0] for p in parts), dH, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(np.concatenate([p[1] for p in parts], axis=1), dW, rtol=1e-12, atol=1e-14)
     assert np.all(parts[1][0][1] == 0)
+
+
+# ---------------------------------------------------------------- full vocabulary
+def full_case(T=7, d=8, dt=6, V=40, seed=21):
+    rng = np.random.default_rng(seed)
+    H = rng.standard_normal((T, d))
+    Ws = rng.standard_normal((d, V)) / np.sqrt(d)
+    Ht = rng.standard_normal((T, dt))
+    Wt = rng.standard_normal((dt, V)) * 1.5 / np.sqrt(dt)
+    return H, Ws, Ht, Wt, rng.standard_normal(T), rng.uniform(0.6, 2.5, T)
+
+
+@pytest.mark.parametrize("per_row_tau", [False, True])
+def test_full_partition_gives_the_unsharded_loss(per_row_tau):
+    H, Ws, Ht, Wt, g, taus = full_case()
+    mask = np.array([1, 1, 0, 1, 1, 1, 1], dtype=np.uint8)
+    tr = taus if per_row_tau else None
+    v = mask != 0
+    for r in (0.0, 0.35):
+        loss, Ls, Lt, krev = O.full_loss_forward(H, Ws, Ht, Wt, mask, 1.1, tau_rows=tr, rev_weight=r)
+        parts = [O.full_shard_terms(H, Ws[:, a:a + n], Ht, Wt[:, a:a + n], mask, 1.1, tau_rows=tr)
+                 for a, n in shards()]
+        ls, lt, ef, er = (np.stack([p[i] for p in parts]) for i in range(4))
+        np.testing.assert_allclose(sps.logsumexp(ls[:, v], axis=0), Ls[v], rtol=1e-13)
+        np.testing.assert_allclose(sps.logsumexp(lt[:, v], axis=0), Lt[v], rtol=1e-13)
+        fwd = (np.exp(lt - Lt) * ef).sum(0) - Lt + Ls
+        rev = (np.exp(ls - Ls) * er).sum(0) - Ls + Lt
+        np.testing.assert_allclose(((1 - r) * fwd + r * rev)[v], loss[v], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(rev[v], krev[v], rtol=1e-11, atol=1e-13)
+        for p in parts:
+            for x in p:
+                assert np.all(x[~v] == 0)
+
+
+def test_full_shard_terms_against_scipy():
+    # each shard's terms are the KL pieces of the two softmaxes restricted to its columns
+    H, Ws, Ht, Wt, g, taus = full_case(seed=22)
+    for a, n in shards():
+        ls, lt, ef, er = O.full_shard_terms(H, Ws[:, a:a + n], Ht, Wt[:, a:a + n], None, 0.8)
+        s, u = (H @ Ws[:, a:a + n]) / 0.8, (Ht @ Wt[:, a:a + n]) / 0.8
+        np.testing.assert_allclose(ls, sps.logsumexp(s, axis=1), rtol=1e-14)
+        np.testing.assert_allclose(lt, sps.logsumexp(u, axis=1), rtol=1e-14)
+        P, Q = sps.softmax(u, axis=1), sps.softmax(s, axis=1)
+        # sum P (u - s) = KL(P || Q) + lse_t - lse_s over the shard's columns, likewise e_rev
+        np.testing.assert_allclose(ef, sps.rel_entr(P, Q).sum(1) + lt - ls, rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(er, sps.rel_entr(Q, P).sum(1) + ls - lt, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("r", [0.0, 0.4])
+def test_full_backward_partials_make_up_the_gradient(r):
+    H, Ws, Ht, Wt, g, taus = full_case(seed=23)
+    mask = np.array([1, 1, 1, 0, 1, 1, 1], dtype=np.uint8)
+    dH, dW = O.full_loss_backward(H, Ws, Ht, Wt, mask, 1.2, g, tau_rows=taus, rev_weight=r)
+    parts = [O.full_shard_backward(H, Ws, Ht, Wt, a, n, mask, 1.2, g, tau_rows=taus, rev_weight=r)
+             for a, n in shards()]
+    np.testing.assert_allclose(sum(p[0] for p in parts), dH, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(np.concatenate([p[1] for p in parts], axis=1), dW, rtol=1e-12, atol=1e-14)
+    assert np.all(parts[0][0][3] == 0)

@@ -172,3 +172,134 @@ def test_headline_shape_eight_shards_sampled_rows():
     # every row of dZ sums to zero over the whole head (mass 1), so each row of
     # dW, made of the 8 slices, sums to zero up to dZ's bf16 rounding
     assert np.all(np.abs(dW_rowsum.cpu().numpy()) <= 2e-2 * np.sqrt(dW_rowsq.cpu().numpy()))
+
+
+# ---------------------------------------------------------------- full vocabulary
+def run_full_shards(inp, cuts, chunk_rows=0, backward=True):
+    H, Ws, Ht, Wt, M, g = (dev(inp[k]) for k in ("H", "Ws", "Ht", "Wt", "mask", "g"))
+    tau, r = inp["tau"], inp.get("rev_weight", 0.0)
+    tr = dev(inp.get("tau_rows"))
+    parts = []
+    for v0, v1 in zip(cuts[:-1], cuts[1:]):
+        Wsc, Wtc = Ws[:, v0:v1].contiguous(), Wt[:, v0:v1].contiguous()
+        rec = kd.full_kl_shard_forward(H, Wsc, Ht, Wtc, M, tau, tau_rows=tr)
+        parts.append(dict(v0=v0, vs=v1 - v0, Wsc=Wsc, Wtc=Wtc, rec=rec))
+    kl, ls, lt, krev = kd.full_kl_shard_combine([p["rec"] for p in parts], M, r, want_kl_rev=True)
+    if backward:
+        for p in parts:
+            p["dH"], p["dW"] = kd.full_kl_shard_backward(H, p["Wsc"], Ht, p["Wtc"], M, tau, ls, lt, g, chunk_rows,
+                                                         tau_rows=tr, rev_weight=r, kl_rev=krev)
+    torch.cuda.synchronize()
+    return parts, dict(kl=kl, lse_s=ls, lse_t=lt, kl_rev=krev)
+
+
+def full_kw(inp):
+    return dict(tau_rows=inp.get("tau_rows"), rev_weight=inp.get("rev_weight", 0.0))
+
+
+def check_full_records(parts, inp, dtype, rows=None):
+    sel = (lambda x: x) if rows is None else (lambda x: None if x is None else x[rows])
+    H, Ht, mask, tr = sel(inp["H"]), sel(inp["Ht"]), sel(inp["mask"]), sel(inp.get("tau_rows"))
+    v = np.ones(H.shape[0], bool) if mask is None else mask.numpy() != 0
+    for p in parts:
+        c = slice(p["v0"], p["v0"] + p["vs"])
+        ls, lt, ef, er = O.full_shard_terms(H, inp["Ws"][:, c], Ht, inp["Wt"][:, c], mask, inp["tau"], tau_rows=tr)
+        rec = sel(np64(p["rec"]))
+        one = lambda x: np.where(v, x, 1.0)
+        assert_lse(LN2 * (rec[:, 0] + np.log2(one(rec[:, 1]))), ls, dtype, v)
+        assert_lse(LN2 * (rec[:, 2] + np.log2(one(rec[:, 3]))), lt, dtype, v)
+        # expectations of logit differences under the shard's softmaxes: on the
+        # scale of the logits
+        scale = np.abs(np.concatenate([ls[v], lt[v]])).max()
+        np.testing.assert_allclose(LN2 * rec[v, 4] / rec[v, 3], ef[v], rtol=1e-3, atol=2e-3 * scale)
+        np.testing.assert_allclose(LN2 * rec[v, 5] / rec[v, 1], er[v], rtol=1e-3, atol=2e-3 * scale)
+        assert np.all(rec[~v] == 0)
+
+
+def check_full_combined(parts, got, inp, dtype):
+    kw = full_kw(inp)
+    kl, ls, lt, krev = O.full_loss_forward(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], inp["mask"], inp["tau"], **kw)
+    dH, dW = O.full_loss_backward(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], inp["mask"], inp["tau"], inp["g"], **kw)
+    T = kl.shape[0]
+    v = np.ones(T, bool) if inp["mask"] is None else inp["mask"].numpy() != 0
+    assert_kl(np64(got["kl"]), kl, dtype, v)
+    assert_lse(np64(got["lse_s"]), ls, dtype, v)
+    assert_lse(np64(got["lse_t"]), lt, dtype, v)
+    assert_kl(np64(got["kl_rev"]), krev, dtype, v)
+    assert_grad(sum(np64(p["dH"]) for p in parts), dH, dtype, "sum of dH partials")
+    assert_grad(np.concatenate([np64(p["dW"]) for p in parts], axis=1), dW, dtype, "dWs slices")
+    for p in parts:
+        assert p["dH"].dtype == torch.float32
+        assert np.all(np64(p["dH"])[~v] == 0)
+    for x in got.values():
+        assert np.all(np64(x)[~v] == 0)
+
+
+FULL_CASES = [
+    # dtype, T, d, dt, V, cuts, chunk_rows, options
+    (torch.bfloat16, 700, 384, 256, 2568, (0, 640, 1288, 1800, 2568), 256, {}),
+    (torch.bfloat16, 700, 384, 256, 2568, (0, 1288, 2568), 256, dict(tau_rows=True, rev_weight=0.3)),
+    (torch.bfloat16, 300, 136, 72, 1032, (0, 8, 520, 1032), 0, dict(rev_weight=1.0)),
+    (torch.float32, 260, 64, 128, 520, (0, 260, 520), 256, dict(tau_rows=True)),
+]
+
+
+@pytest.mark.parametrize("dtype,T,d,dt,V,cuts,chunk,opts", FULL_CASES)
+def test_full_shards_match_the_oracle(dtype, T, d, dt, V, cuts, chunk, opts):
+    inp = G.make_full(T, d, dt, V, dtype, tau=1.1, mask="random10", number=84, g="normal")
+    if opts:
+        inp = G.add_full_options(inp, number=84, **opts)
+    say(f"full vocab shards {cuts} T={T} d={d} dt={dt} V={V} {dtype} {opts}")
+    parts, got = run_full_shards(inp, cuts, chunk)
+    check_full_records(parts, inp, dtype)
+    check_full_combined(parts, got, inp, dtype)
+
+
+def test_full_one_shard_is_the_unsharded_call():
+    inp = G.make_full(700, 384, 256, 2568, torch.bfloat16, tau=0.9, mask="random10", number=85, g="normal")
+    say("full vocab: one shard = the plain calls")
+    parts, got = run_full_shards(inp, (0, 2568), 256)
+    H, Ws, Ht, Wt, M, g = (dev(inp[k]) for k in ("H", "Ws", "Ht", "Wt", "mask", "g"))
+    kl0, ls0, lt0 = kd.full_kl_forward(H, Ws, Ht, Wt, M, 0.9)
+    dH0, dW0 = kd.full_kl_backward(H, Ws, Ht, Wt, M, 0.9, ls0, lt0, g, 256)
+    torch.cuda.synchronize()
+    for a, b in ((got["kl"], kl0), (got["lse_s"], ls0), (got["lse_t"], lt0), (parts[0]["dW"], dW0)):
+        np.testing.assert_array_equal(np64(a), np64(b))
+    np.testing.assert_array_equal(np64(parts[0]["dH"].to(torch.bfloat16)), np64(dH0))
+
+
+def test_full_t16384_eight_shards_sampled_rows():
+    p = G.PRESETS["full_vocab_t16384"]
+    inp = G.make_preset(p, g="normal")
+    V = p.V
+    cuts = tuple(range(0, V + 1, V // 8))
+    say(f"full vocab T=16384 in 8 shards of {V // 8} columns")
+    H, Ws, Ht, Wt, g = (dev(inp[k]) for k in ("H", "Ws", "Ht", "Wt", "g"))
+    parts = []
+    for v0, v1 in zip(cuts[:-1], cuts[1:]):
+        Wsc, Wtc = Ws[:, v0:v1].contiguous(), Wt[:, v0:v1].contiguous()
+        parts.append(dict(v0=v0, vs=v1 - v0, Wsc=Wsc, Wtc=Wtc, rec=kd.full_kl_shard_forward(H, Wsc, Ht, Wtc, None,
+                                                                                             p.tau)))
+    kl, ls, lt, _ = kd.full_kl_shard_combine([q["rec"] for q in parts], None)
+    rng = np.random.default_rng(10)
+    rows = np.array(sorted(set(rng.choice(p.T, 48, replace=False).tolist()) | {0, 4095, 4096, p.T - 1}))
+    rows_d = torch.as_tensor(rows, device="cuda")
+    dH_rows = torch.zeros(rows.size, p.d, dtype=torch.float64, device="cuda")
+    dW_rowsum = torch.zeros(p.d, dtype=torch.float64, device="cuda")
+    dW_rowsq = torch.zeros(p.d, dtype=torch.float64, device="cuda")
+    for q in parts:
+        dH, dW = kd.full_kl_shard_backward(H, q["Wsc"], Ht, q["Wtc"], None, p.tau, ls, lt, g, 0)
+        dH_rows += dH.index_select(0, rows_d).double()
+        dW_rowsum += dW.double().sum(dim=1)
+        dW_rowsq += dW.double().square().sum(dim=1)
+        assert bool(torch.isfinite(dW).all())
+        del dH, dW
+    torch.cuda.synchronize()
+    want = O.full_loss_rows(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], None, p.tau, inp["g"], rows)
+    assert_kl(np64(kl)[rows], want[0], torch.bfloat16)
+    assert_lse(np64(ls)[rows], want[1], torch.bfloat16)
+    assert_lse(np64(lt)[rows], want[2], torch.bfloat16)
+    assert_grad(dH_rows.cpu().numpy(), want[4], torch.bfloat16, "sum of dH partials, sampled rows")
+    check_full_records([parts[0], parts[7]], inp, torch.bfloat16, rows=rows)
+    # rows of dZ sum to zero over the whole vocabulary, so do the rows of dWs
+    assert np.all(np.abs(dW_rowsum.cpu().numpy()) <= 2e-2 * np.sqrt(dW_rowsq.cpu().numpy()))
