@@ -35,6 +35,8 @@ PINS = [
     lambda: S.test_partition_gives_the_unsharded_loss("every", True),
     S.test_whole_head_as_one_shard, S.test_terms_against_scipy_and_the_dense_teacher,
     lambda: S.test_backward_partials_make_up_the_gradient("every"),
+    lambda: S.test_full_partition_gives_the_unsharded_loss(True), S.test_full_shard_terms_against_scipy,
+    lambda: S.test_full_backward_partials_make_up_the_gradient(0.4),
 ]
 
 
@@ -232,11 +234,31 @@ def _shard_terms_entropy_unweighted(*args, labels=None, ce_weight=0.0, **kw):
 def _shard_bwd_first_columns(H, W, v0, Vs, *args, **kw):
     return _ORIG_SHARD_BWD(H, W, 0, Vs, *args, **kw)
 
+
+_ORIG_FULL_SHARD_TERMS = O.full_shard_terms
+_ORIG_FULL_SHARD_BWD = O.full_shard_backward
+
+
+def _full_shard_heads_swapped(H, Ws_shard, Ht, Wt_shard, *args, **kw):
+    ls, lt, ef, er = _ORIG_FULL_SHARD_TERMS(H, Ws_shard, Ht, Wt_shard, *args, **kw)
+    return ls, lt, er, ef  # forward and reverse expectations exchanged
+
+
+def _full_shard_tau_rows_ignored(*args, tau_rows=None, **kw):
+    return _ORIG_FULL_SHARD_TERMS(*args, **kw)
+
+
+def _full_shard_bwd_no_mixing(*args, rev_weight=0.0, **kw):
+    return _ORIG_FULL_SHARD_BWD(*args, **kw)
+
 MUTATIONS = {
     "shard_indices_not_shifted": ("topk_shard_terms", _shard_terms_unshifted),
     "shard_ce_term_ignored": ("topk_shard_terms", _shard_terms_ce_ignored),
     "shard_entropy_unweighted": ("topk_shard_terms", _shard_terms_entropy_unweighted),
     "shard_backward_wrong_columns": ("topk_shard_backward", _shard_bwd_first_columns),
+    "full_shard_expectations_swapped": ("full_shard_terms", _full_shard_heads_swapped),
+    "full_shard_tau_rows_ignored": ("full_shard_terms", _full_shard_tau_rows_ignored),
+    "full_shard_backward_mixing_ignored": ("full_shard_backward", _full_shard_bwd_no_mixing),
     "full_dz_reverse_baseline_dropped": ("_full_loss_dz", _full_dz_no_klr),
     "full_dz_reverse_sign": ("_full_loss_dz", _full_dz_reverse_sign),
     "full_mix_weights_swapped": ("full_loss_forward", _full_loss_mix_swapped),
