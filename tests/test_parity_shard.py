@@ -303,3 +303,30 @@ def test_full_t16384_eight_shards_sampled_rows():
     check_full_records([parts[0], parts[7]], inp, torch.bfloat16, rows=rows)
     # rows of dZ sum to zero over the whole vocabulary, so do the rows of dWs
     assert np.all(np.abs(dW_rowsum.cpu().numpy()) <= 2e-2 * np.sqrt(dW_rowsq.cpu().numpy()))
+
+
+@pytest.mark.parametrize("head", ["topk", "full"])
+def test_shards_are_deterministic_and_follow_the_callers_stream(head):
+    if head == "topk":
+        inp = G.make_topk(700, 384, 2568, 16, torch.bfloat16, tau=1.1, mask="random10", number=86, g="normal")
+    else:
+        inp = G.make_full(700, 384, 256, 2568, torch.bfloat16, tau=1.1, mask="random10", number=87, g="normal")
+
+    def run():
+        if head == "topk":
+            parts, kl, lse = run_shards(inp, (0, 1288, 2568), 256)
+            outs = [kl, lse]
+        else:
+            parts, got = run_full_shards(inp, (0, 1288, 2568), 256)
+            outs = list(got.values())
+        return [np64(x) for x in outs] + [np64(p[k]) for p in parts for k in ("rec", "dH", "dW")]
+
+    say(f"{head} shards: two runs, then on a second stream")
+    a, b = run(), run()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        c = run()
+    for i, (x, y, z) in enumerate(zip(a, b, c)):
+        np.testing.assert_array_equal(x, y, err_msg=f"output {i}, second run")
+        np.testing.assert_array_equal(x, z, err_msg=f"output {i}, second stream")
