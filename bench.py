@@ -356,6 +356,57 @@ def run_topk_shard(p, T: int, R: int, steps: int, warmup: int, chunk_rows: int):
     return out
 
 
+def run_full_shard(p, R: int, steps: int, warmup: int, chunk_rows: int):
+    """Time one rank's step of the full-vocabulary loss with both heads split
+    by vocabulary over R ranks (rank 0: columns [0, V/R) of each head): its
+    forward, the combine of R records and its backward.  As in
+    run_topk_shard, the other ranks' records are copies of its own, made once
+    before timing."""
+    import torch
+    import chunked_kl_loss_logit_amd as kd
+    import kdinputs as G
+
+    T, d, dt, tau = p.T, p.d, p.dt_hidden, p.tau
+    Vs = p.V // R
+    inp = G.make_full(T, d, dt, p.V, p.dtype, tau=tau, number=p.number, g="mean")
+    dev = torch.device("cuda:0")
+    H, Ht, g = (inp[k].to(dev) for k in ("H", "Ht", "g"))
+    Ws = inp["Ws"][:, :Vs].contiguous().to(dev)
+    Wt = inp["Wt"][:, :Vs].contiguous().to(dev)
+    del inp
+    rec = torch.empty(R, T, 8, device=dev)
+    kl, ls, lt = (torch.empty(T, device=dev) for _ in range(3))
+    dH = torch.empty(T, d, device=dev)
+    dW = torch.empty(d, Vs, device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    ws = torch.empty(kd.kd_full_kl_workspace_size(T, d, dt, Vs, p.dtype, chunk_rows), dtype=torch.uint8, device=dev)
+
+    def step():
+        kd.kd_full_kl_fwd_shard(H, Ws, Ht, Wt, None, tau, None, rec[0], ws)
+        kd.kd_full_kl_shard_combine(rec, None, 0.0, kl, ls, lt, None)
+        kd.kd_full_kl_bwd_shard(H, Ws, Ht, Wt, None, tau, None, ls, lt, None, g, dH, dW, chunk_rows, ws)
+
+    kd.kd_full_kl_fwd_shard(H, Ws, Ht, Wt, None, tau, None, rec[0], ws)
+    rec[1:].copy_(rec[0].expand(R - 1, T, 8))
+    step()
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated() - base + (rec.numel() + 2 * T) * 4
+    ms, prof = timed(step, steps, warmup)
+    fl = {"full_fwd_tile": 2.0 * T * (d + dt) * Vs, "full_dz_tile": 2.0 * T * (d + dt) * Vs,
+          "dh_tile": 2.0 * T * d * Vs, "dw_tile": 2.0 * T * d * Vs}
+    dom, achieved = dominant(prof, fl, steps)
+    cred = (2.0 * (d + dt) * Vs + 4.0 * d * Vs) * T / (ms * 1e-3) / 1e12
+    out = {"workload": f"{p.name}_vshard{R}", "T": T, "V_shard": Vs, "ms_per_step": ms,
+           "tokens_per_s": T / (ms * 1e-3), "credited_tflops": cred, "mfma_frac_credited": cred / PEAK_BF16_TFLOPS,
+           "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
+           "kernels": kernel_table(prof, ms, steps), "steps_timed": steps}
+    del H, Ht, g, Ws, Wt, rec, kl, ls, lt, dH, dW, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def brief(r):
     keep = ("workload", "T", "V_shard", "valid_rows", "ms_per_step", "tokens_per_s", "valid_tokens_per_s", "credited_tflops",
             "mfma_frac_credited", "mfma_frac_executed", "peak_extra_hbm_bytes", "dominant", "dominant_tflops")
@@ -439,6 +490,8 @@ def main():
                         fv.name + "_one_call": brief(run_full(fv, 3, 1, a.chunk_rows, one_call=True))}
         sh = run_topk_shard(p, T, 8, a.steps, a.warmup, a.chunk_rows)
         out["extra"][sh["workload"]] = brief(sh)
+        fs = run_full_shard(fv, 8, 3, 1, a.chunk_rows)
+        out["extra"][fs["workload"]] = brief(fs)
     print(json.dumps(out))
 
 
