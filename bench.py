@@ -3,6 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
     python bench.py --sweep          # loss-only scaling sweep, one line per T
     python bench.py --copy-probe N   # plain copy of N bytes (counter calibration)
+    python bench.py --workload head_topk_t4096_vshard8   # one rank of an 8-way vocabulary split
+                                                         # (also full_vocab_t16384_vshard8)
 
 A step of the top-K workloads is one kd_topk_kl_fwd plus one kd_topk_kl_bwd
 over one batch of synthetic rows (inputs already in HBM): the output
@@ -433,6 +435,17 @@ def main():
             steps = max(2, min(a.steps, (4 * 4096 * 10) // T))
             r, _ = run_topk(p, T, steps, 1, a.chunk_rows)
             print(json.dumps({"sweep": p.name, "steps": steps, **brief(r)}), flush=True)
+        return
+
+    if a.workload.endswith("_vshard8"):  # one rank's step of an 8-way vocabulary split, on its own
+        base = G.PRESETS.get(a.workload[:-len("_vshard8")])
+        if base is None:
+            print(f"unknown workload {a.workload}", file=sys.stderr)
+            sys.exit(2)
+        r = (run_full_shard(base, 8, a.steps, a.warmup, a.chunk_rows) if base.full_vocab
+             else run_topk_shard(base, base.T, 8, a.steps, a.warmup, a.chunk_rows))
+        print(json.dumps({"metric": "one rank's fwd+bwd tokens/s, head split 8 ways by vocabulary",
+                          "value": r["tokens_per_s"], "unit": "tokens/s", **brief(r)}))
         return
 
     p = G.PRESETS.get(a.workload)
