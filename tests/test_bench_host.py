@@ -50,3 +50,10 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_unknown_workloads_are_refused_before_any_gpu_work():
+    for name in ("no_such_workload", "no_such_workload_vshard8"):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", name], capture_output=True,
+                           text=True, timeout=300)
+        assert r.returncode == 2 and "unknown workload" in r.stderr, (name, r.stderr[-300:])
