@@ -309,12 +309,12 @@ __device__ inline void store_block(StPair st, char* dst, long ld, long row0, lon
       const float4 a = st_read4(st, r, q);
       o = u32x4_t{__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w)};
     }
-    // streaming (non-temporal) store: the block is read back only by a later
-    // kernel, and evict-first lines leave L2 to the operands the other
-    // workgroups of the XCD are still reusing
+    // a plain store: the next kernels read the block back soon (dH and dW the
+    // dZ chunk, the elementwise pass a chunk's logits), and measured against
+    // evict-first stores it was as fast for dZ and 1-2% faster for the logits
     const long byte = col * E::kElem;
     char* p = dst + (prows ? panel_off(prows, row0 + r, byte) : (row0 + r) * ld * E::kElem + byte);
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(p));
+    *reinterpret_cast<u32x4_t*>(p) = o;
   }
 }
 
