@@ -330,3 +330,19 @@ def test_shards_are_deterministic_and_follow_the_callers_stream(head):
     for i, (x, y, z) in enumerate(zip(a, b, c)):
         np.testing.assert_array_equal(x, y, err_msg=f"output {i}, second run")
         np.testing.assert_array_equal(x, z, err_msg=f"output {i}, second stream")
+
+
+@pytest.mark.parametrize("head", ["topk", "full"])
+def test_shards_with_every_row_masked(head):
+    say(f"{head} shards, every row masked")
+    if head == "topk":
+        inp = G.make_topk(300, 256, 1288, 8, torch.bfloat16, mask="random10", n_masked=300, number=88, g="normal")
+        parts, kl, lse = run_shards(inp, (0, 640, 1288), 256)
+        outs = [kl, lse]
+    else:
+        inp = G.make_full(300, 256, 128, 1288, torch.bfloat16, mask="random10", n_masked=300, number=89, g="normal")
+        parts, got = run_full_shards(inp, (0, 640, 1288), 256)
+        outs = list(got.values())
+    assert int(inp["mask"].sum()) == 0
+    for x in outs + [p[k] for p in parts for k in ("rec", "dH", "dW")]:
+        assert np.all(np64(x) == 0)
