@@ -75,3 +75,24 @@ def assert_lse(got, want, dtype, valid=None):
 def assert_grad(got, want, dtype, what):
     r = rel_fro(got, want)
     assert r <= TOL[dtype]["grad"], f"{what}: rel Frobenius {r:.3e}"
+
+
+def run_topk_sampled(inp, rows, chunk_rows=0, want_z=True):
+    """The top-K forward + backward on the GPU at any T, copying back only the
+    sampled rows' kl, lse, z_topk and dH, plus per-row statistics of dW
+    (its row sums and norms, in float64) and whether all of dW is finite."""
+    H, W, I, A, M, g = (dev(inp[k]) for k in ("H", "W", "I", "A", "mask", "g"))
+    tau = inp["tau"]
+    kl, lse, z = kd.topk_kl_forward(H, W, I, A, M, tau, want_z_topk=want_z)
+    dH, dW = kd.topk_kl_backward(H, W, I, A, M, tau, lse, g, chunk_rows)
+    r = torch.from_numpy(np.asarray(rows, dtype=np.int64)).cuda()
+    out = dict(kl=kl[r].cpu().double().numpy(), lse=lse[r].cpu().double().numpy(),
+               z=None if z is None else z[r].cpu().double().numpy(), dH=dH[r].cpu().double().numpy(),
+               dW_rowsum=dW.double().sum(dim=1).cpu().numpy(), dW_rownorm=dW.double().norm(dim=1).cpu().numpy(),
+               dW_finite=bool(torch.isfinite(dW).all().item()),
+               kl_masked_zero=True if M is None else bool((kl[M == 0] == 0).all().item()),
+               dH_masked_zero=True if M is None else bool((dH[M == 0] == 0).all().item()))
+    torch.cuda.synchronize()
+    del H, W, I, A, M, g, kl, lse, z, dH, dW
+    torch.cuda.empty_cache()
+    return out

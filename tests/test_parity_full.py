@@ -63,7 +63,8 @@ def test_full_t16384_sampled_rows():
     say("full T=16384 sampled rows")
     got = run_full(inp)
     rng = np.random.default_rng(1)
-    rows = np.array(sorted(set(rng.choice(16384, 48, replace=False).tolist()) | {0, 255, 256, 16383}))
+    rows = np.array(sorted(set(rng.choice(16384, 256, replace=False).tolist())
+                           | {0, 255, 256, 4095, 4096, 8191, 8192, 12287, 12288, 16383}))
     kl, ls, lt, dH = O.full_kl_rows(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], None, p.tau, inp["g"], rows)
     assert_kl(got["kl"][rows], kl, torch.bfloat16)
     assert_lse(got["lse_s"][rows], ls, torch.bfloat16)
@@ -82,7 +83,7 @@ def test_full_largest_direct_load_chunk_sampled_rows():
     say("full T=17000, chunk_rows=32768 (capped at 16384)")
     got = run_full(inp, chunk_rows=32768)
     rng = np.random.default_rng(9)
-    rows = np.array(sorted(set(rng.choice(T, 24, replace=False).tolist()) | {0, 8400, 16383, 16384, 16639, T - 1}))
+    rows = np.array(sorted(set(rng.choice(T, 256, replace=False).tolist()) | {0, 8400, 16383, 16384, 16639, T - 1}))
     kl, ls, lt, dH = O.full_kl_rows(inp["H"], inp["Ws"], inp["Ht"], inp["Wt"], None, 1.0, inp["g"], rows)
     assert_kl(got["kl"][rows], kl, torch.bfloat16)
     assert_lse(got["lse_s"][rows], ls, torch.bfloat16)

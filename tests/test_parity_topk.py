@@ -217,7 +217,7 @@ def check_sampled(got, inp, rows, dtype):
     np.testing.assert_allclose(got["z"][rows][v], z[v], rtol=1e-4, atol=1e-5)
     assert_grad(got["dH"][rows], dH, dtype, "dH rows")
     # each sampled row's own dH within tolerance, not just the block
-    for i in np.nonzero(v)[0][:64]:
+    for i in np.nonzero(v)[0]:
         assert_grad(got["dH"][rows[i]], dH[i], dtype, f"dH row {rows[i]}")
 
 
@@ -226,7 +226,7 @@ def test_head_t4096_sampled_rows():
     inp = G.make_preset(p, g="normal")
     say("head T=4096 sampled rows")
     got = run_topk(inp)
-    check_sampled(got, inp, sample_rows(4096, None, n=192), torch.bfloat16)
+    check_sampled(got, inp, sample_rows(4096, None, n=256), torch.bfloat16)
     assert np.all(np.isfinite(got["dW"]))
 
 
@@ -235,7 +235,7 @@ def test_head_t32768_packed_sampled_rows():
     inp = G.make_preset(p, g="normal")
     say("head T=32768 packed tau=2 sampled rows")
     got = run_topk(inp)
-    rows = sample_rows(32768, inp["mask"], n=160, extra=[4096 * k - 206 for k in range(1, 9)]
+    rows = sample_rows(32768, inp["mask"], n=256, extra=[4096 * k - 206 for k in range(1, 9)]
                        + [4096 * k - 205 for k in range(1, 9)] + [4096 * k for k in range(1, 8)])
     check_sampled(got, inp, rows, torch.bfloat16)
     m = inp["mask"].numpy() == 0
@@ -281,7 +281,7 @@ def test_largest_direct_load_chunk_sampled_rows():
     say("head T=17000, chunk_rows=32768 (capped at 16384)")
     got = run_topk(inp, want_z=False, chunk_rows=32768)
     rng = np.random.default_rng(8)
-    rows = np.array(sorted(set(rng.choice(T, 24, replace=False).tolist()) | {0, 8400, 16383, 16384, 16639, T - 1}))
+    rows = np.array(sorted(set(rng.choice(T, 256, replace=False).tolist()) | {0, 8400, 16383, 16384, 16639, T - 1}))
     kl, lse, _, dH = O.topk_kl_rows(inp["H"], inp["W"], inp["I"], inp["A"], None, 1.0, inp["g"], rows)
     assert_kl(got["kl"][rows], kl, torch.bfloat16)
     assert_lse(got["lse"][rows], lse, torch.bfloat16)
