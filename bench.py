@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the packed and full-vocabulary workloads")
     ap.add_argument("--one-call", action="store_true",
                     help="full-vocabulary workload: time the single forward + backward call")
+    ap.add_argument("--no-protocol", action="store_true",
+                    help="skip the pages' 15-iteration protocol pass (short profiling runs)")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--sweep", action="store_true", help="T in 4096, 16384, 65536, 262144: one line each")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -115,45 +117,85 @@ def cpu_baseline(inp, rows: int):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": rows / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {rows} of {inp['H'].shape[0]} rows, forward + backward, fp64 NumPy "
                       f"(BLAS threads = cores), {dt:.1f} s"}
 
 
 def timed(step, steps: int, warmup: int):
-    """Run warmup + timed steps; returns (ms per step, {kernel: (launches, total ms)})."""
+    """Warmup steps, then exactly `steps` timed steps with the library's
+    per-launch profiling off (the timed region is the plain calls); then, in
+    a pass of its own, the same number of steps with every launch bracketed
+    by HIP events on its stream, for the per-kernel table.  Returns (ms per
+    step, {kernel: (launches, total ms)}, steps of the kernel pass)."""
     import torch
     import chunked_kl_loss_logit_amd as kd
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    kd.profile_reset()
-    kd.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    kd.profile_reset()
+    kd.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     kd.profile_enable(False)
-    return elapsed / steps * 1e3, kd.profile_read()
+    return elapsed / steps * 1e3, kd.profile_read(), steps
 
 
-def kernel_table(prof, ms: float, steps: int):
-    return {k: {"launches": n, "avg_ms": tot / n, "share": tot / (ms * steps)} for k, (n, tot) in prof.items()}
+def pages_protocol(step, iterations: int = 15, first: int = 10, last: int = 13):
+    """The loss benchmark's own protocol ("Efficient Knowledge Distillation for
+    LLMs ...", App. A "Profiling": 15-iteration runs, captured over iterations
+    10-13): `iterations` steps each bracketed by HIP events on the current
+    stream, and the mean step time of iterations first..last (1-based)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iterations)]
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    cap = ms[first - 1:last]
+    return {"iterations": iterations, "captured": f"{first}-{last}", "ms_per_step": sum(cap) / len(cap),
+            "ms_captured": [round(x, 4) for x in cap]}
+
+
+def kernel_table(prof, steps: int):
+    per_step = sum(tot for _, tot in prof.values()) / steps
+    return {k: {"launches": n, "avg_ms": tot / n, "ms_per_step": tot / steps, "share": tot / steps / per_step}
+            for k, (n, tot) in prof.items()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def dominant(prof, flops_per_step: dict, steps: int):
-    """The tile kernel with the most GPU time, and its achieved rate:
-    algorithmic flops of one launch / its average launch duration."""
+    """The tile kernel with the most GPU time in the kernel pass, and its
+    achieved rate: algorithmic flops of one launch / its average launch
+    duration (HIP events on the launch stream)."""
     dom = max((k for k in prof if k in TILE_KERNELS), key=lambda k: prof[k][1])
     n_l, tot_ms = prof[dom]
     per_launch = flops_per_step[dom] / (n_l / steps)
     return dom, per_launch / (tot_ms / n_l * 1e-3) / 1e12
 
 
-def run_topk(p, T: int, steps: int, warmup: int, chunk_rows: int):
-    """Time the top-K loss on preset p at T rows."""
+def run_topk(p, T: int, steps: int, warmup: int, chunk_rows: int, protocol: bool = False):
+    """Time the top-K loss on preset p at T rows (with protocol, also the
+    pages' 15-iteration protocol in a pass of its own)."""
     import torch
     import chunked_kl_loss_logit_amd as kd
     import kdinputs as G
@@ -185,17 +227,19 @@ def run_topk(p, T: int, steps: int, warmup: int, chunk_rows: int):
         kd.kd_topk_kl_fwd(H, W, I, A, M, tau, kl, lse, None, ws)
         kd.kd_topk_kl_bwd(H, W, I, A, M, tau, lse, g, dH, dW, chunk_rows, ws)
 
-    ms, prof = timed(step, steps, warmup)
+    ms, prof, ksteps = timed(step, steps, warmup)
     # algorithmic flops per step of each tile kernel (valid rows only)
     fl = {k: 2.0 * n_valid * d * V for k in ("topk_fwd_tile", "topk_dz_tile", "dh_tile", "dw_tile")}
-    dom, achieved = dominant(prof, fl, steps)
+    dom, achieved = dominant(prof, fl, ksteps)
     out = {"workload": p.name, "T": T, "valid_rows": n_valid, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
            "valid_tokens_per_s": n_valid / (ms * 1e-3),
            "credited_tflops": 6.0 * n_valid * d * V / (ms * 1e-3) / 1e12,
            "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
-           "kernels": kernel_table(prof, ms, steps), "steps_timed": steps}
+           "kernels": kernel_table(prof, ksteps), "steps_timed": steps}
     out["mfma_frac_credited"] = out["credited_tflops"] / PEAK_BF16_TFLOPS
     out["mfma_frac_executed"] = out["mfma_frac_credited"] * 8.0 / 6.0  # the backward recomputes the projection
+    if protocol:
+        out["pages_protocol"] = pages_protocol(step)
     del H, W, I, A, g, M, kl, lse, dH, dW, ws
     torch.cuda.empty_cache()
     return out, inp
@@ -231,15 +275,15 @@ def run_topk_fused(p, T: int, steps: int, warmup: int, chunk_rows: int):
     step()
     torch.cuda.synchronize()
     peak_extra = torch.cuda.max_memory_allocated() - base
-    ms, prof = timed(step, steps, warmup)
+    ms, prof, ksteps = timed(step, steps, warmup)
     fl = {k: 2.0 * n_valid * d * V for k in ("topk_fwd_tile", "dh_tile", "dw_tile")}
-    dom, achieved = dominant(prof, fl, steps)
+    dom, achieved = dominant(prof, fl, ksteps)
     cred = 6.0 * n_valid * d * V / (ms * 1e-3) / 1e12
     out = {"workload": p.name + "_one_call", "T": T, "valid_rows": n_valid, "ms_per_step": ms,
            "tokens_per_s": T / (ms * 1e-3), "valid_tokens_per_s": n_valid / (ms * 1e-3), "credited_tflops": cred,
            "mfma_frac_credited": cred / PEAK_BF16_TFLOPS, "mfma_frac_executed": cred / PEAK_BF16_TFLOPS,
            "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
-           "kernels": kernel_table(prof, ms, steps), "steps_timed": steps}
+           "kernels": kernel_table(prof, ksteps), "steps_timed": steps}
     del H, W, I, A, g, M, kl, lse, dH, dW, ws
     torch.cuda.empty_cache()
     return out
@@ -283,11 +327,11 @@ def run_full(p, steps: int, warmup: int, chunk_rows: int, one_call: bool = False
     step()
     torch.cuda.synchronize()
     peak_extra = torch.cuda.max_memory_allocated() - base + (0 if one_call else 2 * T * 4)  # + saved lse_s, lse_t
-    ms, prof = timed(step, steps, warmup)
+    ms, prof, ksteps = timed(step, steps, warmup)
     fl = {"full_fwd_tile": 2.0 * T * (d + dt) * V, "full_dz_tile": 2.0 * T * (d + dt) * V,
           "full_teacher_tile": 2.0 * T * dt * V, "full_student_tile": 2.0 * T * d * V,
           "dh_tile": 2.0 * T * d * V, "dw_tile": 2.0 * T * d * V}
-    dom, achieved = dominant(prof, fl, steps)
+    dom, achieved = dominant(prof, fl, ksteps)
     credited = (2.0 * (d + dt) + 4.0 * d) * V * T
     executed = ((2.0 if one_call else 4.0) * (d + dt) + 4.0 * d) * V * T
     out = {"workload": p.name + ("_one_call" if one_call else ""), "T": T, "ms_per_step": ms,
@@ -296,7 +340,7 @@ def run_full(p, steps: int, warmup: int, chunk_rows: int, one_call: bool = False
            "mfma_frac_credited": credited / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
            "mfma_frac_executed": executed / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
            "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
-           "kernels": kernel_table(prof, ms, steps), "steps_timed": steps}
+           "kernels": kernel_table(prof, ksteps), "steps_timed": steps}
     del H, Ws, Ht, Wt, g, kl, ls, lt, dH, dW, ws
     torch.cuda.empty_cache()
     return out
@@ -344,15 +388,15 @@ def run_topk_shard(p, T: int, R: int, steps: int, warmup: int, chunk_rows: int):
     step()
     torch.cuda.synchronize()
     peak_extra = torch.cuda.max_memory_allocated() - base + (rec.numel() + trow.numel() + lse.numel()) * 4
-    ms, prof = timed(step, steps, warmup)
+    ms, prof, ksteps = timed(step, steps, warmup)
     fl = {k: 2.0 * n_valid * d * Vs for k in ("topk_fwd_tile", "topk_dz_tile", "dh_tile", "dw_tile")}
-    dom, achieved = dominant(prof, fl, steps)
+    dom, achieved = dominant(prof, fl, ksteps)
     cred = 6.0 * n_valid * d * Vs / (ms * 1e-3) / 1e12
     out = {"workload": f"{p.name}_vshard{R}", "T": T, "V_shard": Vs, "valid_rows": n_valid, "ms_per_step": ms,
            "tokens_per_s": T / (ms * 1e-3), "valid_tokens_per_s": n_valid / (ms * 1e-3), "credited_tflops": cred,
            "mfma_frac_credited": cred / PEAK_BF16_TFLOPS, "mfma_frac_executed": cred / PEAK_BF16_TFLOPS * 8.0 / 6.0,
            "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
-           "kernels": kernel_table(prof, ms, steps), "steps_timed": steps}
+           "kernels": kernel_table(prof, ksteps), "steps_timed": steps}
     del H, W, I, A, g, M, rec, trow, kl, lse, dH, dW, ws
     torch.cuda.empty_cache()
     return out
@@ -395,26 +439,31 @@ def run_full_shard(p, R: int, steps: int, warmup: int, chunk_rows: int):
     step()
     torch.cuda.synchronize()
     peak_extra = torch.cuda.max_memory_allocated() - base + (rec.numel() + 2 * T) * 4
-    ms, prof = timed(step, steps, warmup)
+    ms, prof, ksteps = timed(step, steps, warmup)
     fl = {"full_fwd_tile": 2.0 * T * (d + dt) * Vs, "full_dz_tile": 2.0 * T * (d + dt) * Vs,
           "dh_tile": 2.0 * T * d * Vs, "dw_tile": 2.0 * T * d * Vs}
-    dom, achieved = dominant(prof, fl, steps)
+    dom, achieved = dominant(prof, fl, ksteps)
     cred = (2.0 * (d + dt) * Vs + 4.0 * d * Vs) * T / (ms * 1e-3) / 1e12
     out = {"workload": f"{p.name}_vshard{R}", "T": T, "V_shard": Vs, "ms_per_step": ms,
            "tokens_per_s": T / (ms * 1e-3), "credited_tflops": cred, "mfma_frac_credited": cred / PEAK_BF16_TFLOPS,
            "peak_extra_hbm_bytes": int(peak_extra), "dominant": dom, "dominant_tflops": achieved,
-           "kernels": kernel_table(prof, ms, steps), "steps_timed": steps}
+           "kernels": kernel_table(prof, ksteps), "steps_timed": steps}
     del H, Ht, g, Ws, Wt, rec, kl, ls, lt, dH, dW, ws
     torch.cuda.empty_cache()
     return out
 
 
+def progress(msg: str):
+    """One line on stderr per finished workload (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def brief(r):
+    progress(f"{r['workload']}: {r['ms_per_step']:.3f} ms per step")
     keep = ("workload", "T", "V_shard", "valid_rows", "ms_per_step", "tokens_per_s", "valid_tokens_per_s", "credited_tflops",
             "mfma_frac_credited", "mfma_frac_executed", "peak_extra_hbm_bytes", "dominant", "dominant_tflops")
     out = {k: r[k] for k in keep if k in r}
-    out["kernel_ms"] = {k: round(v["avg_ms"] * v["launches"] / r["steps_timed"], 4) for k, v in r["kernels"].items()} \
-        if "steps_timed" in r else None
+    out["kernel_ms"] = {k: round(v["ms_per_step"], 4) for k, v in r["kernels"].items()} if "kernels" in r else None
     return out
 
 
@@ -459,7 +508,8 @@ def main():
         return
 
     T = a.T or p.T
-    r, inp = run_topk(p, T, a.steps, a.warmup, a.chunk_rows)
+    r, inp = run_topk(p, T, a.steps, a.warmup, a.chunk_rows, protocol=not a.no_protocol)
+    progress(f"{p.name}: {r['ms_per_step']:.3f} ms per step")
     workload = p.name if not a.T else f"{p.name}_T{T}"
     dom = r["dominant"]
     n_l = r["kernels"][dom]["launches"]
@@ -486,12 +536,17 @@ def main():
         "peak_extra_hbm_bytes": r["peak_extra_hbm_bytes"],
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": r["dominant_tflops"], "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": r["dominant_tflops"] / PEAK_BF16_TFLOPS,
+                     "source": "the tile kernel with the most time in a pass of its own after the timed steps, "
+                               "each launch timed by HIP events on its stream",
                      "traffic": traffic_from_profiles(dom, workload),
                      "flops_per_launch": 2.0 * rows_per_launch * p.d * p.V},
         "kernels": r["kernels"],
     }
+    if "pages_protocol" in r:
+        out["pages_protocol"] = r["pages_protocol"]
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, min(a.cpu_rows, T))
+        progress(f"oracle on the host: {out['cpu_baseline']['sample']}")
     del inp
     if not a.no_extra and not a.T and a.workload == "head_topk_t4096":
         pk = G.PRESETS["head_topk_t32768_packed"]
@@ -501,11 +556,37 @@ def main():
                         pk.name: brief(run_topk(pk, pk.T, 3, 1, a.chunk_rows)[0]),
                         fv.name: brief(run_full(fv, 3, 1, a.chunk_rows)),
                         fv.name + "_one_call": brief(run_full(fv, 3, 1, a.chunk_rows, one_call=True))}
+        pk16 = brief(run_topk(pk, pk.T, 3, 1, 16384)[0])
+        pk16["workload"] = pk.name + "_chunk16384"
+        out["extra"][pk16["workload"]] = pk16
         sh = run_topk_shard(p, T, 8, a.steps, a.warmup, a.chunk_rows)
         out["extra"][sh["workload"]] = brief(sh)
         fs = run_full_shard(fv, 8, 3, 1, a.chunk_rows)
         out["extra"][fs["workload"]] = brief(fs)
+        # the loss-only sweep's longer points: throughput and peak extra HBM,
+        # which must grow linearly in T (no [T, V] buffer anywhere)
+        pts = [(T, r["peak_extra_hbm_bytes"])]
+        for Ts in G.SWEEP_T:
+            if Ts == T:
+                continue
+            sw = brief(run_topk(G.sweep_preset(Ts), Ts, 2, 1, a.chunk_rows)[0])
+            out["extra"][sw["workload"]] = sw
+            pts.append((Ts, sw["peak_extra_hbm_bytes"]))
+        out["extra"]["peak_extra_hbm_fit"] = linear_fit(pts)
     print(json.dumps(out))
+
+
+def linear_fit(pts):
+    """Least-squares a + b T through (T, bytes) points, and the largest
+    relative residual."""
+    n = len(pts)
+    mt = sum(t for t, _ in pts) / n
+    mb = sum(b for _, b in pts) / n
+    b = sum((t - mt) * (y - mb) for t, y in pts) / sum((t - mt) ** 2 for t, _ in pts)
+    a0 = mb - b * mt
+    res = max(abs(a0 + b * t - y) / y for t, y in pts)
+    return {"points": [[t, y] for t, y in sorted(pts)], "bytes_const": a0, "bytes_per_token": b,
+            "max_rel_residual": res}
 
 
 if __name__ == "__main__":

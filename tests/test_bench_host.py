@@ -24,9 +24,22 @@ def test_dominant_is_the_slowest_tile_kernel_and_its_rate_is_per_launch():
 
 
 def test_kernel_table_shares():
-    t = bench.kernel_table({"a": (2, 3.0), "b": (1, 1.0)}, ms=2.0, steps=2)
-    assert t["a"] == {"launches": 2, "avg_ms": 1.5, "share": 0.75}
+    # shares of the kernel pass's own GPU time; per-step times over its steps
+    t = bench.kernel_table({"a": (2, 3.0), "b": (1, 1.0)}, steps=2)
+    assert t["a"] == {"launches": 2, "avg_ms": 1.5, "ms_per_step": 1.5, "share": 0.75}
     assert t["b"]["share"] == pytest.approx(0.25)
+
+
+def test_linear_fit_of_peak_extra_memory():
+    pts = [(4096, 1000 + 678 * 4096), (16384, 1000 + 678 * 16384), (262144, 1000 + 678 * 262144)]
+    f = bench.linear_fit(pts)
+    assert f["bytes_per_token"] == pytest.approx(678)
+    assert f["bytes_const"] == pytest.approx(1000, abs=1e-6)
+    assert f["max_rel_residual"] < 1e-12
+
+
+def test_cpu_model_is_named():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
 
 
 def test_traffic_is_null_for_another_workload_or_changed_sources(monkeypatch):
