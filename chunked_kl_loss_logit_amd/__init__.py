@@ -21,7 +21,7 @@ from ._binding import (  # noqa: F401
     kd_full_kl_fwd_bwd, kd_full_kl_fwd_bwd_workspace_size, kd_full_kl_workspace_size, kd_topk_kl_bwd_ex,
     kd_topk_kl_fwd_bwd_ex, kd_topk_kl_fwd_ex, topk_opts, kd_full_kl_fwd_ex, kd_full_kl_bwd_ex, kd_full_kl_fwd_bwd_ex,
     full_opts, kd_topk_kl_bwd, kd_topk_kl_fwd, kd_topk_kl_fwd_bwd, kd_topk_kl_fwd_bwd_workspace_size,
-    kd_topk_kl_workspace_size, kd_version, lib,
+    kd_topk_kl_workspace_size, kd_version, lib, kd_topk_kl_fwd_noalloc, KD_NOALLOC_SCRATCH_BYTES,
     profile_enable, profile_read, profile_reset,
     kd_topk_kl_shard_workspace_size, kd_topk_kl_fwd_shard, kd_topk_kl_shard_combine, kd_topk_kl_bwd_shard,
     kd_full_kl_fwd_shard, kd_full_kl_shard_combine, kd_full_kl_bwd_shard,
@@ -32,7 +32,8 @@ __all__ = [
     "full_kl_backward", "full_kl_forward_backward", "kd_topk_kl_fwd", "kd_topk_kl_bwd", "kd_topk_kl_fwd_bwd",
     "kd_full_kl_fwd", "kd_full_kl_bwd", "kd_full_kl_fwd_bwd", "kd_topk_kl_workspace_size",
     "kd_topk_kl_fwd_bwd_workspace_size", "kd_full_kl_workspace_size", "kd_full_kl_fwd_bwd_workspace_size", "KDError",
-    "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex", "topk_opts", "kd_full_kl_fwd_ex",
+    "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex", "kd_topk_kl_fwd_noalloc", "topk_opts",
+    "kd_full_kl_fwd_ex",
     "kd_full_kl_bwd_ex", "kd_full_kl_fwd_bwd_ex", "full_opts",
     "topk_kl_shard_forward", "topk_kl_shard_combine", "topk_kl_shard_backward", "kd_topk_kl_shard_workspace_size",
     "kd_topk_kl_fwd_shard", "kd_topk_kl_shard_combine", "kd_topk_kl_bwd_shard",

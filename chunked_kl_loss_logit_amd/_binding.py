@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libkdloss.so")
 KD_F32, KD_BF16 = 0, 1
 KD_MAX_K = 8192
 KD_DEFAULT_CHUNK_ROWS = 4096
+KD_NOALLOC_SCRATCH_BYTES = 64 << 20
 STATUS = {
     0: "KD_OK", 1: "KD_ERR_INVALID_ARG", 2: "KD_ERR_UNSUPPORTED", 3: "KD_ERR_ALIGNMENT",
     4: "KD_ERR_WORKSPACE_TOO_SMALL", 5: "KD_ERR_INDEX_OUT_OF_RANGE", 6: "KD_ERR_HIP",
@@ -26,7 +27,7 @@ STATUS = {
 EXPORTS = (
     "kd_topk_kl_workspace_size", "kd_topk_kl_fwd", "kd_topk_kl_bwd",
     "kd_topk_kl_fwd_bwd_workspace_size", "kd_topk_kl_fwd_bwd",
-    "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex",
+    "kd_topk_kl_fwd_ex", "kd_topk_kl_bwd_ex", "kd_topk_kl_fwd_bwd_ex", "kd_topk_kl_fwd_noalloc",
     "kd_topk_kl_shard_workspace_size", "kd_topk_kl_fwd_shard", "kd_topk_kl_shard_combine", "kd_topk_kl_bwd_shard",
     "kd_full_kl_fwd_shard", "kd_full_kl_shard_combine", "kd_full_kl_bwd_shard",
     "kd_full_kl_workspace_size", "kd_full_kl_fwd", "kd_full_kl_bwd",
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.kd_topk_kl_fwd_bwd_workspace_size.argtypes = [i64, i64, i64, i64, st, i64, ctypes.POINTER(sz)]
     L.kd_topk_kl_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp, vp, vp, i64,
                                      vp, sz, vp]
+    L.kd_topk_kl_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, i64, i64, st, vp, vp, vp, vp]
+    L.kd_topk_kl_fwd_noalloc.restype = st
     op = ctypes.POINTER(KdTopkOpts)
     L.kd_topk_kl_fwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, op, i64, i64, i64, i64, st, vp, vp, vp, vp, sz, vp]
     L.kd_topk_kl_bwd_ex.argtypes = [vp, vp, vp, vp, vp, f32, op, i64, i64, i64, i64, st, vp, vp, vp, vp, i64, vp, sz,
@@ -287,6 +290,15 @@ def kd_topk_kl_fwd(H, W, topk_idx, topk_logits, mask, tau, kl, lse, z_topk, work
     _check(lib().kd_topk_kl_fwd(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask), float(tau),
                                 T, d, V, K, _dtype_code(H.dtype), _ptr(kl), _ptr(lse), _ptr(z_topk),
                                 _ptr(workspace), nb, _stream(stream)), "kd_topk_kl_fwd")
+
+
+def kd_topk_kl_fwd_noalloc(H, W, topk_idx, topk_logits, mask, tau, kl, lse, z_topk, stream=None):
+    """kd_topk_kl_fwd without a workspace: the library's fixed scratch array serves instead (for callers
+    that cannot allocate); calls that overlap on one GPU race."""
+    T, d, V, K, _ = _topk_fwd_checked(H, W, topk_idx, topk_logits, mask, None, kl, lse, z_topk, None)
+    _check(lib().kd_topk_kl_fwd_noalloc(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask),
+                                        float(tau), T, d, V, K, _dtype_code(H.dtype), _ptr(kl), _ptr(lse),
+                                        _ptr(z_topk), _stream(stream)), "kd_topk_kl_fwd_noalloc")
 
 
 def kd_topk_kl_bwd(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl, dH, dW, chunk_rows, workspace,

@@ -35,10 +35,14 @@ std::vector<ProfEvent> g_prof_pending;
 std::vector<std::string> g_prof_names;
 std::map<std::string, std::pair<int64_t, double>> g_prof_tot;
 
+// Set while a call that may not allocate runs on this thread: its launches
+// are not bracketed by events (hipEventCreate allocates).
+thread_local bool g_no_alloc = false;
+
 // Runs one launcher; while profiling, brackets it with events on `st`.
 template <class F>
 hipError_t run(const char* name, hipStream_t st, F&& launch) {
-  if (!g_prof_on) return launch();
+  if (!g_prof_on || g_no_alloc) return launch();
   hipEvent_t a = nullptr, b = nullptr;
   if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return launch();
   (void)hipEventRecord(a, st);
@@ -614,6 +618,64 @@ kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_id
                             void* workspace, size_t workspace_bytes, void* stream) {
   return topk_fwd(H, W, topk_idx, topk_logits, mask, tau, opts, T, d, V, K, dt, kl, lse, z_topk, nullptr, workspace,
                   workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------- the forward's fixed scratch
+// The scratch of kd_topk_kl_fwd_noalloc: one array per GPU, loaded with the
+// library's code object.  Host code never uses its name as an address (on
+// the host it is only a stand-in); the device address comes from
+// hipGetSymbolAddress, read once per device with that device current, and is
+// what the kernels get.
+static __device__ __align__(256) char scratch[KD_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;  // device ordinal -> the array's device address there
+
+kd_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KD_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(KD_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kd_status kd_topk_kl_fwd_noalloc(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,
+                                 const uint8_t* mask, float tau, int64_t T, int64_t d, int64_t V, int64_t K,
+                                 kd_dtype dt, float* kl, float* lse, float* z_topk, void* stream) {
+  g_err.clear();
+  KD_TRY(check_common(T, d, V, dt, tau));
+  KD_TRY(check_k(T, K, V));
+  if (T == 0) return KD_OK;
+  const size_t want = plan_topk(T, d, V, K, elem_of(dt), 0).fwd_total;
+  if (want > KD_NOALLOC_SCRATCH_BYTES)
+    return fail(KD_ERR_UNSUPPORTED, "this forward needs " + std::to_string(want) +
+                                        " bytes of scratch, above KD_NOALLOC_SCRATCH_BYTES (" +
+                                        std::to_string((size_t)KD_NOALLOC_SCRATCH_BYTES) +
+                                        "); use kd_topk_kl_fwd with a workspace");
+  void* ptr = nullptr;
+  KD_TRY(scratch_on_current_device(&ptr));
+  g_no_alloc = true;
+  const kd_status s = topk_fwd(H, W, topk_idx, topk_logits, mask, tau, nullptr, T, d, V, K, dt, kl, lse, z_topk,
+                               nullptr, ptr, KD_NOALLOC_SCRATCH_BYTES, stream);
+  g_no_alloc = false;
+  return s;
 }
 
 kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logits,

@@ -405,6 +405,30 @@ kd_status kd_full_kl_bwd_shard(const void* H, const void* Ws, const void* Ht, co
                                const float* grad_kl, float* dH, float* dWs, int64_t chunk_rows,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- top-K forward without a workspace
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, outputs and bits as kd_topk_kl_fwd, without the workspace: the
+ * forward's scratch (the sorted teacher entries, the compaction list, the
+ * split partials and the panel copy of a chunk's rows of H) lives in a fixed
+ * device array of KD_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends.  The call allocates nothing (no
+ * hipMalloc, hipFree or event; the kd_profile_* record skips it) and reads
+ * the array's device address once per device, on its first call there, with
+ * that device current; `stream` must belong to the current device.
+ * A shape whose forward needs more scratch than that returns
+ * KD_ERR_UNSUPPORTED before anything is enqueued (at d = 3072,
+ * V = 128256, K = 64 in bf16, about 37,000 rows fit); the other argument
+ * errors are kd_topk_kl_fwd's.  Every call on one GPU shares its array:
+ * calls that overlap on one GPU (other streams, other host threads) race
+ * and must be ordered by the caller.  Nothing in the array needs to start
+ * at zero; each call writes what it reads. */
+#define KD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kd_status kd_topk_kl_fwd_noalloc(const void* H, const void* W, const int32_t* topk_idx,
+                                 const float* topk_logits, const uint8_t* mask, float tau,
+                                 int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
+                                 float* kl, float* lse, float* z_topk, void* stream);
+
 /* ---------------------------------------------------------------- errors, version */
 
 const char* kd_status_string(kd_status s);

@@ -29,7 +29,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 30
+    assert len(names) == 31
     for n in names:
         assert hasattr(L, n), f"{n} declared in kdloss.h but not exported"
     assert sorted(kdl.EXPORTS) == names
@@ -412,3 +412,24 @@ def test_full_shard_checks(L):
                                                  None, 8, 64, 64, 256, kdl.KD_BF16, vp(FAKE), vp(FAKE), None,
                                                  vp(FAKE), vp(dH) if dH else None, vp(FAKE), 0, vp(FAKE), 16, None)
     assert bwd(dH=0) == 1 and bwd(dH=FAKE + 8) == 3 and bwd() == 4
+
+
+# ---------------------------------------------------------------- the forward without a workspace
+def noalloc(T=8, d=64, V=256, K=4, dt=kdl.KD_BF16, tau=1.0, kl=FAKE):
+    vp = ctypes.c_void_p
+    return kdl.lib().kd_topk_kl_fwd_noalloc(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(tau), T, d,
+                                            V, K, dt, vp(kl) if kl else None, vp(FAKE), None, None)
+
+
+def test_noalloc_forward_rejects_shapes_beyond_its_scratch(L):
+    # checked on the host before the scratch array is looked up or anything is
+    # enqueued: 64 MiB holds the forward of ~37,000 rows of the output head
+    assert noalloc(T=200000, d=3072, V=128256, K=64) == 2
+    msg = last_error()
+    assert "KD_NOALLOC_SCRATCH_BYTES" in msg and "needs" in msg
+    assert noalloc(T=-1) == 1
+    assert noalloc(tau=0.0) == 1
+    assert noalloc(K=0) == 1
+    assert noalloc(d=12) == 2
+    assert noalloc(T=0) == 0  # nothing to do, nothing touched
+    assert kdl.KD_NOALLOC_SCRATCH_BYTES == 64 << 20
