@@ -193,6 +193,22 @@ __device__ inline void mma_frags(const Frags<NB, NDS>& f, f32x16_t (&acc)[4][NB]
       for (int nb = 0; nb < NB; ++nb) Bf16::mma(acc[mb][nb], f.a[kg][mb], f.b[kg][nb]);
 }
 
+// The same products with the operands exchanged: block (mb, nb) then holds
+// B's block nb times A's block mb transposed, so lane l owns A row
+// 32 mb + l % 32 and, in register i, B column 32 nb + 8 (i / 4) + 4 (l / 32)
+// + i % 4 (the A and B operand layouts of the matrix instruction are the
+// same, so exchanging them transposes the product).  Epilogues that reduce
+// along B's columns per A row then find 16 of a row's values in each lane.
+template <int NB, int NDS>
+__device__ inline void mma_frags_t(const Frags<NB, NDS>& f, f32x16_t (&acc)[4][NB]) {
+#pragma unroll
+  for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) Bf16::mma(acc[mb][nb], f.b[kg][nb], f.a[kg][mb]);
+}
+
 template <int BN>
 using FragsNN = Frags<BN / 64, 2 * (4 + 2 * (BN / 64))>;  // b128 A reads, two transposing reads per B
 

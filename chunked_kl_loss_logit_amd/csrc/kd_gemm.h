@@ -76,6 +76,12 @@ __device__ inline int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+// the same for a uniform pointer (kept in scalar registers)
+template <class T>
+__device__ inline T* opaque_ptr(T* p) {
+  asm volatile("" : "+s"(p));
+  return p;
+}
 
 // ------------------------------------------------------------------ synchronisation
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding)

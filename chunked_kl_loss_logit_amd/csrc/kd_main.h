@@ -256,8 +256,9 @@ struct DmaNN {
 
   // Tiles t = 0 .. ntiles-1 described by at(t), through one ring; done(t,
   // acc) after each (see ring_run for what it may do).  Every tile must lie
-  // inside both operands: no row or column is clamped.
-  template <class At, class Done>
+  // inside both operands: no row or column is clamped.  kT: the
+  // accumulators hold the transposed tile (mma_frags_t).
+  template <bool kT = false, class At, class Done>
   __device__ inline void run(const Slots& sl, int ntiles, At&& at, Done&& done) {
     b.init(B, LONG_MAX);
     f32x16_t acc[4][BN / 64];
@@ -270,7 +271,12 @@ struct DmaNN {
           b.issue(s, ta.n0, db);
         },
         [&](const char* slot, FragsNN<BN>& f) { rd.read_nn(slot, f); },
-        [&](const FragsNN<BN>& f) { mma_frags(f, acc); },
+        [&](const FragsNN<BN>& f) {
+          if constexpr (kT)
+            mma_frags_t(f, acc);
+          else
+            mma_frags(f, acc);
+        },
         [&](int t) {
           done(t, acc);
           zero_acc<BN / 64>(acc);

@@ -19,6 +19,9 @@
 //              in step with the column blocks and picks the hits out of LDS.
 //   backward : dZ = (g/tau) (mass 2^(y - L2) - sum of w over hits), written in
 //              the input dtype to the chunk's dZ buffer (panels of C rows).
+//              On the direct-load path (bf16) the tile is accumulated
+//              transposed instead, each lane holding 16 columns of one row
+//              per block, and dZ is computed in registers (topk_dz_t_kernel).
 // Each row carries its own constants (log2(e)/tau, 1/tau, mass) from the prep
 // kernel: per-token temperature, a partial-mass teacher and a cross-entropy
 // entry change those and the weights w, not the tiles.
@@ -74,6 +77,10 @@ struct Cursor {
     const int2 x = pair[c];
     wait_vm<0>();
     return x;
+  }
+  // moves past every entry below `lim` without using it
+  __device__ inline void skip_below(int lim) {
+    while (c < end && entry().x < lim) ++c;
   }
   // calls f(index, p, position) for every entry below `lim`, moving past them
   template <class F>
@@ -327,6 +334,230 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_kernel(TopkDzArgs a) {
       });
 }
 
+// ---------------------------------------------------------------- dZ tiles, accumulators transposed
+// The direct-load (bf16) form of topk_dz_kernel.  The tile's products are
+// accumulated transposed (mma_frags_t): lane l of wave (wm, wn) owns chunk
+// row wm 128 + 32 mb + l % 32 of the tile in block row mb, and register i of
+// block (mb, nb) holds vocabulary column wn 128 + 32 nb + 8 (i / 4) +
+// 4 (l / 32) + i % 4 of it.  dZ of a register is then a function of that
+// register and its row's constants alone, so the epilogue needs neither
+// staged fp32 blocks nor workgroup barriers: each lane turns its values into
+// dZ, subtracts the teacher weights at the cached entries of its rows that
+// fall in its columns (one cursor per row, ascending), rounds to bf16, and
+// each 32 x 32 block goes through a wave-private 2 KB LDS region so that the
+// stores to the dZ panels are whole kilobytes.
+//
+// The main loop leaves few registers free, so only each row's cursor
+// position and end stay in registers.  The rows' constants sit in LDS for
+// the whole kernel, and the two entries at each cursor are brought in by
+// direct-to-LDS loads issued at the end of the previous tile's epilogue:
+// they land while the next tile is contracted, no register waits for them,
+// and no epilogue waits on a load of its own (a third entry of one row in
+// one tile's half, rare, is loaded on the spot as in Cursor::entry).
+constexpr int kStgBytes = 2048;            // per wave: 32 rows x 64 bytes
+constexpr int kWinBytes = 4 * 4 * 64 * 4;  // per wave: 4 rows x 4 words x 64 lanes
+
+// Byte position of 8 bytes (half hh of 16-byte chunk j) of row r in a
+// wave's [32][64 B] staging region.  The chunk is XOR-swizzled with
+// (r / 4) % 4 and the half with (r / 16) % 2: the 32 rows a half-wave writes
+// at once land in 32 distinct 8-byte bank groups, and the 4 chunks of the
+// 4 rows a quarter-wave reads back in 16 distinct 16-byte ones.
+__device__ inline int stg8(int r, int j, int hh) {
+  return r * 64 + ((j ^ ((r >> 2) & 3)) << 4) + ((hh ^ ((r >> 4) & 1)) << 3);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two floats to bf16 bits, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ inline uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// A row's cached entries as the transposed epilogues walk them: the position
+// and end live in registers; the window (the entries at the position when
+// the epilogue starts) was loaded into LDS by refill().
+struct TCursor {
+  int c, end;
+  int c0;       // position of the window (the cursor at the epilogue's start)
+  int2 e0, e1;  // window entries c0, c0 + 1 (meaningful below end)
+  __device__ inline int2 entry(const int2* pair) const {
+    if (c == c0) return e0;
+    if (c == c0 + 1) return e1;
+    const int2 x = pair[c];
+    wait_vm<0>();
+    return x;
+  }
+  __device__ inline void skip_below(const int2* pair, int lim) {
+    while (c < end && entry(pair).x < lim) ++c;
+  }
+  template <class F>
+  __device__ inline void take_below(const int2* pair, int lim, F&& f) {
+    while (c < end) {
+      const int2 x = entry(pair);
+      if (x.x >= lim) break;
+      f(x.x, __int_as_float(x.y), c);
+      ++c;
+    }
+  }
+};
+
+// Direct-to-LDS loads of the window of each of a lane's four rows: word q of
+// row mb at win + (4 mb + q) * 256 + 4 lane.
+__device__ inline void twin_refill(__amdgpu_buffer_rsrc_t rs, const int (&c)[4], const int (&end)[4], char* win) {
+  win = reinterpret_cast<char*>(opaque_ptr(win));
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pos = c[mb] + (q >> 1);
+      const uint32_t off = (uint32_t)(pos < end[mb] ? pos : 0) * 8u + 4u * (q & 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (KD_LDS void*)(win + (4 * mb + q) * 256), 4, (int)off, 0, 0, 0);
+    }
+}
+__device__ inline void twin_read(const char* win, int mb, TCursor& t) {
+  const int lane = opaque((int)threadIdx.x) & 63;
+  const int* w = reinterpret_cast<const int*>(win + 1024 * mb) + lane;
+  t.e0 = make_int2(w[0 * 64], w[1 * 64]);
+  t.e1 = make_int2(w[2 * 64], w[3 * 64]);
+}
+
+// One 32 x 32 block (mb, nb) of the wave's share of a tile: dZ of the lane's
+// row mb at its 16 columns, staged as bf16 and written to the chunk's panels.
+// Columns [lo, hi) are the tile's own (a shifted last tile starts before lo;
+// columns at or past V read as zero), stored from lo on.  rk = (L2, gs, c2)
+// of the row; gs = 0 on rows past the chunk's valid rows (dZ = 0 there).
+template <bool kFull>
+__device__ inline void dz_block_t(const f32x16_t& v, const float4 rk, TCursor& cur, const int2* pair, int cb,
+                                  int lo, int hi, char* stg, char* dz, long C, long brow0) {
+  // lane quantities recomputed per block (opaque), not hoisted out of the
+  // tile loop where they would hold registers through the main loop
+  const int lane = opaque((int)threadIdx.x) & 63, h = lane >> 5, cl = lane & 31;
+  float o[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float e = rk.y * fast_exp2(fmaf(v[i], rk.z, -rk.x));
+    if constexpr (kFull)
+      o[i] = e;
+    else
+      o[i] = cb + 8 * (i >> 2) + 4 * h + (i & 3) < hi ? e : 0.f;
+  }
+  // scatter-add of the teacher weights at the row's cached entries in the
+  // block (each lane takes those in its own columns)
+  cur.take_below(pair, min(cb + 32, hi), [&](int idx, float p, int) {
+    const int dcol = idx - cb;
+    if (((dcol >> 2) & 1) == h) {
+      const int at = ((dcol >> 3) << 2) | (dcol & 3);
+      const float gp = rk.y * p;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i] = i == at ? o[i] - gp : o[i];
+    }
+  });
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<uint2*>(stg + stg8(cl, j, h)) =
+        make_uint2(pk_bf16(o[4 * j], o[4 * j + 1]), pk_bf16(o[4 * j + 2], o[4 * j + 3]));
+  // back out of LDS (the same wave: its LDS accesses complete in order, no
+  // barrier), 16 bytes per lane, 16 consecutive rows of one 64-byte panel
+  // piece per store instruction
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int r = k * 16 + (lane >> 2), j = lane & 3;
+    const uint4 q = *reinterpret_cast<const uint4*>(stg + r * 64 + ((j ^ ((r >> 2) & 3)) << 4));
+    const uint4 w = ((r >> 4) & 1) ? make_uint4(q.z, q.w, q.x, q.y) : q;  // halves stored exchanged
+    const int col = cb + 8 * j;
+    if (kFull || col >= lo) *reinterpret_cast<uint4*>(dz + panel_off(C, brow0 + r, (long)col * 2)) = w;
+  }
+}
+
+template <bool kFull>
+__device__ inline void dz_tile_t(const f32x16_t (&acc)[4][4], const float4* rowk, TCursor (&R)[4], const int2* pair,
+                                 int base, int lo, int hi, char* stg, char* dz, long C, int wrow0, int trow0) {
+  const int lane = opaque((int)threadIdx.x) & 63;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const float4 rk = rowk[trow0 + mb * 32 + (lane & 31)];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      dz_block_t<kFull>(acc[mb][nb], rk, R[mb], pair, base + 32 * nb, lo, hi, stg, dz, C, wrow0 + mb * 32);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void topk_dz_t_kernel(TopkDzArgs a) {
+  __shared__ __attribute__((aligned(16))) char sl_0[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char sl_1[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char sl_2[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char sl_3[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char stg_all[4 * kStgBytes];
+  __shared__ __attribute__((aligned(16))) float4 rowk[kBM];
+  __shared__ __attribute__((aligned(16))) char win_all[4 * kWinBytes];
+  const Slots sl{sl_0, sl_1, sl_2, sl_3, nullptr};
+
+  const long count = *a.c.count;
+  const long M = min(a.C, count - a.c0);  // valid rows in this chunk
+  if (M <= 0) return;
+  int rb, sp;
+  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, a.group, rb, sp);
+  const int row0 = rb * kBM;
+  if (row0 >= M) return;
+  const int tb = (int)((long)a.ntiles * sp / a.S);
+  const int te = (int)((long)a.ntiles * (sp + 1) / a.S);
+  const int V = (int)a.V;
+  const int32_t* rows = a.c.rows + a.c0;
+  const int2* pair = a.rd.pair;
+
+  DmaNN<kBN> mainloop;
+  mainloop.init(
+      a.Hp, [&](int r) -> const char* { return row0 + r < M ? a.Hp + (row0 + r) * kRowB : nullptr; }, a.W,
+      a.V * 2, a.V, a.d, a.C * kRowB);
+
+  const int w = wave_id(), wm = w >> 1, wn = w & 1;
+  const int lane = (int)threadIdx.x & 63;
+  const int trow0 = wm * 128;        // the wave's first row of the tile
+  const int wrow0 = row0 + trow0;    // ... of the chunk
+  char* stg = stg_all + w * kStgBytes;
+  char* win = win_all + w * kWinBytes;
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(reinterpret_cast<const char*>(pair));
+  int cpos[4], cend[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int ti = wrow0 + mb * 32 + (lane & 31);
+    const bool rv = ti < M;
+    const long t = rv ? rows[ti] : 0;
+    cend[mb] = (int)(t * a.K + (rv ? a.K : 0));
+    cpos[mb] = lower_bound(pair, (int)(t * a.K), cend[mb], (long)tb * kBN);
+    if (wn == 0 && lane < 32) {
+      const float4 rc = rv ? a.rd.rowc[t] : make_float4(0.f, 0.f, 1.f, 0.f);
+      rowk[trow0 + mb * 32 + lane] = make_float4(rv ? a.lse[t] * kLog2e - rc.w : 0.f, rv ? a.g[t] * rc.y : 0.f,
+                                                 rc.x, 0.f);
+    }
+  }
+  twin_refill(prs, cpos, cend, win);  // lands before the ring's first wait
+
+  mainloop.template run<true>(
+      sl, te - tb, [&](int i) { return TileAt{0, tile_n0(tb + i, V)}; },
+      [&](int i, const f32x16_t (&acc)[4][4]) {
+        const int vt = tb + i, n0 = tile_n0(vt, V), lo = vt * kBN, hi = min(lo + kBN, V);
+        const int base = n0 + wn * 128;
+        TCursor R[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          R[mb].c = R[mb].c0 = cpos[mb];
+          R[mb].end = cend[mb];
+          twin_read(win, mb, R[mb]);
+          // entries before this wave's columns (the other wave's half of the
+          // previous tile) are passed over
+          R[mb].skip_below(pair, max(base, lo));
+        }
+        if (n0 == lo && lo + kBN <= hi)
+          dz_tile_t<true>(acc, rowk, R, pair, base, lo, hi, stg, a.dz, a.C, wrow0, trow0);
+        else
+          dz_tile_t<false>(acc, rowk, R, pair, base, lo, hi, stg, a.dz, a.C, wrow0, trow0);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) cpos[mb] = R[mb].c;
+        twin_refill(prs, cpos, cend, win);
+      });
+}
+
 // ---------------------------------------------------------------- dZ from stored logits
 constexpr int kDzzRows = 64;    // rows per block of the top-K elementwise dZ pass
 constexpr int kDzzRanges = 64;  // column ranges per block row
@@ -424,7 +655,8 @@ hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st) {
 hipError_t launch_topk_dz(int elem, const TopkDzArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
   if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.C * a.d * 2) && fits32(a.d * a.V * 2))
-    hipLaunchKernelGGL((topk_dz_kernel<DmaNN<kBN>, Bf16>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((fits32((a.T * a.K + 2) * 8) ? topk_dz_t_kernel : topk_dz_kernel<DmaNN<kBN>, Bf16>), grid,
+                       block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((topk_dz_kernel<GenNN<Bf16, kBN>, Bf16>), grid, block, 0, st, a);
   else
