@@ -19,9 +19,11 @@
 //              in step with the column blocks and picks the hits out of LDS.
 //   backward : dZ = (g/tau) (mass 2^(y - L2) - sum of w over hits), written in
 //              the input dtype to the chunk's dZ buffer (panels of C rows).
-//              On the direct-load path (bf16) the tile is accumulated
-//              transposed instead, each lane holding 16 columns of one row
-//              per block, and dZ is computed in registers (topk_dz_t_kernel).
+// On the direct-load path (bf16) both are accumulated transposed instead,
+// each lane holding 16 columns of one row per 32 x 32 block, and the
+// epilogues work in registers (topk_fwd_t_kernel, topk_dz_t_kernel): the
+// forward keeps per-lane running maxima and sums that two lane exchanges
+// merge at the end of a split, the backward turns each register into dZ.
 // Each row carries its own constants (log2(e)/tau, 1/tau, mass) from the prep
 // kernel: per-token temperature, a partial-mass teacher and a cross-entropy
 // entry change those and the weights w, not the tiles.
@@ -558,6 +560,224 @@ __global__ __launch_bounds__(kThreads, 1) void topk_dz_t_kernel(TopkDzArgs a) {
       });
 }
 
+// ---------------------------------------------------------------- forward tiles, accumulators transposed
+// The direct-load (bf16) form of topk_fwd_kernel, with the tile accumulated
+// transposed as in topk_dz_t_kernel.  Each lane keeps, for each of its four
+// rows, a running base-2 maximum and scaled sum over its own columns (16 per
+// block, 64 per tile) and its part of the gather, Σ w z over the cached
+// entries that fall in its columns; these live in LDS between tiles (the
+// main loop leaves no registers for them).  After the split's last tile the
+// two lanes of a row and then the two waves of a row (its column halves)
+// merge their parts in a fixed order into the split's partial (m2, l, x).
+// With zout set the raw logits also go out, fp32, 16 bytes per lane.
+constexpr int kFstBytes = 3 * 4 * 64 * 4;  // per wave: (m2, l, x) of 4 rows x 64 lanes
+
+// One row's update from its 64 values in the lane (val(nb, i): column
+// base + 32 nb + 8 (i / 4) + 4 (l / 32) + i % 4, -inf where the column is not
+// the tile's own): running maximum and scaled sum, then the gather of the
+// cached entries in the lane's columns.
+template <bool kZ, class Val>
+__device__ inline void fwd_row_t(Val&& val, float c2, float* st, TCursor& cur, const int2* pair, int base, int hi,
+                                 const TopkFwdArgs& a) {
+  const int lane = opaque((int)threadIdx.x) & 63, h = lane >> 5;
+  float m2 = st[0], l = st[64], x = st[128];
+  float cm = -INFINITY;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cm = fmaxf(cm, val(nb, i));
+  const float cmy = cm * c2;
+  l = cmy > m2 ? l * fast_exp2(m2 - cmy) : l;  // 2^(-inf) = 0 while l is still 0
+  m2 = fmaxf(m2, cmy);
+  float sum = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += fast_exp2(fmaf(val(nb, i), c2, -m2));  // -inf columns add 0
+  // a lane whose columns are all outside the tile keeps m2 = -inf and adds
+  // nothing (2^(-inf - -inf) would be NaN)
+  l += cm == -INFINITY ? 0.f : sum;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int cb = base + 32 * nb;
+    cur.take_below(pair, min(cb + 32, hi), [&](int idx, float p, int c) {
+      const int dcol = idx - cb;
+      if (((dcol >> 2) & 1) == h) {
+        const int at = ((dcol >> 3) << 2) | (dcol & 3);
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z = i == at ? val(nb, i) : z;
+        x = fmaf(p, z, x);
+        if constexpr (kZ) {
+          const int k = a.rd.perm[c];
+          if (k < a.Kz) a.z_topk[(long)(c / a.K) * a.Kz + k] = z;
+        }
+      }
+    });
+  }
+  st[0] = m2;
+  st[64] = l;
+  st[128] = x;
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// The tile's raw logits of one row (the columns from lo on), fp32, 16 bytes
+// per lane: four consecutive accumulator registers per store, taken as they
+// are (gfx950 stores take accumulator registers as data).
+template <int NB, int J>
+__device__ inline void zout4(const f32x16_t (&acc)[4], float* zr, int base, int lo, int h) {
+  const int col = base + 32 * NB + 8 * J + 4 * h;
+  if (col >= lo)
+    *reinterpret_cast<f32x4_t*>(zr + col) =
+        __builtin_shufflevector(acc[NB], acc[NB], 4 * J, 4 * J + 1, 4 * J + 2, 4 * J + 3);
+}
+template <int NB>
+__device__ inline void zout_nb(const f32x16_t (&acc)[4], float* zr, int base, int lo, int h) {
+  zout4<NB, 0>(acc, zr, base, lo, h);
+  zout4<NB, 1>(acc, zr, base, lo, h);
+  zout4<NB, 2>(acc, zr, base, lo, h);
+  zout4<NB, 3>(acc, zr, base, lo, h);
+}
+__device__ inline void fwd_zout_t(const f32x16_t (&acc)[4], float* zr, int base, int lo) {
+  const int h = (opaque((int)threadIdx.x) >> 5) & 1;
+  zout_nb<0>(acc, zr, base, lo, h);
+  zout_nb<1>(acc, zr, base, lo, h);
+  zout_nb<2>(acc, zr, base, lo, h);
+  zout_nb<3>(acc, zr, base, lo, h);
+}
+
+// base-2 (max, sum, cross) parts of one row over two column sets, merged
+__device__ inline void merge_part(float& m2, float& l, float& x, float om2, float ol, float ox) {
+  const float m = fmaxf(m2, om2);
+  l = (m2 == -INFINITY ? 0.f : l * fast_exp2(m2 - m)) + (om2 == -INFINITY ? 0.f : ol * fast_exp2(om2 - m));
+  m2 = m;
+  x += ox;
+}
+
+template <bool kZ, bool kOut>
+__global__ __launch_bounds__(kThreads, 1) void topk_fwd_t_kernel(TopkFwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char sl_0[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char sl_1[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char sl_2[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char sl_3[kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char win_all[4 * kWinBytes];
+  __shared__ __attribute__((aligned(16))) float fst_all[4 * kFstBytes / 4];
+  __shared__ float c2k[kBM];
+  const Slots sl{sl_0, sl_1, sl_2, sl_3, nullptr};
+
+  const long count = *a.c.count;
+  const long M = min(a.C, count - a.c0);  // rows of this launch
+  if (M <= 0) return;
+  int rb, sp;
+  grouped_coords(xcd_remap(blockIdx.x, gridDim.x), a.nrb, a.S, a.group, rb, sp);
+  const int row0 = rb * kBM;
+  if (row0 >= M) return;
+  const int tb = (int)((long)a.ntiles * sp / a.S);
+  const int te = (int)((long)a.ntiles * (sp + 1) / a.S);
+  const int V = (int)a.V;
+  const int32_t* rows = a.c.rows + a.c0;
+  const int2* pair = a.rd.pair;
+
+  DmaNN<kBN> mainloop;
+  mainloop.init(
+      a.Hp, [&](int r) -> const char* { return row0 + r < M ? a.Hp + (row0 + r) * kRowB : nullptr; }, a.W,
+      a.V * 2, a.V, a.d, a.C * kRowB);
+
+  const int w = wave_id(), wm = w >> 1, wn = w & 1;
+  const int lane = (int)threadIdx.x & 63;
+  const int trow0 = wm * 128;
+  char* win = win_all + w * kWinBytes;
+  float* fst = fst_all + w * (kFstBytes / 4);
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(reinterpret_cast<const char*>(pair));
+  int cpos[4], cend[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int ti = row0 + trow0 + mb * 32 + (lane & 31);
+    const bool rv = ti < M;
+    const long t = rv ? rows[ti] : 0;
+    cend[mb] = (int)(t * a.K + (rv ? a.K : 0));
+    cpos[mb] = lower_bound(pair, (int)(t * a.K), cend[mb], (long)tb * kBN);
+    if (wn == 0 && lane < 32) c2k[trow0 + mb * 32 + lane] = rv ? a.rd.rowc[t].x : 1.f;
+    fst[mb * 192 + lane] = -INFINITY;
+    fst[mb * 192 + 64 + lane] = 0.f;
+    fst[mb * 192 + 128 + lane] = 0.f;
+  }
+  twin_refill(prs, cpos, cend, win);  // lands before the ring's first wait
+
+  mainloop.template run<true>(
+      sl, te - tb, [&](int i) { return TileAt{0, tile_n0(tb + i, V)}; },
+      [&](int i, const f32x16_t (&acc)[4][4]) {
+        const int vt = tb + i, n0 = tile_n0(vt, V), lo = vt * kBN, hi = min(lo + kBN, V);
+        const int base = n0 + wn * 128;
+        const bool full = n0 == lo && lo + kBN <= hi;
+        const int ln = opaque((int)threadIdx.x) & 63;
+        if constexpr (kOut) {  // the logits first, straight from the accumulators
+          const int zr0 = opaque(row0 + trow0 + (ln & 31));  // the lane's row of block row 0
+          float* zp = a.zout + (long)zr0 * a.ldz;
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+            if (zr0 + mb * 32 < M) fwd_zout_t(acc[mb], zp + (long)mb * 32 * a.ldz, base, lo);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          TCursor R;
+          R.c = R.c0 = cpos[mb];
+          R.end = cend[mb];
+          twin_read(win, mb, R);
+          R.skip_below(pair, max(base, lo));
+          const float c2 = c2k[trow0 + mb * 32 + (ln & 31)];
+          float* st = fst + mb * 192 + ln;
+          if (full) {
+            fwd_row_t<kZ>([&](int nb, int i) { return acc[mb][nb][i]; }, c2, st, R, pair, base, hi, a);
+          } else {
+            // only the tile's own columns [lo, hi) count: a group of four
+            // (lo, hi and base are multiples of 8) outside them gets -inf
+            // added, which drops it from the maximum and the sum
+            float pen[16];
+            const int h4 = 4 * (ln >> 5);
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+              const int col = base + 32 * (g >> 2) + 8 * (g & 3) + h4;
+              pen[g] = col >= lo && col < hi ? 0.f : -INFINITY;
+            }
+            fwd_row_t<kZ>([&](int nb, int i) { return acc[mb][nb][i] + pen[4 * nb + (i >> 2)]; }, c2, st, R, pair,
+                          base, hi, a);
+          }
+          cpos[mb] = R.c;
+        }
+        twin_refill(prs, cpos, cend, win);
+      });
+
+  // the split's partial per row: lane halves, then column halves (wave wn = 1
+  // hands its parts to wave wn = 0 through slot 0, free after the ring)
+  float4* xch = reinterpret_cast<float4*>(sl_0);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    float m2 = fst[mb * 192 + lane], l = fst[mb * 192 + 64 + lane], x = fst[mb * 192 + 128 + lane];
+    const float om2 = __shfl_xor(m2, 32), ol = __shfl_xor(l, 32), ox = __shfl_xor(x, 32);
+    if (lane < 32) merge_part(m2, l, x, om2, ol, ox);
+    if (wn == 1 && lane < 32) xch[trow0 + mb * 32 + lane] = make_float4(m2, l, x, 0.f);
+    fst[mb * 192 + lane] = m2;
+    fst[mb * 192 + 64 + lane] = l;
+    fst[mb * 192 + 128 + lane] = x;
+  }
+  __syncthreads();
+  if (wn == 0 && lane < 32) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int ti = row0 + trow0 + mb * 32 + lane;
+      if (ti >= M) continue;
+      float m2 = fst[mb * 192 + lane], l = fst[mb * 192 + 64 + lane], x = fst[mb * 192 + 128 + lane];
+      const float4 o = xch[trow0 + mb * 32 + lane];
+      merge_part(m2, l, x, o.x, o.y, o.z);
+      float4* dst = reinterpret_cast<float4*>(a.part) + (long)sp * a.part_stride + (a.c0 - a.part_row0) + ti;
+      *dst = make_float4(m2, l, x, 0.f);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dZ from stored logits
 constexpr int kDzzRows = 64;    // rows per block of the top-K elementwise dZ pass
 constexpr int kDzzRanges = 64;  // column ranges per block row
@@ -636,7 +856,13 @@ hipError_t launch_topk_dz_from_z(int elem, const TopkDzFromZArgs& a, hipStream_t
 template <bool kZ>
 static void launch_topk_fwd_z(int elem, const TopkFwdArgs& a, hipStream_t st) {
   const dim3 grid(a.nrb * a.S), block(kThreads);
-  if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.C * a.d * 2) && fits32(a.d * a.V * 2))
+  if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.C * a.d * 2) && fits32(a.d * a.V * 2) &&
+      fits32((a.T * a.K + 2) * 8))
+    if (a.zout)
+      hipLaunchKernelGGL((topk_fwd_t_kernel<kZ, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((topk_fwd_t_kernel<kZ, false>), grid, block, 0, st, a);
+  else if (elem == 2 && a.d % kDmaKMult == 0 && a.V >= kBN && fits32(a.C * a.d * 2) && fits32(a.d * a.V * 2))
     hipLaunchKernelGGL((topk_fwd_kernel<DmaNN<kBN>, Bf16, kZ>), grid, block, 0, st, a);
   else if (elem == 2)
     hipLaunchKernelGGL((topk_fwd_kernel<GenNN<Bf16, kBN>, Bf16, kZ>), grid, block, 0, st, a);
