@@ -39,9 +39,9 @@ EXPORTS = (
 
 
 class KdTopkOpts(ctypes.Structure):
-    """kd_topk_opts of kdloss.h: device pointers (0 = NULL) and the CE weight."""
+    """kd_topk_opts of kdloss.h: device pointers (0 = NULL), the CE weight and the index-check flag."""
     _fields_ = [("tau_rows", ctypes.c_void_p), ("teacher_lse", ctypes.c_void_p), ("labels", ctypes.c_void_p),
-                ("ce_weight", ctypes.c_float)]
+                ("ce_weight", ctypes.c_float), ("check_indices", ctypes.c_int32)]
 
 
 class KdFullOpts(ctypes.Structure):
@@ -317,18 +317,19 @@ def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logits, mask, tau, grad_kl, kl, lse,
                           chunk_rows, workspace, stream, _name="kd_topk_kl_fwd_bwd")
 
 
-def topk_opts(tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0):
+def topk_opts(tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0, check_indices=False):
     """The kd_topk_opts struct for these device tensors (or None when no option is set).  The
     tensors must stay alive until the call that takes the struct has been enqueued; the struct
-    keeps a reference to them, and each call checks them against its T."""
-    if tau_rows is None and teacher_lse is None and labels is None and not ce_weight:
+    keeps a reference to them, and each call checks them against its T.  check_indices asks
+    for the device-side index range check (the call then synchronises its stream once)."""
+    if tau_rows is None and teacher_lse is None and labels is None and not ce_weight and not check_indices:
         return None
     kept = (("tau_rows", tau_rows, _F32), ("teacher_lse", teacher_lse, _F32), ("labels", labels, _I32))
     for name, t, dtypes in kept:
         _need(name, t, None, dtypes, optional=True)
         if t is not None and t.dim() != 1:
             raise ValueError(f"{name} must be 1-D [T], got shape {tuple(t.shape)}")
-    o = KdTopkOpts(None, None, None, float(ce_weight))
+    o = KdTopkOpts(None, None, None, float(ce_weight), 1 if check_indices else 0)
     o._tensors = kept
     return o
 

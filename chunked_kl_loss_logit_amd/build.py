@@ -74,6 +74,42 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# ---------------------------------------------------------------- host sanitizer build
+# The host code of the C ABI (argument checks, workspace planning, launch
+# sequences) compiled with the address and undefined-behaviour sanitizers,
+# linked with the uninstrumented kernels and a driver that runs the ABI's
+# rejection and workspace-size cases on the CPU (tests/host/abi_driver.cpp).
+ASAN_DIR = os.path.join(BUILD, "host_sanitizers")
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitizer_driver() -> str:
+    """Build the sanitizer-instrumented ABI driver; returns its path.  Needs
+    the kernels' objects of a regular build (build() makes them)."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    api = os.path.join(CSRC, "kd_api.cpp")
+    kernels = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in sources() if s.endswith(".hip")]
+    missing = [k for k in kernels if not os.path.exists(k)]
+    if missing:
+        build()
+    api_o = os.path.join(ASAN_DIR, "kd_api.o")
+    drv_src = os.path.join(ROOT, "tests", "host", "abi_driver.cpp")
+    drv_o = os.path.join(ASAN_DIR, "abi_driver.o")
+    exe = os.path.join(ASAN_DIR, "abi_driver")
+    flags = [f for f in _flags() if f != "-O3"] + ["-O1", "-g"]
+    steps = [
+        [_hipcc(), "-xhip", *flags, *ASAN_HOST, "-c", api, "-o", api_o],
+        [_hipcc(), *flags, *ASAN_HOST, "-c", drv_src, "-o", drv_o],
+        [_hipcc(), f"--offload-arch={ARCH}", *ASAN_HOST, "-o", exe, drv_o, api_o, *kernels],
+    ]
+    for cmd in steps:
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitizer build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return exe
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)

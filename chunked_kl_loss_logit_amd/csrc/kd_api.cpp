@@ -238,7 +238,7 @@ struct TopkPlan {
   // hold one chunk; the chunk's rows of H in panels
   int ntiles;
   int64_t Cf;
-  size_t o_pair, o_perm, o_ent, o_rowc, o_rows, o_count, o_part, o_hp_f;
+  size_t o_pair, o_perm, o_ent, o_rowc, o_rows, o_count, o_bad, o_part, o_hp_f;
   ChunkPlan ch;
   size_t fwd_total, total;  // bytes the forward call needs; bytes both calls need
   // single-call forward + backward: per-chunk partials, the chunk's fp32
@@ -259,6 +259,7 @@ TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t
   p.o_rowc = cv.take((size_t)T * 16);
   p.o_rows = cv.take((size_t)T * 4);
   p.o_count = cv.take(16);
+  p.o_bad = cv.take(16);  // the index check's counter
   Carver fw = cv, bw = cv;  // forward partials and backward chunk buffers overlap
   p.o_part = fw.take((size_t)max_splits(p.ntiles) * p.Cf * 16);
   p.o_hp_f = fw.take(panel_bytes(p.Cf, d * elem));
@@ -443,6 +444,7 @@ namespace {
 struct TopkOpts {
   kd::TopkPrepOpts prep;
   int64_t KE;
+  bool check;  // the index check on request
 };
 
 kd_status resolve_opts(const kd_topk_opts* o, float tau, int64_t K, TopkOpts& r) {
@@ -450,7 +452,9 @@ kd_status resolve_opts(const kd_topk_opts* o, float tau, int64_t K, TopkOpts& r)
   r.prep.c2 = (float)(1.4426950408889634 / (double)tau);
   r.prep.inv_tau = 1.0f / tau;
   r.KE = K;
+  r.check = false;
   if (o == nullptr) return KD_OK;
+  r.check = o->check_indices != 0;
   if (!std::isfinite(o->ce_weight) || o->ce_weight < 0.f || o->ce_weight > 1.f)
     return fail(KD_ERR_INVALID_ARG, "ce_weight must be finite and in [0, 1]");
   if (o->ce_weight > 0.f && o->labels == nullptr) return fail(KD_ERR_INVALID_ARG, "ce_weight > 0 needs labels");
@@ -479,6 +483,29 @@ kd_status resolve_full_opts(const kd_full_opts* o, kd::FullMix& mx) {
   return KD_OK;
 }
 
+// The index check on request: the counter is cleared before the prep kernel
+// counts into it, and read back (one synchronisation of the stream) after.
+kd_status start_index_check(TopkOpts& op, void* ws, const TopkPlan& p, int64_t V, hipStream_t st) {
+  if (!op.check) return KD_OK;
+  int32_t* bad = at<int32_t>(ws, p.o_bad);
+  KD_LAUNCH("fill_zero", st, kd::launch_fill_zero(bad, 16, st));  // the counter's whole 16-byte region
+  op.prep.bad = bad;
+  op.prep.V = (int32_t)V;
+  return KD_OK;
+}
+
+kd_status finish_index_check(const TopkOpts& op, hipStream_t st) {
+  if (!op.check) return KD_OK;
+  int32_t n = 0;
+  hipError_t e = hipMemcpyAsync(&n, op.prep.bad, sizeof n, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(KD_ERR_HIP, std::string("index check: ") + hipGetErrorString(e));
+  if (n > 0)
+    return fail(KD_ERR_INDEX_OUT_OF_RANGE,
+                std::to_string(n) + " cached indices or labels of valid rows lie outside [0, V)");
+  return KD_OK;
+}
+
 kd::TopkRowData row_data(void* ws, const TopkPlan& p) {
   return kd::TopkRowData{at<int2>(ws, p.o_pair), at<uint16_t>(ws, p.o_perm), at<float>(ws, p.o_ent),
                          at<float4>(ws, p.o_rowc)};
@@ -494,8 +521,10 @@ struct Shard {
   float* trow;
 };
 
-kd_status check_shard(int64_t T, int64_t K, int64_t V, int64_t v0) {
+kd_status check_shard(int64_t T, int64_t K, int64_t V, int64_t v0, const kd_topk_opts* o = nullptr) {
   KD_TRY(check_k(T, K, V, false));
+  if (o != nullptr && o->check_indices != 0)
+    return fail(KD_ERR_UNSUPPORTED, "check_indices: a shard does not know the whole head's width");
   if (v0 < 0) return fail(KD_ERR_INVALID_ARG, "v0 must be >= 0");
   if (v0 + V > INT32_MAX / 2) return fail(KD_ERR_UNSUPPORTED, "v0 + V must be below 2^30");
   return KD_OK;
@@ -534,7 +563,7 @@ kd_status topk_fwd(const void* H, const void* W, const int32_t* topk_idx, const 
                    size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
-  KD_TRY(shard ? check_shard(T, K, V, shard->v0) : check_k(T, K, V));
+  KD_TRY(shard ? check_shard(T, K, V, shard->v0, opts) : check_k(T, K, V));
   TopkOpts op;
   KD_TRY(resolve_opts(opts, tau, K, op));
   if (shard) {
@@ -572,7 +601,9 @@ kd_status topk_fwd(const void* H, const void* W, const int32_t* topk_idx, const 
   float* part = at<float>(workspace, p.o_part);
 
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
+  KD_TRY(start_index_check(op, workspace, p, V, st));
   KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, op.KE, op.prep, rd, z_topk, st));
+  KD_TRY(finish_index_check(op, st));
   char* hp = at<char>(workspace, p.o_hp_f);
   kd::TopkFwdArgs a{};
   a.Hp = hp;
@@ -697,7 +728,7 @@ kd_status topk_bwd(const void* H, const void* W, const int32_t* topk_idx, const 
                    int64_t chunk_rows, const Shard* shard, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   KD_TRY(check_common(T, d, V, dt, tau));
-  KD_TRY(shard ? check_shard(T, K, V, shard->v0) : check_k(T, K, V));
+  KD_TRY(shard ? check_shard(T, K, V, shard->v0, opts) : check_k(T, K, V));
   TopkOpts op;
   KD_TRY(resolve_opts(opts, tau, K, op));
   if (shard) {
@@ -733,7 +764,9 @@ kd_status topk_bwd(const void* H, const void* W, const int32_t* topk_idx, const 
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
   const kd::TopkRowData rd = row_data(workspace, p);
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
+  KD_TRY(start_index_check(op, workspace, p, V, st));
   KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, op.KE, op.prep, rd, nullptr, st));
+  KD_TRY(finish_index_check(op, st));
   const int dh_elem = shard ? 4 : elem;
   KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * dh_elem, dH, st));
 
@@ -1333,7 +1366,9 @@ kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* top
   float* dhp = at<float>(workspace, ch.o_dhp);
 
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
+  KD_TRY(start_index_check(op, workspace, p, V, st));
   KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, op.KE, op.prep, rd, z_topk, st));
+  KD_TRY(finish_index_check(op, st));
   KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * elem, dH, st));
   const int64_t nchunks = cdiv(T, ch.C);
   for (int64_t k = 0; k < nchunks; ++k) {

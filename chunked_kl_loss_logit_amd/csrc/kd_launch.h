@@ -32,6 +32,8 @@ struct TopkPrepOpts {
   float beta;                // weight of the cross-entropy term (labels set)
   float c2, inv_tau;         // log2(e) / tau and 1 / tau of the scalar temperature
   int32_t v0, vs;            // columns [v0, v0 + vs) of a vocabulary shard of W (vs = 0: the whole head)
+  int32_t* bad;              // nullable: counts the cached indices and labels of valid rows outside [0, V)
+  int32_t V;                 // the vocabulary size the check uses
 };
 
 struct Compact {
@@ -109,6 +111,8 @@ inline int64_t dz_tail_bytes(int64_t C, int64_t V, int64_t ldz) { return (ldz - 
 hipError_t launch_reduce_dh(const float* part, int S, int64_t C, int64_t d, Compact c, int64_t c0, void* dH,
                             int elem, hipStream_t st);
 hipError_t launch_zero_masked_rows(const uint8_t* mask, int64_t T, int64_t row_bytes, void* out, hipStream_t st);
+// Zeroes `bytes` bytes at p in whole 16-byte units (a remainder below 16 is
+// left as it is): p 16-byte aligned, bytes normally a multiple of 16.
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t st);
 
 // ---------------------------------------------------------------- top-K tiles

@@ -170,6 +170,7 @@ __global__ __launch_bounds__(NT) void topk_prep_kernel(const float* logits, cons
   // sort (index, position) pairs by index; ties keep position order
   for (int j = threadIdx.x; j < KP; j += NT) {
     int32_t v = j < K ? idx[base + j] : (j < KE ? o.labels[t] : 0);
+    if (o.bad && j < KE && (uint32_t)v >= (uint32_t)o.V) atomicAdd(o.bad, 1);  // the check on request
     if (o.vs > 0) {  // a vocabulary shard: local column, or a sentinel past every column
       v -= o.v0;
       v = (uint32_t)v < (uint32_t)o.vs ? v : INT32_MAX;

@@ -63,9 +63,10 @@
  *  - Errors: arguments are checked on the host before any kernel is
  *    enqueued; a failed check returns its status and enqueues nothing.  A
  *    failed launch returns KD_ERR_HIP.  kd_last_error() gives a message for
- *    the last failure on the calling thread.  Index range is not checked on
- *    the device: an index outside [0, V) in a valid row is ignored by the
- *    gather (its teacher probability still counts in the teacher terms).
+ *    the last failure on the calling thread.  Index range is checked on the
+ *    device only on request (kd_topk_opts.check_indices); otherwise an index
+ *    outside [0, V) in a valid row is ignored by the gather (its teacher
+ *    probability still counts in the teacher terms).
  *  - T = 0: the forward calls enqueue nothing; the backward calls set dW to
  *    zero (the gradient of an empty sum) and touch nothing else.
  *  - Deterministic: split reductions run in a fixed order, so the same call
@@ -90,11 +91,15 @@ typedef enum kd_status {
   KD_ERR_UNSUPPORTED = 2,          /* valid but not handled: K > KD_MAX_K, d or V not a multiple of 8/4 */
   KD_ERR_ALIGNMENT = 3,            /* a pointer is not aligned as required */
   KD_ERR_WORKSPACE_TOO_SMALL = 4,  /* workspace_bytes below the size query's answer */
-  KD_ERR_INDEX_OUT_OF_RANGE = 5,   /* reserved for an index check; not returned by the calls below */
+  KD_ERR_INDEX_OUT_OF_RANGE = 5,   /* a cached index or label of a valid row outside [0, V), found by the
+                                      index check that kd_topk_opts.check_indices asks for */
   KD_ERR_HIP = 6                   /* a HIP launch or runtime call failed */
 } kd_status;
 
-typedef enum kd_dtype { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
+/* KD_DTYPE_MAX_ENUM makes every non-negative int a value of the type, so
+ * that a wrong code from a C caller is a value the checks reject
+ * (KD_ERR_INVALID_ARG) rather than an out-of-range enumeration. */
+typedef enum kd_dtype { KD_F32 = 0, KD_BF16 = 1, KD_DTYPE_MAX_ENUM = 0x7fffffff } kd_dtype;
 
 /* ---------------------------------------------------------------- top-K */
 
@@ -189,12 +194,23 @@ kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_i
  * K = KD_MAX_K: KD_ERR_UNSUPPORTED (the label is entry K + 1); misaligned
  * arrays: KD_ERR_ALIGNMENT.  Values are not checked: tau_rows must be
  * finite and > 0 and labels in [0, V) on valid rows (masked rows are never
- * read). */
+ * read).
+ * Index check on request (check_indices != 0): the teacher preparation
+ * counts, on the device, the cached indices (and labels) of valid rows that
+ * lie outside [0, V); the call then waits for that count (one
+ * synchronisation of `stream`) and, if it is not zero, returns
+ * KD_ERR_INDEX_OUT_OF_RANGE without enqueuing anything more: kl, lse,
+ * z_topk, dH and dW are left as they were.  Masked rows are not checked.
+ * Without it an out-of-range index of a valid row matches no vocabulary
+ * column (its probability still counts in the teacher terms).  The shard
+ * calls do not know the whole head's width and reject the flag
+ * (KD_ERR_UNSUPPORTED). */
 typedef struct kd_topk_opts {
   const float* tau_rows;     /* [T] per-token temperature, or NULL */
   const float* teacher_lse;  /* [T] teacher log-normaliser at tau_t (partial mass), or NULL */
   const int32_t* labels;     /* [T] next-token labels of the CE term, or NULL */
   float ce_weight;           /* weight of the CE term in [0, 1]; 0 = distillation only */
+  int32_t check_indices;     /* nonzero: check the index range on the device (see above) */
 } kd_topk_opts;
 
 kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_idx,

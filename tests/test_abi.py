@@ -258,8 +258,28 @@ def fwd_ex(opts, T=8, d=64, V=256, K=4, wsb=0):
                                kdl.KD_BF16, vp(FAKE), vp(FAKE), None, vp(FAKE), wsb, None)
 
 
-def opts(tau_rows=0, teacher_lse=0, labels=0, ce_weight=0.0):
-    return kdl._binding.KdTopkOpts(tau_rows or None, teacher_lse or None, labels or None, ce_weight)
+def opts(tau_rows=0, teacher_lse=0, labels=0, ce_weight=0.0, check=0):
+    return kdl._binding.KdTopkOpts(tau_rows or None, teacher_lse or None, labels or None, ce_weight, check)
+
+
+def test_topk_opts_layout_matches_the_header(L):
+    # three pointers, the CE weight and the index-check flag
+    assert ctypes.sizeof(kdl._binding.KdTopkOpts) == 32
+    assert kdl._binding.KdTopkOpts.check_indices.offset == 28
+
+
+def test_index_check_is_an_option_of_the_whole_head_only(L):
+    # a valid request reaches the workspace check (nothing is enqueued before it)
+    assert fwd_ex(opts(check=1)) == 4
+    # a shard does not know the whole head's width
+    vp = ctypes.c_void_p
+    o = ctypes.byref(opts(check=1))
+    assert L.kd_topk_kl_fwd_shard(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), o, 8, 64, 256,
+                                  512, 4, kdl.KD_BF16, vp(FAKE), vp(FAKE), None, vp(FAKE), 0, None) == 2
+    assert "check_indices" in last_error()
+    assert L.kd_topk_kl_bwd_shard(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), o, 8, 64, 256,
+                                  512, 4, kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 0, vp(FAKE), 0,
+                                  None) == 2
 
 
 @pytest.mark.parametrize("o,code", [
