@@ -283,6 +283,8 @@ struct DmaNN {
         });
   }
 
+  // kT: the accumulators hold the transposed tile (mma_frags_t)
+  template <bool kT = false>
   __device__ inline void tile(const Slots& sl, long n0, f32x16_t (&acc)[4][BN / 64]) {
     if (b_prows)
       b.init_panels(B, n0, N - n0, b_prows);
@@ -296,7 +298,12 @@ struct DmaNN {
           b.issue(s, db);
         },
         [&](const char* slot, FragsNN<BN>& f) { rd.read_nn(slot, f); },
-        [&](const FragsNN<BN>& f) { mma_frags(f, acc); });
+        [&](const FragsNN<BN>& f) {
+          if constexpr (kT)
+            mma_frags_t(f, acc);
+          else
+            mma_frags(f, acc);
+        });
   }
 };
 
