@@ -324,27 +324,57 @@ __device__ inline void store_block(StPair st, char* dst, long ld, long row0, lon
   }
 }
 
-// Float32 destination: store (or add to) a staged [256][32] block, rows
-// [max(row0, rlo), min(row0 + 256, nrows)).
-__device__ inline void rmw_block_f32(StPair st, float* dst, long ld, long row0, long col0, long nrows,
-                                     long ncols, bool accumulate, long rlo = 0) {
+// Float32 destination: store (or add to) two staged [256][32] blocks, st0 at
+// columns [col0, col0 + 32) and st1 at [col1, col1 + 32), rows [row0,
+// min(row0 + 256, nrows)).  A thread owns one float4 chunk of every 32nd
+// row.  Adding issues all of the thread's loads of both blocks first and
+// waits once, so the read-modify-write costs one memory round trip per
+// round instead of one per row (vector-memory counters complete in order,
+// so a wait for a load also waits for every earlier store).
+__device__ inline void rmw_pair_f32(StPair st0, StPair st1, float* dst, long ld, long row0, long col0, long col1,
+                                    long nrows, long ncols, bool accumulate) {
+  constexpr int kRowsPer = kBM / (kThreads / 8);  // rows per thread and block
   const int tid = opaque((int)threadIdx.x);
   const int q = tid & 7;  // float4 chunk of the row
-  const long col = col0 + 4 * q;
-  if (col >= ncols) return;
-  for (int r = tid >> 3; r < kBM; r += kThreads / 8) {
-    if (row0 + r >= nrows) break;
-    if (row0 + r < rlo) continue;
-    float4 v = st_read4(st, r, q);
-    float4* p = reinterpret_cast<float4*>(dst + (row0 + r) * ld + col);
-    if (accumulate) {
-      const float4 o = *p;
-      v.x += o.x;
-      v.y += o.y;
-      v.z += o.z;
-      v.w += o.w;
+  const int rt = tid >> 3;
+  const long ca = col0 + 4 * q, cb = col1 + 4 * q;
+  const bool oka = ca < ncols, okb = cb < ncols;
+  if (!accumulate) {
+    for (int r = rt; r < kBM; r += kThreads / 8) {
+      if (row0 + r >= nrows) break;
+      if (oka) *reinterpret_cast<float4*>(dst + (row0 + r) * ld + ca) = st_read4(st0, r, q);
+      if (okb) *reinterpret_cast<float4*>(dst + (row0 + r) * ld + cb) = st_read4(st1, r, q);
     }
-    *p = v;
+    return;
+  }
+  float4 oa[kRowsPer], ob[kRowsPer];
+#pragma unroll
+  for (int it = 0; it < kRowsPer; ++it) {
+    const long r = row0 + rt + it * (kThreads / 8);
+    const bool rv = r < nrows;
+    oa[it] = rv && oka ? *reinterpret_cast<const float4*>(dst + r * ld + ca) : make_float4(0.f, 0.f, 0.f, 0.f);
+    ob[it] = rv && okb ? *reinterpret_cast<const float4*>(dst + r * ld + cb) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int it = 0; it < kRowsPer; ++it) {
+    const int r = rt + it * (kThreads / 8);
+    if (row0 + r >= nrows) break;
+    if (oka) {
+      float4 v = st_read4(st0, r, q);
+      v.x += oa[it].x;
+      v.y += oa[it].y;
+      v.z += oa[it].z;
+      v.w += oa[it].w;
+      *reinterpret_cast<float4*>(dst + (row0 + r) * ld + ca) = v;
+    }
+    if (okb) {
+      float4 v = st_read4(st1, r, q);
+      v.x += ob[it].x;
+      v.y += ob[it].y;
+      v.z += ob[it].z;
+      v.w += ob[it].w;
+      *reinterpret_cast<float4*>(dst + (row0 + r) * ld + cb) = v;
+    }
   }
 }
 

@@ -29,8 +29,7 @@ __device__ inline void f32_round(const Slots& sl, const f32x16_t (&acc)[4][4], f
   const StPair s0 = st_pair<0>(sl), s1 = st_pair<1>(sl);
   stage_block<NBI, 4>(s0, s1, acc);
   __syncthreads();
-  rmw_block_f32(s0, dst, ld, row0, n0 + NBI * 32, nrows, ncols, accumulate);
-  rmw_block_f32(s1, dst, ld, row0, n0 + 128 + NBI * 32, nrows, ncols, accumulate);
+  rmw_pair_f32(s0, s1, dst, ld, row0, n0 + NBI * 32, n0 + 128 + NBI * 32, nrows, ncols, accumulate);
   __syncthreads();
 }
 
