@@ -54,9 +54,19 @@ constexpr int kDmaKMult = kRing * kDmaKs;  // the contraction length must be a m
 // its address from registers that are rewritten while it is in flight makes
 // the compiler wait for every outstanding load first; loop-invariant offset
 // registers avoid that.  Operands must therefore span less than 4 GiB.
+// `base` must be the same in every lane.  It is read from the first active
+// lane, so the compiler keeps the descriptor in scalar registers even where
+// it cannot prove the pointer uniform; otherwise it wraps every load that
+// uses the descriptor in a loop over the distinct values.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const char* base) {
+  // the builtin takes and returns int: widen through uint32_t, or a low
+  // half with bit 31 set would be sign-extended over the high half
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  const uint64_t u = (uint64_t)lo | ((uint64_t)hi << 32);
   // raw buffer, no stride, full 32-bit range, gfx9 data format dword
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)0xffffffff, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(u), (short)0, (int)0xffffffff, 0x00020000);
 }
 
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, char* lds_wave_base) {

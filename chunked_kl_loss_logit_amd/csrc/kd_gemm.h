@@ -339,12 +339,17 @@ __device__ inline void rmw_pair_f32(StPair st0, StPair st1, float* dst, long ld,
   const int rt = tid >> 3;
   const long ca = col0 + 4 * q, cb = col1 + 4 * q;
   const bool oka = ca < ncols, okb = cb < ncols;
-  if (!accumulate) {
-    for (int r = rt; r < kBM; r += kThreads / 8) {
-      if (row0 + r >= nrows) break;
-      if (oka) *reinterpret_cast<float4*>(dst + (row0 + r) * ld + ca) = st_read4(st0, r, q);
-      if (okb) *reinterpret_cast<float4*>(dst + (row0 + r) * ld + cb) = st_read4(st1, r, q);
-    }
+  if (!accumulate) {  // one block after the other
+    if (oka)
+      for (int r = rt; r < kBM; r += kThreads / 8) {
+        if (row0 + r >= nrows) break;
+        *reinterpret_cast<float4*>(dst + (row0 + r) * ld + ca) = st_read4(st0, r, q);
+      }
+    if (okb)
+      for (int r = rt; r < kBM; r += kThreads / 8) {
+        if (row0 + r >= nrows) break;
+        *reinterpret_cast<float4*>(dst + (row0 + r) * ld + cb) = st_read4(st1, r, q);
+      }
     return;
   }
   float4 oa[kRowsPer], ob[kRowsPer];
