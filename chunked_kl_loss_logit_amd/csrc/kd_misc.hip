@@ -529,10 +529,44 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(const U* H, long 
   }
 }
 
+// The same for bf16 when d and C are multiples of 64, 16 bytes per access:
+// a thread loads 8 consecutive hidden values of a row and stores 8
+// consecutive rows of one hidden index (16 bytes of one 64-byte piece), so a
+// wave's store covers two contiguous 512-byte runs of the panels.
+__global__ __launch_bounds__(256) void gather_transpose16_kernel(const uint16_t* H, long d, Compact c, long c0, long C,
+                                                                uint16_t* out) {
+  constexpr int kLd = 72;  // row stride of the LDS tile in elements (16-byte aligned rows)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kLd];
+  const long M = min(C, (long)*c.count - c0);
+  const long i0 = (long)blockIdx.x * 64, j0 = (long)blockIdx.y * 64;
+  const int t = threadIdx.x, q = t & 7;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int ii = (t >> 3) + 32 * r;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (i0 + ii < M) v = *reinterpret_cast<const u32x4_t*>(H + (long)c.rows[c0 + i0 + ii] * d + j0 + 8 * q);
+    *reinterpret_cast<u32x4_t*>(tile + ii * kLd + 8 * q) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int jj = (t >> 3) + 32 * r;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[(8 * q + 2 * e) * kLd + jj] | ((uint32_t)tile[(8 * q + 2 * e + 1) * kLd + jj] << 16);
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(out) + panel_off(d, j0 + jj, (i0 + 8 * q) * 2)) =
+        u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
 hipError_t launch_gather_transpose(const void* H, int elem, int64_t d, Compact c, int64_t c0, int64_t C, void* out,
                                    hipStream_t st) {
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((d + 63) / 64));
-  if (elem == 2)
+  if (elem == 2 && d % 64 == 0 && C % 64 == 0)
+    hipLaunchKernelGGL(gather_transpose16_kernel, grid, dim3(256), 0, st, (const uint16_t*)H, (long)d, c, (long)c0,
+                       (long)C, (uint16_t*)out);
+  else if (elem == 2)
     hipLaunchKernelGGL(gather_transpose_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)H, (long)d, c,
                        (long)c0, (long)C, (uint16_t*)out);
   else
