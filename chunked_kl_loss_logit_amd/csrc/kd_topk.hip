@@ -813,6 +813,9 @@ __global__ __launch_bounds__(256) void topk_dz_from_z_kernel(TopkDzFromZArgs a) 
     c = lower_bound(a.rd.pair, (int)(t * a.K), ce, pb * PC);
   }
   const float* zr = a.z + i * a.ldz;
+  // the row's next cached entry, kept in registers between pieces (most
+  // pieces hold none of the row's K entries)
+  int2 nx = rv && c < ce ? a.rd.pair[c] : make_int2(INT_MAX, 0);
   for (long p = pb; p < pe; ++p) {
     const long v0 = p * PC + sub * EPT;
     if (v0 >= a.V) break;
@@ -826,12 +829,13 @@ __global__ __launch_bounds__(256) void topk_dz_from_z_kernel(TopkDzFromZArgs a) 
         o[e + 2] = gs * fast_exp2(fmaf(z4.z, c2, -L2));
         o[e + 3] = gs * fast_exp2(fmaf(z4.w, c2, -L2));
       }
-      for (; c < ce; ++c) {
-        const int2 pr = a.rd.pair[c];
-        if ((long)pr.x >= v0 + EPT) break;
-        if ((long)pr.x < v0) continue;  // another thread's columns
+      while ((long)nx.x < v0 + EPT) {  // entries below v0 are another thread's columns
+        if ((long)nx.x >= v0) {
 #pragma unroll
-        for (int q = 0; q < EPT; ++q) o[q] = (long)pr.x == v0 + q ? o[q] - gs * __int_as_float(pr.y) : o[q];
+          for (int q = 0; q < EPT; ++q) o[q] = (long)nx.x == v0 + q ? o[q] - gs * __int_as_float(nx.y) : o[q];
+        }
+        ++c;
+        nx = c < ce ? a.rd.pair[c] : make_int2(INT_MAX, 0);
       }
     } else {
 #pragma unroll
