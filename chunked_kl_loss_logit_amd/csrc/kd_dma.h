@@ -219,6 +219,29 @@ __device__ inline void mma_frags_t(const Frags<NB, NDS>& f, f32x16_t (&acc)[4][N
       for (int nb = 0; nb < NB; ++nb) Bf16::mma(acc[mb][nb], f.b[kg][nb], f.a[kg][mb]);
 }
 
+// The first stage of a tile: k-group 0 starts every accumulator afresh.
+template <bool kT, int NB, int NDS>
+__device__ inline void mma_frags_first(const Frags<NB, NDS>& f, f32x16_t (&acc)[4][NB]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if constexpr (kT)
+        Bf16::mma0(acc[mb][nb], f.b[0][nb], f.a[0][mb]);
+      else
+        Bf16::mma0(acc[mb][nb], f.a[0][mb], f.b[0][nb]);
+    }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if constexpr (kT)
+        Bf16::mma(acc[mb][nb], f.b[1][nb], f.a[1][mb]);
+      else
+        Bf16::mma(acc[mb][nb], f.a[1][mb], f.b[1][nb]);
+    }
+}
+
 template <int BN>
 using FragsNN = Frags<BN / 64, 2 * (4 + 2 * (BN / 64))>;  // b128 A reads, two transposing reads per B
 
@@ -392,14 +415,15 @@ __device__ inline void run_step(const Slots& sl, long it, int is, Frag& cur, Fra
 // through one ring that never drains between tiles: the last four steps of
 // tile t issue the first four stages of tile t + 1, and while `done(t)`
 // consumes the accumulators the loads keep landing.  `issue(t, s, A, B)`,
-// `read` and `mma` are as in ring_contract.  done(t) runs after the last
-// multiply of tile t, on every wave; it may use the epilogue array and
-// ring_barrier(), but not the slots, and must not wait for vector memory
-// (__syncthreads would).  Loads and stores it issues only make the next
-// step's wait longer.
-template <int LPW, class Frag, class Issue, class Read, class Mma, class Done>
+// `read` and `mma` are as in ring_contract; `mma0` multiplies a tile's first
+// stage into fresh accumulators (so they need no clearing between tiles).
+// done(t) runs after the last multiply of tile t, on every wave; it may use
+// the epilogue array and ring_barrier(), but not the slots, and must not
+// wait for vector memory (__syncthreads would).  Loads and stores it issues
+// only make the next step's wait longer.
+template <int LPW, class Frag, class Issue, class Read, class Mma, class Mma0, class Done>
 __device__ inline void ring_run(const Slots& sl, int ntiles, int nst, Issue&& issue, Read&& read, Mma&& mma,
-                                Done&& done) {
+                                Mma0&& mma0, Done&& done) {
   static_assert(LPW * kRing < 64, "vmcnt range");
   wait_vm<0>();
   __syncthreads();
@@ -413,17 +437,25 @@ __device__ inline void ring_run(const Slots& sl, int ntiles, int nst, Issue&& is
     ring_barrier();
     read(static_cast<const char*>(sl.A<0>()), f0);
     for (int t = 0; t < ntiles; ++t) {
-      for (int s = 0; s + kRing < nst; s += kRing) {
-        run_step<0, LPW, true>(sl, t, s + 4, f0, f1, issue, read, mma);
-        run_step<1, LPW, true>(sl, t, s + 5, f1, f0, issue, read, mma);
-        run_step<2, LPW, true>(sl, t, s + 6, f0, f1, issue, read, mma);
-        run_step<3, LPW, true>(sl, t, s + 7, f1, f0, issue, read, mma);
-      }
-      // last four stages: issue the next tile's first four (after the last
-      // tile, this tile's last stage again, into slots nobody reads)
       const bool more = t + 1 < ntiles;
       const long tn = more ? t + 1 : t;
-      run_step<0, LPW, true>(sl, tn, more ? 0 : nst - 1, f0, f1, issue, read, mma);
+      if (nst > kRing) {
+        run_step<0, LPW, true>(sl, t, 4, f0, f1, issue, read, mma0);
+        run_step<1, LPW, true>(sl, t, 5, f1, f0, issue, read, mma);
+        run_step<2, LPW, true>(sl, t, 6, f0, f1, issue, read, mma);
+        run_step<3, LPW, true>(sl, t, 7, f1, f0, issue, read, mma);
+        for (int s = kRing; s + kRing < nst; s += kRing) {
+          run_step<0, LPW, true>(sl, t, s + 4, f0, f1, issue, read, mma);
+          run_step<1, LPW, true>(sl, t, s + 5, f1, f0, issue, read, mma);
+          run_step<2, LPW, true>(sl, t, s + 6, f0, f1, issue, read, mma);
+          run_step<3, LPW, true>(sl, t, s + 7, f1, f0, issue, read, mma);
+        }
+        // last four stages: issue the next tile's first four (after the last
+        // tile, this tile's last stage again, into slots nobody reads)
+        run_step<0, LPW, true>(sl, tn, more ? 0 : nst - 1, f0, f1, issue, read, mma);
+      } else {
+        run_step<0, LPW, true>(sl, tn, more ? 0 : nst - 1, f0, f1, issue, read, mma0);
+      }
       run_step<1, LPW, true>(sl, tn, more ? 1 : nst - 1, f1, f0, issue, read, mma);
       run_step<2, LPW, true>(sl, tn, more ? 2 : nst - 1, f0, f1, issue, read, mma);
       run_step<3, LPW, false>(sl, tn, more ? 3 : nst - 1, f1, f0, issue, read, mma);

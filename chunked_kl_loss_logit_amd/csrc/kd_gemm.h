@@ -42,6 +42,12 @@ struct Bf16 {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
   }
+  // the same product into a fresh accumulator (the instruction's C operand
+  // is the constant 0, so nothing has to clear the accumulator first)
+  __device__ static inline void mma0(f32x16_t& acc, u32x4_t a, u32x4_t b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), f32x16_t{}, 0, 0, 0);
+  }
   // float -> bf16 bits, round to nearest even (NaN stays NaN)
   __device__ static inline uint32_t pack2(float lo, float hi) { return cvt(lo) | (cvt(hi) << 16); }
   __device__ static inline uint32_t cvt(float f) {

@@ -262,7 +262,6 @@ struct DmaNN {
   __device__ inline void run(const Slots& sl, int ntiles, At&& at, Done&& done) {
     b.init(B, LONG_MAX);
     f32x16_t acc[4][BN / 64];
-    zero_acc<BN / 64>(acc);
     ring_run<kLpw, FragsNN<BN>>(
         sl, ntiles, nst,
         [&](long t, int s, char* da, char* db) {
@@ -277,10 +276,7 @@ struct DmaNN {
           else
             mma_frags(f, acc);
         },
-        [&](int t) {
-          done(t, acc);
-          zero_acc<BN / 64>(acc);
-        });
+        [&](const FragsNN<BN>& f) { mma_frags_first<kT>(f, acc); }, [&](int t) { done(t, acc); });
   }
 
   // kT: the accumulators hold the transposed tile (mma_frags_t)
