@@ -42,6 +42,14 @@ design notes of this repository):
     (1 - beta) KD + beta CE.
   * KL mixing (full vocabulary): (1 - r) KL(p || q) + r KL(q || p), both at
     the row's temperature.
+  * KL mixing (top-K): the reverse direction needs the teacher wherever the
+    student has mass, and outside the K cached entries the teacher is unknown.
+    Both sides are therefore restricted to the cached entries and renormalised
+    there: q~ = softmax over the K entries of s[I_tk], p^ = softmax(A_t / tau_t)
+    (the cached probabilities renormalised, also with a partial mass), each
+    entry its own outcome (a duplicated index counts once per entry), and
+        RKL_t = sum_k q~_k (log q~_k - log p^_k),
+        loss_t = (1 - beta) [(1 - r) KD_t + r RKL_t] + beta CE_t.
   * Both teacher and student logits are divided by tau; there is no tau^2.
   * The output is per token; the caller reduces.  ``g`` is dLoss/dKL_t.
   * mask[t] == 1 marks a valid row.  Masked rows give KL = 0, lse = 0,
@@ -232,7 +240,7 @@ def _loss_block(H, W, A, rb, taus, tlse):
 
 
 def topk_loss_forward(H, W, I, A, mask, tau, tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0,
-                      row_block=64):
+                      rev_weight=0.0, row_block=64):
     """Per-token top-K distillation loss with the optional parts of the method.
 
     For a valid row t, with tau_t the row's temperature ([AKD]; tau when
@@ -242,6 +250,8 @@ def topk_loss_forward(H, W, I, A, mask, tau, tau_rows=None, teacher_lse=None, la
         KD_t = sum_k p_k log p_k - sum_k p_k s[I_tk] + m_t L_t
     (teacher-entropy, cross and mass terms; only L_t needs the vocabulary).
     With labels y ([TS]):  CE_t = L_t - s[y_t],  loss_t = (1 - beta) KD_t + beta CE_t.
+    With r = rev_weight > 0 ([KLD], KL mixing restricted to the cached
+    entries, _support_reverse): KD_t is replaced by (1 - r) KD_t + r RKL_t.
     Returns (loss [T], lse [T] = L_t, z_topk [T, K])."""
     H, W, A = as_f64(H), as_f64(W), as_f64(A)
     I = np.asarray(I.cpu().numpy() if hasattr(I, "cpu") else I, dtype=np.int64)
@@ -251,6 +261,7 @@ def topk_loss_forward(H, W, I, A, mask, tau, tau_rows=None, teacher_lse=None, la
     y = None if labels is None else np.asarray(labels.cpu().numpy() if hasattr(labels, "cpu") else labels,
                                                dtype=np.int64)
     beta = float(ce_weight)
+    r = float(rev_weight)
     valid = _valid_rows(mask, T)
     loss, lse, ztk = np.zeros(T), np.zeros(T), np.zeros((T, K))
     rows = np.nonzero(valid)[0]
@@ -259,6 +270,9 @@ def topk_loss_forward(H, W, I, A, mask, tau, tau_rows=None, teacher_lse=None, la
         z, s, L, p, logp, m = _loss_block(H, W, A, rb, taus, tlse)
         s_at = np.take_along_axis(s, I[rb], axis=1)
         kd = (p * logp).sum(axis=1) - (p * s_at).sum(axis=1) + m * L
+        if r != 0.0:
+            rkl, _ = _support_reverse(s_at, A[rb] / taus[rb][:, None])
+            kd = (1.0 - r) * kd + r * rkl
         if y is not None and beta != 0.0:
             ce = L - s[np.arange(rb.size), y[rb]]
             loss[rb] = (1.0 - beta) * kd + beta * ce
@@ -267,6 +281,21 @@ def topk_loss_forward(H, W, I, A, mask, tau, tau_rows=None, teacher_lse=None, la
         lse[rb] = L
         ztk[rb] = np.take_along_axis(z, I[rb], axis=1)
     return loss, lse, ztk
+
+
+def _support_reverse(a, b):
+    """Reverse KL over the K cached entries ([KLD] reverse token-level KL, on
+    the support where the teacher is known): a [n, K] the student's scaled
+    logits at the entries, b [n, K] the teacher's A / tau.  With
+    q~ = softmax(a) and p^ = softmax(b) over the K entries,
+        RKL = sum_k q~_k (log q~_k - log p^_k),
+        dRKL/da_k = q~_k (log q~_k - log p^_k - RKL).
+    Returns (RKL [n], dRKL/da [n, K])."""
+    lq = a - logsumexp_rows(a)[:, None]
+    lp = b - logsumexp_rows(b)[:, None]
+    q = np.exp(lq)
+    rkl = (q * (lq - lp)).sum(axis=1)
+    return rkl, q * (lq - lp - rkl[:, None])
 
 
 def _loss_dz(s, L, I_rows, p, m, y_rows, beta, g_rows, tau_rows):
@@ -284,10 +313,13 @@ def _loss_dz(s, L, I_rows, p, m, y_rows, beta, g_rows, tau_rows):
 
 
 def topk_loss_backward(H, W, I, A, mask, tau, g, tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0,
-                       row_block=64, v_panel=16384, want_dw=True):
+                       rev_weight=0.0, row_block=64, v_panel=16384, want_dw=True):
     """Gradients of sum_t g_t loss_t (topk_loss_forward) w.r.t. H and W:
     dZ_t as in _loss_dz, dH = dZ W^T, dW = H^T dZ, masked rows contribute
-    nothing.  Returns (dH [T, d], dW [d, V] or None without want_dw)."""
+    nothing.  With r = rev_weight > 0 the forward-KL part is weighted 1 - r
+    (p and m scaled, the dZ being linear in both) and the reverse part adds
+    (g_t / tau_t)(1 - beta) r dRKL/da_k at column I_tk (scatter-add).
+    Returns (dH [T, d], dW [d, V] or None without want_dw)."""
     H, W, A, g = as_f64(H), as_f64(W), as_f64(A), as_f64(g)
     I = np.asarray(I.cpu().numpy() if hasattr(I, "cpu") else I, dtype=np.int64)
     T, d = H.shape
@@ -297,13 +329,21 @@ def topk_loss_backward(H, W, I, A, mask, tau, g, tau_rows=None, teacher_lse=None
     y = None if labels is None else np.asarray(labels.cpu().numpy() if hasattr(labels, "cpu") else labels,
                                                dtype=np.int64)
     beta = float(ce_weight)
+    r = float(rev_weight)
     valid = _valid_rows(mask, T)
     dH, dW = np.zeros((T, d)), (np.zeros((d, V)) if want_dw else None)
     rows = np.nonzero(valid)[0]
     for r0 in range(0, rows.size, row_block):
         rb = rows[r0:r0 + row_block]
         _, s, L, p, _, m = _loss_block(H, W, A, rb, taus, tlse)
-        D = _loss_dz(s, L, I[rb], p, m, None if y is None else y[rb], beta, g[rb], taus[rb])
+        D = _loss_dz(s, L, I[rb], (1.0 - r) * p, (1.0 - r) * m, None if y is None else y[rb], beta, g[rb],
+                     taus[rb])
+        if r != 0.0:
+            _, da = _support_reverse(np.take_along_axis(s, I[rb], axis=1), A[rb] / taus[rb][:, None])
+            wr = r * (1.0 - beta if y is not None else 1.0) * g[rb] / taus[rb]
+            n = rb.size
+            np.add.at(D, (np.repeat(np.arange(n), I.shape[1]), I[rb].reshape(-1)),
+                      (da * wr[:, None]).reshape(-1))  # duplicates add
         dH[rb] = D @ W.T
         if want_dw:
             for v0 in range(0, V, v_panel):
@@ -311,13 +351,14 @@ def topk_loss_backward(H, W, I, A, mask, tau, g, tau_rows=None, teacher_lse=None
     return dH, dW
 
 
-def topk_loss_rows(H, W, I, A, mask, tau, g, rows, tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0):
+def topk_loss_rows(H, W, I, A, mask, tau, g, rows, tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0,
+                   rev_weight=0.0):
     """loss, lse, z_topk and dH of topk_loss_* for selected rows only."""
     rows = np.asarray(rows, dtype=np.int64)
     Hr, Ir, Ar = as_f64(_take_rows(H, rows)), _take_rows(I, rows), _take_rows(A, rows)
     mr, gr = _take_rows(mask, rows), _take_rows(g, rows)
     kw = dict(tau_rows=_take_rows(tau_rows, rows), teacher_lse=_take_rows(teacher_lse, rows),
-              labels=_take_rows(labels, rows), ce_weight=ce_weight)
+              labels=_take_rows(labels, rows), ce_weight=ce_weight, rev_weight=rev_weight)
     W = as_f64(W)
     loss, lse, ztk = topk_loss_forward(Hr, W, Ir, Ar, mr, tau, **kw)
     dH, _ = topk_loss_backward(Hr, W, Ir, Ar, mr, tau, gr, want_dw=False, **kw)

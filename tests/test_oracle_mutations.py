@@ -31,6 +31,9 @@ PINS = [
     Q.test_full_reverse_kl_is_torch_kl_div_swapped, Q.test_full_kl_mixing_is_the_convex_combination,
     Q.test_full_per_token_tau_is_row_scaling, Q.test_full_mixed_gradient_matches_torch_autograd,
     Q.test_full_mixed_finite_differences_and_mask,
+    Q.test_topk_reverse_with_every_entry_is_the_full_vocab_reverse, Q.test_topk_reverse_is_torch_kl_div_on_the_support,
+    Q.test_topk_mixed_gradient_matches_torch_autograd, Q.test_topk_reverse_finite_differences,
+    Q.test_topk_reverse_zero_when_student_matches_teacher_on_support,
     lambda: S.test_partition_gives_the_unsharded_loss("plain", False),
     lambda: S.test_partition_gives_the_unsharded_loss("every", True),
     S.test_whole_head_as_one_shard, S.test_terms_against_scipy_and_the_dense_teacher,
@@ -251,7 +254,57 @@ def _full_shard_tau_rows_ignored(*args, tau_rows=None, **kw):
 def _full_shard_bwd_no_mixing(*args, rev_weight=0.0, **kw):
     return _ORIG_FULL_SHARD_BWD(*args, **kw)
 
+_ORIG_SUPPORT_REV = O._support_reverse
+_ORIG_LOSS_BWD = O.topk_loss_backward
+
+
+def _support_rev_no_baseline(a, b):
+    lq = a - O.logsumexp_rows(a)[:, None]
+    lp = b - O.logsumexp_rows(b)[:, None]
+    q = np.exp(lq)
+    return (q * (lq - lp)).sum(axis=1), q * (lq - lp)  # the -RKL baseline dropped
+
+
+def _support_rev_teacher_unnormalised(a, b):
+    lq = a - O.logsumexp_rows(a)[:, None]
+    q = np.exp(lq)
+    rkl = (q * (lq - b)).sum(axis=1)  # A / tau taken as log p^ without renormalising
+    return rkl, q * (lq - b - rkl[:, None])
+
+
+def _support_rev_direction_swapped(a, b):
+    return _ORIG_SUPPORT_REV(b, a)[0], _ORIG_SUPPORT_REV(a, b)[1]  # KL(p^ || q~) in the forward
+
+
+def _support_rev_student_unnormalised(a, b):
+    lp = b - O.logsumexp_rows(b)[:, None]
+    q = np.exp(a - O.logsumexp_rows(a)[:, None])
+    rkl = (q * (a - lp)).sum(axis=1)  # log q~ without its log-normaliser
+    return rkl, q * (a - lp - rkl[:, None])
+
+
+def _loss_fwd_rev_swapped(*args, rev_weight=0.0, **kw):
+    return _ORIG_LOSS_FWD(*args, rev_weight=1.0 - rev_weight if rev_weight else 0.0, **kw)
+
+
+def _loss_bwd_rev_ignores_ce(*args, labels=None, ce_weight=0.0, rev_weight=0.0, **kw):
+    # the reverse part's gradient taken at full weight r, not (1 - beta) r
+    dH, dW = _ORIG_LOSS_BWD(*args, labels=labels, ce_weight=ce_weight, rev_weight=rev_weight, **kw)
+    if labels is None or ce_weight == 0.0 or rev_weight == 0.0:
+        return dH, dW
+    a = _ORIG_LOSS_BWD(*args, labels=labels, ce_weight=ce_weight, rev_weight=0.0, **kw)
+    b = _ORIG_LOSS_BWD(*args, labels=labels, ce_weight=ce_weight, rev_weight=rev_weight, **kw)
+    k = 1.0 / (1.0 - ce_weight)
+    return tuple(None if x is None else x0 + k * (x1 - x0) for x, x0, x1 in zip((dH, dW), a, b))
+
+
 MUTATIONS = {
+    "topk_reverse_baseline_dropped": ("_support_reverse", _support_rev_no_baseline),
+    "topk_reverse_teacher_unnormalised": ("_support_reverse", _support_rev_teacher_unnormalised),
+    "topk_reverse_direction_swapped": ("_support_reverse", _support_rev_direction_swapped),
+    "topk_reverse_student_unnormalised": ("_support_reverse", _support_rev_student_unnormalised),
+    "topk_reverse_mix_weights_swapped": ("topk_loss_forward", _loss_fwd_rev_swapped),
+    "topk_reverse_gradient_ignores_ce_weight": ("topk_loss_backward", _loss_bwd_rev_ignores_ce),
     "shard_indices_not_shifted": ("topk_shard_terms", _shard_terms_unshifted),
     "shard_ce_term_ignored": ("topk_shard_terms", _shard_terms_ce_ignored),
     "shard_entropy_unweighted": ("topk_shard_terms", _shard_terms_entropy_unweighted),

@@ -1,5 +1,6 @@
 """Pins of the oracle's general top-K loss (``topk_loss_*``): the partial-mass
-teacher, per-token temperature and the LM cross-entropy mix.  CPU only.
+teacher, per-token temperature, the LM cross-entropy mix and KL mixing over the
+cached entries; and of the full-vocabulary KL mixing.  CPU only.
 
 Sources: "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits and a
 Fused Chunked KL Loss", §3 "Offline distillation" (cached probabilities keep
@@ -7,7 +8,8 @@ their unnormalised partial mass; teacher-entropy, cross and mass terms over
 the support, plus the one full-vocabulary log Z) and "Offline
 implementations" (the dense reconstruction is the correctness baseline); the
 adaptive-distillation abstract on the WASD page (per-token temperature); the
-teacher-strength abstract (mixing the LM and KD losses).  Every pin checks the
+teacher-strength abstract (mixing the LM and KD losses); the KL-direction
+abstract (forward and reverse token-level KL and their mixture).  Every pin checks the
 oracle against something other than its own formula: a library routine, an
 identity that relates it to the already pinned renormalised oracle, autograd
 of the dense reconstruction, or finite differences.
@@ -223,13 +225,157 @@ def test_masked_rows_ignore_garbage_options():
 def test_rows_helper_matches_full_functions():
     H, W, I, A, g, taus, y = case(T=9, seed=19)
     tl, _ = teacher_lse_for_mass(A, taus, np.random.default_rng(20))
-    kw = dict(tau_rows=taus, teacher_lse=tl, labels=y, ce_weight=0.3)
+    kw = dict(tau_rows=taus, teacher_lse=tl, labels=y, ce_weight=0.3, rev_weight=0.4)
     v, lse, z = O.topk_loss_forward(H, W, I, A, None, 1.0, **kw)
     dH, _ = O.topk_loss_backward(H, W, I, A, None, 1.0, g, **kw)
     rows = [0, 4, 8]
     rv, rl, rz, rdH = O.topk_loss_rows(H, W, I, A, None, 1.0, g, rows, **kw)
     np.testing.assert_allclose(rv, v[rows], rtol=1e-14)
     np.testing.assert_allclose(rdH, dH[rows], rtol=1e-13, atol=1e-16)
+
+
+# ---------------------------------------------------------------- top-K: KL mixing over the cached entries
+def _torch_support_kls(H, W, I, A, taus):
+    """Forward and reverse KL between the student and the teacher restricted
+    to the K cached entries and renormalised there, with torch's kl_div."""
+    tau = torch.tensor(taus)[:, None]
+    a = torch.gather(torch.tensor(H @ W) / tau, 1, torch.tensor(I))
+    logq = torch.log_softmax(a, dim=1)
+    logp = torch.log_softmax(torch.tensor(A) / tau, dim=1)
+    rev = torch.nn.functional.kl_div(logp, logq, log_target=True, reduction="none").sum(1).numpy()
+    fwd = torch.nn.functional.kl_div(logq, logp, log_target=True, reduction="none").sum(1).numpy()
+    return fwd, rev
+
+
+def test_topk_reverse_with_every_entry_is_the_full_vocab_reverse():
+    # K = V (a permutation of the vocabulary per row): the cached entries are
+    # the whole vocabulary, so the mixed top-K loss and its gradient must be
+    # the full-vocabulary mixed loss of a teacher whose logits are U (teacher
+    # head = identity, its hidden state = U), itself pinned to torch above
+    rng = np.random.default_rng(40)
+    T, d, V = 5, 7, 18
+    H = rng.standard_normal((T, d))
+    W = rng.standard_normal((d, V)) / np.sqrt(d)
+    U = rng.standard_normal((T, V)) * 1.8
+    I = np.stack([rng.permutation(V) for _ in range(T)])
+    A = np.take_along_axis(U, I, axis=1)
+    g = rng.standard_normal(T)
+    taus = rng.uniform(0.7, 2.0, T)
+    for r in (0.0, 0.35, 1.0):
+        got = O.topk_loss_forward(H, W, I, A, None, 1.0, tau_rows=taus, rev_weight=r)
+        want = O.full_loss_forward(H, W, U, np.eye(V), None, 1.0, tau_rows=taus, rev_weight=r)
+        np.testing.assert_allclose(got[0], want[0], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(got[1], want[1], rtol=1e-13)
+        dH, dW = O.topk_loss_backward(H, W, I, A, None, 1.0, g, tau_rows=taus, rev_weight=r)
+        fH, fW = O.full_loss_backward(H, W, U, np.eye(V), None, 1.0, g, tau_rows=taus, rev_weight=r)
+        np.testing.assert_allclose(dH, fH, rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(dW, fW, rtol=1e-10, atol=1e-13)
+
+
+def test_topk_reverse_is_torch_kl_div_on_the_support():
+    # r = 1: the loss is KL(q~ || p^) over the K entries; the partial mass
+    # leaves it unchanged (both sides are renormalised on the support)
+    H, W, I, A, g, taus, _ = case(T=8, V=40, K=6, seed=41, dup=True)
+    fwd, rev = _torch_support_kls(H, W, I, A, taus)
+    got, _, _ = O.topk_loss_forward(H, W, I, A, None, 1.0, tau_rows=taus, rev_weight=1.0)
+    np.testing.assert_allclose(got, rev, rtol=1e-12, atol=1e-14)
+    tl, _ = teacher_lse_for_mass(A, taus, np.random.default_rng(42))
+    got2, _, _ = O.topk_loss_forward(H, W, I, A, None, 1.0, tau_rows=taus, teacher_lse=tl, rev_weight=1.0)
+    np.testing.assert_allclose(got2, rev, rtol=1e-12, atol=1e-14)
+    assert np.all(rev >= 0) and np.all(np.abs(rev - fwd) > 1e-6)  # the two directions differ here
+    # mixing: the convex combination with the (already pinned) forward-KL loss
+    kd, _, _ = O.topk_loss_forward(H, W, I, A, None, 1.0, tau_rows=taus, teacher_lse=tl)
+    for r in (0.2, 0.7):
+        mix, _, _ = O.topk_loss_forward(H, W, I, A, None, 1.0, tau_rows=taus, teacher_lse=tl, rev_weight=r)
+        np.testing.assert_allclose(mix, (1 - r) * kd + r * rev, rtol=1e-12, atol=1e-14)
+
+
+def test_topk_mixed_gradient_matches_torch_autograd():
+    # every option at once, duplicates and a masked row, against autograd of
+    # the loss written with torch's log_softmax, kl_div and cross_entropy
+    H, W, I, A, g, taus, y = case(T=6, d=7, V=30, K=5, seed=43, dup=True)
+    y[2] = I[2, 3]
+    tl, _ = teacher_lse_for_mass(A, taus, np.random.default_rng(44))
+    mask = np.array([1, 1, 0, 1, 1, 1], dtype=np.uint8)
+    for r, beta in ((0.5, 0.0), (0.3, 0.25), (1.0, 0.6)):
+        Hv = torch.tensor(H, requires_grad=True)
+        Wv = torch.tensor(W, requires_grad=True)
+        tau = torch.tensor(taus)[:, None]
+        s = (Hv @ Wv) / tau
+        logq = torch.log_softmax(s, dim=1)
+        p = torch.exp(torch.tensor(A) / tau - torch.tensor(tl)[:, None])
+        kd = (p * torch.log(p)).sum(1) - (p * torch.gather(logq, 1, torch.tensor(I))).sum(1)
+        lqs = torch.log_softmax(torch.gather(s, 1, torch.tensor(I)), dim=1)
+        lps = torch.log_softmax(torch.tensor(A) / tau, dim=1)
+        rkl = torch.nn.functional.kl_div(lps, lqs, log_target=True, reduction="none").sum(1)
+        ce = torch.nn.functional.cross_entropy(s, torch.tensor(y), reduction="none")
+        loss = (1 - beta) * ((1 - r) * kd + r * rkl) + beta * ce
+        m = torch.tensor(mask, dtype=torch.float64)
+        (loss * m * torch.tensor(g)).sum().backward()
+        kw = dict(tau_rows=taus, teacher_lse=tl, labels=y, ce_weight=beta, rev_weight=r)
+        got, _, _ = O.topk_loss_forward(H, W, I, A, mask, 1.0, **kw)
+        np.testing.assert_allclose(got, (loss * m).detach().numpy(), rtol=1e-11, atol=1e-13)
+        dH, dW = O.topk_loss_backward(H, W, I, A, mask, 1.0, g, **kw)
+        np.testing.assert_allclose(dH, Hv.grad.numpy(), rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(dW, Wv.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_topk_reverse_finite_differences():
+    H, W, I, A, g, taus, y = case(T=4, d=8, V=32, K=4, seed=45, dup=True)
+    tl, _ = teacher_lse_for_mass(A, taus, np.random.default_rng(46))
+    mask = np.array([1, 1, 0, 1], dtype=np.uint8)
+    kw = dict(tau_rows=taus, teacher_lse=tl, labels=y, ce_weight=0.2, rev_weight=0.65)
+    dH, dW = O.topk_loss_backward(H, W, I, A, mask, 1.0, g, **kw)
+
+    def loss(Hx, Wx):
+        v, _, _ = O.topk_loss_forward(Hx, Wx, I, A, mask, 1.0, **kw)
+        return float((v * g).sum())
+
+    h = 1e-6
+    rng = np.random.default_rng(47)
+    for _ in range(10):
+        t, j = rng.integers(4), rng.integers(8)
+        Hp, Hm = H.copy(), H.copy()
+        Hp[t, j] += h
+        Hm[t, j] -= h
+        assert (loss(Hp, W) - loss(Hm, W)) / (2 * h) == pytest.approx(dH[t, j], rel=1e-7, abs=1e-9)
+    for _ in range(10):
+        j, v = rng.integers(8), I[rng.integers(4), rng.integers(4)]  # columns on the support
+        Wp, Wm = W.copy(), W.copy()
+        Wp[j, v] += h
+        Wm[j, v] -= h
+        assert (loss(H, Wp) - loss(H, Wm)) / (2 * h) == pytest.approx(dW[j, v], rel=1e-7, abs=1e-9)
+    assert np.all(dH[2] == 0)
+
+
+def test_topk_reverse_zero_when_student_matches_teacher_on_support():
+    # identity head (d = V, W = I): z = H.  Put A_t + c_t at the cached columns
+    # of H_t (anything elsewhere): the student renormalised on the support is
+    # the teacher's p^, so RKL = 0 and the mixed loss and gradient are (1 - r)
+    # times the forward-KL ones.  K = 1 has a single outcome: RKL = 0 too.
+    rng = np.random.default_rng(48)
+    T, V, K = 5, 16, 4
+    I = np.stack([rng.choice(V, K, replace=False) for _ in range(T)])
+    A = rng.standard_normal((T, K)) * 1.5
+    H = rng.standard_normal((T, V))
+    c = rng.standard_normal(T) * 3.0
+    for t in range(T):
+        H[t, I[t]] = A[t] + c[t]
+    W = np.eye(V)
+    g = rng.standard_normal(T)
+    for tau in (1.0, 1.9):
+        kd, _, _ = O.topk_loss_forward(H, W, I, A, None, tau)
+        dH0, dW0 = O.topk_loss_backward(H, W, I, A, None, tau, g)
+        for r in (0.4, 1.0):
+            got, _, _ = O.topk_loss_forward(H, W, I, A, None, tau, rev_weight=r)
+            np.testing.assert_allclose(got, (1 - r) * kd, rtol=1e-12, atol=1e-13)
+            dH, dW = O.topk_loss_backward(H, W, I, A, None, tau, g, rev_weight=r)
+            np.testing.assert_allclose(dH, (1 - r) * dH0, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(dW, (1 - r) * dW0, rtol=1e-11, atol=1e-13)
+    H1, W1, I1, A1, g1, _, _ = case(T=5, K=1, seed=49)
+    kd1, _, _ = O.topk_loss_forward(H1, W1, I1, A1, None, 1.2)
+    got1, _, _ = O.topk_loss_forward(H1, W1, I1, A1, None, 1.2, rev_weight=0.3)
+    np.testing.assert_allclose(got1, 0.7 * kd1, rtol=1e-12)
 
 
 # ---------------------------------------------------------------- full vocabulary: KL mixing, per-token tau
