@@ -49,14 +49,18 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 # Optional parts of the top-K loss, as keyword arguments of the functions below
 # (kd_topk_opts of kdloss.h): tau_rows [T] float32 per-token temperature,
 # teacher_lse [T] float32 teacher log-normaliser (partial-mass teacher),
-# labels [T] int32 with ce_weight in [0, 1] (loss = (1 - w) KD + w CE).
+# labels [T] int32 with ce_weight in [0, 1] (loss = (1 - w) KD + w CE),
+# rev_weight r in [0, 1] (KD = (1 - r) KL(p || q) + r times the reverse KL on
+# the cached entries; the backward then also takes the forward's z_topk).
 def topk_kl_forward(H, W, topk_idx, topk_logits, mask=None, tau=1.0, want_z_topk=False, workspace=None,
                     **options):
-    """Per-token loss, log-normaliser and (optionally) the gathered raw logits."""
+    """Per-token loss, log-normaliser and the gathered raw logits (None unless
+    want_z_topk, or rev_weight > 0, which needs them)."""
     T, d = H.shape
     V, K = W.shape[1], topk_idx.shape[1]
     kl = torch.empty(T, dtype=torch.float32, device=H.device)
     lse = torch.empty(T, dtype=torch.float32, device=H.device)
+    want_z_topk = want_z_topk or bool(options.get("rev_weight"))
     z = torch.empty(T, K, dtype=torch.float32, device=H.device) if want_z_topk else None
     if workspace is None:
         workspace = _workspace(kd_topk_kl_workspace_size(T, d, V, K, H.dtype), H.device)
@@ -80,11 +84,13 @@ def topk_kl_backward(H, W, topk_idx, topk_logits, mask, tau, lse, grad_kl, chunk
 
 def topk_kl_forward_backward(H, W, topk_idx, topk_logits, mask, tau, grad_kl, chunk_rows=0, want_z_topk=False,
                              workspace=None, **options):
-    """kl, lse, z_topk (or None), dH and dW in one call, for a known grad_kl."""
+    """kl, lse, z_topk (None unless want_z_topk or rev_weight > 0), dH and dW
+    in one call, for a known grad_kl."""
     T, d = H.shape
     V, K = W.shape[1], topk_idx.shape[1]
     kl = torch.empty(T, dtype=torch.float32, device=H.device)
     lse = torch.empty(T, dtype=torch.float32, device=H.device)
+    want_z_topk = want_z_topk or bool(options.get("rev_weight"))
     z = torch.empty(T, K, dtype=torch.float32, device=H.device) if want_z_topk else None
     dH = torch.empty_like(H)
     dW = torch.empty(d, V, dtype=torch.float32, device=H.device)
@@ -231,15 +237,16 @@ def full_kl_forward_backward(H, Ws, Ht, Wt, mask, tau, grad_kl, chunk_rows=0, wo
 class _TopkKL(torch.autograd.Function):
     @staticmethod
     def forward(ctx, H, W, topk_idx, topk_logits, mask, tau, chunk_rows, options):
-        kl, lse, _ = topk_kl_forward(H, W, topk_idx, topk_logits, mask, tau, **options)
-        ctx.save_for_backward(H, W, topk_idx, topk_logits, lse)
+        kl, lse, z = topk_kl_forward(H, W, topk_idx, topk_logits, mask, tau, **options)
+        ctx.save_for_backward(H, W, topk_idx, topk_logits, lse, z)
         ctx.mask, ctx.tau, ctx.chunk_rows, ctx.options = mask, tau, chunk_rows, options
         return kl
 
     @staticmethod
     def backward(ctx, g):
-        H, W, idx, logits, lse = ctx.saved_tensors
-        dH, dW = topk_kl_backward(H, W, idx, logits, ctx.mask, ctx.tau, lse, g, ctx.chunk_rows, **ctx.options)
+        H, W, idx, logits, lse, z = ctx.saved_tensors
+        opts = dict(ctx.options, z_topk=z) if z is not None else ctx.options
+        dH, dW = topk_kl_backward(H, W, idx, logits, ctx.mask, ctx.tau, lse, g, ctx.chunk_rows, **opts)
         return dH, dW.to(W.dtype), None, None, None, None, None, None
 
 
@@ -262,12 +269,13 @@ class _FullKL(torch.autograd.Function):
 
 
 def topk_kl(H, W, topk_idx, topk_logits, mask=None, tau=1.0, chunk_rows=0, tau_rows=None, teacher_lse=None,
-            labels=None, ce_weight=0.0):
+            labels=None, ce_weight=0.0, rev_weight=0.0):
     """Per-token KL(p_teacher || q_student) with a top-K teacher (with the
     options: the mixed loss of kd_topk_opts); differentiable in H and W (W's
     gradient is cast to W's dtype; the float32 one is available from
     topk_kl_backward)."""
-    options = dict(tau_rows=tau_rows, teacher_lse=teacher_lse, labels=labels, ce_weight=float(ce_weight))
+    options = dict(tau_rows=tau_rows, teacher_lse=teacher_lse, labels=labels, ce_weight=float(ce_weight),
+                   rev_weight=float(rev_weight))
     return _TopkKL.apply(H, W, topk_idx, topk_logits, mask, float(tau), int(chunk_rows), options)
 
 

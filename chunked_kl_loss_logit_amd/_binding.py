@@ -39,9 +39,11 @@ EXPORTS = (
 
 
 class KdTopkOpts(ctypes.Structure):
-    """kd_topk_opts of kdloss.h: device pointers (0 = NULL), the CE weight and the index-check flag."""
+    """kd_topk_opts of kdloss.h: device pointers (0 = NULL), the CE weight, the index-check flag, the
+    reverse-KL weight and the forward's z_topk (read by the backward under KL mixing)."""
     _fields_ = [("tau_rows", ctypes.c_void_p), ("teacher_lse", ctypes.c_void_p), ("labels", ctypes.c_void_p),
-                ("ce_weight", ctypes.c_float), ("check_indices", ctypes.c_int32)]
+                ("ce_weight", ctypes.c_float), ("check_indices", ctypes.c_int32), ("rev_weight", ctypes.c_float),
+                ("z_topk", ctypes.c_void_p)]
 
 
 class KdFullOpts(ctypes.Structure):
@@ -212,16 +214,16 @@ def _full_in(H, Ws, Ht, Wt, mask):
     return T, d, dt, V
 
 
-def _opts_in(opts, T):
+def _opts_in(opts, T, K=None):
     """The tensors an options struct points at (kept on it by topk_opts /
-    full_opts) are [T] and of their documented dtype."""
+    full_opts) are [T] (z_topk: [T, K]) and of their documented dtype."""
     if opts is None:
         return ()
     kept = getattr(opts, "_tensors", None)
     if kept is None:
         raise TypeError("options must come from topk_opts(...) or full_opts(...)")
     for name, t, dtypes in kept:
-        _need(name, t, (T,), dtypes, optional=True)
+        _need(name, t, (T, K) if name == "z_topk" else (T,), dtypes, optional=True)
     return tuple(t for _, t, _ in kept)
 
 
@@ -269,7 +271,7 @@ def _topk_fwd_checked(H, W, topk_idx, topk_logits, mask, opts, kl, lse, z_topk, 
     _need("lse", lse, (T,), _F32)
     _need("z_topk", z_topk, (T, K), _F32, optional=True)
     nbytes = _ws_bytes(workspace)
-    _one_device(H, W, topk_idx, topk_logits, mask, kl, lse, z_topk, workspace, *_opts_in(opts, T))
+    _one_device(H, W, topk_idx, topk_logits, mask, kl, lse, z_topk, workspace, *_opts_in(opts, T, K))
     return T, d, V, K, nbytes
 
 
@@ -280,7 +282,7 @@ def _topk_bwd_checked(H, W, topk_idx, topk_logits, mask, opts, lse, grad_kl, dH,
     _need("dH", dH, (T, d), (dh_dtype or H.dtype,))
     _need("dW", dW, (d, V), _F32)
     nbytes = _ws_bytes(workspace)
-    _one_device(H, W, topk_idx, topk_logits, mask, lse, grad_kl, dH, dW, workspace, *_opts_in(opts, T))
+    _one_device(H, W, topk_idx, topk_logits, mask, lse, grad_kl, dH, dW, workspace, *_opts_in(opts, T, K))
     return T, d, V, K, nbytes
 
 
@@ -317,19 +319,24 @@ def kd_topk_kl_fwd_bwd(H, W, topk_idx, topk_logits, mask, tau, grad_kl, kl, lse,
                           chunk_rows, workspace, stream, _name="kd_topk_kl_fwd_bwd")
 
 
-def topk_opts(tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0, check_indices=False):
+def topk_opts(tau_rows=None, teacher_lse=None, labels=None, ce_weight=0.0, check_indices=False, rev_weight=0.0,
+              z_topk=None):
     """The kd_topk_opts struct for these device tensors (or None when no option is set).  The
     tensors must stay alive until the call that takes the struct has been enqueued; the struct
-    keeps a reference to them, and each call checks them against its T.  check_indices asks
+    keeps a reference to them, and each call checks them against its T (z_topk: [T, K], the
+    forward's output, which the backward reads when rev_weight > 0).  check_indices asks
     for the device-side index range check (the call then synchronises its stream once)."""
-    if tau_rows is None and teacher_lse is None and labels is None and not ce_weight and not check_indices:
+    if (tau_rows is None and teacher_lse is None and labels is None and not ce_weight and not check_indices
+            and not rev_weight and z_topk is None):
         return None
-    kept = (("tau_rows", tau_rows, _F32), ("teacher_lse", teacher_lse, _F32), ("labels", labels, _I32))
+    kept = (("tau_rows", tau_rows, _F32), ("teacher_lse", teacher_lse, _F32), ("labels", labels, _I32),
+            ("z_topk", z_topk, _F32))
     for name, t, dtypes in kept:
         _need(name, t, None, dtypes, optional=True)
-        if t is not None and t.dim() != 1:
-            raise ValueError(f"{name} must be 1-D [T], got shape {tuple(t.shape)}")
-    o = KdTopkOpts(None, None, None, float(ce_weight), 1 if check_indices else 0)
+        want = 2 if name == "z_topk" else 1
+        if t is not None and t.dim() != want:
+            raise ValueError(f"{name} must be {want}-D, got shape {tuple(t.shape)}")
+    o = KdTopkOpts(None, None, None, float(ce_weight), 1 if check_indices else 0, float(rev_weight), None)
     o._tensors = kept
     return o
 
@@ -373,7 +380,8 @@ def kd_topk_kl_fwd_bwd_ex(H, W, topk_idx, topk_logits, mask, tau, opts, grad_kl,
     _need("dH", dH, (T, d), (H.dtype,))
     _need("dW", dW, (d, V), _F32)
     nb = _ws_bytes(workspace)
-    _one_device(H, W, topk_idx, topk_logits, mask, grad_kl, kl, lse, z_topk, dH, dW, workspace, *_opts_in(opts, T))
+    _one_device(H, W, topk_idx, topk_logits, mask, grad_kl, kl, lse, z_topk, dH, dW, workspace,
+                *_opts_in(opts, T, K))
     if _name == "kd_topk_kl_fwd_bwd":
         st = lib().kd_topk_kl_fwd_bwd(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask), float(tau),
                                       T, d, V, K, _dtype_code(H.dtype), _ptr(grad_kl), _ptr(kl), _ptr(lse),
@@ -403,7 +411,7 @@ def kd_topk_kl_fwd_shard(H, W, v0, topk_idx, topk_logits, mask, tau, opts, rec, 
     _need("trow", trow, (T, 2), _F32)
     _need("z_topk", z_topk, (T, K), _F32, optional=True)
     nb = _ws_bytes(workspace)
-    _one_device(H, W, topk_idx, topk_logits, mask, rec, trow, z_topk, workspace, *_opts_in(opts, T))
+    _one_device(H, W, topk_idx, topk_logits, mask, rec, trow, z_topk, workspace, *_opts_in(opts, T, K))
     _check(lib().kd_topk_kl_fwd_shard(_ptr(H), _ptr(W), _ptr(topk_idx), _ptr(topk_logits), _ptr(mask), float(tau),
                                       _opts_ref(opts), T, d, V, int(v0), K, _dtype_code(H.dtype), _ptr(rec),
                                       _ptr(trow), _ptr(z_topk), _ptr(workspace), nb, _stream(stream)),

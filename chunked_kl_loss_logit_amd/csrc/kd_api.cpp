@@ -444,7 +444,9 @@ namespace {
 struct TopkOpts {
   kd::TopkPrepOpts prep;
   int64_t KE;
-  bool check;  // the index check on request
+  bool check;          // the index check on request
+  float wr;            // weight of the reverse KL on the cached entries: r (1 - beta with a CE label)
+  const float* z_in;   // the forward's z_topk, for the backward's reverse part
 };
 
 kd_status resolve_opts(const kd_topk_opts* o, float tau, int64_t K, TopkOpts& r) {
@@ -453,14 +455,19 @@ kd_status resolve_opts(const kd_topk_opts* o, float tau, int64_t K, TopkOpts& r)
   r.prep.inv_tau = 1.0f / tau;
   r.KE = K;
   r.check = false;
+  r.wr = 0.f;
+  r.z_in = nullptr;
   if (o == nullptr) return KD_OK;
   r.check = o->check_indices != 0;
   if (!std::isfinite(o->ce_weight) || o->ce_weight < 0.f || o->ce_weight > 1.f)
     return fail(KD_ERR_INVALID_ARG, "ce_weight must be finite and in [0, 1]");
+  if (!std::isfinite(o->rev_weight) || o->rev_weight < 0.f || o->rev_weight > 1.f)
+    return fail(KD_ERR_INVALID_ARG, "rev_weight must be finite and in [0, 1]");
   if (o->ce_weight > 0.f && o->labels == nullptr) return fail(KD_ERR_INVALID_ARG, "ce_weight > 0 needs labels");
   KD_TRY(need_align(o->tau_rows, 4, "tau_rows"));
   KD_TRY(need_align(o->teacher_lse, 4, "teacher_lse"));
   KD_TRY(need_align(o->labels, 4, "labels"));
+  KD_TRY(need_align(o->z_topk, 4, "opts.z_topk"));
   r.prep.tau_rows = o->tau_rows;
   r.prep.teacher_lse = o->teacher_lse;
   if (o->ce_weight > 0.f) {
@@ -469,6 +476,9 @@ kd_status resolve_opts(const kd_topk_opts* o, float tau, int64_t K, TopkOpts& r)
     r.prep.beta = o->ce_weight;
     r.KE = K + 1;
   }
+  r.prep.rev = o->rev_weight;
+  r.wr = o->rev_weight * (o->ce_weight > 0.f ? 1.f - o->ce_weight : 1.f);
+  r.z_in = o->z_topk;
   return KD_OK;
 }
 
@@ -525,6 +535,9 @@ kd_status check_shard(int64_t T, int64_t K, int64_t V, int64_t v0, const kd_topk
   KD_TRY(check_k(T, K, V, false));
   if (o != nullptr && o->check_indices != 0)
     return fail(KD_ERR_UNSUPPORTED, "check_indices: a shard does not know the whole head's width");
+  if (o != nullptr && o->rev_weight != 0.f)
+    return fail(KD_ERR_UNSUPPORTED, "rev_weight: the reverse KL needs the student's logits at all K entries, "
+                                    "which no one shard holds");
   if (v0 < 0) return fail(KD_ERR_INVALID_ARG, "v0 must be >= 0");
   if (v0 + V > INT32_MAX / 2) return fail(KD_ERR_UNSUPPORTED, "v0 + V must be below 2^30");
   return KD_OK;
@@ -591,6 +604,7 @@ kd_status topk_fwd(const void* H, const void* W, const int32_t* topk_idx, const 
   KD_TRY(need_align(topk_idx, 4, "topk_idx"));
   KD_TRY(need_align(topk_logits, 4, "topk_logits"));
   KD_TRY(need_align(z_topk, 4, "z_topk"));
+  if (op.prep.rev > 0.f) KD_TRY(need(z_topk, "z_topk (rev_weight > 0 reads it)"));
   const int elem = elem_of(dt);
   const TopkPlan p = plan_topk(T, d, V, K, elem, 0);
   KD_TRY(check_workspace(workspace, workspace_bytes, p.fwd_total));
@@ -635,6 +649,10 @@ kd_status topk_fwd(const void* H, const void* W, const int32_t* topk_idx, const 
     else
       KD_LAUNCH("topk_combine", st,
                 kd::launch_topk_combine(part, sh.S, p.Cf, c, mask, rd, T, kl, lse, c0, c0 + p.Cf, c0 == 0, st));
+    if (op.prep.rev > 0.f)
+      KD_LAUNCH("topk_reverse", st,
+                kd::launch_topk_reverse(z_topk, topk_logits, c, T, K, op.KE, op.wr, rd, kl, false, c0, c0 + p.Cf,
+                                        st));
   }
   return KD_OK;
 }
@@ -757,6 +775,7 @@ kd_status topk_bwd(const void* H, const void* W, const int32_t* topk_idx, const 
   KD_TRY(need_align(lse, 4, "lse"));
   KD_TRY(need_align(grad_kl, 4, "grad_kl"));
   if (chunk_rows < 0) return fail(KD_ERR_INVALID_ARG, "chunk_rows must be >= 0");
+  if (op.prep.rev > 0.f) KD_TRY(need(op.z_in, "opts.z_topk (rev_weight > 0 reads it)"));
   const int elem = elem_of(dt);
   const TopkPlan p = plan_topk(T, d, V, K, elem, chunk_rows);
   KD_TRY(check_workspace(workspace, workspace_bytes, p.total));
@@ -767,6 +786,9 @@ kd_status topk_bwd(const void* H, const void* W, const int32_t* topk_idx, const 
   KD_TRY(start_index_check(op, workspace, p, V, st));
   KD_LAUNCH("topk_prep", st, kd::launch_topk_prep(topk_logits, topk_idx, mask, T, K, op.KE, op.prep, rd, nullptr, st));
   KD_TRY(finish_index_check(op, st));
+  if (op.prep.rev > 0.f)  // the reverse part's gradient folded into the support weights
+    KD_LAUNCH("topk_reverse", st,
+              kd::launch_topk_reverse(op.z_in, topk_logits, c, T, K, op.KE, op.wr, rd, nullptr, true, 0, T, st));
   const int dh_elem = shard ? 4 : elem;
   KD_LAUNCH("zero_masked_rows", st, kd::launch_zero_masked_rows(mask, T, d * dh_elem, dH, st));
 
@@ -1352,6 +1374,7 @@ kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* top
   KD_TRY(need_align(kl, 4, "kl"));
   KD_TRY(need_align(lse, 4, "lse"));
   KD_TRY(need_align(z_topk, 4, "z_topk"));
+  if (op.prep.rev > 0.f) KD_TRY(need(z_topk, "z_topk (rev_weight > 0 reads it)"));
   const int elem = elem_of(dt);
   const TopkPlan p = plan_topk(T, d, V, K, elem, chunk_rows);
   KD_TRY(check_workspace(workspace, workspace_bytes, p.fused_total));
@@ -1402,6 +1425,10 @@ kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* top
     KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
     KD_LAUNCH("topk_combine", st,
               kd::launch_topk_combine(part, sh.S, ch.C, c, mask, rd, T, kl, lse, c0, c0 + ch.C, k == 0, st));
+    if (op.prep.rev > 0.f)  // the reverse part: into kl, and into the weights the dZ pass scatters
+      KD_LAUNCH("topk_reverse", st,
+                kd::launch_topk_reverse(z_topk, topk_logits, c, T, K, op.KE, op.wr, rd, kl, true, c0, c0 + ch.C,
+                                        st));
     // dZ from the kept logits: no second projection
     kd::TopkDzFromZArgs za{};
     za.z = z;

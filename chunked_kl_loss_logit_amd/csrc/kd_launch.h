@@ -30,6 +30,7 @@ struct TopkPrepOpts {
   const float* teacher_lse;  // nullable [T]: partial mass, p = exp(A / tau - teacher_lse)
   const int32_t* labels;     // nullable [T]: labels of the cross-entropy term
   float beta;                // weight of the cross-entropy term (labels set)
+  float rev;                 // weight r of the reverse KL: the forward-KL weights are scaled by 1 - r
   float c2, inv_tau;         // log2(e) / tau and 1 / tau of the scalar temperature
   int32_t v0, vs;            // columns [v0, v0 + vs) of a vocabulary shard of W (vs = 0: the whole head)
   int32_t* bad;              // nullable: counts the cached indices and labels of valid rows outside [0, V)
@@ -58,6 +59,15 @@ inline int ew_ranges(int elem, int64_t V) {
 hipError_t launch_compact(const uint8_t* mask, int64_t T, Compact c, hipStream_t st);
 hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8_t* mask, int64_t T, int64_t K,
                             int64_t KE, const TopkPrepOpts& o, TopkRowData rd, float* z_topk, hipStream_t st);
+// KL mixing on the cached entries, for compacted rows [jb, je): each row's
+// reverse KL between the student and the teacher restricted to the K entries
+// and renormalised there, from z_topk [T,K] and the cached logits.  kl
+// (nullable) gains wr * RKL; with upd, the row's support weights become
+// w - wr * q~_k (log q~_k - log p^_k - RKL), so that a dZ pass scattering
+// them adds the reverse gradient.  Needs the prep's per-row constants.
+hipError_t launch_topk_reverse(const float* z_topk, const float* logits, Compact c, int64_t T, int64_t K,
+                               int64_t KE, float wr, TopkRowData rd, float* kl, bool upd, int64_t jb, int64_t je,
+                               hipStream_t st);
 // Merges the split partials of compacted rows [jb, je) (partial row p holds
 // compacted row jb + p) into kl and lse; with zero_masked, also zeroes kl and
 // lse of every masked row.

@@ -161,10 +161,12 @@ __global__ __launch_bounds__(NT) void topk_prep_kernel(const float* logits, cons
   float mass = 1.f;  // renormalised: exactly one
   if (o.teacher_lse) mass = block_sum<NT>(m, red);
   const bool ce = KE > K;
-  const float wk = ce ? 1.f - o.beta : 1.f;
-  if (ce) {
+  // weight of the forward-KL part: 1 - beta with a CE label, times 1 - r
+  // under KL mixing (the reverse part comes from topk_reverse_kernel)
+  const float wk = (ce ? 1.f - o.beta : 1.f) * (1.f - o.rev);
+  if (ce || o.rev != 0.f) {
     ent *= wk;
-    mass = fmaf(wk, mass, o.beta);
+    mass = fmaf(wk, mass, ce ? o.beta : 0.f);
   }
 
   // sort (index, position) pairs by index; ties keep position order
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(NT) void topk_prep_kernel(const float* logits, cons
   for (int j = threadIdx.x; j < KE; j += NT) {
     const uint64_t kv = key[j];
     const uint32_t k = (uint32_t)(kv & 0xffffffffu);
-    const float w = k < (uint32_t)K ? (ce ? wk * p[k] : p[k]) : o.beta;
+    const float w = k < (uint32_t)K ? wk * p[k] : o.beta;
     rd.pair[pbase + j] = make_int2((int32_t)((uint32_t)(kv >> 32) ^ 0x80000000u), __float_as_int(w));
     rd.perm[pbase + j] = (uint16_t)k;
   }
@@ -223,6 +225,72 @@ hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8
   else
     hipLaunchKernelGGL(topk_prep_kernel<256>, grid, dim3(256), shm, st, logits, idx, mask, (int)K, (int)KE, KP, o,
                        rd, z_topk);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ KL mixing on the cached entries
+// One block per compacted row: a = z_topk / tau_t and b = A / tau_t over the
+// K entries, q~ = softmax(a), p^ = softmax(b), RKL = sum q~ (log q~ - log p^).
+// The entries are read from global memory once per pass (K floats each).
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_reverse_kernel(const float* z_topk, const float* logits, Compact c,
+                                                          int K, int KE, float wr, TopkRowData rd, float* kl,
+                                                          int upd, long jb, long je) {
+  __shared__ float red[NT / 64 > 0 ? NT / 64 : 1];
+  const long j = jb + blockIdx.x;
+  if (j >= je || j >= (long)*c.count) return;
+  const long t = c.rows[j];
+  const float it = rd.rowc[t].y;  // 1 / tau_t
+  const float* za = z_topk + t * K;
+  const float* zb = logits + t * K;
+  float ma = -INFINITY, mb = -INFINITY;
+  for (int k = threadIdx.x; k < K; k += NT) {
+    ma = fmaxf(ma, za[k] * it);
+    mb = fmaxf(mb, zb[k] * it);
+  }
+  ma = block_max<NT>(ma, red);
+  mb = block_max<NT>(mb, red);
+  float sa = 0.f, sb = 0.f;
+  for (int k = threadIdx.x; k < K; k += NT) {
+    sa += expf(za[k] * it - ma);
+    sb += expf(zb[k] * it - mb);
+  }
+  sa = block_sum<NT>(sa, red);
+  sb = block_sum<NT>(sb, red);
+  const float la = ma + logf(sa), lb = mb + logf(sb);
+  float rk = 0.f;
+  for (int k = threadIdx.x; k < K; k += NT) {
+    const float lq = za[k] * it - la;
+    rk = fmaf(expf(lq), lq - (zb[k] * it - lb), rk);
+  }
+  rk = block_sum<NT>(rk, red);
+  if (kl != nullptr && threadIdx.x == 0) kl[t] = fmaf(wr, rk, kl[t]);
+  if (upd) {
+    const long pb = t * KE;
+    for (int i = threadIdx.x; i < KE; i += NT) {
+      const int k = rd.perm[pb + i];
+      if (k >= K) continue;  // the CE label's entry
+      const float lq = za[k] * it - la;
+      const float v = expf(lq) * (lq - (zb[k] * it - lb) - rk);
+      int2 e = rd.pair[pb + i];
+      e.y = __float_as_int(fmaf(-wr, v, __int_as_float(e.y)));
+      rd.pair[pb + i] = e;
+    }
+  }
+}
+
+hipError_t launch_topk_reverse(const float* z_topk, const float* logits, Compact c, int64_t T, int64_t K,
+                               int64_t KE, float wr, TopkRowData rd, float* kl, bool upd, int64_t jb, int64_t je,
+                               hipStream_t st) {
+  if (je > T) je = T;
+  if (je <= jb) return hipSuccess;
+  const dim3 grid((unsigned)(je - jb));
+  if (K <= 64)
+    hipLaunchKernelGGL(topk_reverse_kernel<64>, grid, dim3(64), 0, st, z_topk, logits, c, (int)K, (int)KE, wr, rd,
+                       kl, upd ? 1 : 0, (long)jb, (long)je);
+  else
+    hipLaunchKernelGGL(topk_reverse_kernel<256>, grid, dim3(256), 0, st, z_topk, logits, c, (int)K, (int)KE, wr,
+                       rd, kl, upd ? 1 : 0, (long)jb, (long)je);
   return hipGetLastError();
 }
 

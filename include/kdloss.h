@@ -180,6 +180,22 @@ kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_i
  *   kl_t  = (1 - ce_weight) KD_t + ce_weight CE_t
  *   dZ_t  = (g_t / tau_t) ((1 - ce_weight)(m_t softmax(s) - scatter_add(I_t, p))
  *                          + ce_weight (softmax(s) - onehot(labels[t])))
+ * KL mixing (rev_weight = r > 0) adds the reverse direction on the cached
+ * entries, where both sides are known: with q~ = softmax_k(s[I_tk]) and
+ * p^ = softmax_k(A_tk / tau_t), both over the K entries (each entry its own
+ * outcome, p^ renormalised also under a partial mass),
+ *   RKL_t = sum_k q~_k (log q~_k - log p^_k)
+ *   KD_t is replaced by (1 - r) KD_t + r RKL_t in kl_t, and dZ_t gains
+ *   (g_t / tau_t)(1 - ce_weight) r q~_k (log q~_k - log p^_k - RKL_t)
+ *   at column I_tk (scatter-add).
+ * q~ is computed from the forward's z_topk: the forward and single calls
+ * need their z_topk output, the backward call gets the forward's z_topk in
+ * opts.z_topk (KD_ERR_INVALID_ARG if NULL then).  Source: forward and
+ * reverse token-level KL and their mixture, the KL-direction abstract
+ * (thelatestinai.com/papers/2606.20005); the restriction to the cached
+ * entries is this library's reading, since the teacher is known only there.
+ * The vocabulary shard calls reject r > 0 (KD_ERR_UNSUPPORTED): q~ needs the
+ * student's logits at all K entries.
  * Sources: per-token temperature, the adaptive-distillation abstract on the
  * WASD page (thelatestinai.com/papers/2610.07706); cached probabilities with
  * their unnormalised partial mass and the support identity above, §3
@@ -189,8 +205,9 @@ kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_i
  * same loss at the same temperature (tau = 1 gives the plain LM loss).
  * Only the per-row constants and the weights of the support entries change,
  * so every option keeps the tiles, workspace size and speed of the plain
- * call.  Argument errors: ce_weight outside [0, 1] or not finite, or
- * ce_weight > 0 without labels: KD_ERR_INVALID_ARG; ce_weight > 0 with
+ * call (KL mixing adds one small per-row pass).  Argument errors: ce_weight
+ * or rev_weight outside [0, 1] or not finite, ce_weight > 0 without labels,
+ * or rev_weight > 0 without z_topk: KD_ERR_INVALID_ARG; ce_weight > 0 with
  * K = KD_MAX_K: KD_ERR_UNSUPPORTED (the label is entry K + 1); misaligned
  * arrays: KD_ERR_ALIGNMENT.  Values are not checked: tau_rows must be
  * finite and > 0 and labels in [0, V) on valid rows (masked rows are never
@@ -211,6 +228,8 @@ typedef struct kd_topk_opts {
   const int32_t* labels;     /* [T] next-token labels of the CE term, or NULL */
   float ce_weight;           /* weight of the CE term in [0, 1]; 0 = distillation only */
   int32_t check_indices;     /* nonzero: check the index range on the device (see above) */
+  float rev_weight;          /* weight r of the reverse KL on the cached entries in [0, 1]; 0 = none */
+  const float* z_topk;       /* [T,K] the forward's z_topk, read by the backward call when r > 0 */
 } kd_topk_opts;
 
 kd_status kd_topk_kl_fwd_ex(const void* H, const void* W, const int32_t* topk_idx,

@@ -77,6 +77,23 @@ int main() {
   EXPECT(kd_topk_kl_fwd_ex(F, F, f<int32_t>(), f<float>(), nullptr, 1.f, &o, 8, 64, 256, 4, KD_BF16, f<float>(),
                            f<float>(), nullptr, F, 0, nullptr) == KD_ERR_INVALID_ARG);
   o = kd_topk_opts{};
+  o.rev_weight = -0.5f;  // outside [0, 1]
+  EXPECT(kd_topk_kl_fwd_ex(F, F, f<int32_t>(), f<float>(), nullptr, 1.f, &o, 8, 64, 256, 4, KD_BF16, f<float>(),
+                           f<float>(), f<float>(), F, 0, nullptr) == KD_ERR_INVALID_ARG);
+  o.rev_weight = 0.5f;  // without z_topk: the forward, the backward and the single call
+  EXPECT(kd_topk_kl_fwd_ex(F, F, f<int32_t>(), f<float>(), nullptr, 1.f, &o, 8, 64, 256, 4, KD_BF16, f<float>(),
+                           f<float>(), nullptr, F, 0, nullptr) == KD_ERR_INVALID_ARG);
+  EXPECT(kd_topk_kl_bwd_ex(F, F, f<int32_t>(), f<float>(), nullptr, 1.f, &o, 8, 64, 256, 4, KD_BF16, f<float>(),
+                           f<float>(), F, f<float>(), 0, F, 0, nullptr) == KD_ERR_INVALID_ARG);
+  EXPECT(kd_topk_kl_fwd_bwd_ex(F, F, f<int32_t>(), f<float>(), nullptr, 1.f, &o, 8, 64, 256, 4, KD_BF16, f<float>(),
+                               f<float>(), f<float>(), nullptr, F, f<float>(), 0, F, 0, nullptr) == KD_ERR_INVALID_ARG);
+  o.z_topk = f<float>(2);  // misaligned
+  EXPECT(kd_topk_kl_bwd_ex(F, F, f<int32_t>(), f<float>(), nullptr, 1.f, &o, 8, 64, 256, 4, KD_BF16, f<float>(),
+                           f<float>(), F, f<float>(), 0, F, 0, nullptr) == KD_ERR_ALIGNMENT);
+  o.z_topk = f<float>();  // a shard cannot form the reverse part
+  EXPECT(kd_topk_kl_fwd_shard(F, F, f<int32_t>(), f<float>(), nullptr, 1.f, &o, 8, 64, 256, 512, 4, KD_BF16,
+                              f<float>(), f<float>(), f<float>(), F, 0, nullptr) == KD_ERR_UNSUPPORTED);
+  o = kd_topk_opts{};
   o.check_indices = 1;
   EXPECT(kd_topk_kl_fwd_shard(F, F, f<int32_t>(), f<float>(), nullptr, 1.f, &o, 8, 64, 256, 512, 4, KD_BF16,
                               f<float>(), f<float>(), nullptr, F, 0, nullptr) == KD_ERR_UNSUPPORTED);

@@ -258,14 +258,18 @@ def fwd_ex(opts, T=8, d=64, V=256, K=4, wsb=0):
                                kdl.KD_BF16, vp(FAKE), vp(FAKE), None, vp(FAKE), wsb, None)
 
 
-def opts(tau_rows=0, teacher_lse=0, labels=0, ce_weight=0.0, check=0):
-    return kdl._binding.KdTopkOpts(tau_rows or None, teacher_lse or None, labels or None, ce_weight, check)
+def opts(tau_rows=0, teacher_lse=0, labels=0, ce_weight=0.0, check=0, rev=0.0, z=0):
+    return kdl._binding.KdTopkOpts(tau_rows or None, teacher_lse or None, labels or None, ce_weight, check, rev,
+                                   z or None)
 
 
 def test_topk_opts_layout_matches_the_header(L):
-    # three pointers, the CE weight and the index-check flag
-    assert ctypes.sizeof(kdl._binding.KdTopkOpts) == 32
+    # three pointers, the CE weight, the index-check flag, the reverse-KL
+    # weight and the forward's z_topk
+    assert ctypes.sizeof(kdl._binding.KdTopkOpts) == 48
     assert kdl._binding.KdTopkOpts.check_indices.offset == 28
+    assert kdl._binding.KdTopkOpts.rev_weight.offset == 32
+    assert kdl._binding.KdTopkOpts.z_topk.offset == 40
 
 
 def test_index_check_is_an_option_of_the_whole_head_only(L):
@@ -300,6 +304,45 @@ def test_topk_options_label_needs_room_for_one_more_entry(L):
     assert fwd_ex(o, V=16384, K=kdl.KD_MAX_K) == 2
     assert fwd_ex(o, V=16384, K=kdl.KD_MAX_K - 1) == 4
     assert fwd_ex(None, V=16384, K=kdl.KD_MAX_K) == 4
+
+
+def test_topk_reverse_option_checks(L):
+    vp = ctypes.c_void_p
+    L_ = kdl.lib()
+
+    def fwd(o, z):
+        return L_.kd_topk_kl_fwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0),
+                                    ctypes.byref(o), 8, 64, 256, 4, kdl.KD_BF16, vp(FAKE), vp(FAKE),
+                                    vp(z) if z else None, vp(FAKE), 0, None)
+
+    def bwd(o):
+        return L_.kd_topk_kl_bwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0),
+                                    ctypes.byref(o), 8, 64, 256, 4, kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(FAKE),
+                                    vp(FAKE), 0, vp(FAKE), 0, None)
+
+    def one(o, z):
+        return L_.kd_topk_kl_fwd_bwd_ex(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0),
+                                        ctypes.byref(o), 8, 64, 256, 4, kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(FAKE),
+                                        vp(z) if z else None, vp(FAKE), vp(FAKE), 0, vp(FAKE), 0, None)
+
+    for r in (-0.1, 1.5, math.nan, math.inf):
+        assert fwd(opts(rev=r), FAKE) == 1 and "rev_weight" in last_error()
+    # the forward and the single call need their z_topk output, the backward the forward's
+    assert fwd(opts(rev=0.5), 0) == 1 and "z_topk" in last_error()
+    assert one(opts(rev=0.5), 0) == 1 and "z_topk" in last_error()
+    assert bwd(opts(rev=0.5)) == 1 and "z_topk" in last_error()
+    assert bwd(opts(rev=0.5, z=FAKE + 2)) == 3
+    # valid requests reach the workspace check
+    assert fwd(opts(rev=0.5), FAKE) == 4 and one(opts(rev=1.0), FAKE) == 4 and bwd(opts(rev=0.5, z=FAKE)) == 4
+    assert fwd(opts(rev=0.0), 0) == 4  # no reverse part: z_topk stays optional
+    # a vocabulary shard cannot form the reverse part
+    o = ctypes.byref(opts(rev=0.5, z=FAKE))
+    assert L_.kd_topk_kl_fwd_shard(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), o, 8, 64, 256,
+                                   512, 4, kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 0, None) == 2
+    assert "rev_weight" in last_error()
+    assert L_.kd_topk_kl_bwd_shard(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), None, ctypes.c_float(1.0), o, 8, 64, 256,
+                                   512, 4, kdl.KD_BF16, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 0, vp(FAKE), 0,
+                                   None) == 2
 
 
 def test_topk_ex_calls_check_their_options_too(L):

@@ -76,6 +76,9 @@ def test_topk_fwd_rejects(over, err, match):
     (dict(labels=z(T, dtype=torch.int64), ce_weight=0.5), TypeError, "labels must be torch.int32"),
     (dict(labels=z(T, 2, dtype=i32), ce_weight=0.5), ValueError, "labels must be 1-D"),
     (dict(tau_rows=z(T, device="meta")), ValueError, "one device"),
+    (dict(rev_weight=0.5, z_topk=z(T, K + 1)), ValueError, "z_topk must have shape"),
+    (dict(rev_weight=0.5, z_topk=z(T * K)), ValueError, "z_topk must be 2-D"),
+    (dict(rev_weight=0.5, z_topk=z(T, K, dtype=bf)), TypeError, "z_topk must be torch.float32"),
 ])
 def test_topk_options_are_checked_against_the_call(kw, err, match):
     def call():
@@ -86,6 +89,8 @@ def test_topk_options_are_checked_against_the_call(kw, err, match):
 def test_topk_options_good_reach_the_device_test():
     o = B.topk_opts(tau_rows=z(T), teacher_lse=z(T), labels=z(T, dtype=i32), ce_weight=0.25)
     on_gpu_only(lambda: B.kd_topk_kl_fwd_ex(**{**topk_fwd_args(), "opts": o}))
+    o = B.topk_opts(rev_weight=0.5, z_topk=z(T, K))
+    on_gpu_only(lambda: B.kd_topk_kl_bwd_ex(**{**topk_bwd_args(), "opts": o}))
     assert B.topk_opts() is None
 
 
