@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true", help="T in 4096, 16384, 65536, 262144: one line each")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 4 times (calibrates HBM byte counters)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor GEMM (torch.matmul) on the head's three contraction shapes")
     return ap.parse_args()
 
 
@@ -467,6 +469,40 @@ def brief(r):
     return out
 
 
+def vendor_gemm(steps: int, warmup: int):
+    """The vendor BLAS GEMM (torch.matmul, bf16 in) on the three contractions of
+    the head's step: H.W (forward and the backward's recompute), dZ.W^T (dH)
+    and H^T.dZ (dW, bf16 out, then also into an fp32 array as the loss's dW
+    is).  Plain products with no loss epilogue: a reference for what this chip
+    sustains on these shapes at its loaded clock, timed like the loss steps."""
+    import torch
+    dev = torch.device("cuda:0")
+    T, d, V = 4096, 3072, 128256
+    gen = torch.Generator(device=dev).manual_seed(7)
+    H = torch.randn(T, d, device=dev, dtype=torch.bfloat16, generator=gen)
+    W = (torch.randn(d, V, device=dev, dtype=torch.bfloat16, generator=gen) / d ** 0.5).to(torch.bfloat16)
+    dZ = (torch.randn(T, V, device=dev, dtype=torch.bfloat16, generator=gen) * 1e-3).to(torch.bfloat16)
+    Z = torch.empty(T, V, device=dev, dtype=torch.bfloat16)
+    dWf = torch.empty(d, V, device=dev, dtype=torch.float32)
+    flops = 2 * T * d * V
+    cases = (("H.W -> bf16 [T,V]", lambda: torch.matmul(H, W, out=Z)),
+             ("dZ.W^T -> bf16 [T,d]", lambda: torch.matmul(dZ, W.t())),  # plain 2-D product, W read in place
+             ("H^T.dZ -> bf16 [d,V]", lambda: torch.matmul(H.t(), dZ)),
+             ("H^T.dZ -> fp32 [d,V] (bf16 product, then copied)", lambda: dWf.copy_(torch.matmul(H.t(), dZ))))
+    for name, f in cases:
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            f()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        print(json.dumps({"vendor_gemm": name, "T": T, "d": d, "V": V, "ms": round(ms, 4),
+                          "tflops": round(flops / ms / 1e9, 1), "frac_of_2.5PF": round(flops / ms / 1e9 / 2500, 4)}),
+              flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -474,6 +510,9 @@ def main():
         sys.exit(2)
     if a.copy_probe:
         copy_probe(a.copy_probe)
+        return
+    if a.vendor_gemm:
+        vendor_gemm(a.steps, a.warmup)
         return
 
     import kdinputs as G
