@@ -1,9 +1,10 @@
 """GPU parity over a seeded sweep of shapes: the HIP path against the fp64
 oracle on configurations drawn once from a fixed seed, so that the kernel
 selections (direct-load ring or register-staged loop), partial vocabulary and
-row tiles, backward chunk counts, K, temperatures and masks are exercised in
-combinations the hand-picked cases do not list.  Every case is small enough
-for the oracle to finish in about a second.
+row tiles, backward chunk counts, K, temperatures, masks and (in a stream of
+its own) KL mixing with the other options are exercised in combinations the
+hand-picked cases do not list.  Every case is small enough for the oracle to
+finish in about a second.
 """
 import numpy as np
 import pytest
@@ -54,6 +55,33 @@ def _draw_full(n):
 TOPK_CASES = _draw_topk(20)
 FULL_CASES = _draw_full(10)
 
+_rng_rev = np.random.default_rng(20261205)  # its own stream: the cases above stay as they were
+
+
+def _draw_rev(n):
+    """Top-K cases with KL mixing (rev_weight) and a random subset of the
+    other options; half of them through the single call."""
+    out = []
+    for i in range(n):
+        dtype = torch.bfloat16 if i % 3 else torch.float32
+        d = int(_rng_rev.choice([128, 256, 96, 200] if dtype == torch.bfloat16 else [64, 96]))
+        V = int(8 * _rng_rev.integers(33, 400))
+        T = int(_rng_rev.integers(1, 500))
+        K = int(min(V, _rng_rev.integers(1, 90)))
+        tau = float(np.round(_rng_rev.uniform(0.5, 2.0), 3))
+        r = float(np.round(_rng_rev.uniform(0.05, 1.0), 3))
+        opts = dict(tau_rows=bool(_rng_rev.integers(0, 2)), partial_mass=bool(_rng_rev.integers(0, 2)))
+        if _rng_rev.integers(0, 2):
+            opts.update(labels=True, ce_weight=float(np.round(_rng_rev.uniform(0.1, 0.9), 3)))
+        mask = str(_rng_rev.choice(["none", "random10"]))
+        chunk = int(_rng_rev.choice([0, 64, 256]))
+        one_call = bool(_rng_rev.integers(0, 2))
+        out.append((i, dtype, T, d, V, K, tau, r, opts, mask, chunk, one_call))
+    return out
+
+
+REV_CASES = _draw_rev(10)
+
 
 def _valid(inp):
     T = inp["H"].shape[0]
@@ -101,3 +129,42 @@ def test_full_sweep(case):
     assert np.all(got["kl"][~v] == 0) and np.all(got["dH"][~v] == 0)
     assert_grad(got["dH"], dH, dtype, "dH")
     assert_grad(got["dW"], dW, dtype, "dWs")
+
+
+@pytest.mark.parametrize("case", REV_CASES, ids=[f"rev{c[0]}" for c in REV_CASES])
+def test_topk_reverse_sweep(case):
+    import chunked_kl_loss_logit_amd as kd
+    i, dtype, T, d, V, K, tau, r, opts, mask, chunk, one_call = case
+    inp = G.make_topk(T, d, V, K, dtype, tau=tau, mask=mask, number=500 + i, g="normal")
+    inp = G.add_topk_options(inp, number=500 + i, **opts)
+    if K > 1 and T > 3:
+        I = inp["I"].clone()
+        I[::3, 1] = I[::3, 0]  # repeated indices in every third row
+        inp["I"] = I
+    say(f"sweep reverse #{i} T={T} d={d} V={V} K={K} tau={tau} r={r} {opts} mask={mask} chunk={chunk} "
+        f"one_call={one_call} {dtype}")
+    dev = lambda x: None if x is None else x.cuda().contiguous()  # noqa: E731
+    H, W, I, A, M, g = (dev(inp[k]) for k in ("H", "W", "I", "A", "mask", "g"))
+    o = {k: dev(inp[k]) for k in ("tau_rows", "teacher_lse", "labels") if k in inp}
+    if "labels" in inp:
+        o["ce_weight"] = inp["ce_weight"]
+    if one_call:
+        kl, lse, _, dH, dW = kd.topk_kl_forward_backward(H, W, I, A, M, tau, g, chunk_rows=chunk, rev_weight=r, **o)
+    else:
+        kl, lse, z = kd.topk_kl_forward(H, W, I, A, M, tau, rev_weight=r, **o)
+        dH, dW = kd.topk_kl_backward(H, W, I, A, M, tau, lse, g, chunk, rev_weight=r, z_topk=z, **o)
+    torch.cuda.synchronize()
+    kw = {k: inp[k] for k in ("tau_rows", "teacher_lse", "labels") if k in inp}
+    if "labels" in inp:
+        kw["ce_weight"] = inp["ce_weight"]
+    want_kl, want_lse, _ = O.topk_loss_forward(inp["H"], inp["W"], inp["I"], inp["A"], inp["mask"], tau,
+                                               rev_weight=r, **kw)
+    wdH, wdW = O.topk_loss_backward(inp["H"], inp["W"], inp["I"], inp["A"], inp["mask"], tau, inp["g"],
+                                    rev_weight=r, **kw)
+    v = _valid(inp)
+    got_kl = kl.cpu().double().numpy()
+    assert_kl(got_kl, want_kl, dtype, v)
+    assert_lse(lse.cpu().double().numpy(), want_lse, dtype, v)
+    assert np.all(got_kl[~v] == 0) and np.all(dH.cpu().double().numpy()[~v] == 0)
+    assert_grad(dH.cpu().double().numpy(), wdH, dtype, "dH")
+    assert_grad(dW.cpu().double().numpy(), wdW, dtype, "dW")
