@@ -180,6 +180,13 @@ kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_i
  *   kl_t  = (1 - ce_weight) KD_t + ce_weight CE_t
  *   dZ_t  = (g_t / tau_t) ((1 - ce_weight)(m_t softmax(s) - scatter_add(I_t, p))
  *                          + ce_weight (softmax(s) - onehot(labels[t])))
+ * Sources: per-token temperature, the adaptive-distillation abstract on the
+ * WASD page (thelatestinai.com/papers/2610.07706); cached probabilities with
+ * their unnormalised partial mass and the support identity above, §3
+ * "Offline distillation"; the language-modelling loss mixed with the
+ * distillation loss, the teacher-strength abstract
+ * (thelatestinai.com/papers/2605.11513), with CE the one-entry case of the
+ * same loss at the same temperature (tau = 1 gives the plain LM loss).
  * KL mixing (rev_weight = r > 0) adds the reverse direction on the cached
  * entries, where both sides are known: with q~ = softmax_k(s[I_tk]) and
  * p^ = softmax_k(A_tk / tau_t), both over the K entries (each entry its own
@@ -188,21 +195,15 @@ kd_status kd_topk_kl_fwd_bwd(const void* H, const void* W, const int32_t* topk_i
  *   KD_t is replaced by (1 - r) KD_t + r RKL_t in kl_t, and dZ_t gains
  *   (g_t / tau_t)(1 - ce_weight) r q~_k (log q~_k - log p^_k - RKL_t)
  *   at column I_tk (scatter-add).
- * q~ is computed from the forward's z_topk: the forward and single calls
- * need their z_topk output, the backward call gets the forward's z_topk in
- * opts.z_topk (KD_ERR_INVALID_ARG if NULL then).  Source: forward and
+ * q~ is computed from the raw logits at the cached entries that the forward
+ * writes to z_topk: with r > 0 the forward and single calls need their
+ * z_topk output, and the backward call gets the forward's z_topk in
+ * opts.z_topk (KD_ERR_INVALID_ARG if NULL).  Source: forward and
  * reverse token-level KL and their mixture, the KL-direction abstract
  * (thelatestinai.com/papers/2606.20005); the restriction to the cached
  * entries is this library's reading, since the teacher is known only there.
  * The vocabulary shard calls reject r > 0 (KD_ERR_UNSUPPORTED): q~ needs the
  * student's logits at all K entries.
- * Sources: per-token temperature, the adaptive-distillation abstract on the
- * WASD page (thelatestinai.com/papers/2610.07706); cached probabilities with
- * their unnormalised partial mass and the support identity above, §3
- * "Offline distillation"; the language-modelling loss mixed with the
- * distillation loss, the teacher-strength abstract
- * (thelatestinai.com/papers/2605.11513), with CE the one-entry case of the
- * same loss at the same temperature (tau = 1 gives the plain LM loss).
  * Only the per-row constants and the weights of the support entries change,
  * so every option keeps the tiles, workspace size and speed of the plain
  * call (KL mixing adds one small per-row pass).  Argument errors: ce_weight
