@@ -239,12 +239,14 @@ struct TopkPlan {
   int ntiles;
   int64_t Cf;
   size_t o_pair, o_perm, o_ent, o_rowc, o_rows, o_count, o_bad, o_part, o_hp_f;
+  size_t o_zpair;  // the forward's logits at the sorted entries, when z_topk is asked for
   ChunkPlan ch;
-  size_t fwd_total, total;  // bytes the forward call needs; bytes both calls need
+  // bytes the forward call needs without and with z_topk; bytes both calls need
+  size_t fwd_total, fwd_total_z, total;
   // single-call forward + backward: per-chunk partials, the chunk's fp32
   // logits and the backward chunk buffers all live at once
   ChunkPlan ch_f;
-  size_t o_part_c, o_z, fused_total;
+  size_t o_part_c, o_z, o_zpair_f, fused_total;
 };
 
 TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t chunk_rows) {
@@ -263,13 +265,16 @@ TopkPlan plan_topk(int64_t T, int64_t d, int64_t V, int64_t K, int elem, int64_t
   Carver fw = cv, bw = cv;  // forward partials and backward chunk buffers overlap
   p.o_part = fw.take((size_t)max_splits(p.ntiles) * p.Cf * 16);
   p.o_hp_f = fw.take(panel_bytes(p.Cf, d * elem));
-  p.ch = plan_chunk(T, d, V, elem, chunk_rows, bw);
   p.fwd_total = fw.off;
+  p.o_zpair = fw.take((size_t)T * (K + 1) * 4);  // last, so the forward without z_topk needs no room for it
+  p.fwd_total_z = fw.off;
+  p.ch = plan_chunk(T, d, V, elem, chunk_rows, bw);
   p.total = std::max(fw.off, bw.off);
   Carver fu = cv;
   p.o_part_c = fu.take((size_t)max_splits(p.ntiles) * chunk_of(T, V, elem, chunk_rows) * 16);
   p.ch_f = plan_chunk(T, d, V, elem, chunk_rows, fu);
   p.o_z = fu.take((size_t)p.ch.C * p.ch.ldz * 4);
+  p.o_zpair_f = fu.take((size_t)T * (K + 1) * 4);
   p.fused_total = fu.off;
   return p;
 }
@@ -516,9 +521,12 @@ kd_status finish_index_check(const TopkOpts& op, hipStream_t st) {
   return KD_OK;
 }
 
-kd::TopkRowData row_data(void* ws, const TopkPlan& p) {
+// The per-row data of the prep; with a zpair offset, also the array in
+// which the forward's gather leaves the logits of the sorted entries for
+// z_topk.
+kd::TopkRowData row_data(void* ws, const TopkPlan& p, const size_t* o_zpair = nullptr) {
   return kd::TopkRowData{at<int2>(ws, p.o_pair), at<uint16_t>(ws, p.o_perm), at<float>(ws, p.o_ent),
-                         at<float4>(ws, p.o_rowc)};
+                         at<float4>(ws, p.o_rowc), o_zpair ? at<float>(ws, *o_zpair) : nullptr};
 }
 
 // A vocabulary shard of the head: W holds its columns [v0, v0 + V).  The
@@ -607,11 +615,11 @@ kd_status topk_fwd(const void* H, const void* W, const int32_t* topk_idx, const 
   if (op.prep.rev > 0.f) KD_TRY(need(z_topk, "z_topk (rev_weight > 0 reads it)"));
   const int elem = elem_of(dt);
   const TopkPlan p = plan_topk(T, d, V, K, elem, 0);
-  KD_TRY(check_workspace(workspace, workspace_bytes, p.fwd_total));
+  KD_TRY(check_workspace(workspace, workspace_bytes, z_topk ? p.fwd_total_z : p.fwd_total));
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
-  const kd::TopkRowData rd = row_data(workspace, p);
+  const kd::TopkRowData rd = row_data(workspace, p, z_topk ? &p.o_zpair : nullptr);
   float* part = at<float>(workspace, p.o_part);
 
   KD_LAUNCH("compact", st, kd::launch_compact(mask, T, c, st));
@@ -642,6 +650,8 @@ kd_status topk_fwd(const void* H, const void* W, const int32_t* topk_idx, const 
     a.nrb = sh.nrb;
     a.S = sh.S;
     KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
+    if (z_topk)
+      KD_LAUNCH("topk_zpermute", st, kd::launch_topk_zpermute(rd, c, T, op.KE, K, z_topk, c0, c0 + p.Cf, st));
     if (shard)
       KD_LAUNCH("topk_shard_record", st,
                 kd::launch_topk_shard_record(part, sh.S, p.Cf, c, mask, rd, T, reinterpret_cast<float4*>(shard->rec),
@@ -712,7 +722,8 @@ kd_status kd_topk_kl_fwd_noalloc(const void* H, const void* W, const int32_t* to
   KD_TRY(check_common(T, d, V, dt, tau));
   KD_TRY(check_k(T, K, V));
   if (T == 0) return KD_OK;
-  const size_t want = plan_topk(T, d, V, K, elem_of(dt), 0).fwd_total;
+  const TopkPlan plan = plan_topk(T, d, V, K, elem_of(dt), 0);
+  const size_t want = z_topk ? plan.fwd_total_z : plan.fwd_total;
   if (want > KD_NOALLOC_SCRATCH_BYTES)
     return fail(KD_ERR_UNSUPPORTED, "this forward needs " + std::to_string(want) +
                                         " bytes of scratch, above KD_NOALLOC_SCRATCH_BYTES (" +
@@ -1380,7 +1391,7 @@ kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* top
   KD_TRY(check_workspace(workspace, workspace_bytes, p.fused_total));
 
   kd::Compact c{at<int32_t>(workspace, p.o_rows), at<int32_t>(workspace, p.o_count)};
-  const kd::TopkRowData rd = row_data(workspace, p);
+  const kd::TopkRowData rd = row_data(workspace, p, z_topk ? &p.o_zpair_f : nullptr);
   float* part = at<float>(workspace, p.o_part_c);
   float* z = at<float>(workspace, p.o_z);
   const ChunkPlan& ch = p.ch_f;
@@ -1423,6 +1434,8 @@ kd_status kd_topk_kl_fwd_bwd_ex(const void* H, const void* W, const int32_t* top
     a.ntiles = p.ntiles;
     a.group = kRasterGroup;
     KD_LAUNCH("topk_fwd_tile", st, kd::launch_topk_fwd(elem, a, st));
+    if (z_topk)
+      KD_LAUNCH("topk_zpermute", st, kd::launch_topk_zpermute(rd, c, T, op.KE, K, z_topk, c0, c0 + ch.C, st));
     KD_LAUNCH("topk_combine", st,
               kd::launch_topk_combine(part, sh.S, ch.C, c, mask, rd, T, kl, lse, c0, c0 + ch.C, k == 0, st));
     if (op.prep.rev > 0.f)  // the reverse part: into kl, and into the weights the dZ pass scatters

@@ -22,6 +22,7 @@ struct TopkRowData {
   uint16_t* perm;   // original position k of each sorted entry (K: the label)
   float* ent;       // [T] sum_k w_k log p_k (the teacher-entropy term)
   float4* rowc;     // [T] (log2(e) / tau_t, 1 / tau_t, mass, log2(mass)) of row t
+  float* zpair;     // nullable: the forward's logit at each sorted entry (zeroed by the prep), for z_topk
 };
 
 // Optional parts of the top-K loss, as the prep kernel applies them.
@@ -59,6 +60,11 @@ inline int ew_ranges(int elem, int64_t V) {
 hipError_t launch_compact(const uint8_t* mask, int64_t T, Compact c, hipStream_t st);
 hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8_t* mask, int64_t T, int64_t K,
                             int64_t KE, const TopkPrepOpts& o, TopkRowData rd, float* z_topk, hipStream_t st);
+// z_topk of compacted rows [jb, je) from the logits the forward gathered at
+// the sorted entries (rd.zpair): entry i of row t goes to z_topk[t][perm[i]]
+// (the label entry, perm == Kz, nowhere).
+hipError_t launch_topk_zpermute(const TopkRowData& rd, Compact c, int64_t T, int64_t KE, int64_t Kz, float* z_topk,
+                                int64_t jb, int64_t je, hipStream_t st);
 // KL mixing on the cached entries, for compacted rows [jb, je): each row's
 // reverse KL between the student and the teacher restricted to the K entries
 // and renormalised there, from z_topk [T,K] and the cached logits.  kl

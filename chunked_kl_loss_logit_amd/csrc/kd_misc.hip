@@ -201,6 +201,7 @@ __global__ __launch_bounds__(NT) void topk_prep_kernel(const float* logits, cons
     const float w = k < (uint32_t)K ? wk * p[k] : o.beta;
     rd.pair[pbase + j] = make_int2((int32_t)((uint32_t)(kv >> 32) ^ 0x80000000u), __float_as_int(w));
     rd.perm[pbase + j] = (uint16_t)k;
+    if (rd.zpair) rd.zpair[pbase + j] = 0.f;  // an entry no tile matches reads as 0
   }
   if (threadIdx.x == 0) {
     rd.ent[t] = ent;
@@ -225,6 +226,29 @@ hipError_t launch_topk_prep(const float* logits, const int32_t* idx, const uint8
   else
     hipLaunchKernelGGL(topk_prep_kernel<256>, grid, dim3(256), shm, st, logits, idx, mask, (int)K, (int)KE, KP, o,
                        rd, z_topk);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ z_topk from the sorted entries
+// One block of 64 threads per compacted row.
+__global__ __launch_bounds__(64) void topk_zpermute_kernel(TopkRowData rd, Compact c, int KE, int Kz, float* z_topk,
+                                                           long jb, long je) {
+  const long j = jb + blockIdx.x;
+  if (j >= je || j >= (long)*c.count) return;
+  const long t = c.rows[j];
+  const long pb = t * KE;
+  for (int i = threadIdx.x; i < KE; i += 64) {
+    const int k = rd.perm[pb + i];
+    if (k < Kz) z_topk[t * Kz + k] = rd.zpair[pb + i];
+  }
+}
+
+hipError_t launch_topk_zpermute(const TopkRowData& rd, Compact c, int64_t T, int64_t KE, int64_t Kz, float* z_topk,
+                                int64_t jb, int64_t je, hipStream_t st) {
+  if (je > T) je = T;
+  if (je <= jb) return hipSuccess;
+  hipLaunchKernelGGL(topk_zpermute_kernel, dim3((unsigned)(je - jb)), dim3(64), 0, st, rd, c, (int)KE, (int)Kz,
+                     z_topk, (long)jb, (long)je);
   return hipGetLastError();
 }
 

@@ -104,17 +104,17 @@ __device__ inline void block_range(int cb, int clo, int chi, int& lo, int& hi) {
   hi = max(0, min(32, chi - cb));
 }
 
-// kZ: the caller asked for z_topk.  Without it the gather keeps no output
-// state, which leaves the epilogue enough registers that nothing spills (a
-// spilled cursor word reloaded in the hit path made every round wait for all
-// vector memory, the next tile's operand loads and earlier stores included).
+// kZ: the caller asked for z_topk.  A hit then stores its logit at the
+// entry's sorted position (rd.zpair, one address from the cursor), and a
+// small kernel puts them in z_topk's order afterwards: mapping to the
+// original position in the hit path (the permutation load and the row's
+// offset) cost registers, and a spilled cursor word reloaded there made
+// every round wait for all vector memory, the next tile's operand loads and
+// earlier stores included.
 template <bool kZ>
 struct FwdRow {
   Cursor cur;
-  const uint16_t* perm;  // uniform bases, indexed by pair position
-  float* ztk;            // z_topk, indexed by row_k + original position (kZ)
-  long row_k;            // t * Kz
-  int kz;                // cached entries per row (a label entry has perm == kz)
+  float* zp;  // rd.zpair, indexed by pair position (kZ)
   float m2, l, x, c2;
   bool rv;
 
@@ -150,10 +150,7 @@ struct FwdRow {
     cur.take_below(cb + hi, [&](int v, float pv, int c) {
       const float z = st_row(st, r)[st_pos(r, v - cb)];
       x = fmaf(pv, z, x);
-      if constexpr (kZ) {
-        const int k = perm[c];
-        if (k < kz) ztk[row_k + k] = z;
-      }
+      if constexpr (kZ) zp[c] = z;
     });
   }
 };
@@ -257,10 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_fwd_kernel(TopkFwdArgs a) {
   R.cur.end = (int)(t * a.K + (R.rv ? a.K : 0));
   R.cur.c = lower_bound(a.rd.pair, (int)(t * a.K), R.cur.end, (long)tb * kBN);
   R.cur.refill();
-  R.perm = a.rd.perm;
-  R.ztk = a.z_topk;
-  R.row_k = t * a.Kz;
-  R.kz = (int)a.Kz;
+  R.zp = a.rd.zpair;
   R.m2 = -INFINITY;
   R.l = 0.f;
   R.x = 0.f;
@@ -608,10 +602,7 @@ __device__ inline void fwd_row_t(Val&& val, float c2, float* st, TCursor& cur, c
 #pragma unroll
         for (int i = 0; i < 16; ++i) z = i == at ? val(nb, i) : z;
         x = fmaf(p, z, x);
-        if constexpr (kZ) {
-          const int k = a.rd.perm[c];
-          if (k < a.Kz) a.z_topk[(long)(c / a.K) * a.Kz + k] = z;
-        }
+        if constexpr (kZ) a.rd.zpair[c] = z;
       }
     });
   }
@@ -875,6 +866,7 @@ static void launch_topk_fwd_z(int elem, const TopkFwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_topk_fwd(int elem, const TopkFwdArgs& a, hipStream_t st) {
+  if (a.z_topk && !a.rd.zpair) return hipErrorInvalidValue;  // the gather writes the sorted entries' logits there
   if (a.z_topk)
     launch_topk_fwd_z<true>(elem, a, st);
   else

@@ -156,7 +156,8 @@ kd_status kd_topk_kl_bwd(const void* H, const void* W, const int32_t* topk_idx,
  * them instead of from a second projection.  That trades the pages'
  * recompute (§3 "Fused chunked KL": one extra output projection per chunk,
  * like output-head gradient checkpointing) for C * roundup(V, 256) * 4 more
- * workspace bytes, where C is the chunk size.  kd_topk_kl_fwd_bwd_workspace_size
+ * workspace bytes, where C is the chunk size, plus T * (K + 1) * 4 for the
+ * z_topk gather.  kd_topk_kl_fwd_bwd_workspace_size
  * gives the size; T = 0 sets dW to zero and touches nothing else. */
 kd_status kd_topk_kl_fwd_bwd_workspace_size(int64_t T, int64_t d, int64_t V, int64_t K, kd_dtype dt,
                                             int64_t chunk_rows, size_t* bytes);
@@ -454,7 +455,8 @@ kd_status kd_full_kl_bwd_shard(const void* H, const void* Ws, const void* Ht, co
  * that device current; `stream` must belong to the current device.
  * A shape whose forward needs more scratch than that returns
  * KD_ERR_UNSUPPORTED before anything is enqueued (at d = 3072,
- * V = 128256, K = 64 in bf16, about 37,000 rows fit); the other argument
+ * V = 128256, K = 64 in bf16, 37,823 rows fit, or 27,293 with z_topk,
+ * whose gather needs 4 (K + 1) bytes more per row); the other argument
  * errors are kd_topk_kl_fwd's.  Every call on one GPU shares its array:
  * calls that overlap on one GPU (other streams, other host threads) race
  * and must be ordered by the caller.  Nothing in the array needs to start

@@ -170,13 +170,15 @@ def test_topk_fwd_bwd_rejects(L, kw, code):
 
 def test_fwd_bwd_workspace_adds_one_fp32_logit_chunk(L):
     # same per-row buffers and backward chunk buffers as the two-call path, plus
-    # per-chunk forward partials and the chunk's fp32 logits [C, roundup(V, 256)]
+    # per-chunk forward partials, the chunk's fp32 logits [C, roundup(V, 256)]
+    # and the gathered logits at the sorted entries [T, K + 1] (for z_topk)
     for T, chunk in ((4096, 0), (10000, 1024), (300, 0)):
         out = ctypes.c_size_t(0)
         assert L.kd_topk_kl_fwd_bwd_workspace_size(T, 3072, 128256, 64, kdl.KD_BF16, chunk, ctypes.byref(out)) == 0
         C = min(4096 if chunk == 0 else chunk, (T + 255) // 256 * 256)
         two_call = ws_topk(T, chunk=chunk)[1]
-        assert two_call + C * 128256 * 4 <= out.value <= two_call + C * 128256 * 4 + 256 * C * 16 + (1 << 20)
+        zsort = T * 65 * 4
+        assert two_call + C * 128256 * 4 <= out.value <= two_call + C * 128256 * 4 + 256 * C * 16 + zsort + (1 << 20)
     out = ctypes.c_size_t(0)
     assert L.kd_topk_kl_fwd_bwd_workspace_size(0, 3072, 128256, 64, kdl.KD_BF16, 0, ctypes.byref(out)) == 0
     assert out.value == 0
