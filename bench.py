@@ -59,6 +59,10 @@ def parse():
                     help="only run a plain device copy of BYTES bytes 4 times (calibrates HBM byte counters)")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only time the vendor GEMM (torch.matmul) on the head's three contraction shapes")
+    ap.add_argument("--operand-probe", choices=("seeded", "zero"), default=None,
+                    help="only time the headline's two calls on its seeded operands or on all-zero H and W "
+                         "(same shapes and instructions): a diagnostic of how the clock depends on the data, "
+                         "not the metric")
     return ap.parse_args()
 
 
@@ -503,6 +507,45 @@ def vendor_gemm(steps: int, warmup: int):
               flush=True)
 
 
+def operand_probe(kind: str, steps: int, warmup: int):
+    """The headline workload's forward and backward calls on its seeded
+    operands, or with H and W all zero.  The kernels run the same
+    instructions either way; under matrix load the chip's clock follows the
+    power its operands draw, so the two show how much of the distance to the
+    published peak is the clock rather than the kernels' share of busy
+    cycles (read with rocprofv3 counters).  Prints one diagnostic line."""
+    import torch
+    import chunked_kl_loss_logit_amd as kd
+    import kdinputs as G
+    p = G.PRESETS["head_topk_t4096"]
+    inp = G.make_preset(p, g="mean")
+    dev = torch.device("cuda:0")
+    H, W, I, A, g = (inp[k].to(dev) for k in ("H", "W", "I", "A", "g"))
+    del inp
+    if kind == "zero":
+        H.zero_()
+        W.zero_()
+    T, d, V, K = p.T, p.d, p.V, p.K
+    kl, lse = torch.empty(T, device=dev), torch.empty(T, device=dev)
+    dH, dW = torch.empty_like(H), torch.empty(d, V, device=dev)
+    ws = torch.empty(kd.kd_topk_kl_workspace_size(T, d, V, K, p.dtype, 0), dtype=torch.uint8, device=dev)
+
+    def step():
+        kd.kd_topk_kl_fwd(H, W, I, A, None, p.tau, kl, lse, None, ws)
+        kd.kd_topk_kl_bwd(H, W, I, A, None, p.tau, lse, g, dH, dW, 0, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    print(json.dumps({"operand_probe": kind, "workload": p.name, "steps": steps, "ms_per_step": round(ms, 4),
+                      "note": "diagnostic of the clock's dependence on the operands; not the metric"}), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -513,6 +556,9 @@ def main():
         return
     if a.vendor_gemm:
         vendor_gemm(a.steps, a.warmup)
+        return
+    if a.operand_probe:
+        operand_probe(a.operand_probe, a.steps, a.warmup)
         return
 
     import kdinputs as G
